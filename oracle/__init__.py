@@ -1,0 +1,178 @@
+"""Float64 CPU oracle for the row-softmax family (ctypes wrapper over xr_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package. The product path (``cross_entropy_reductions_amd``) never imports it
+and shares no code with it.
+
+What each function computes, and the passage it follows:
+
+* ``softmax_fwd`` -- safe softmax of each row (page "python sum function
+  examples", Triton kernels ``softmax_kernel`` / ``_softmax``).
+* ``softmax_bwd`` -- ``dx = y * (dy - sum(y * dy))`` per row (same page,
+  kernel ``_backward``, block-sparse scale taken as 1).
+* ``xent_count``, ``xent_rows``, ``mean``, ``xent`` -- Liger-Kernel
+  ``cross_entropy.py``: ``liger_cross_entropy_kernel`` steps 1-6 (ignore
+  early-out, loss ``m + log d - x_y``, gradient ``(softmax - onehot)/n``) and
+  ``LigerCrossEntropyFunction.forward`` (``n`` counts non-ignored targets, mean
+  loss ``sum(loss)/n``).
+
+Inputs are host numpy arrays holding exactly the bytes the GPU receives:
+``uint16`` arrays carry bf16 bit patterns, ``float32`` arrays carry fp32.
+A 2-D array of shape ``(M, ld)`` is read as M rows of row stride ``ld``, of
+which the first ``N`` (or ``V``) columns are the row; the rest is padding that
+is never read. Outputs are float64.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` (invariants,
+closed forms, finite differences, independent library routines) and the pins
+are shown to catch planted mistakes by ``tests/test_oracle_mutants.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "xr_oracle.c")
+LIBRARY = os.path.join(_HERE, "libxr_oracle.so")
+
+F32, BF16 = 0, 1
+
+_c_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def compile_library(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the oracle with gcc (C99, OpenMP, -O2, IEEE semantics kept)."""
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", *extra_flags,
+           source, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+class Oracle:
+    """One loaded copy of the oracle library (tests may load planted-mistake builds)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            compile_library(output=path)
+        lib = ctypes.CDLL(path)
+        lib.xro_softmax_fwd.argtypes = [_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _p]
+        lib.xro_softmax_fwd.restype = None
+        lib.xro_softmax_bwd.argtypes = [_p, _c_i64, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _p]
+        lib.xro_softmax_bwd.restype = None
+        lib.xro_xent_count.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p]
+        lib.xro_xent_count.restype = None
+        lib.xro_xent_rows.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                      _c_i64, _p, _p]
+        lib.xro_xent_rows.restype = None
+        lib.xro_mean.argtypes = [_p, _c_i64, _c_i64]
+        lib.xro_mean.restype = ctypes.c_double
+        lib.xro_num_threads.argtypes = []
+        lib.xro_num_threads.restype = ctypes.c_int
+        lib.xro_set_num_threads.argtypes = [ctypes.c_int]
+        lib.xro_set_num_threads.restype = None
+        self.lib = lib
+        self.path = path
+
+    # -- helpers -------------------------------------------------------------
+    @staticmethod
+    def _matrix(a: np.ndarray):
+        """(pointer, row stride, rows, dtype code) of a 2-D uint16/float32 array."""
+        if a.ndim != 2:
+            raise ValueError("expected a 2-D array")
+        if a.dtype == np.uint16:
+            code = BF16
+        elif a.dtype == np.float32:
+            code = F32
+        else:
+            raise TypeError(f"unsupported dtype {a.dtype}: uint16 (bf16 bits) or float32")
+        if a.strides[1] != a.itemsize or a.strides[0] % a.itemsize:
+            raise ValueError("rows must be unit-stride in their last dimension")
+        ld = a.strides[0] // a.itemsize
+        return a.ctypes.data, ld, a.shape[0], code
+
+    def num_threads(self) -> int:
+        return int(self.lib.xro_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.xro_set_num_threads(int(n))
+
+    # -- operations ----------------------------------------------------------
+    def softmax_fwd(self, x: np.ndarray, n_cols: int | None = None) -> np.ndarray:
+        ptr, ld, M, code = self._matrix(x)
+        N = x.shape[1] if n_cols is None else int(n_cols)
+        if not 0 < N <= x.shape[1]:
+            raise ValueError("n_cols out of range")
+        y = np.full((M, N), np.nan, dtype=np.float64)
+        self.lib.xro_softmax_fwd(ptr, ld, M, N, code, y.ctypes.data)
+        return y
+
+    def softmax_bwd(self, y: np.ndarray, dy: np.ndarray, n_cols: int | None = None) -> np.ndarray:
+        py, ldy, M, code = self._matrix(y)
+        pd, ldd, M2, code2 = self._matrix(dy)
+        if M != M2 or code != code2:
+            raise ValueError("y and dy must have the same rows and dtype")
+        N = y.shape[1] if n_cols is None else int(n_cols)
+        if not 0 < N <= min(y.shape[1], dy.shape[1]):
+            raise ValueError("n_cols out of range")
+        dx = np.full((M, N), np.nan, dtype=np.float64)
+        self.lib.xro_softmax_bwd(py, ldy, pd, ldd, M, N, code, dx.ctypes.data)
+        return dx
+
+    def xent_count(self, target: np.ndarray, V: int, ignore_index: int = -100):
+        t = np.ascontiguousarray(target, dtype=np.int64)
+        counts = np.zeros(2, dtype=np.int64)
+        self.lib.xro_xent_count(t.ctypes.data, t.shape[0], int(V), int(ignore_index),
+                                counts.ctypes.data)
+        return int(counts[0]), int(counts[1])
+
+    def xent_rows(self, logits: np.ndarray, target: np.ndarray, V: int, n: int,
+                  ignore_index: int = -100, rows=None, want_grad: bool = True):
+        """(grad [len(rows), V] or None, loss [len(rows)]) for the given rows."""
+        ptr, ld, M, code = self._matrix(logits)
+        if not 0 < V <= logits.shape[1]:
+            raise ValueError("V out of range")
+        t = np.ascontiguousarray(target, dtype=np.int64)
+        if t.shape[0] != M:
+            raise ValueError("target length must equal the number of rows")
+        if rows is None:
+            ridx, nr = None, M
+        else:
+            ridx = np.ascontiguousarray(rows, dtype=np.int64)
+            if ridx.size and (ridx.min() < 0 or ridx.max() >= M):
+                raise ValueError("row index out of range")
+            nr = ridx.shape[0]
+        # Outputs start as NaN, so an element the library never writes cannot pass as a value.
+        grad = np.full((nr, V), np.nan, dtype=np.float64) if want_grad else None
+        loss = np.full(nr, np.nan, dtype=np.float64)
+        self.lib.xro_xent_rows(ptr, ld, t.ctypes.data, None if ridx is None else ridx.ctypes.data,
+                               nr, int(V), int(ignore_index), code, int(n),
+                               None if grad is None else grad.ctypes.data, loss.ctypes.data)
+        return grad, loss
+
+    def mean(self, loss: np.ndarray, n: int) -> float:
+        lo = np.ascontiguousarray(loss, dtype=np.float64)
+        return float(self.lib.xro_mean(lo.ctypes.data, lo.shape[0], int(n)))
+
+    def xent(self, logits: np.ndarray, target: np.ndarray, V: int, ignore_index: int = -100,
+             want_grad: bool = True):
+        """(grad or None, row losses, mean loss, (n_non_ignore, n_bad))."""
+        n, bad = self.xent_count(target, V, ignore_index)
+        grad, loss = self.xent_rows(logits, target, V, n, ignore_index, None, want_grad)
+        return grad, loss, self.mean(loss, n), (n, bad)
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from xr_oracle.c (compiled on first use if missing)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,193 @@
+/*
+ * xr_oracle.c -- plain float64 CPU oracle for the row-softmax family.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The product path (the
+ * HIP library under cross_entropy_reductions_amd/) never links, imports or
+ * calls it, and this file shares no source with it.
+ *
+ * Every routine is the plain definition, computed in double precision, one
+ * row after another within a thread, with no blocking, fusion or reordering
+ * beyond what the definition states:
+ *
+ *   softmax forward   -- the "safe softmax" of the Triton fused-softmax
+ *                        examples on the page "python sum function examples"
+ *                        (kernels `softmax_kernel` and `_softmax`): subtract
+ *                        the row maximum, exponentiate, divide by the row sum.
+ *   softmax backward  -- the fused softmax backward of the `_backward` kernel
+ *                        on the same page, with its block-sparse scale taken
+ *                        as 1: dx_j = y_j * (dy_j - sum_k y_k * dy_k).
+ *   cross-entropy     -- Liger-Kernel `cross_entropy.py`,
+ *                        `liger_cross_entropy_kernel` steps 1-6 and
+ *                        `LigerCrossEntropyFunction.forward`: per-row loss
+ *                        m + log d - x_y, gradient (softmax - onehot)/n where
+ *                        n counts the targets that differ from ignore_index,
+ *                        zero rows (gradient and loss) for ignored targets,
+ *                        and the mean of the row losses over n.
+ *
+ * The oracle deliberately uses the two-pass safe form (max first, then the
+ * sum with that max), not the online running max/sum of the GPU path; both
+ * reach the same value up to rounding.
+ *
+ * Readings of points the pages leave open (each one is stated where it acts):
+ *   - bf16 inputs are decoded exactly: bits << 16 reinterpreted as a float.
+ *   - a target outside [0, V) that is not ignore_index is counted as a bad
+ *     target; its row gets a zero gradient and a zero loss (Liger reads such
+ *     a target unchecked).
+ *   - n counts every target that is not ignore_index (bad targets included),
+ *     exactly as `(target != ignore_index).sum()` does on the Liger page.
+ *   - n == 0 gives mean = 0/0 = NaN.
+ *   - ignore_index is compared before any range check, so an ignore_index
+ *     that lies inside [0, V) still ignores its rows.
+ *
+ * Parallelism: rows are independent, so rows are spread over OpenMP threads.
+ * Within a row every sum runs left to right in double. The mean is a serial
+ * left-to-right sum in row order.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { XRO_F32 = 0, XRO_BF16 = 1 };
+
+/* Element idx (in elements from base) of a bf16 or fp32 buffer, as double. */
+static double load_elem(const void* base, int64_t idx, int dtype) {
+  if (dtype == XRO_BF16) {
+    uint16_t h;
+    memcpy(&h, (const char*)base + 2 * idx, 2);
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+  } else {
+    float f;
+    memcpy(&f, (const char*)base + 4 * idx, 4);
+    return (double)f;
+  }
+}
+
+int xro_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void xro_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* Safe softmax of one row: y[j] = exp(x_j - max) / sum_k exp(x_k - max). */
+static void softmax_row(const void* x, int64_t row_off, int64_t N, int dtype, double* y) {
+  double m = -INFINITY;
+  for (int64_t j = 0; j < N; ++j) {
+    double v = load_elem(x, row_off + j, dtype);
+    if (v > m) m = v;
+  }
+  double d = 0.0;
+  for (int64_t j = 0; j < N; ++j) {
+    double e = exp(load_elem(x, row_off + j, dtype) - m);
+    y[j] = e;
+    d += e;
+  }
+  for (int64_t j = 0; j < N; ++j) y[j] = y[j] / d;
+}
+
+/* y[M][N] (contiguous doubles) = softmax over each row of x (row stride ld_x). */
+void xro_softmax_fwd(const void* x, int64_t ld_x, int64_t M, int64_t N, int dtype, double* y) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) softmax_row(x, i * ld_x, N, dtype, y + i * N);
+}
+
+/* dx[M][N] = y * (dy - sum_k y_k dy_k) per row; y and dy are read in dtype. */
+void xro_softmax_bwd(const void* y, int64_t ld_y, const void* dy, int64_t ld_dy, int64_t M,
+                     int64_t N, int dtype, double* dx) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) {
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+      s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_dy + j, dtype);
+    for (int64_t j = 0; j < N; ++j)
+      dx[i * N + j] = load_elem(y, i * ld_y + j, dtype) * (load_elem(dy, i * ld_dy + j, dtype) - s);
+  }
+}
+
+/* counts[0] = #{i : t_i != ignore_index}; counts[1] = those among them outside [0, V). */
+void xro_xent_count(const int64_t* target, int64_t M, int64_t V, int64_t ignore_index,
+                    int64_t* counts) {
+  int64_t n = 0, bad = 0;
+  for (int64_t i = 0; i < M; ++i) {
+    if (target[i] == ignore_index) continue;
+    ++n;
+    if (target[i] < 0 || target[i] >= V) ++bad;
+  }
+  counts[0] = n;
+  counts[1] = bad;
+}
+
+/*
+ * Cross-entropy loss and gradient for a list of rows.
+ *   rows     : row indices into logits/target, or NULL for rows 0..nrows-1
+ *   n        : the batch's non-ignored count (from xro_xent_count)
+ *   grad     : [nrows][V] contiguous doubles, or NULL to skip the gradient
+ *   loss     : [nrows] doubles
+ */
+void xro_xent_rows(const void* logits, int64_t ld, const int64_t* target, const int64_t* rows,
+                   int64_t nrows, int64_t V, int64_t ignore_index, int dtype, int64_t n,
+                   double* grad, double* loss) {
+  int64_t r;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (r = 0; r < nrows; ++r) {
+    int64_t i = rows ? rows[r] : r;
+    int64_t t = target[i];
+    double* g = grad ? grad + r * V : NULL;
+    if (t == ignore_index || t < 0 || t >= V) {
+      loss[r] = 0.0;
+      if (g)
+        for (int64_t j = 0; j < V; ++j) g[j] = 0.0;
+      continue;
+    }
+    int64_t off = i * ld;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < V; ++j) {
+      double v = load_elem(logits, off + j, dtype);
+      if (v > m) m = v;
+    }
+    double d = 0.0;
+    for (int64_t j = 0; j < V; ++j) d += exp(load_elem(logits, off + j, dtype) - m);
+    double xt = load_elem(logits, off + t, dtype);
+    loss[r] = m + log(d) - xt;
+    if (g) {
+      for (int64_t j = 0; j < V; ++j) {
+        double p = exp(load_elem(logits, off + j, dtype) - m) / d;
+        g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;
+      }
+    }
+  }
+}
+
+/* mean = (sum_i loss_i) / n, summed left to right in row order; n == 0 gives NaN. */
+double xro_mean(const double* loss, int64_t M, int64_t n) {
+  double s = 0.0;
+  for (int64_t i = 0; i < M; ++i) s += loss[i];
+  return s / (double)n;
+}
+
+/* The whole fused cross-entropy on M rows; grad may be NULL. */
+double xro_xent(const void* logits, int64_t ld, const int64_t* target, int64_t M, int64_t V,
+                int64_t ignore_index, int dtype, double* grad, double* loss, int64_t* counts) {
+  xro_xent_count(target, M, V, ignore_index, counts);
+  xro_xent_rows(logits, ld, target, NULL, M, V, ignore_index, dtype, counts[0], grad, loss);
+  return xro_mean(loss, M, counts[0]);
+}

@@ -1,0 +1,322 @@
+"""Pins for the float64 oracle: checks against facts the oracle cannot produce by itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises ``AssertionError``
+when the oracle disagrees with the fact it checks. The facts are
+
+* invariants of the definitions (rows sum to 1, gradients sum to 0, shift
+  invariance, exact zeros for ignored rows and -inf logits);
+* closed forms (uniform rows give 1/N and loss log V, two columns give the
+  logistic function, hand-worked examples in ``golden/worked_examples.json``);
+* central finite differences of the oracle's own forward quantities;
+* independent library routines evaluated in float64 (``torch.softmax``,
+  ``torch.nn.functional.cross_entropy`` and autograd, ``scipy.special``).
+
+``tests/test_oracle_pins.py`` runs every pin against the real oracle;
+``tests/test_oracle_mutants.py`` builds copies of the oracle with planted
+mistakes and requires each copy to fail at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "worked_examples.json")
+_MATH = {"log": math.log, "exp": math.exp, "inf": math.inf, "__builtins__": {}}
+
+
+def closed_form(expr) -> float:
+    """Evaluate a closed-form expression such as "(1/4-1)/2" or "log(1+exp(2))"."""
+    if isinstance(expr, (int, float)):
+        return float(expr)
+    return float(eval(str(expr), dict(_MATH)))  # noqa: S307 - fixtures are repository text
+
+
+def as_input(rows, dtype: str) -> np.ndarray:
+    """Fixture rows (numbers or "-inf") as the bytes the library receives."""
+    vals = np.array([[closed_form(v) for v in r] for r in rows], dtype=np.float32)
+    return synth.bf16_bits_from_f32(vals) if dtype == "bf16" else vals
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bits or float32 values, widened exactly to float64."""
+    if a.dtype == np.uint16:
+        return synth.f32_from_bf16_bits(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _grid_rows(seed: int, M: int, N: int, step: float, lo: float, hi: float) -> np.ndarray:
+    """Rows of values on a coarse grid (exact in bf16 and fp32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = rng.integers(int(lo / step), int(hi / step) + 1, size=(M, N))
+    return (k * step).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- softmax forward
+def pin_softmax_rows_sum_to_one(o):
+    for seed, (M, N, dtype, scale) in enumerate([(7, 1, "f32", 1.0), (9, 2, "bf16", 3.0),
+                                                 (16, 7, "f32", 8.0), (8, 1000, "f32", 3.0),
+                                                 (4, 4096, "bf16", 1.0)]):
+        x = synth.random_rows(100 + seed, M, N, dtype=dtype, scale=scale)
+        y = o.softmax_fwd(x)
+        assert np.all(y >= 0), "softmax output must be non-negative"
+        assert np.max(np.abs(y.sum(axis=1) - 1.0)) <= 1e-12, "softmax rows must sum to 1"
+
+
+def pin_softmax_shift_invariance(o):
+    base = _grid_rows(11, 6, 33, 1.0 / 8, -4.0, 4.0)
+    for dtype, shifts in (("bf16", (-2.0, 0.5, 4.0)), ("f32", (-48.0, 0.5, 1024.0))):
+        conv = synth.bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a)
+        y0 = o.softmax_fwd(conv(base))
+        for c in shifts:
+            shifted = (base + np.float32(c)).astype(np.float32)
+            assert np.array_equal(shifted - np.float32(c), base), "shift must be exact"
+            y1 = o.softmax_fwd(conv(shifted))
+            assert np.all(np.isfinite(y1)), f"shift {c} must not overflow"
+            assert np.max(np.abs(y1 - y0) / y0) <= 1e-12, f"softmax not invariant to shift {c}"
+
+
+def pin_softmax_uniform_row(o):
+    for N in (1, 3, 1000, 4096):
+        y = o.softmax_fwd(np.full((2, N), 7.25, dtype=np.float32))
+        assert np.max(np.abs(y - 1.0 / N)) <= 1e-15 / N * 4, "a uniform row gives 1/N"
+
+
+def pin_softmax_two_columns_logistic(o):
+    x = _grid_rows(12, 50, 2, 1.0 / 16, -12.0, 12.0)
+    y = o.softmax_fwd(x)
+    xd = x.astype(np.float64)
+    for i in range(x.shape[0]):
+        a, b = xd[i]
+        sig = 1.0 / (1.0 + math.exp(b - a))
+        assert abs(y[i, 0] - sig) <= 1e-15 and abs(y[i, 1] - (1.0 - sig)) <= 1e-15
+
+
+def pin_softmax_matches_libraries(o):
+    import scipy.special
+    import torch
+    for seed, (M, N, dtype, scale) in enumerate([(5, 1000, "f32", 3.0), (6, 513, "bf16", 2.0),
+                                                 (3, 4096, "bf16", 1.0)]):
+        x = synth.random_rows(200 + seed, M, N, dtype=dtype, scale=scale)
+        y = o.softmax_fwd(x)
+        xd = decode(x)
+        ref_t = torch.softmax(torch.from_numpy(xd), dim=1).numpy()
+        ref_s = scipy.special.softmax(xd, axis=1)
+        assert np.max(np.abs(y - ref_t)) <= 1e-15, "disagrees with torch.softmax (float64)"
+        assert np.max(np.abs(y - ref_s)) <= 1e-15, "disagrees with scipy.special.softmax"
+
+
+def pin_softmax_row_stride_and_padding(o):
+    for dtype in ("f32", "bf16"):
+        padded = synth.random_rows(300, 9, 100, ld=136, dtype=dtype, scale=2.0)
+        dense = np.ascontiguousarray(padded[:, :100])
+        y_p = o.softmax_fwd(padded, n_cols=100)
+        y_d = o.softmax_fwd(dense)
+        assert np.all(np.isfinite(y_p)), "padding (NaN) must never be read"
+        assert np.array_equal(y_p, y_d), "strided rows must give the dense result"
+
+
+def pin_softmax_neg_inf_entries(o):
+    x = synth.random_rows(301, 4, 64, dtype="f32", scale=2.0)
+    x[:, ::3] = -np.inf
+    y = o.softmax_fwd(x)
+    assert np.all(y[:, ::3] == 0.0), "-inf logits get probability exactly 0"
+    assert np.max(np.abs(y.sum(axis=1) - 1.0)) <= 1e-12
+    finite = np.ascontiguousarray(x[:, [j for j in range(64) if j % 3]])
+    assert np.max(np.abs(o.softmax_fwd(finite) - y[:, [j for j in range(64) if j % 3]])) <= 1e-16
+
+
+# --------------------------------------------------------------------------- softmax backward
+def pin_softmax_bwd_rows_sum_to_zero(o):
+    # Dyadic probability rows sum to exactly 1, so each dx row sums to 0 up to rounding.
+    y = np.array([[0.5, 0.25, 0.125, 0.125], [0.25, 0.25, 0.25, 0.25], [1.0, 0.0, 0.0, 0.0]],
+                 dtype=np.float32)
+    dy = synth.random_rows(400, 3, 4, dtype="f32", scale=3.0)
+    dx = o.softmax_bwd(y, dy)
+    assert np.max(np.abs(dx.sum(axis=1))) <= 1e-14, "dx rows must sum to 0 when sum(y) = 1"
+
+
+def pin_softmax_bwd_finite_differences(o):
+    # phi(x) = sum_j softmax(x)_j dy_j; its gradient is the backward of softmax at y = softmax(x).
+    x = _grid_rows(13, 3, 6, 1.0 / 4, -2.0, 2.0)
+    dy = _grid_rows(14, 3, 6, 1.0 / 4, -2.0, 2.0)
+    h = 2.0 ** -14
+    y = o.softmax_fwd(x)
+    dx = o.softmax_bwd(y.astype(np.float32), dy)
+    for i in range(x.shape[0]):
+        for k in range(x.shape[1]):
+            xp = x[i:i + 1].copy()
+            xm = x[i:i + 1].copy()
+            xp[0, k] += np.float32(h)
+            xm[0, k] -= np.float32(h)
+            fd = ((o.softmax_fwd(xp) - o.softmax_fwd(xm)) @ dy[i].astype(np.float64))[0] / (2 * h)
+            # y is rounded to fp32 before the backward: allow that rounding (~1e-7 relative).
+            assert abs(fd - dx[i, k]) <= 2e-6 * max(1.0, np.max(np.abs(dx[i]))), \
+                f"softmax backward disagrees with finite differences at ({i},{k})"
+
+
+def pin_softmax_bwd_matches_torch(o):
+    import torch
+    for seed, (M, N, dtype) in enumerate([(4, 300, "f32"), (5, 4096, "bf16"), (3, 7, "bf16")]):
+        y = synth.random_rows(500 + seed, M, N, dtype=dtype, scale=0.2)
+        dy = synth.random_rows(600 + seed, M, N, dtype=dtype, scale=1.0)
+        dx = o.softmax_bwd(y, dy)
+        ref = torch._softmax_backward_data(torch.from_numpy(decode(dy)),
+                                           torch.from_numpy(decode(y)), 1,
+                                           torch.float64).numpy()
+        assert np.max(np.abs(dx - ref)) <= 1e-13, "disagrees with torch softmax backward (float64)"
+
+
+def pin_softmax_bwd_row_strides(o):
+    y = synth.random_rows(700, 5, 50, ld=64, dtype="bf16", scale=0.3)
+    dy = synth.random_rows(701, 5, 50, ld=80, dtype="bf16", scale=1.0)
+    dx = o.softmax_bwd(y, dy, n_cols=50)
+    dense = o.softmax_bwd(np.ascontiguousarray(y[:, :50]), np.ascontiguousarray(dy[:, :50]))
+    assert np.all(np.isfinite(dx)) and np.array_equal(dx, dense), "row strides / padding"
+
+
+# --------------------------------------------------------------------------- cross-entropy
+def pin_xent_uniform_logits_loss_is_log_v(o):
+    with open(GOLDEN) as f:
+        lnv = json.load(f)["lnV"]["values"]
+    for V_str, expect in lnv.items():
+        V = int(V_str)
+        assert abs(math.log(V) - expect) <= 1e-15 * expect
+        x = np.full((3, V), -1.5, dtype=np.float32)
+        t = np.array([0, V - 1, V // 2], dtype=np.int64)
+        grad, loss, mean, (n, bad) = o.xent(x, t, V)
+        assert n == 3 and bad == 0
+        assert np.max(np.abs(loss - expect)) <= 1e-12 * expect, f"uniform logits: loss = log {V}"
+        assert abs(mean - expect) <= 1e-12 * expect
+        # all-equal rows: gradient (1/V - [j == t]) / n
+        want = np.full(V, 1.0 / V / n)
+        for r in range(3):
+            w = want.copy()
+            w[t[r]] = (1.0 / V - 1.0) / n
+            assert np.max(np.abs(grad[r] - w)) <= 1e-15, "all-equal row gradient"
+
+
+def pin_xent_loss_is_logsumexp_minus_target(o):
+    import scipy.special
+    x = synth.random_rows(800, 16, 3001, dtype="bf16", scale=4.0)
+    t = synth.random_targets(801, 16, 3001, ignore_frac=0.25)
+    n, _ = o.xent_count(t, 3001)
+    _, loss = o.xent_rows(x, t, 3001, n, want_grad=False)
+    xd = decode(x)
+    for i in range(16):
+        want = 0.0 if t[i] == -100 else scipy.special.logsumexp(xd[i]) - xd[i, t[i]]
+        assert abs(loss[i] - want) <= 1e-12 * max(1.0, abs(want)), f"row {i} loss"
+
+
+def pin_xent_matches_torch(o):
+    import torch
+    import torch.nn.functional as F
+    for seed, (M, V, dtype, scale, ign, ii) in enumerate([
+            (12, 1000, "f32", 3.0, 0.25, -100), (9, 513, "bf16", 2.0, 0.3, -100),
+            (7, 64, "f32", 8.0, 0.3, 5)]):
+        x = synth.random_rows(900 + seed, M, V, dtype=dtype, scale=scale)
+        t = synth.random_targets(950 + seed, M, V, ignore_frac=ign, ignore_index=ii)
+        grad, loss, mean, (n, bad) = o.xent(x, t, V, ignore_index=ii)
+        xt = torch.from_numpy(decode(x)).requires_grad_(True)
+        tt = torch.from_numpy(t)
+        ref_mean = F.cross_entropy(xt, tt, ignore_index=ii, reduction="mean")
+        ref_none = F.cross_entropy(xt.detach(), tt, ignore_index=ii, reduction="none").numpy()
+        ref_mean.backward()
+        assert n == int((t != ii).sum()) and bad == 0
+        assert abs(mean - ref_mean.item()) <= 1e-13 * abs(ref_mean.item()), "mean loss vs torch"
+        assert np.max(np.abs(loss - ref_none)) <= 1e-12, "row losses vs torch"
+        assert np.max(np.abs(grad - xt.grad.numpy())) <= 1e-15, "gradient vs torch autograd"
+
+
+def pin_xent_gradient_structure(o):
+    x = synth.random_rows(1000, 10, 777, dtype="f32", scale=3.0)
+    x[3, ::2] = -np.inf
+    t = synth.random_targets(1001, 10, 777, ignore_frac=0.3)
+    t[3] = 1  # a finite column of the half -inf row
+    grad, loss, mean, (n, _) = o.xent(x, t, 777)
+    for i in range(10):
+        if t[i] == -100:
+            assert np.all(grad[i] == 0.0) and not np.signbit(grad[i]).any(), "ignored row is +0"
+            assert loss[i] == 0.0
+        else:
+            assert abs(grad[i].sum()) <= 1e-15 * 777, "gradient rows sum to 0"
+            assert grad[i, t[i]] < 0 and np.all(np.delete(grad[i], t[i]) >= 0)
+            assert loss[i] > 0
+    assert np.all(grad[3, ::2] == 0.0), "-inf logits get exactly zero gradient"
+
+
+def pin_xent_finite_differences(o):
+    M, V = 5, 7
+    x = _grid_rows(15, M, V, 1.0 / 4, -2.0, 2.0)
+    t = np.array([3, -100, 0, 6, -100], dtype=np.int64)
+    grad, _, _, (n, _) = o.xent(x, t, V)
+    assert n == 3
+    h = 2.0 ** -14
+    for i in range(M):
+        for j in range(V):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += np.float32(h)
+            xm[i, j] -= np.float32(h)
+            fd = (o.xent(xp, t, V, want_grad=False)[2] - o.xent(xm, t, V, want_grad=False)[2]) / (2 * h)
+            assert abs(fd - grad[i, j]) <= 1e-8, f"gradient vs finite differences at ({i},{j})"
+
+
+def pin_xent_count_and_mean(o):
+    t = synth.random_targets(1100, 1000, 50, ignore_frac=0.37)
+    t[5] = 50   # out of range, not ignored
+    t[6] = -7   # out of range, not ignored
+    n, bad = o.xent_count(t, 50)
+    assert n == sum(1 for v in t.tolist() if v != -100) and bad == 2
+    x = synth.random_rows(1101, 1000, 50, dtype="bf16", scale=2.0)
+    grad, loss, mean, _ = o.xent(x, t, 50)
+    assert abs(mean - math.fsum(loss.tolist()) / n) <= 1e-12 * abs(mean), "mean = fsum(loss)/n"
+    for r in (5, 6):
+        assert loss[r] == 0.0 and np.all(grad[r] == 0.0), "bad target rows are zero"
+    all_ignored = np.full(4, -100, dtype=np.int64)
+    g0, l0, m0, (n0, _) = o.xent(x[:4], all_ignored, 50)
+    assert n0 == 0 and math.isnan(m0) and np.all(g0 == 0.0) and np.all(l0 == 0.0)
+
+
+def pin_xent_row_subset_and_padding(o):
+    x = synth.random_rows(1200, 20, 300, ld=333, dtype="f32", scale=4.0)
+    t = synth.random_targets(1201, 20, 300, ignore_frac=0.2)
+    g_all, l_all, _, (n, _) = o.xent(x, t, 300)
+    assert np.all(np.isfinite(g_all)), "padding (NaN) must never be read"
+    rows = np.array([19, 0, 7, 7, 13])
+    g_sub, l_sub = o.xent_rows(x, t, 300, n, rows=rows)
+    assert np.array_equal(g_sub, g_all[rows]) and np.array_equal(l_sub, l_all[rows])
+    dense = np.ascontiguousarray(x[:, :300])
+    g_d, l_d, _, _ = o.xent(dense, t, 300)
+    assert np.array_equal(g_d, g_all) and np.array_equal(l_d, l_all)
+
+
+# --------------------------------------------------------------------------- worked examples
+def pin_golden_worked_examples(o):
+    with open(GOLDEN) as f:
+        gold = json.load(f)
+    for case in gold["softmax_fwd"]:
+        y = o.softmax_fwd(as_input(case["x"], case["dtype"]))
+        want = np.array([[closed_form(v) for v in r] for r in case["y"]])
+        assert np.max(np.abs(y - want)) <= 1e-15, case["name"]
+    for case in gold["softmax_bwd"]:
+        dx = o.softmax_bwd(as_input(case["y"], case["dtype"]), as_input(case["dy"], case["dtype"]))
+        want = np.array([[closed_form(v) for v in r] for r in case["dx"]])
+        assert np.max(np.abs(dx - want)) <= 1e-15, case["name"]
+    for case in gold["xent"]:
+        x = as_input(case["x"], case["dtype"])
+        t = np.array(case["target"], dtype=np.int64)
+        V = x.shape[1]
+        grad, loss, mean, (n, bad) = o.xent(x, t, V, ignore_index=case["ignore_index"])
+        assert n == case["n"] and bad == 0, case["name"]
+        assert np.max(np.abs(loss - [closed_form(v) for v in case["loss"]])) <= 1e-15, case["name"]
+        assert abs(mean - closed_form(case["mean"])) <= 1e-15, case["name"]
+        want = np.array([[closed_form(v) for v in r] for r in case["grad"]])
+        assert np.max(np.abs(grad - want)) <= 1e-15, case["name"]
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,77 @@
+"""The oracle pins catch plausible mistakes: each planted mistake must fail at least one pin.
+
+Each mutant is the oracle's C source with one textual edit (a dropped term, a
+wrong sign, index or stride, a swapped operand), compiled on the CPU into a
+temporary library. The real oracle source is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "softmax drops the max shift": ("double e = exp(load_elem(x, row_off + j, dtype) - m);",
+                                    "double e = exp(load_elem(x, row_off + j, dtype));"),
+    "softmax takes the min": ("    if (v > m) m = v;\n  }\n  double d = 0.0;\n  for (int64_t j = 0; j < N; ++j) {\n    double e",
+                              "    if (v < m) m = v;\n  }\n  double d = 0.0;\n  for (int64_t j = 0; j < N; ++j) {\n    double e"),
+    "softmax skips the division": ("for (int64_t j = 0; j < N; ++j) y[j] = y[j] / d;",
+                                   "for (int64_t j = 0; j < N; ++j) y[j] = y[j];"),
+    "bf16 decoded with a wrong shift": ("uint32_t bits = (uint32_t)h << 16;",
+                                        "uint32_t bits = (uint32_t)h << 15;"),
+    "softmax ignores the row stride": ("softmax_row(x, i * ld_x, N, dtype, y + i * N);",
+                                       "softmax_row(x, i * N, N, dtype, y + i * N);"),
+    "softmax backward flips the sign of s": ("(load_elem(dy, i * ld_dy + j, dtype) - s);",
+                                             "(load_elem(dy, i * ld_dy + j, dtype) + s);"),
+    "softmax backward multiplies by dy": (
+        "dx[i * N + j] = load_elem(y, i * ld_y + j, dtype) *",
+        "dx[i * N + j] = load_elem(dy, i * ld_dy + j, dtype) *"),
+    "softmax backward uses y's stride for dy": (
+        "s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_dy + j, dtype);",
+        "s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_y + j, dtype);"),
+    "loss adds the target logit": ("loss[r] = m + log(d) - xt;", "loss[r] = m + log(d) + xt;"),
+    "loss drops log d": ("loss[r] = m + log(d) - xt;", "loss[r] = m - xt;"),
+    "target logit read from row 0": ("double xt = load_elem(logits, off + t, dtype);",
+                                     "double xt = load_elem(logits, t, dtype);"),
+    "gradient not divided by n": ("g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;",
+                                  "g[j] = (j == t) ? (p - 1.0) / (double)n : p;"),
+    "onehot at the wrong column": ("g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;",
+                                   "g[j] = (j == t + 1) ? (p - 1.0) / (double)n : p / (double)n;"),
+    "onehot added instead of subtracted": ("g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;",
+                                           "g[j] = (j == t) ? (p + 1.0) / (double)n : p / (double)n;"),
+    "ignored rows keep stale gradient": ("        for (int64_t j = 0; j < V; ++j) g[j] = 0.0;\n      continue;",
+                                         "        for (int64_t j = 0; j < V; ++j) (void)g;\n      continue;"),
+    "ignored rows counted in n": ("    if (target[i] == ignore_index) continue;\n    ++n;",
+                                  "    ++n;"),
+    "mean divides by the row count": ("return s / (double)n;", "return s / (double)M;"),
+    "ignore_index checked only outside [0, V)": ("if (t == ignore_index || t < 0 || t >= V) {",
+                                                 "if (t < 0 || t >= V) {"),
+    "exp of the shifted logit uses the wrong sign": (
+        "double p = exp(load_elem(logits, off + j, dtype) - m) / d;",
+        "double p = exp(m - load_elem(logits, off + j, dtype)) / d;"),
+    "sum of exponentials skips the last column": (
+        "for (int64_t j = 0; j < V; ++j) d += exp(load_elem(logits, off + j, dtype) - m);",
+        "for (int64_t j = 0; j + 1 < V; ++j) d += exp(load_elem(logits, off + j, dtype) - m);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    find, replace = MUTANTS[name]
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(find) == 1, f"mutation site for {name!r} must occur exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(find, replace))
+    lib = oracle.compile_library(str(mutant_src), str(tmp_path / "libmutant.so"))
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, FloatingPointError, ValueError):
+            failed.append(pin.__name__)
+        if failed:
+            break
+    assert failed, f"no pin catches the planted mistake {name!r}"
