@@ -1,0 +1,421 @@
+// xr_api.cpp -- the C ABI of libxr: argument validation, launch planning, kernel launches.
+//
+// Validation runs before any HIP call, so argument errors are reported without a device.
+// Planning picks, from the row length, the dtype, the batch size and the device's compute
+// unit count, one of three paths (row-resident, split row, stream); see include/xr.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/xr.h"
+#include "xr_internal.h"
+
+namespace xr {
+namespace {
+
+constexpr int32_t kVersion = 10000;  // 1.0.0
+constexpr int64_t kMinChunkVecs = 256;
+
+// ----------------------------------------------------------------------------- options
+struct Options {
+  int64_t path = 0, split = 0, threads = 0, grid = 0;
+};
+Options g_opt;
+
+// Profiling hook: events recorded around the row kernel of each call (xr_set_profile_events).
+hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+
+// ----------------------------------------------------------------------------- device cache
+struct DeviceInfo {
+  int cus = 0;
+  int coop = 0;
+};
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_dev;
+std::map<std::pair<int, const void*>, std::map<int, int>> g_occ;  // (device, kernel) -> threads -> blocks/CU
+
+xr_status_t device_info(int* dev_out, DeviceInfo* info) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return XR_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end()) {
+    DeviceInfo di;
+    if (hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        di.cus <= 0)
+      return XR_ERR_DEVICE;
+    if (hipDeviceGetAttribute(&di.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
+      di.coop = 0;
+    it = g_dev.emplace(dev, di).first;
+  }
+  *dev_out = dev;
+  *info = it->second;
+  return XR_OK;
+}
+
+// Resident workgroups per compute unit for a kernel at a workgroup size.
+int blocks_per_cu(int dev, const void* kernel, int threads) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_occ.find({dev, kernel});
+    if (it != g_occ.end()) {
+      auto jt = it->second.find(threads);
+      if (jt != it->second.end()) return jt->second;
+    }
+  }
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, 0) != hipSuccess)
+    blocks = 0;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_occ[{dev, kernel}][threads] = blocks;
+  return blocks;
+}
+
+// ----------------------------------------------------------------------------- helpers
+int elt_bytes(xr_dtype_t dt) { return dt == XR_BF16 ? 2 : 4; }
+int elts_per_vec(xr_dtype_t dt) { return dt == XR_BF16 ? 8 : 4; }
+bool valid_dtype(int dt) { return dt == XR_F32 || dt == XR_BF16; }
+
+// 16-byte vectors a row of n elements can touch, whatever its alignment.
+int64_t row_vecs_max(int64_t n, xr_dtype_t dt) {
+  const int64_t epv = elts_per_vec(dt);
+  return (epv - 1 + n + epv - 1) / epv;
+}
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Do two row-major matrices (M rows, n columns, strides in elements) overlap in memory?
+bool overlaps(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t n,
+              int eb) {
+  if (M == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t a1 = a0 + (uintptr_t)(((M - 1) * lda + n) * eb);
+  const uintptr_t b1 = b0 + (uintptr_t)(((M - 1) * ldb + n) * eb);
+  return a0 < b1 && b0 < a1;
+}
+bool bad_alias(const void* out, int64_t ldo, const void* in, int64_t ldi, int64_t M, int64_t n,
+               int eb) {
+  if (out == in && ldo == ldi) return false;  // exactly in place
+  return overlaps(out, ldo, in, ldi, M, n, eb);
+}
+
+// Every row of both matrices sits at the same address modulo 16 bytes.
+bool same_lead(const void* a, int64_t lda, const void* b, int64_t ldb, int eb) {
+  const intptr_t d = reinterpret_cast<intptr_t>(a) - reinterpret_cast<intptr_t>(b);
+  return (d % 16) == 0 && (((lda - ldb) * eb) % 16) == 0;
+}
+
+// Smallest shape of the menu holding `vecs` vectors per workgroup (optionally a forced size).
+const Shape* pick_shape(const Shape* menu, int count, int64_t vecs) {
+  for (int i = 0; i < count; ++i) {
+    const Shape& s = menu[i];
+    if (g_opt.threads && s.threads != g_opt.threads) continue;
+    if ((int64_t)s.threads * s.vpt >= vecs) return &s;
+  }
+  return nullptr;
+}
+
+struct Plan {
+  int path = kPathStream;
+  Shape shape{kStreamThreads, 0};
+  int S = 1;
+  int64_t grid = 0;
+  bool coop = false;
+  int64_t chunk_vecs = 0;
+  const void* kernel = nullptr;
+};
+
+// Does every row of a matrix start on a 16-byte boundary?
+bool rows_on_16(const void* p, int64_t ld, int64_t M, int eb) {
+  return aligned_to(p, 16) && (M <= 1 || ((ld * eb) % 16) == 0);
+}
+
+// op: 0 softmax fwd, 1 softmax bwd, 2 cross-entropy. `aligned`: every operand row has the
+// same address modulo 16; `on16`: moreover every row starts on a 16-byte boundary (then a
+// row touches exactly ceil(N / elements-per-vector) vectors).
+xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned, bool on16,
+                      Plan* plan) {
+  int dev = 0;
+  DeviceInfo di;
+  if (xr_status_t st = device_info(&dev, &di)) return st;
+  const bool bwd = op == 1;
+  const Shape* menu = bwd ? kBwdShapes : kFwdShapes;
+  const int nmenu = bwd ? kNumBwdShapes : kNumFwdShapes;
+  const int64_t nvm = on16 ? (N + elts_per_vec(dt) - 1) / elts_per_vec(dt) : row_vecs_max(N, dt);
+  const int64_t cap_max = (int64_t)menu[nmenu - 1].threads * menu[nmenu - 1].vpt;
+  Plan p;
+  p.grid = M;
+
+  const int64_t want = g_opt.path;
+  if (want == kPathStream || !aligned) {
+    if (want && want != kPathStream) return XR_ERR_SHAPE;
+    p.kernel = op == 0 ? softmax_fwd_stream_kernel_ptr(dt)
+                       : op == 1 ? softmax_bwd_stream_kernel_ptr(dt) : xent_stream_kernel_ptr(dt);
+    *plan = p;
+    return XR_OK;
+  }
+
+  // Workgroups per row: enough for the row to fit, and (cross-entropy only) enough rows'
+  // chunks to give every compute unit work when the batch is short.
+  int64_t S = 1;
+  if (op == 2) {
+    const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
+    int64_t s_par = 1;
+    if (M > 0 && M < di.cus) {
+      s_par = (di.cus + M - 1) / M;
+      s_par = std::min(s_par, std::max<int64_t>(1, nvm / kMinChunkVecs));
+    }
+    S = std::max(s_cap, s_par);
+    if (g_opt.split) S = g_opt.split;
+    if (want == kPathResident && g_opt.split == 0) S = s_cap;
+    if (want == kPathSplit && g_opt.split == 0) S = std::max<int64_t>(2, S);
+    if (want == kPathResident && S != 1) return XR_ERR_SHAPE;
+    if (want == kPathSplit && S < 2) return XR_ERR_SHAPE;
+  } else if (nvm > cap_max || want == kPathSplit) {
+    if (want == kPathResident || want == kPathSplit) return XR_ERR_SHAPE;
+    p.kernel = op == 0 ? softmax_fwd_stream_kernel_ptr(dt) : softmax_bwd_stream_kernel_ptr(dt);
+    *plan = p;
+    return XR_OK;
+  }
+
+  const int64_t chunk = (nvm + S - 1) / S;
+  const Shape* sh = pick_shape(menu, nmenu, chunk);
+  if (!sh) {
+    if (want) return XR_ERR_SHAPE;
+    p.kernel = op == 0 ? softmax_fwd_stream_kernel_ptr(dt)
+                       : op == 1 ? softmax_bwd_stream_kernel_ptr(dt) : xent_stream_kernel_ptr(dt);
+    *plan = p;
+    return XR_OK;
+  }
+  p.shape = *sh;
+  p.S = (int)S;
+  p.chunk_vecs = chunk;
+  p.kernel = op == 0 ? softmax_fwd_kernel_ptr(dt, *sh)
+                     : op == 1 ? softmax_bwd_kernel_ptr(dt, *sh) : xent_rows_kernel_ptr(dt, *sh);
+  if (!p.kernel) return XR_ERR_SHAPE;
+  const int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
+  if (per_cu <= 0) return XR_ERR_DEVICE;
+  const int64_t resident = (int64_t)di.cus * per_cu;
+  if (S == 1) {
+    p.path = kPathResident;
+    int64_t g = resident;
+    if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
+    if (g_opt.grid < 0) g = M;
+    p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
+  } else {
+    p.path = kPathSplit;
+    if (!di.coop) return XR_ERR_DEVICE;
+    int64_t slots = resident;
+    if (g_opt.grid > 0) slots = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
+    const int64_t groups = std::min<int64_t>(std::max<int64_t>(M, 1), slots / S);
+    if (groups < 1) {
+      if (want) return XR_ERR_SHAPE;
+      Plan q;
+      q.grid = M;
+      q.kernel = xent_stream_kernel_ptr(dt);
+      *plan = q;
+      return XR_OK;
+    }
+    p.grid = groups * S;
+    p.coop = true;
+  }
+  *plan = p;
+  return XR_OK;
+}
+
+xr_status_t launch(const Plan& p, void* params, hipStream_t stream, int threads) {
+  void* args[] = {params};
+  if (p.grid <= 0) return XR_OK;
+  if (p.grid > 0x7FFFFFFF) return XR_ERR_SHAPE;
+  const dim3 grid((unsigned)p.grid), block((unsigned)threads);
+  if (g_ev_start && hipEventRecord(g_ev_start, stream) != hipSuccess) return XR_ERR_LAUNCH;
+  hipError_t e = p.coop ? hipLaunchCooperativeKernel(p.kernel, grid, block, args, 0, stream)
+                        : hipLaunchKernel(p.kernel, grid, block, args, 0, stream);
+  if (e != hipSuccess) return XR_ERR_LAUNCH;
+  if (g_ev_stop && hipEventRecord(g_ev_stop, stream) != hipSuccess) return XR_ERR_LAUNCH;
+  return XR_OK;
+}
+
+size_t xent_ws_bytes(const Plan& p, int64_t M) {
+  return kWsPartials + (p.path == kPathSplit ? (size_t)M * (size_t)p.S * sizeof(uint64_t) : 0);
+}
+
+}  // namespace
+}  // namespace xr
+
+using namespace xr;
+
+extern "C" {
+
+const char* xr_status_string(xr_status_t s) {
+  switch (s) {
+    case XR_OK: return "ok";
+    case XR_ERR_NULL: return "a required pointer is NULL";
+    case XR_ERR_SHAPE: return "invalid or unsupported sizes";
+    case XR_ERR_STRIDE: return "row stride smaller than the row length";
+    case XR_ERR_DTYPE: return "unknown dtype";
+    case XR_ERR_ALIAS: return "an output partially overlaps an input";
+    case XR_ERR_WORKSPACE: return "workspace missing or too small";
+    case XR_ERR_ALIGN: return "pointer not aligned to its element size";
+    case XR_ERR_DEVICE: return "no usable HIP device";
+    case XR_ERR_LAUNCH: return "kernel launch failed";
+    case XR_ERR_OPTION: return "unknown option or value";
+  }
+  return "unknown status";
+}
+
+int32_t xr_version(void) { return kVersion; }
+
+xr_status_t xr_set_option(xr_option_t option, int64_t value) {
+  switch (option) {
+    case XR_OPT_PATH:
+      if (value < 0 || value > 3) return XR_ERR_OPTION;
+      g_opt.path = value;
+      return XR_OK;
+    case XR_OPT_SPLIT:
+      if (value < 0 || value == 1 || value > 4096) return XR_ERR_OPTION;
+      g_opt.split = value;
+      return XR_OK;
+    case XR_OPT_THREADS:
+      if (value != 0 && value != 64 && value != 128 && value != 256 && value != 512 && value != 1024)
+        return XR_ERR_OPTION;
+      g_opt.threads = value;
+      return XR_OK;
+    case XR_OPT_GRID:
+      if (value < -1 || value > 64) return XR_ERR_OPTION;
+      g_opt.grid = value;
+      return XR_OK;
+  }
+  return XR_ERR_OPTION;
+}
+
+xr_status_t xr_set_profile_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return XR_ERR_NULL;
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+  return XR_OK;
+}
+
+xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
+                    xr_plan_t* out) {
+  if (!out) return XR_ERR_NULL;
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (op < 0 || op > 2 || M < 0 || N < 1) return XR_ERR_SHAPE;
+  Plan p;
+  if (xr_status_t st = make_plan(op, M, N, dtype, op == 2 ? true : aligned != 0, aligned == 2, &p))
+    return st;
+  out->path = p.path;
+  out->threads = p.path == kPathStream ? kStreamThreads : p.shape.threads;
+  out->vec_per_thread = p.path == kPathStream ? 0 : p.shape.vpt;
+  out->split = p.S;
+  out->grid = (int32_t)std::min<int64_t>(p.grid, 0x7FFFFFFF);
+  out->cooperative = p.coop ? 1 : 0;
+  out->chunk_vecs = p.chunk_vecs;
+  return XR_OK;
+}
+
+xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, int64_t M,
+                           int64_t N, xr_dtype_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (ld_x < N || ld_y < N) return XR_ERR_STRIDE;
+  if (M == 0) return XR_OK;
+  if (!x || !y) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if (!aligned_to(x, eb) || !aligned_to(y, eb)) return XR_ERR_ALIGN;
+  if (bad_alias(y, ld_y, x, ld_x, M, N, eb)) return XR_ERR_ALIAS;
+  Plan p;
+  const bool on16 = rows_on_16(x, ld_x, M, eb) && rows_on_16(y, ld_y, M, eb);
+  if (xr_status_t st = make_plan(0, M, N, dtype, same_lead(x, ld_x, y, ld_y, eb), on16, &p))
+    return st;
+  SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N};
+  return launch(p, &prm, static_cast<hipStream_t>(stream),
+                p.path == kPathStream ? kStreamThreads : p.shape.threads);
+}
+
+xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y, const void* dy,
+                           int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (ld_dx < N || ld_y < N || ld_dy < N) return XR_ERR_STRIDE;
+  if (M == 0) return XR_OK;
+  if (!dx || !y || !dy) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if (!aligned_to(dx, eb) || !aligned_to(y, eb) || !aligned_to(dy, eb)) return XR_ERR_ALIGN;
+  if (bad_alias(dx, ld_dx, y, ld_y, M, N, eb) || bad_alias(dx, ld_dx, dy, ld_dy, M, N, eb))
+    return XR_ERR_ALIAS;
+  const bool aligned = same_lead(y, ld_y, dy, ld_dy, eb) && same_lead(y, ld_y, dx, ld_dx, eb);
+  const bool on16 = rows_on_16(y, ld_y, M, eb) && rows_on_16(dy, ld_dy, M, eb) &&
+                    rows_on_16(dx, ld_dx, M, eb);
+  Plan p;
+  if (xr_status_t st = make_plan(1, M, N, dtype, aligned, on16, &p)) return st;
+  SoftmaxBwdParams prm{static_cast<const char*>(y), ld_y * eb, static_cast<const char*>(dy),
+                       ld_dy * eb, static_cast<char*>(dx), ld_dx * eb, M, N};
+  return launch(p, &prm, static_cast<hipStream_t>(stream),
+                p.path == kPathStream ? kStreamThreads : p.shape.threads);
+}
+
+size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype) {
+  if (!valid_dtype(dtype) || M < 0 || V < 1) return 0;
+  // Worst-case row alignment: a call's plan never uses more split slots than this one.
+  Plan p;
+  if (make_plan(2, M, V, dtype, true, false, &p) != XR_OK) return 0;
+  return xent_ws_bytes(p, M);
+}
+
+xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int64_t M,
+                            int64_t V, int64_t ignore_index, xr_dtype_t dtype, float* row_loss,
+                            float* mean_loss, int32_t* counts, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || V < 1) return XR_ERR_SHAPE;
+  if (ld < V) return XR_ERR_STRIDE;
+  if (!mean_loss || !workspace) return XR_ERR_NULL;
+  if (M > 0 && (!logits || !target || !row_loss)) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if ((logits && !aligned_to(logits, eb)) || (target && !aligned_to(target, 8)) ||
+      (row_loss && !aligned_to(row_loss, 4)) || !aligned_to(mean_loss, 4) ||
+      (counts && !aligned_to(counts, 4)) || !aligned_to(workspace, 8))
+    return XR_ERR_ALIGN;
+  Plan p;
+  const bool on16 = logits == nullptr || rows_on_16(logits, ld, M, eb);
+  if (xr_status_t st = make_plan(2, M, V, dtype, true, on16, &p)) return st;
+  if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ws_counts = reinterpret_cast<int32_t*>(ws + kWsCounts);
+  uint64_t* partials = reinterpret_cast<uint64_t*>(ws + kWsPartials);
+  const int64_t nslots = p.path == kPathSplit ? M * p.S : 0;
+
+  {
+    const int64_t* tgt = target;
+    int64_t mm = M, vv = V, ii = ignore_index;
+    void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, &partials, const_cast<int64_t*>(&nslots)};
+    if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3(1), dim3(kScanThreads), args, 0, s) != hipSuccess)
+      return XR_ERR_LAUNCH;
+  }
+  if (M > 0) {
+    XentParams prm{static_cast<char*>(logits), ld * eb, target, M, V, ignore_index, row_loss,
+                   ws_counts, ws_counts + 2, partials, p.chunk_vecs, p.S,
+                   (int)(p.path == kPathSplit ? p.grid / p.S : p.grid)};
+    if (xr_status_t st = launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads))
+      return st;
+  }
+  {
+    const float* rl = row_loss;
+    int64_t mm = M;
+    const int32_t* wc = ws_counts;
+    void* args[] = {&rl, &mm, &wc, &mean_loss, &counts};
+    if (hipLaunchKernel(xent_mean_kernel_ptr(), dim3(1), dim3(kScanThreads), args, 0, s) != hipSuccess)
+      return XR_ERR_LAUNCH;
+  }
+  return XR_OK;
+}
+
+}  // extern "C"

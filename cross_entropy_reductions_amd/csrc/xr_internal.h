@@ -1,0 +1,79 @@
+// xr_internal.h -- launch plans and kernel launchers shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xr {
+
+// Byte offsets inside the cross-entropy workspace.
+constexpr size_t kWsCounts = 0;      // int32[4]: n_non_ignore, n_bad_target, error flags, spare
+constexpr size_t kWsPartials = 256;  // uint64[M * S]: (m, d) pairs of split rows
+
+// Error flags (workspace int32 [2], copied to counts[2]).
+constexpr int32_t kFlagExchangeTimeout = 1;
+
+// Sentinel marking an unpublished (m, d) pair of a split row.
+constexpr uint64_t kPartialEmpty = ~0ull;
+
+enum Path : int { kPathAuto = 0, kPathResident = 1, kPathSplit = 2, kPathStream = 3 };
+
+struct XentParams {
+  char* logits;           // row 0 of the logits (overwritten by the gradient)
+  int64_t ld_bytes;       // row pitch in bytes
+  const int64_t* target;  // [M]
+  int64_t M, V, ignore_index;
+  float* row_loss;        // [M]
+  const int32_t* ws_counts;  // workspace counts (n is read from [0])
+  int32_t* ws_flags;         // workspace error flags
+  uint64_t* partials;        // [M * S] when S > 1
+  int64_t chunk_vecs;     // 16-byte vectors per chunk (the whole row when S == 1)
+  int S;                  // workgroups per row
+  int groups;             // row groups in the grid; grid = groups * S
+};
+
+struct SoftmaxFwdParams {
+  const char* x;
+  int64_t ldx_bytes;
+  char* y;
+  int64_t ldy_bytes;
+  int64_t M, N;
+};
+
+struct SoftmaxBwdParams {
+  const char* y;
+  int64_t ldy_bytes;
+  const char* dy;
+  int64_t lddy_bytes;
+  char* dx;
+  int64_t lddx_bytes;
+  int64_t M, N;
+};
+
+// One kernel configuration: workgroup size and 16-byte vectors per thread.
+struct Shape {
+  int threads;
+  int vpt;
+};
+
+// Kernel lookup (nullptr when the (dtype, shape) pair is not instantiated).
+const void* xent_rows_kernel_ptr(int dtype, Shape s);
+const void* softmax_fwd_kernel_ptr(int dtype, Shape s);
+const void* softmax_bwd_kernel_ptr(int dtype, Shape s);
+const void* xent_stream_kernel_ptr(int dtype);
+const void* softmax_fwd_stream_kernel_ptr(int dtype);
+const void* softmax_bwd_stream_kernel_ptr(int dtype);
+const void* xent_scan_kernel_ptr();
+const void* xent_mean_kernel_ptr();
+
+// Workgroup size of the stream, scan and mean kernels.
+constexpr int kStreamThreads = 256;
+constexpr int kScanThreads = 1024;
+
+// Shapes available to the row-resident kernels, smallest capacity first.
+constexpr int kNumFwdShapes = 7;
+extern const Shape kFwdShapes[kNumFwdShapes];  // xent and softmax forward
+constexpr int kNumBwdShapes = 6;
+extern const Shape kBwdShapes[kNumBwdShapes];  // softmax backward (two row operands)
+
+}  // namespace xr

@@ -1,0 +1,176 @@
+/*
+ * xr.h -- C ABI of libxr: numerically stable row softmax, softmax backward and fused
+ * cross-entropy (loss + in-place gradient) for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ *   - Pointers named for tensors are DEVICE pointers (HIP device memory of the current
+ *     device). Host pointers are marked as such.
+ *   - Matrices are row-major: row i of a matrix starts at element i * ld of its pointer
+ *     ("row stride", counted in ELEMENTS, ld >= number of columns); columns are unit stride.
+ *     Columns [N, ld) of a row are padding: they are never read and never written.
+ *   - dtype selects the floating type of every floating tensor argument of the call except
+ *     row_loss / mean_loss, which are always fp32. bf16 values are rounded to nearest-even
+ *     when stored. All arithmetic is fp32 whatever the storage type.
+ *   - stream is a hipStream_t (NULL = the legacy default stream). Every entry point only
+ *     enqueues work on it: nothing is synchronised, nothing is allocated or freed, and no
+ *     device memory is read or written by the host.
+ *   - Arguments are validated before anything is enqueued; on an error nothing is enqueued
+ *     and the status says which argument is wrong. No C++ exception crosses this ABI.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
+ *   - The library keeps no state across calls except a per-device cache of device
+ *     properties, and the process-wide overrides of xr_set_option().
+ */
+#ifndef XR_H_
+#define XR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum xr_dtype {
+  XR_F32 = 0,  /* IEEE binary32 */
+  XR_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} xr_dtype_t;
+
+typedef enum xr_status {
+  XR_OK = 0,
+  XR_ERR_NULL = 1,      /* a required pointer is NULL */
+  XR_ERR_SHAPE = 2,     /* M < 0, N (or V) < 1, or a size beyond what the library supports */
+  XR_ERR_STRIDE = 3,    /* a row stride is smaller than the number of columns */
+  XR_ERR_DTYPE = 4,     /* unknown dtype */
+  XR_ERR_ALIAS = 5,     /* an output overlaps an input without being exactly the same matrix */
+  XR_ERR_WORKSPACE = 6, /* workspace NULL or smaller than xr_xent_workspace_bytes() */
+  XR_ERR_ALIGN = 7,     /* a tensor pointer is not aligned to its element size */
+  XR_ERR_DEVICE = 8,    /* no usable HIP device, or a device query failed */
+  XR_ERR_LAUNCH = 9,    /* a kernel launch failed (the HIP error is reported by HIP) */
+  XR_ERR_OPTION = 10    /* unknown option or value in xr_set_option() */
+} xr_status_t;
+
+/*
+ * Softmax forward, one row at a time:
+ *   y[i, j] = exp(x[i, j] - m_i) / d_i,  m_i = max_j x[i, j],  d_i = sum_j exp(x[i, j] - m_i)
+ * The safe softmax of the Triton fused-softmax kernels `softmax_kernel` and `_softmax` on
+ * the page "python sum function examples" (subtract the row max, exponentiate, divide by
+ * the row sum; masked lanes are -inf, so -inf inputs get probability 0).
+ *   y, ld_y   output [M, N] of dtype; may be exactly x (y == x and ld_y == ld_x, in place)
+ *   x, ld_x   input  [M, N] of dtype
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1
+ * A row that is entirely -inf, or holds NaN or +inf, gives NaN outputs.
+ */
+xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, int64_t M,
+                           int64_t N, xr_dtype_t dtype, void* stream);
+
+/*
+ * Softmax backward, one row at a time:
+ *   dx[i, j] = y[i, j] * (dy[i, j] - s_i),  s_i = sum_k y[i, k] * dy[i, k]
+ * The fused softmax backward of the Triton kernel `_backward` on the page "python sum
+ * function examples", with its block-sparse scale taken as 1 and dense rows.
+ *   dx, ld_dx  output [M, N] of dtype; may be exactly y or exactly dy (in place)
+ *   y, ld_y    the softmax output [M, N];  dy, ld_dy  the upstream gradient [M, N]
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1
+ */
+xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y, const void* dy,
+                           int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream);
+
+/*
+ * Bytes of device workspace xr_xent_fwd_bwd() needs for these sizes on the current device
+ * (host query; 0 if the sizes are invalid). The caller owns the workspace; its contents
+ * need no initialisation and are scratch between calls.
+ */
+size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype);
+
+/*
+ * Fused cross-entropy loss and gradient (hard labels, mean over non-ignored rows), from
+ * Liger-Kernel `cross_entropy.py`: `liger_cross_entropy_kernel` steps 1-6 and
+ * `LigerCrossEntropyFunction.forward`. With n = #{i : target[i] != ignore_index}:
+ *   row_loss[i] = m_i + log d_i - logits[i, t_i]               (0 for ignored rows)
+ *   logits[i, j] <- (softmax(logits[i, :])_j - [j == t_i]) / n   (0 for ignored rows)
+ *   *mean_loss   = (sum_i row_loss[i]) / n                       (NaN when n == 0)
+ *   logits, ld     [M, V] of dtype, overwritten IN PLACE by the gradient; columns [V, ld)
+ *                  are never touched
+ *   target         int64 [M], device; ignore_index is compared first, so an ignore_index
+ *                  inside [0, V) still ignores its rows
+ *   row_loss       fp32 [M], device, required
+ *   mean_loss      fp32 [1], device, required
+ *   counts         int32 [3], device, or NULL: counts[0] = n, counts[1] = targets that are
+ *                  neither ignore_index nor inside [0, V) (their rows get zero gradient and
+ *                  zero loss, but still count in n), counts[2] = error flags (0 = none;
+ *                  bit 0: a split-row exchange timed out and the row holds NaN)
+ *   workspace      device scratch of at least xr_xent_workspace_bytes(M, V, dtype) bytes
+ *   M >= 0 (M == 0 still writes mean_loss = NaN and counts = {0, 0, 0}), V >= 1
+ * Rows whose only finite logits are missing (all -inf), or a target logit of -inf, give
+ * NaN / +inf; NaN and +inf logits are outside the contract.
+ * logits must not overlap target, row_loss, mean_loss, counts or the workspace.
+ */
+xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int64_t M,
+                            int64_t V, int64_t ignore_index, xr_dtype_t dtype, float* row_loss,
+                            float* mean_loss, int32_t* counts, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code (host). */
+const char* xr_status_string(xr_status_t status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int32_t xr_version(void);
+
+/*
+ * How a call is carried out (host query, nothing enqueued). path: 1 = row-resident
+ * (a row or a row chunk per workgroup, held in registers: one read of the input),
+ * 2 = split row (S > 1 workgroups per row exchanging (max, sum) pairs), 3 = stream
+ * (one workgroup per row, several passes over global memory).
+ * op: 0 = softmax forward, 1 = softmax backward, 2 = cross-entropy.
+ * aligned: 0 = the operand rows sit at different addresses modulo 16 bytes (stream path),
+ * 1 = they share their address modulo 16 (rows may start anywhere), 2 = moreover every row
+ * starts on a 16-byte boundary (the usual contiguous tensors). The cross-entropy has one
+ * operand, so 0 is read as 1 for it.
+ */
+typedef struct xr_plan {
+  int32_t path;
+  int32_t threads;         /* workgroup size */
+  int32_t vec_per_thread;  /* 16-byte vectors held per thread and operand */
+  int32_t split;           /* workgroups per row (S) */
+  int32_t grid;            /* workgroups launched */
+  int32_t cooperative;     /* 1 if launched as a cooperative grid */
+  int64_t chunk_vecs;      /* 16-byte vectors per workgroup chunk of a row */
+} xr_plan_t;
+
+xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
+                    xr_plan_t* plan /* host */);
+
+/*
+ * Process-wide overrides for tests and benchmarks (not for concurrent use with calls in
+ * flight). Value 0 restores the automatic choice.
+ *   XR_OPT_PATH     1 resident, 2 split, 3 stream (a forced path the sizes cannot take
+ *                   returns XR_ERR_SHAPE from the entry point)
+ *   XR_OPT_SPLIT    workgroups per row for the split path (>= 2)
+ *   XR_OPT_THREADS  workgroup size of the row-resident kernels (64 .. 1024)
+ *   XR_OPT_GRID     workgroups per compute unit of the persistent grids (>= 1), or -1 for
+ *                   one workgroup per row (S == 1 only)
+ */
+typedef enum xr_option {
+  XR_OPT_PATH = 1,
+  XR_OPT_SPLIT = 2,
+  XR_OPT_THREADS = 3,
+  XR_OPT_GRID = 4
+} xr_option_t;
+
+xr_status_t xr_set_option(xr_option_t option, int64_t value);
+
+/*
+ * Profiling hook (process-wide, not for concurrent use): while set, every entry point records
+ * hipEvent_t `start` on its stream right before launching its row kernel (the kernel that
+ * reads and writes the rows; not the small target-scan and mean kernels of the
+ * cross-entropy) and `stop` right after it, so hipEventElapsedTime(start, stop) is that
+ * kernel's duration. The events are created and owned by the caller. Both NULL clears the
+ * hook; exactly one NULL is XR_ERR_NULL.
+ */
+xr_status_t xr_set_profile_events(void* start, void* stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XR_H_ */

@@ -1,0 +1,372 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element.
+
+Inputs come from the seeded generators in ``synth``; expected values only from
+``oracle``. Cases cover the five benchmark workloads (at full size; the largest
+ones compare every row loss, the mean and a sample of full gradient rows, plus
+properties that hold on every row), several-tile and ragged sizes, unaligned row
+starts and strides, degenerate rows and batches, every launch path, and
+run-to-run determinism.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_pins
+import synth
+from gpu_util import (check_bf16, check_fp32, check_losses, check_output, to_device, to_host,
+                      widen)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import cross_entropy_reductions_amd as xr
+else:  # collected on a machine without a GPU: every test here is skipped
+    xr = None
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no HIP device")]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    xr.reset_options()
+    yield
+    xr.reset_options()
+
+
+def run_xent(x_host: np.ndarray, target: np.ndarray, V: int, ignore_index: int = -100):
+    """Run the library on a copy of x_host (M, ld); returns (grad bits/values (M, ld), rows, mean, counts)."""
+    x = to_device(x_host)
+    t = to_device(target)
+    mean, rows, counts = xr.xent_fwd_bwd(x[:, :V], t, ignore_index)
+    torch.cuda.synchronize()
+    return to_host(x), to_host(rows), float(mean.item()), to_host(counts)
+
+
+def compare_xent(orc, x_host, target, V, grad_gpu, rows_gpu, mean_gpu, counts_gpu, what,
+                 ignore_index=-100, rows=None):
+    """Counts, every row loss, the mean, and the gradient of every row (rows=None: grad_gpu is
+    the whole (M, ld) matrix, whose padding must be unchanged) or of the listed rows
+    (grad_gpu[i] is row rows[i])."""
+    n, bad = orc.xent_count(target, V, ignore_index)
+    assert int(counts_gpu[0]) == n and int(counts_gpu[1]) == bad, f"{what}: counts"
+    assert int(counts_gpu[2]) == 0, f"{what}: error flags {int(counts_gpu[2])}"
+    _, loss_all = orc.xent_rows(x_host, target, V, n, ignore_index, want_grad=False)
+    check_losses(rows_gpu, mean_gpu, loss_all, orc.mean(loss_all, n), what)
+    sel = np.arange(x_host.shape[0]) if rows is None else np.asarray(rows)
+    for c0 in range(0, sel.size, 256):
+        part = sel[c0:c0 + 256]
+        g, _ = orc.xent_rows(x_host, target, V, n, ignore_index, rows=part)
+        got = grad_gpu[part, :V] if rows is None else grad_gpu[c0:c0 + 256, :V]
+        check_output(got, g, f"{what} rows {part[0]}..")
+    if rows is None and x_host.shape[1] > V:
+        assert np.array_equal(grad_gpu[:, V:].view(np.uint8), x_host[:, V:].view(np.uint8)), \
+            f"{what}: padding changed"
+
+
+# ----------------------------------------------------------------------------- worked examples
+def test_worked_examples():
+    with open(oracle_pins.GOLDEN) as f:
+        gold = json.load(f)
+    for case in gold["softmax_fwd"]:
+        x = oracle_pins.as_input(case["x"], case["dtype"])
+        y = to_host(xr.softmax_fwd(to_device(x)))
+        want = np.array([[oracle_pins.closed_form(v) for v in r] for r in case["y"]])
+        check_output(y, want, case["name"])
+    for case in gold["softmax_bwd"]:
+        y = oracle_pins.as_input(case["y"], case["dtype"])
+        dy = oracle_pins.as_input(case["dy"], case["dtype"])
+        dx = to_host(xr.softmax_bwd(to_device(y), to_device(dy)))
+        want = np.array([[oracle_pins.closed_form(v) for v in r] for r in case["dx"]])
+        check_output(dx, want, case["name"])
+    for case in gold["xent"]:
+        x = oracle_pins.as_input(case["x"], case["dtype"])
+        t = np.array(case["target"], dtype=np.int64)
+        g, rows, mean, counts = run_xent(x, t, x.shape[1], case["ignore_index"])
+        assert int(counts[0]) == case["n"]
+        want_g = np.array([[oracle_pins.closed_form(v) for v in r] for r in case["grad"]])
+        check_output(g, want_g, case["name"])
+        want_l = np.array([oracle_pins.closed_form(v) for v in case["loss"]])
+        check_losses(rows, mean, want_l, oracle_pins.closed_form(case["mean"]), case["name"])
+
+
+# ----------------------------------------------------------------------------- the five workloads
+def test_c1_softmax_fp32(orc):
+    w = synth.softmax_c1()
+    y = to_host(xr.softmax_fwd(to_device(w["x"])))
+    check_fp32(y, orc.softmax_fwd(w["x"]), "c1 softmax")
+
+
+def test_c2_softmax_fwd_bwd_bf16(orc):
+    w = synth.softmax_c2()
+    x, dy = to_device(w["x"]), to_device(w["dy"])
+    y = xr.softmax_fwd(x)
+    dx = xr.softmax_bwd(y, dy)
+    y_h, dx_h = to_host(y), to_host(dx)
+    check_bf16(y_h, orc.softmax_fwd(w["x"]), "c2 softmax forward")
+    # The backward is checked on the GPU's own bf16 y, which isolates the backward kernel.
+    check_bf16(dx_h, orc.softmax_bwd(y_h, w["dy"]), "c2 softmax backward")
+    # dx rows sum to ~0 (sum y ~ 1 up to bf16 rounding of y).
+    s = widen(dx_h).sum(axis=1)
+    assert np.max(np.abs(s)) < 0.05
+
+
+def test_c3_xent_bf16(orc):
+    w = synth.xent_c3()
+    g, rows, mean, counts = run_xent(w["x"], w["target"], w["N"])
+    compare_xent(orc, w["x"], w["target"], w["N"], g, rows, mean, counts, "c3")
+
+
+def test_c4_xent_bf16_large_vocab(orc):
+    w = synth.xent_c4()
+    x_host, t, V = w["x"], w["target"], w["N"]
+    x = to_device(x_host)
+    mean, rows, counts = xr.xent_fwd_bwd(x, to_device(t), -100)
+    torch.cuda.synchronize()
+    n, _ = orc.xent_count(t, V)
+    ign = np.flatnonzero(t == -100)
+    keep = np.flatnonzero(t != -100)
+    # Properties on every row: ignored rows are exactly zero, the others sum to ~0: the
+    # entries' magnitudes add up to 2 (1 - p_t) / n <= 2 / n and each is rounded to bf16
+    # with a relative error of at most 2^-8, so |row sum| <= 2^-7 / n (+5 % for the fp32 sum).
+    assert bool((x[torch.from_numpy(ign).cuda()] == 0).all()), "ignored rows must be zero"
+    sums = x.float().sum(dim=1)[torch.from_numpy(keep).cuda()].abs().max().item()
+    assert sums <= 1.05 * 2.0 ** -7 / n, f"gradient row sums up to {sums}"
+    # Every row loss and the mean; full gradient rows on a sample.
+    rng = np.random.Generator(np.random.PCG64(44))
+    sample = np.unique(np.concatenate([[0, x_host.shape[0] - 1], ign[:16],
+                                       rng.choice(keep, 160, replace=False)]))
+    g_sample = to_host(x[torch.from_numpy(sample).cuda()])
+    compare_xent(orc, x_host, t, V, g_sample, to_host(rows), float(mean.item()), to_host(counts),
+                 "c4", rows=sample)
+
+
+def test_c5_xent_fp32_padded(orc):
+    w = synth.xent_c5()
+    V = w["N"]
+    g, rows, mean, counts = run_xent(w["x"], w["target"], V)
+    compare_xent(orc, w["x"], w["target"], V, g, rows, mean, counts, "c5")
+    # Special rows: the all-equal rows have loss log V, -inf entries get exactly 0.
+    assert np.allclose(rows[w["equal_rows"]], math.log(V), rtol=1e-5)
+    for r in w["half_inf_rows"]:
+        assert np.all(g[r, :V][np.isneginf(w["x"][r, :V])] == 0.0)
+
+
+# ----------------------------------------------------------------------------- shapes and layouts
+XENT_SHAPES = [
+    # (M, V, ld, dtype, ignore_frac, scale)
+    (1, 1, 1, "f32", 0.0, 1.0),
+    (3, 7, 7, "bf16", 0.0, 2.0),
+    (5, 8, 8, "bf16", 0.2, 2.0),
+    (17, 100, 103, "bf16", 0.2, 3.0),
+    (9, 1000, 1000, "f32", 0.1, 3.0),
+    (33, 4099, 4101, "bf16", 0.1, 2.0),
+    (64, 32005, 32005, "bf16", 0.1, 2.0),
+    (7, 32000, 32003, "f32", 0.0, 8.0),
+    (300, 5000, 5000, "bf16", 0.05, 1.0),
+    (12, 128256, 128256, "bf16", 0.25, 1.0),
+    (4, 131073, 131080, "bf16", 0.0, 1.0),
+    (6, 256000, 256064, "f32", 0.0, 8.0),
+    (3, 70001, 70001, "f32", 0.0, 4.0),
+]
+
+
+@pytest.mark.parametrize("M,V,ld,dtype,ign,scale", XENT_SHAPES,
+                         ids=[f"{m}x{v}ld{l}-{d}" for m, v, l, d, _, _ in XENT_SHAPES])
+def test_xent_shapes(orc, M, V, ld, dtype, ign, scale):
+    x = synth.random_rows(7000 + M + V, M, V, ld=ld, dtype=dtype, scale=scale)
+    t = synth.random_targets(8000 + M + V, M, V, ignore_frac=ign)
+    if M >= 2:
+        t[0], t[-1] = 0, V - 1  # first and last columns as targets
+        if ign == 0.0 and M > 2:
+            t[1] = -100
+    g, rows, mean, counts = run_xent(x, t, V)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"xent {M}x{V}")
+
+
+@pytest.mark.parametrize("shift", [1, 3, 5])
+def test_xent_unaligned_rows(orc, shift):
+    """Row starts off the 16-byte grid (a view that starts `shift` elements in)."""
+    M, V, ld = 11, 3001, 3011
+    x = synth.random_rows(9100 + shift, M, ld, dtype="bf16", scale=2.0)
+    t = synth.random_targets(9200 + shift, M, V, ignore_frac=0.2)
+    t[2] = V - 1
+    xd = to_device(x)
+    view = xd[:, shift:shift + V]
+    mean, rows, counts = xr.xent_fwd_bwd(view, to_device(t))
+    torch.cuda.synchronize()
+    g = to_host(xd)
+    sub = np.ascontiguousarray(x[:, shift:shift + V])
+    compare_xent(orc, sub, t, V, np.ascontiguousarray(g[:, shift:shift + V]), to_host(rows),
+                 float(mean.item()), to_host(counts), f"unaligned +{shift}")
+    # Elements outside the view are untouched.
+    assert np.array_equal(g[:, :shift], x[:, :shift])
+    assert np.array_equal(g[:, shift + V:], x[:, shift + V:])
+
+
+def test_xent_degenerate(orc):
+    V = 4096
+    x = synth.random_rows(9300, 6, V, dtype="bf16", scale=2.0)
+    # Every row ignored: n = 0, zero gradient and loss, mean NaN.
+    t = np.full(6, -100, dtype=np.int64)
+    g, rows, mean, counts = run_xent(x, t, V)
+    assert int(counts[0]) == 0 and math.isnan(mean)
+    assert np.all(g == 0) and np.all(rows == 0)
+    # Out-of-range targets are counted and their rows zeroed; they still count in n.
+    t = np.array([5, -3, V, 7, -100, V - 1], dtype=np.int64)
+    g, rows, mean, counts = run_xent(x, t, V)
+    assert int(counts[1]) == 2
+    assert np.all(g[[1, 2, 4]] == 0) and np.all(rows[[1, 2, 4]] == 0)
+    assert int(counts[0]) == orc.xent_count(t, V)[0]
+    # ignore_index inside [0, V) is compared first.
+    t = np.array([3, 3, 0, 9, 3, 1], dtype=np.int64)
+    g, rows, mean, counts = run_xent(x, t, V, ignore_index=3)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, "ignore_index=3", ignore_index=3)
+    # M = 0: mean NaN, counts zero, nothing else touched.
+    xd = torch.zeros((0, V), dtype=torch.bfloat16, device="cuda")
+    mean, rows, counts = xr.xent_fwd_bwd(xd, torch.zeros(0, dtype=torch.int64, device="cuda"))
+    assert math.isnan(mean.item()) and to_host(counts).tolist() == [0, 0, 0]
+
+
+def test_xent_neg_inf_chunks(orc):
+    """-inf runs covering whole workgroup chunks, and -inf in the first and last columns."""
+    M, V = 4, 200000
+    x = synth.random_rows(9400, M, V, dtype="f32", scale=4.0)
+    x[0, :150000] = -np.inf
+    x[1, 100:] = -np.inf
+    x[2, ::2] = -np.inf
+    x[3, 0] = -np.inf
+    x[3, -1] = -np.inf
+    t = np.array([160000, 5, 1, 17], dtype=np.int64)
+    for path in (0, 2, 3):
+        xr.set_option("path", path)
+        g, rows, mean, counts = run_xent(x, t, V)
+        compare_xent(orc, x, t, V, g, rows, mean, counts, f"-inf chunks path {path}")
+        assert np.all(g[np.isneginf(x)] == 0)
+
+
+# ----------------------------------------------------------------------------- paths
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_xent_all_paths_agree(orc, dtype):
+    M, V = 40, 50000
+    x = synth.random_rows(9500, M, V, dtype=dtype, scale=3.0)
+    t = synth.random_targets(9501, M, V, ignore_frac=0.1)
+    outs = {}
+    for name, path, split in (("auto", 0, 0), ("resident", 1, 0), ("split2", 2, 2),
+                              ("split5", 2, 5), ("stream", 3, 0)):
+        xr.set_option("path", path)
+        xr.set_option("split", split)
+        g, rows, mean, counts = run_xent(x, t, V)
+        compare_xent(orc, x, t, V, g, rows, mean, counts, f"{dtype} {name}")
+        outs[name] = g
+    xr.reset_options()
+
+
+@pytest.mark.parametrize("threads", [64, 128, 256, 512, 1024])
+def test_xent_workgroup_sizes(orc, threads):
+    M, V = 10, 8000
+    x = synth.random_rows(9600, M, V, dtype="bf16", scale=2.0)
+    t = synth.random_targets(9601, M, V, ignore_frac=0.2)
+    xr.set_option("threads", threads)
+    xr.set_option("split", 2 if threads == 64 else 0)
+    g, rows, mean, counts = run_xent(x, t, V)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"threads {threads}")
+
+
+@pytest.mark.parametrize("grid", [1, 2, -1])
+def test_xent_grid_shapes(orc, grid):
+    M, V = 700, 3000
+    x = synth.random_rows(9700, M, V, dtype="bf16", scale=2.0)
+    t = synth.random_targets(9701, M, V, ignore_frac=0.1)
+    xr.set_option("grid", grid)
+    g, rows, mean, counts = run_xent(x, t, V)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"grid {grid}")
+
+
+def test_xent_deterministic():
+    w = synth.xent_c3(M=600)
+    outs = [run_xent(w["x"], w["target"], w["N"]) for _ in range(3)]
+    for g, rows, mean, counts in outs[1:]:
+        assert np.array_equal(g, outs[0][0]) and np.array_equal(rows, outs[0][1])
+        assert mean == outs[0][2]
+
+
+def test_xent_small_batch_uses_split(orc):
+    p = xr.plan("xent", 8, 128256, torch.bfloat16)
+    assert p["path"] == "split" and p["split"] > 1
+    x = synth.random_rows(9800, 8, 128256, dtype="bf16", scale=1.0)
+    t = synth.random_targets(9801, 8, 128256)
+    g, rows, mean, counts = run_xent(x, t, 128256)
+    compare_xent(orc, x, t, 128256, g, rows, mean, counts, "small batch")
+
+
+# ----------------------------------------------------------------------------- softmax
+SOFTMAX_SHAPES = [(1, 1, "f32"), (3, 2, "bf16"), (5, 7, "bf16"), (19, 257, "f32"),
+                  (128, 1000, "f32"), (64, 4096, "bf16"), (8, 4099, "bf16"),
+                  (6, 33333, "f32"), (4, 65536, "bf16"), (3, 70000, "f32"), (2, 300000, "bf16")]
+
+
+@pytest.mark.parametrize("M,N,dtype", SOFTMAX_SHAPES, ids=[f"{m}x{n}-{d}" for m, n, d in SOFTMAX_SHAPES])
+def test_softmax_shapes(orc, M, N, dtype):
+    x = synth.random_rows(10000 + N, M, N, dtype=dtype, scale=3.0)
+    dy = synth.random_rows(11000 + N, M, N, dtype=dtype, scale=1.0)
+    y = xr.softmax_fwd(to_device(x))
+    y_h = to_host(y)
+    check_output(y_h, orc.softmax_fwd(x), f"softmax {M}x{N}")
+    dx = to_host(xr.softmax_bwd(y, to_device(dy)))
+    check_output(dx, orc.softmax_bwd(y_h, dy), f"softmax bwd {M}x{N}")
+
+
+def test_softmax_in_place_and_strides(orc):
+    M, N, ld = 9, 3000, 3016
+    x = synth.random_rows(12000, M, N, ld=ld, dtype="bf16", scale=3.0)
+    want = orc.softmax_fwd(x, n_cols=N)
+    xd = to_device(x)
+    xr.softmax_fwd(xd[:, :N], xd[:, :N])  # exactly in place
+    got = to_host(xd)
+    check_bf16(got[:, :N], want, "in place")
+    assert np.array_equal(got[:, N:], x[:, N:]), "padding changed"
+    # Output with a different row stride and alignment than the input (stream path).
+    out = torch.full((M, N + 5), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xr.softmax_fwd(to_device(x)[:, :N], out[:, 1:N + 1])
+    got = to_host(out)
+    check_bf16(got[:, 1:N + 1], want, "misaligned output")
+    assert np.all(np.isnan(widen(got[:, 0]))) and np.all(np.isnan(widen(got[:, N + 1:])))
+
+
+def test_softmax_bwd_aliases(orc):
+    M, N = 7, 5000
+    y = synth.random_rows(12100, M, N, dtype="f32", scale=0.01)
+    dy = synth.random_rows(12101, M, N, dtype="f32", scale=1.0)
+    want = orc.softmax_bwd(y, dy)
+    yd, dyd = to_device(y), to_device(dy)
+    xr.softmax_bwd(yd, dyd, dyd)  # dx == dy
+    check_fp32(to_host(dyd), want, "dx == dy")
+    yd, dyd = to_device(y), to_device(dy)
+    xr.softmax_bwd(yd, dyd, yd)  # dx == y
+    check_fp32(to_host(yd), want, "dx == y")
+
+
+def test_softmax_neg_inf(orc):
+    x = synth.random_rows(12200, 5, 3000, dtype="f32", scale=3.0)
+    x[0, :2999] = -np.inf
+    x[1, ::3] = -np.inf
+    y = to_host(xr.softmax_fwd(to_device(x)))
+    check_fp32(y, orc.softmax_fwd(x), "softmax -inf")
+    assert np.all(y[np.isneginf(x)] == 0)
+
+
+def test_partial_overlap_is_rejected():
+    x = torch.zeros((4, 100), dtype=torch.float32, device="cuda")
+    with pytest.raises(xr.XrError, match="overlap"):
+        xr.softmax_fwd(x[:, :50], x[:, 10:60])
