@@ -41,14 +41,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: set HIPCC or install ROCm")
 
 
-def build(verbose: bool = False, output: str = LIBRARY) -> str:
+def build(verbose: bool = False, output: str = LIBRARY, defines=()) -> str:
     """Compile every source and link libxr.so; always rebuilds. Returns the library path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="xr_build_") as tmp:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIPCC_FLAGS, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             res = subprocess.run(cmd, capture_output=True, text=True)

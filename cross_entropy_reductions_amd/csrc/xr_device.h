@@ -79,8 +79,14 @@ template <> struct OutVec<kBF16> {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
 // Cache-policy bits of the buffer instructions: 1 = sc0, 2 = nt, 16 = sc1.
-constexpr int kLoadPolicy = 2;
-constexpr int kStorePolicy = 2;
+#ifndef XR_LOAD_POLICY
+#define XR_LOAD_POLICY 2
+#endif
+#ifndef XR_STORE_POLICY
+#define XR_STORE_POLICY 2
+#endif
+constexpr int kLoadPolicy = XR_LOAD_POLICY;
+constexpr int kStorePolicy = XR_STORE_POLICY;
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -270,14 +276,16 @@ template <int D> struct Chunk {
     toff = (uint32_t)__builtin_amdgcn_readfirstlane(tail * 16);
   }
 
-  // Resource for the slot starting at chunk vector s0 < nvec: lane l addresses vector
-  // s0 + l at byte 16 l, and lanes at or past the chunk's end fall outside num_records
-  // (loads give zeros, stores are dropped). Built in scalar registers at each use (a plain
-  // scalar subtraction: a saturating one would be selected as a vector instruction and
-  // make the compiler wrap every access in a loop over distinct resources).
+  // Resource for the slot starting at chunk vector s0: lane l addresses vector s0 + l at
+  // byte 16 l, and lanes at or past the chunk's end fall outside num_records (loads give
+  // zeros without touching memory, stores are dropped). Built in scalar registers at each
+  // use; the clamp is a signed max (an unsigned saturating subtraction would be selected
+  // as a vector instruction and make the compiler wrap every access in a loop over
+  // distinct resources).
   __device__ __forceinline__ Rsrc slot(int s0) const {
-    const uint32_t skip = (uint32_t)s0 * 16u, total = (uint32_t)nvec * 16u;
-    return make_rsrc(reinterpret_cast<const void*>(base + skip), total - skip);
+    const int rem = (nvec - s0) * 16;  // signed: max() below is a scalar instruction
+    return make_rsrc(reinterpret_cast<const void*>(base + (uint32_t)s0 * 16u),
+                     (uint32_t)(rem > 0 ? rem : 0));
   }
 };
 

@@ -11,6 +11,9 @@
 //                    (Liger-Kernel cross_entropy.py page, liger_cross_entropy_kernel steps 1-6,
 //                    LigerCrossEntropyFunction.forward)
 //
+// Register budget: every row kernel is compiled for at least 4 waves per SIMD (128 VGPRs),
+// so a 1024-thread workgroup fits a compute unit and smaller ones can share it.
+//
 // How, on MI355X:
 //   * Row-resident kernels keep a whole row (or, for split rows, one chunk of it) in
 //     registers as raw 16-byte vectors, so the logits are read from HBM exactly once:
@@ -53,35 +56,23 @@ __device__ __forceinline__ float pair_m(uint64_t w) { return as_f32((uint32_t)w)
 __device__ __forceinline__ float pair_d(uint64_t w) { return as_f32((uint32_t)(w >> 32)); }
 
 // Issue the loads of a chunk: slot k of thread tid holds chunk vector k*THREADS + tid.
-// Slots wholly past the chunk are not loaded; lanes past its end read zeros (range check).
+// Every slot is loaded, in slot order and without branches (so the compiler can wait for
+// each slot's data separately); lanes past the chunk's end read zeros without a memory
+// access, and the consumers below never look at them.
 template <int D, int THREADS, int VPT>
 __device__ __forceinline__ void issue_loads(u32x4 (&v)[VPT], const Chunk<D>& c) {
   const uint32_t off = threadIdx.x * 16u;
 #pragma unroll
-  for (int k = 0; k < VPT; ++k)
-    if (k * THREADS < c.nvec) v[k] = buf_load(c.slot(k * THREADS), off);
+  for (int k = 0; k < VPT; ++k) v[k] = buf_load(c.slot(k * THREADS), off);
 }
 
-// Before a chunk is used: every element outside the row becomes `fill` (-inf for the
-// softmax rows: the identity of max and a zero term of the sum; 0 for the operands of the
-// softmax-backward dot product). Only slots at the chunk's end and the thread holding a
-// partial first / last vector do any work; every slot index is a compile-time constant.
-template <int D, int THREADS, int VPT>
-__device__ __forceinline__ void fixup(u32x4 (&v)[VPT], const Chunk<D>& c, uint32_t fill) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int s0 = k * THREADS;
-    if (s0 >= c.nvec) {
-      v[k] = splat(fill);
-    } else if (s0 + THREADS > c.nvec) {
-      if (s0 + tid >= c.nvec) v[k] = splat(fill);
-    }
-    if (c.head >= s0 && c.head < s0 + THREADS && tid == c.head - s0)
-      v[k] = mask_vec<D>(v[k], c.h0, c.h1, fill);
-    if (c.tail >= s0 && c.tail < s0 + THREADS && tid == c.tail - s0)
-      v[k] = mask_vec<D>(v[k], c.t0, c.t1, fill);
-  }
+// How slot k relates to a chunk of nvec vectors (workgroup-uniform): every lane inside,
+// some lanes inside (the last slot), or none.
+enum SlotKind { kSlotFull, kSlotPart, kSlotNone };
+template <int THREADS>
+__device__ __forceinline__ SlotKind slot_kind(int k, int nvec) {
+  const int s0 = k * THREADS;
+  return s0 + THREADS <= nvec ? kSlotFull : (s0 < nvec ? kSlotPart : kSlotNone);
 }
 
 // Store slot k of a chunk with one 16-byte store per lane. Lanes past the chunk's end are
@@ -90,7 +81,6 @@ __device__ __forceinline__ void fixup(u32x4 (&v)[VPT], const Chunk<D>& c, uint32
 template <int D, int THREADS>
 __device__ __forceinline__ void store_slot(const Chunk<D>& c, int k, const u32x4& bits) {
   const int s0 = k * THREADS;
-  if (s0 >= c.nvec) return;
   uint32_t off = threadIdx.x * 16u;
   const bool slot_has_partial = (c.head >= s0 && c.head < s0 + THREADS) ||
                                 (c.tail >= s0 && c.tail < s0 + THREADS);
@@ -122,46 +112,86 @@ __device__ __forceinline__ void store_partials(const Chunk<D>& out, const Chunk<
   }
 }
 
-// Compiler barrier on the register-resident vectors: each pass re-widens the bf16 / fp32
-// bits it needs instead of keeping the widened values of an earlier pass alive, which
-// would double or triple the registers a row takes. Placed after the pass that first
-// waits for the loads, so it never delays a load.
+// Compiler barriers on the register-resident vectors. Each pass widens the bf16 / fp32 bits
+// of one slot right before using them: left alone, the compiler widens a whole row at once
+// (or keeps an earlier pass's widened values), which doubles or triples the registers a row
+// takes. pin() makes one slot opaque at its point of use; being volatile, the pins also keep
+// the slots in order with the memory operations between them.
+__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
+// Per-slot pins matter for bf16, whose elements are widened by extra instructions; fp32
+// elements are used as they are, and pinning copies of them only adds register moves.
+template <int D> __device__ __forceinline__ void pin_slot(u32x4& x) {
+  if (D == kBF16) pin(x);
+}
 template <int VPT> __device__ __forceinline__ void reg_barrier(u32x4 (&v)[VPT]) {
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(v[k]));
+  for (int k = 0; k < VPT; ++k) pin(v[k]);
 }
 
-template <int D, int VPT> __device__ __forceinline__ float thread_max(const u32x4 (&v)[VPT]) {
+// Slot k of this thread as the reductions must see it: lanes past the chunk's end and the
+// out-of-row elements of the partial first / last vectors hold `fill` (-inf for softmax
+// rows: the identity of max and a zero term of the sum; 0 for the softmax-backward dot
+// product). The registers themselves are left alone (the output pass needs no masking),
+// and every test is workgroup-uniform except inside the rare slots that need one.
+template <int D, int THREADS>
+__device__ __forceinline__ u32x4 masked_slot(u32x4 x, int k, const Chunk<D>& c, uint32_t fill) {
+  pin_slot<D>(x);
+  const int s0 = k * THREADS;
+  const int tid = threadIdx.x;
+  if (s0 + THREADS > c.nvec) {
+    asm volatile("" ::: "memory");  // a real branch: no speculated wait for the load
+    if (s0 + tid >= c.nvec) x = splat(fill);
+  }
+  if (c.head >= s0 && c.head < s0 + THREADS) {
+    asm volatile("" ::: "memory");
+    if (tid == c.head - s0) x = mask_vec<D>(x, c.h0, c.h1, fill);
+  }
+  if (c.tail >= s0 && c.tail < s0 + THREADS) {
+    asm volatile("" ::: "memory");
+    if (tid == c.tail - s0) x = mask_vec<D>(x, c.t0, c.t1, fill);
+  }
+  return x;
+}
+
+// Maximum over the chunk elements this thread holds (-inf if none).
+template <int D, int THREADS, int VPT>
+__device__ __forceinline__ float thread_max(const u32x4 (&v)[VPT], const Chunk<D>& c) {
   constexpr int EPV = Elt<D>::kPerVec;
   float a = kNegInf, b = kNegInf;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
+    if (slot_kind<THREADS>(k, c.nvec) == kSlotNone) continue;
+    const u32x4 x = masked_slot<D, THREADS>(v[k], k, c, Elt<D>::kNegInfWord);
 #pragma unroll
     for (int e = 0; e < EPV; e += 2) {
-      a = fmaxf(a, elem<D>(v[k], e));
-      b = fmaxf(b, elem<D>(v[k], e + 1));
+      a = fmaxf(a, elem<D>(x, e));
+      b = fmaxf(b, elem<D>(x, e + 1));
     }
   }
   return fmaxf(a, b);
 }
 
-// sum_j exp(x_j - m), computed as exp2(x*log2e - m*log2e), four partial sums.
-template <int D, int VPT>
-__device__ __forceinline__ float thread_sum_exp(const u32x4 (&v)[VPT], float mL) {
+// sum_j exp(x_j - m) over the chunk elements this thread holds, computed as
+// exp2(x*log2e - m*log2e), four partial sums.
+template <int D, int THREADS, int VPT>
+__device__ __forceinline__ float thread_sum_exp(const u32x4 (&v)[VPT], const Chunk<D>& c, float mL) {
   constexpr int EPV = Elt<D>::kPerVec;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
+    if (slot_kind<THREADS>(k, c.nvec) == kSlotNone) continue;
+    const u32x4 x = masked_slot<D, THREADS>(v[k], k, c, Elt<D>::kNegInfWord);
 #pragma unroll
     for (int e = 0; e < EPV; ++e)
-      s[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(v[k], e), kLog2e, -mL));
+      s[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(x, e), kLog2e, -mL));
   }
   return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 // exp2(x*log2e - coff) for every element of one slot, in the element type.
 template <int D>
-__device__ __forceinline__ u32x4 exp_slot(const u32x4& v, float coff) {
+__device__ __forceinline__ u32x4 exp_slot(u32x4 v, float coff) {
+  pin_slot<D>(v);
   OutVec<D> o;
 #pragma unroll
   for (int e = 0; e < Elt<D>::kPerVec; ++e)
@@ -223,7 +253,7 @@ __global__ __launch_bounds__(kScanThreads) void xent_mean_kernel(const float* __
 
 // Row-resident fused cross-entropy; S workgroups per row (S == 1: the whole row).
 template <int D, int THREADS, int VPT>
-__global__ __launch_bounds__(THREADS) void xent_rows_kernel(XentParams p) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void xent_rows_kernel(XentParams p) {
   constexpr int EPV = Elt<D>::kPerVec;
   constexpr int NW = THREADS / kWave;
   __shared__ float red[2][NW];
@@ -269,15 +299,13 @@ __global__ __launch_bounds__(THREADS) void xent_rows_kernel(XentParams p) {
       for (int k = 0; k < VPT; ++k) v[k] = splat(Elt<D>::kNegInfWord);
       coff = __builtin_inff();
     } else {
-      fixup<D, THREADS, VPT>(v, c, Elt<D>::kNegInfWord);
-
       // Chunk maximum.
-      m = block_reduce<THREADS>(thread_max<D, VPT>(v), OpMax(), red[0]);
+      m = block_reduce<THREADS>(thread_max<D, THREADS, VPT>(v, c), OpMax(), red[0]);
       reg_barrier(v);
 
       // sum exp(x - m) over the chunk; an all -inf chunk contributes (-inf, 0).
       d = 0.f;
-      if (m != kNegInf) d = thread_sum_exp<D, VPT>(v, m * kLog2e);
+      if (m != kNegInf) d = thread_sum_exp<D, THREADS, VPT>(v, c, m * kLog2e);
       d = block_reduce<THREADS>(d, OpAdd(), red[1]);
       if (m == kNegInf) d = 0.f;
       reg_barrier(v);
@@ -330,12 +358,17 @@ __global__ __launch_bounds__(THREADS) void xent_rows_kernel(XentParams p) {
     }
 
     // Output pass, with the next row's loads issued into each slot once it is written out.
-    const Chunk<D> cn(row_ptr(pf ? rn : r), p.V, lo, p.chunk_vecs);
-    const uint32_t off = tid * 16u;
+    if (pf) {
+      const Chunk<D> cn(row_ptr(rn), p.V, lo, p.chunk_vecs);
+      const uint32_t off = tid * 16u;
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
-      if (pf && k * THREADS < cn.nvec) v[k] = buf_load(cn.slot(k * THREADS), off);
+      for (int k = 0; k < VPT; ++k) {
+        store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
+        v[k] = buf_load(cn.slot(k * THREADS), off);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
     }
     store_partials<D, THREADS>(c, c, [coff, ignored](float x) {
       return ignored ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
@@ -396,7 +429,7 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams 
 
 // ============================================================================ softmax forward
 template <int D, int THREADS, int VPT>
-__global__ __launch_bounds__(THREADS) void softmax_fwd_kernel(SoftmaxFwdParams p) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_fwd_kernel(SoftmaxFwdParams p) {
   constexpr int NW = THREADS / kWave;
   __shared__ float red[2][NW];
   const int64_t G = gridDim.x;
@@ -409,11 +442,11 @@ __global__ __launch_bounds__(THREADS) void softmax_fwd_kernel(SoftmaxFwdParams p
     const int64_t rn = r + G;
     const Chunk<D> cx(p.x + r * p.ldx_bytes, p.N, 0, cv);
     const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);  // same lead as cx (host-checked)
-    fixup<D, THREADS, VPT>(v, cx, Elt<D>::kNegInfWord);
-    const float m = block_reduce<THREADS>(thread_max<D, VPT>(v), OpMax(), red[0]);
+    const float m = block_reduce<THREADS>(thread_max<D, THREADS, VPT>(v, cx), OpMax(), red[0]);
     reg_barrier(v);
     const float mL = m * kLog2e;
-    const float d = block_reduce<THREADS>(thread_sum_exp<D, VPT>(v, mL), OpAdd(), red[1]);
+    const float d =
+        block_reduce<THREADS>(thread_sum_exp<D, THREADS, VPT>(v, cx, mL), OpAdd(), red[1]);
     reg_barrier(v);
     const float coff = mL + log2f(d);
     if (rn < p.M) {
@@ -422,7 +455,7 @@ __global__ __launch_bounds__(THREADS) void softmax_fwd_kernel(SoftmaxFwdParams p
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         store_slot<D, THREADS>(cy, k, exp_slot<D>(v[k], coff));
-        if (k * THREADS < cn.nvec) v[k] = buf_load(cn.slot(k * THREADS), off);
+        v[k] = buf_load(cn.slot(k * THREADS), off);
       }
     } else {
 #pragma unroll
@@ -467,7 +500,7 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
 
 // ============================================================================ softmax backward
 template <int D, int THREADS, int VPT>
-__global__ __launch_bounds__(THREADS) void softmax_bwd_kernel(SoftmaxBwdParams p) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_bwd_kernel(SoftmaxBwdParams p) {
   constexpr int EPV = Elt<D>::kPerVec;
   constexpr int NW = THREADS / kWave;
   __shared__ float red[2][NW];
@@ -486,15 +519,16 @@ __global__ __launch_bounds__(THREADS) void softmax_bwd_kernel(SoftmaxBwdParams p
     // y, dy and dx rows share their alignment (host-checked), hence their vector layout.
     const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);
     const Chunk<D> cx(p.dx + r * p.lddx_bytes, p.N, 0, cv);
-    // Out-of-row elements of both operands are 0, so they add nothing to the dot product.
-    fixup<D, THREADS, VPT>(vy, cy, 0u);
-    fixup<D, THREADS, VPT>(vd, cy, 0u);
+    // Out-of-row elements of both operands count as 0: they add nothing to the dot product.
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
+      if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) continue;
+      const u32x4 a = masked_slot<D, THREADS>(vy[k], k, cy, 0u);
+      const u32x4 b = masked_slot<D, THREADS>(vd[k], k, cy, 0u);
 #pragma unroll
       for (int e = 0; e < EPV; ++e)
-        s[e & 3] = __builtin_fmaf(elem<D>(vy[k], e), elem<D>(vd[k], e), s[e & 3]);
+        s[e & 3] = __builtin_fmaf(elem<D>(a, e), elem<D>(b, e), s[e & 3]);
     }
     const float dot = block_reduce<THREADS>((s[0] + s[1]) + (s[2] + s[3]), OpAdd(), red[buf]);
     buf ^= 1;
@@ -507,13 +541,13 @@ __global__ __launch_bounds__(THREADS) void softmax_bwd_kernel(SoftmaxBwdParams p
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       OutVec<D> o;
+      u32x4 a = vy[k], b = vd[k];
+      pin_slot<D>(a);
+      pin_slot<D>(b);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float a = elem<D>(vy[k], e), b = elem<D>(vd[k], e);
-        o.v[e] = a * (b - dot);
-      }
+      for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
       store_slot<D, THREADS>(cx, k, o.bits());
-      if (pf && k * THREADS < cyn.nvec) {
+      if (pf) {
         vy[k] = buf_load(cyn.slot(k * THREADS), off);
         vd[k] = buf_load(cdn.slot(k * THREADS), off);
       }
