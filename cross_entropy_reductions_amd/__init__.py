@@ -64,7 +64,7 @@ F32, BF16 = 0, 1
 OK = 0
 PATHS = {1: "resident", 2: "split", 3: "stream"}
 OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2}
-OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4}
+OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4, "load_policy": 5}
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 

@@ -11,13 +11,14 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libxr.so")
-SOURCES = ["xr_kernels.hip", "xr_api.cpp"]
+SOURCES = ["xr_xent.hip", "xr_softmax.hip", "xr_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -45,8 +46,7 @@ def build(verbose: bool = False, output: str = LIBRARY, defines=()) -> str:
     """Compile every source and link libxr.so; always rebuilds. Returns the library path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="xr_build_") as tmp:
-        objs = []
-        for src in SOURCES:
+        def compile_one(src):
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             cmd = [cc, *HIPCC_FLAGS, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src),
                    "-o", obj]
@@ -55,7 +55,10 @@ def build(verbose: bool = False, output: str = LIBRARY, defines=()) -> str:
             res = subprocess.run(cmd, capture_output=True, text=True)
             if res.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
-            objs.append(obj)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
         tmp_out = output + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out]
         res = subprocess.run(cmd, capture_output=True, text=True)

@@ -23,7 +23,7 @@ constexpr int64_t kMinChunkVecs = 256;
 
 // ----------------------------------------------------------------------------- options
 struct Options {
-  int64_t path = 0, split = 0, threads = 0, grid = 0;
+  int64_t path = 0, split = 0, threads = 0, grid = 0, load_policy = 0;
 };
 Options g_opt;
 
@@ -195,17 +195,24 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   p.shape = *sh;
   p.S = (int)S;
   p.chunk_vecs = chunk;
-  p.kernel = op == 0 ? softmax_fwd_kernel_ptr(dt, *sh)
-                     : op == 1 ? softmax_bwd_kernel_ptr(dt, *sh) : xent_rows_kernel_ptr(dt, *sh);
+  // Row loads: non-temporal, except for whole rows of 128 KB and more, which measured
+  // faster with the default policy (the cross-entropy over a 128256-wide bf16 vocabulary).
+  bool nt_loads = !(S == 1 && nvm * 16 >= (128 << 10));
+  if (g_opt.load_policy) nt_loads = g_opt.load_policy == 2;
+  p.kernel = op == 0 ? softmax_fwd_kernel_ptr(dt, *sh, nt_loads)
+                     : op == 1 ? softmax_bwd_kernel_ptr(dt, *sh, nt_loads)
+                               : xent_rows_kernel_ptr(dt, *sh, nt_loads);
   if (!p.kernel) return XR_ERR_SHAPE;
   const int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
   if (per_cu <= 0) return XR_ERR_DEVICE;
   const int64_t resident = (int64_t)di.cus * per_cu;
   if (S == 1) {
+    // One workgroup per row by default (the hardware dispatcher balances the rows and
+    // starts a row as soon as a compute unit frees up: measured faster than a persistent
+    // grid); a persistent grid of `grid` workgroups per compute unit on request.
     p.path = kPathResident;
-    int64_t g = resident;
+    int64_t g = M;
     if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
-    if (g_opt.grid < 0) g = M;
     p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
   } else {
     p.path = kPathSplit;
@@ -289,6 +296,10 @@ xr_status_t xr_set_option(xr_option_t option, int64_t value) {
     case XR_OPT_GRID:
       if (value < -1 || value > 64) return XR_ERR_OPTION;
       g_opt.grid = value;
+      return XR_OK;
+    case XR_OPT_LOAD_POLICY:
+      if (value < 0 || value > 2) return XR_ERR_OPTION;
+      g_opt.load_policy = value;
       return XR_OK;
   }
   return XR_ERR_OPTION;

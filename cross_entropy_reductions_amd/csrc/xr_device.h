@@ -78,22 +78,22 @@ template <> struct OutVec<kBF16> {
 // The offset is always passed as the VGPR operand (soffset = 0) so it is range-checked.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
-// Cache-policy bits of the buffer instructions: 1 = sc0, 2 = nt, 16 = sc1.
-#ifndef XR_LOAD_POLICY
-#define XR_LOAD_POLICY 2
-#endif
+// Cache-policy bits of the buffer instructions: 1 = sc0, 2 = nt, 16 = sc1. Row stores are
+// non-temporal (nothing re-reads them); the load policy is a kernel template parameter,
+// chosen per launch (see the plan in xr_api.cpp).
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyNT = 2;
 #ifndef XR_STORE_POLICY
 #define XR_STORE_POLICY 2
 #endif
-constexpr int kLoadPolicy = XR_LOAD_POLICY;
 constexpr int kStorePolicy = XR_STORE_POLICY;
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kRsrcWord3);
 }
-__device__ __forceinline__ u32x4 buf_load(Rsrc r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadPolicy);
+template <int LP> __device__ __forceinline__ u32x4 buf_load(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, LP);
 }
 __device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, const u32x4& v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStorePolicy);
@@ -204,6 +204,45 @@ __device__ __forceinline__ float block_reduce(float x, Op op, float* slots) {
   float r = slots[0];
 #pragma unroll
   for (int w = 1; w < THREADS / kWave; ++w) r = op(r, slots[w]);
+  return r;
+}
+
+// (m, d) statistics of a set of elements: m their maximum, d = sum exp(x - m). Two sets
+// combine by the online-softmax rule; a set whose maximum is -inf (empty, or all -inf) is
+// the identity. The combine is commutative bit for bit (fp add is), so a butterfly leaves
+// the same pair on every lane.
+struct Stats {
+  float m, d;
+};
+__device__ __forceinline__ Stats combine(Stats a, Stats b) {
+  const float mx = fmaxf(a.m, b.m);
+  if (mx == -__builtin_inff()) return {mx, 0.f};
+  return {mx, a.d * __builtin_amdgcn_exp2f((a.m - mx) * kLog2e) +
+                  b.d * __builtin_amdgcn_exp2f((b.m - mx) * kLog2e)};
+}
+template <int CTRL> __device__ __forceinline__ Stats dpp_stats(Stats s) {
+  return {dpp<CTRL>(s.m), dpp<CTRL>(s.d)};
+}
+__device__ __forceinline__ Stats wave_reduce_stats(Stats s) {
+  s = combine(s, dpp_stats<0xB1>(s));
+  s = combine(s, dpp_stats<0x4E>(s));
+  s = combine(s, dpp_stats<0x141>(s));
+  s = combine(s, dpp_stats<0x140>(s));
+  s = combine(s, {swizzle_xor16(s.m), swizzle_xor16(s.d)});
+  return combine({readlane(s.m, 0), readlane(s.d, 0)}, {readlane(s.m, 32), readlane(s.d, 32)});
+}
+// Workgroup combine through LDS (one slot per wave, read back in wave order). Callers
+// alternate two slot buffers between consecutive calls, so one barrier per call suffices.
+template <int THREADS>
+__device__ __forceinline__ Stats block_reduce_stats(Stats s, float2* slots) {
+  s = wave_reduce_stats(s);
+  if (THREADS == kWave) return s;
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) slots[wave] = make_float2(s.m, s.d);
+  __syncthreads();
+  Stats r = {slots[0].x, slots[0].y};
+#pragma unroll
+  for (int w = 1; w < THREADS / kWave; ++w) r = combine(r, {slots[w].x, slots[w].y});
   return r;
 }
 

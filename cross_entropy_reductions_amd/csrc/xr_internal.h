@@ -56,10 +56,11 @@ struct Shape {
   int vpt;
 };
 
-// Kernel lookup (nullptr when the (dtype, shape) pair is not instantiated).
-const void* xent_rows_kernel_ptr(int dtype, Shape s);
-const void* softmax_fwd_kernel_ptr(int dtype, Shape s);
-const void* softmax_bwd_kernel_ptr(int dtype, Shape s);
+// Kernel lookup (nullptr when the (dtype, shape) pair is not instantiated); nt_loads selects
+// the instantiation whose row loads carry the non-temporal hint.
+const void* xent_rows_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* xent_stream_kernel_ptr(int dtype);
 const void* softmax_fwd_stream_kernel_ptr(int dtype);
 const void* softmax_bwd_stream_kernel_ptr(int dtype);

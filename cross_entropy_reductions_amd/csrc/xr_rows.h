@@ -1,0 +1,185 @@
+// xr_rows.h -- building blocks of the row kernels (included by the kernel sources only).
+#pragma once
+
+#include "xr_device.h"
+#include "xr_internal.h"
+
+namespace xr {
+
+
+inline constexpr float kNegInf = -__builtin_inff();
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ u32x4 splat(uint32_t w) { return (u32x4){w, w, w, w}; }
+
+__device__ __forceinline__ uint64_t pack_pair(float m, float d) {
+  return (uint64_t)as_u32(m) | ((uint64_t)as_u32(d) << 32);
+}
+__device__ __forceinline__ float pair_m(uint64_t w) { return as_f32((uint32_t)w); }
+__device__ __forceinline__ float pair_d(uint64_t w) { return as_f32((uint32_t)(w >> 32)); }
+
+// Issue the loads of a chunk: slot k of thread tid holds chunk vector k*THREADS + tid.
+// Every slot is loaded, in slot order and without branches (so the compiler can wait for
+// each slot's data separately); lanes past the chunk's end read zeros without a memory
+// access, and the consumers below never look at them.
+template <int D, int THREADS, int VPT, int LP>
+__device__ __forceinline__ void issue_loads(u32x4 (&v)[VPT], const Chunk<D>& c) {
+  const uint32_t off = threadIdx.x * 16u;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) v[k] = buf_load<LP>(c.slot(k * THREADS), off);
+}
+
+// How slot k relates to a chunk of nvec vectors (workgroup-uniform): every lane inside,
+// some lanes inside (the last slot), or none.
+enum SlotKind { kSlotFull, kSlotPart, kSlotNone };
+template <int THREADS>
+__device__ __forceinline__ SlotKind slot_kind(int k, int nvec) {
+  const int s0 = k * THREADS;
+  return s0 + THREADS <= nvec ? kSlotFull : (s0 < nvec ? kSlotPart : kSlotNone);
+}
+
+// Store slot k of a chunk with one 16-byte store per lane. Lanes past the chunk's end are
+// dropped by the range check; the lane holding a partial first / last vector is pointed
+// outside the resource, so it stores nothing here (see store_partials).
+template <int D, int THREADS>
+__device__ __forceinline__ void store_slot(const Chunk<D>& c, int k, const u32x4& bits) {
+  const int s0 = k * THREADS;
+  uint32_t off = threadIdx.x * 16u;
+  const bool slot_has_partial = (c.head >= s0 && c.head < s0 + THREADS) ||
+                                (c.tail >= s0 && c.tail < s0 + THREADS);
+  if (slot_has_partial) {
+    const int vi = s0 + (int)threadIdx.x;
+    if (vi == c.head || vi == c.tail) off = kOffNone;
+  }
+  buf_store(c.slot(s0), off, bits);
+}
+
+// The in-row elements of the partial first / last vectors, which store_slot skipped:
+// out[j] = f(x[j]) for the elements of the row inside those vectors. The inputs are
+// re-read from `in` (16 bytes each; the elements have not been written yet, since only
+// this workgroup writes them), by the thread that holds the vector.
+template <int D, int THREADS, class F>
+__device__ __forceinline__ void store_partials(const Chunk<D>& out, const Chunk<D>& in, F f) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int vi = q == 0 ? out.head : out.tail;
+    if (vi < 0 || tid != vi % THREADS) continue;
+    const uint32_t off = q == 0 ? out.hoff : out.toff;
+    const int e0 = q == 0 ? out.h0 : out.t0, e1 = q == 0 ? out.h1 : out.t1;
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(in.rsrc, (int)off, 0, 0);
+    OutVec<D> o;
+#pragma unroll
+    for (int e = 0; e < Elt<D>::kPerVec; ++e) o.v[e] = f(elem<D>(x, e));
+    store_partial<D>(out.rsrc, off, o.bits(), e0, e1);
+  }
+}
+
+// Compiler barriers on the register-resident vectors. Each pass widens the bf16 / fp32 bits
+// of one slot right before using them: left alone, the compiler widens a whole row at once
+// (or keeps an earlier pass's widened values), which doubles or triples the registers a row
+// takes. pin() makes one slot opaque at its point of use; being volatile, the pins also keep
+// the slots in order with the memory operations between them.
+__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
+// Per-slot pins matter for bf16, whose elements are widened by extra instructions; fp32
+// elements are used as they are, and pinning copies of them only adds register moves.
+template <int D> __device__ __forceinline__ void pin_slot(u32x4& x) {
+  if (D == kBF16) pin(x);
+}
+template <int VPT> __device__ __forceinline__ void reg_barrier(u32x4 (&v)[VPT]) {
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) pin(v[k]);
+}
+
+// Slot k of this thread as the reductions must see it: lanes past the chunk's end and the
+// out-of-row elements of the partial first / last vectors hold `fill` (-inf for softmax
+// rows: the identity of max and a zero term of the sum; 0 for the softmax-backward dot
+// product). The registers themselves are left alone (the output pass needs no masking),
+// and every test is workgroup-uniform except inside the rare slots that need one.
+template <int D, int THREADS>
+__device__ __forceinline__ u32x4 masked_slot(u32x4 x, int k, const Chunk<D>& c, uint32_t fill) {
+  pin_slot<D>(x);
+  const int s0 = k * THREADS;
+  const int tid = threadIdx.x;
+  if (s0 + THREADS > c.nvec) {
+    asm volatile("" ::: "memory");  // a real branch: no speculated wait for the load
+    if (s0 + tid >= c.nvec) x = splat(fill);
+  }
+  if (c.head >= s0 && c.head < s0 + THREADS) {
+    asm volatile("" ::: "memory");
+    if (tid == c.head - s0) x = mask_vec<D>(x, c.h0, c.h1, fill);
+  }
+  if (c.tail >= s0 && c.tail < s0 + THREADS) {
+    asm volatile("" ::: "memory");
+    if (tid == c.tail - s0) x = mask_vec<D>(x, c.t0, c.t1, fill);
+  }
+  return x;
+}
+
+// Maximum over the chunk elements this thread holds (-inf if none).
+template <int D, int THREADS, int VPT>
+__device__ __forceinline__ float thread_max(const u32x4 (&v)[VPT], const Chunk<D>& c) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  float a = kNegInf, b = kNegInf;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (slot_kind<THREADS>(k, c.nvec) == kSlotNone) continue;
+    const u32x4 x = masked_slot<D, THREADS>(v[k], k, c, Elt<D>::kNegInfWord);
+#pragma unroll
+    for (int e = 0; e < EPV; e += 2) {
+      a = fmaxf(a, elem<D>(x, e));
+      b = fmaxf(b, elem<D>(x, e + 1));
+    }
+  }
+  return fmaxf(a, b);
+}
+
+// sum_j exp(x_j - m) over the chunk elements this thread holds, computed as
+// exp2(x*log2e - m*log2e), four partial sums.
+template <int D, int THREADS, int VPT>
+__device__ __forceinline__ float thread_sum_exp(const u32x4 (&v)[VPT], const Chunk<D>& c, float mL) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (slot_kind<THREADS>(k, c.nvec) == kSlotNone) continue;
+    const u32x4 x = masked_slot<D, THREADS>(v[k], k, c, Elt<D>::kNegInfWord);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e)
+      s[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(x, e), kLog2e, -mL));
+  }
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+// This thread's (m, d) over its chunk elements: its own maximum, then the sum of
+// exp(x - m) with that maximum. No workgroup barrier sits between the two passes, so each
+// wave streams through its slots as their loads land; the workgroup combines the pairs once.
+template <int D, int THREADS, int VPT>
+__device__ __forceinline__ Stats thread_stats(u32x4 (&v)[VPT], const Chunk<D>& c) {
+  const float m = thread_max<D, THREADS, VPT>(v, c);
+  reg_barrier(v);
+  const float d = (m == kNegInf) ? 0.f : thread_sum_exp<D, THREADS, VPT>(v, c, m * kLog2e);
+  reg_barrier(v);
+  return {m, d};
+}
+
+// exp2(x*log2e - coff) for every element of one slot, in the element type.
+template <int D>
+__device__ __forceinline__ u32x4 exp_slot(u32x4 v, float coff) {
+  pin_slot<D>(v);
+  OutVec<D> o;
+#pragma unroll
+  for (int e = 0; e < Elt<D>::kPerVec; ++e)
+    o.v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(v, e), kLog2e, -coff));
+  return o.bits();
+}
+
+
+// Instantiation lists of the row kernels (the shapes of kFwdShapes / kBwdShapes).
+#define XR_SHAPES_FWD(X, D)                                                                     \
+  X(D, 64, 4) X(D, 64, 8) X(D, 64, 16) X(D, 128, 16) X(D, 256, 16) X(D, 512, 16) X(D, 1024, 16)
+#define XR_SHAPES_BWD(X, D) \
+  X(D, 64, 4) X(D, 64, 8) X(D, 128, 8) X(D, 256, 8) X(D, 512, 8) X(D, 1024, 8)
+
+
+}  // namespace xr

@@ -1,0 +1,207 @@
+// xr_softmax.hip -- softmax forward and backward kernels for gfx950 (the row-kernel design
+// is described at the top of xr_xent.hip).
+#include "xr_rows.h"
+
+namespace xr {
+
+const Shape kFwdShapes[kNumFwdShapes] = {{64, 4},   {64, 8},   {64, 16},  {128, 16},
+                                         {256, 16}, {512, 16}, {1024, 16}};
+const Shape kBwdShapes[kNumBwdShapes] = {{64, 4},  {64, 8},   {128, 8},
+                                         {256, 8}, {512, 8}, {1024, 8}};
+
+// ============================================================================ softmax forward
+template <int D, int THREADS, int VPT, int LP>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_fwd_kernel(SoftmaxFwdParams p) {
+  constexpr int NW = THREADS / kWave;
+  __shared__ float2 red[2][NW];
+  int buf = 0;
+  const int64_t G = gridDim.x;
+  const int64_t cv = p.N + Elt<D>::kPerVec;  // more vectors than any row has: whole rows
+
+  u32x4 v[VPT];
+  int64_t r = blockIdx.x;
+  if (r < p.M) issue_loads<D, THREADS, VPT, LP>(v, Chunk<D>(p.x + r * p.ldx_bytes, p.N, 0, cv));
+  while (r < p.M) {
+    const int64_t rn = r + G;
+    const Chunk<D> cx(p.x + r * p.ldx_bytes, p.N, 0, cv);
+    const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);  // same lead as cx (host-checked)
+    const Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red[buf]);
+    buf ^= 1;
+    const float coff = st.m * kLog2e + log2f(st.d);
+    if (rn < p.M) {
+      const Chunk<D> cn(p.x + rn * p.ldx_bytes, p.N, 0, cv);
+      const uint32_t off = threadIdx.x * 16u;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        store_slot<D, THREADS>(cy, k, exp_slot<D>(v[k], coff));
+        v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(cy, k, exp_slot<D>(v[k], coff));
+    }
+    store_partials<D, THREADS>(cy, cx, [coff](float x) {
+      return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
+    });
+    r = rn;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(SoftmaxFwdParams p) {
+  __shared__ float red[2][kStreamThreads / kWave];
+  const int64_t r = blockIdx.x;
+  if (r >= p.M) return;
+  const char* row = p.x + r * p.ldx_bytes;
+  char* out = p.y + r * p.ldy_bytes;
+  const int tid = threadIdx.x;
+  auto ld = [&](int64_t j) -> float {
+    if (D == kF32) return reinterpret_cast<const float*>(row)[j];
+    return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
+  };
+  float m = kNegInf;
+  for (int64_t j = tid; j < p.N; j += kStreamThreads) m = fmaxf(m, ld(j));
+  m = block_reduce<kStreamThreads>(m, OpMax(), red[0]);
+  const float mL = m * kLog2e;
+  float d = 0.f;
+  for (int64_t j = tid; j < p.N; j += kStreamThreads)
+    d += __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -mL));
+  d = block_reduce<kStreamThreads>(d, OpAdd(), red[1]);
+  // In place (y == x) is safe: every element's output depends only on itself and (m, d),
+  // and all reads of the max / sum passes finished before the barrier above.
+  const float coff = mL + log2f(d);
+  for (int64_t j = tid; j < p.N; j += kStreamThreads) {
+    const float val = __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
+    if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
+    else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+  }
+}
+
+// ============================================================================ softmax backward
+template <int D, int THREADS, int VPT, int LP>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_bwd_kernel(SoftmaxBwdParams p) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int NW = THREADS / kWave;
+  __shared__ float red[2][NW];
+  const int64_t G = gridDim.x;
+  const int64_t cv = p.N + EPV;
+
+  u32x4 vy[VPT], vd[VPT];
+  int64_t r = blockIdx.x;
+  int buf = 0;
+  if (r < p.M) {
+    issue_loads<D, THREADS, VPT, LP>(vy, Chunk<D>(p.y + r * p.ldy_bytes, p.N, 0, cv));
+    issue_loads<D, THREADS, VPT, LP>(vd, Chunk<D>(p.dy + r * p.lddy_bytes, p.N, 0, cv));
+  }
+  while (r < p.M) {
+    const int64_t rn = r + G;
+    // y, dy and dx rows share their alignment (host-checked), hence their vector layout.
+    const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);
+    const Chunk<D> cx(p.dx + r * p.lddx_bytes, p.N, 0, cv);
+    // Out-of-row elements of both operands count as 0: they add nothing to the dot product.
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) continue;
+      const u32x4 a = masked_slot<D, THREADS>(vy[k], k, cy, 0u);
+      const u32x4 b = masked_slot<D, THREADS>(vd[k], k, cy, 0u);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e)
+        s[e & 3] = __builtin_fmaf(elem<D>(a, e), elem<D>(b, e), s[e & 3]);
+    }
+    const float dot = block_reduce<THREADS>((s[0] + s[1]) + (s[2] + s[3]), OpAdd(), red[buf]);
+    buf ^= 1;
+    reg_barrier(vy);
+    reg_barrier(vd);
+    const bool pf = rn < p.M;
+    const Chunk<D> cyn(p.y + (pf ? rn : r) * p.ldy_bytes, p.N, 0, cv);
+    const Chunk<D> cdn(p.dy + (pf ? rn : r) * p.lddy_bytes, p.N, 0, cv);
+    const uint32_t off = threadIdx.x * 16u;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      OutVec<D> o;
+      u32x4 a = vy[k], b = vd[k];
+      pin_slot<D>(a);
+      pin_slot<D>(b);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+      store_slot<D, THREADS>(cx, k, o.bits());
+      if (pf) {
+        vy[k] = buf_load<LP>(cyn.slot(k * THREADS), off);
+        vd[k] = buf_load<LP>(cdn.slot(k * THREADS), off);
+      }
+    }
+    // Partial first / last vectors: re-read y and dy (this workgroup has not written them;
+    // dx may be exactly y or dy) and store only the in-row elements.
+    {
+      const Chunk<D> cd(p.dy + r * p.lddy_bytes, p.N, 0, cv);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int vi = q == 0 ? cx.head : cx.tail;
+        if (vi < 0 || (int)threadIdx.x != vi % THREADS) continue;
+        const uint32_t po = q == 0 ? cx.hoff : cx.toff;
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cy.rsrc, (int)po, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cd.rsrc, (int)po, 0, 0);
+        OutVec<D> o;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+        store_partial<D>(cx.rsrc, po, o.bits(), q == 0 ? cx.h0 : cx.t0, q == 0 ? cx.h1 : cx.t1);
+      }
+    }
+    r = rn;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream_kernel(SoftmaxBwdParams p) {
+  __shared__ float red[kStreamThreads / kWave];
+  const int64_t r = blockIdx.x;
+  if (r >= p.M) return;
+  const char* yr = p.y + r * p.ldy_bytes;
+  const char* dr = p.dy + r * p.lddy_bytes;
+  char* out = p.dx + r * p.lddx_bytes;
+  const int tid = threadIdx.x;
+  auto ld = [&](const char* row, int64_t j) -> float {
+    if (D == kF32) return reinterpret_cast<const float*>(row)[j];
+    return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
+  };
+  float s = 0.f;
+  for (int64_t j = tid; j < p.N; j += kStreamThreads) s += ld(yr, j) * ld(dr, j);
+  s = block_reduce<kStreamThreads>(s, OpAdd(), red);
+  for (int64_t j = tid; j < p.N; j += kStreamThreads) {
+    const float val = ld(yr, j) * (ld(dr, j) - s);
+    if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
+    else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+  }
+}
+
+// ============================================================================ lookup tables
+#define XR_CASE_SFWD(D, T, V)                                                                  \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyNT>)           \
+              : reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyDefault>);
+#define XR_CASE_SBWD(D, T, V)                                                                  \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyNT>)           \
+              : reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyDefault>);
+
+const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_SFWD, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_SFWD, kBF16) }
+  return nullptr;
+}
+const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_BWD(XR_CASE_SBWD, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_BWD(XR_CASE_SBWD, kBF16) }
+  return nullptr;
+}
+const void* softmax_fwd_stream_kernel_ptr(int dtype) {
+  return dtype == kF32 ? reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kF32>)
+                       : reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kBF16>);
+}
+const void* softmax_bwd_stream_kernel_ptr(int dtype) {
+  return dtype == kF32 ? reinterpret_cast<const void*>(&softmax_bwd_stream_kernel<kF32>)
+                       : reinterpret_cast<const void*>(&softmax_bwd_stream_kernel<kBF16>);
+}
+
+}  // namespace xr

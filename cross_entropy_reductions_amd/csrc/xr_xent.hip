@@ -1,0 +1,278 @@
+// xr_xent.hip -- fused cross-entropy kernels (and the notes on every row kernel) for gfx950.
+//
+// What is computed (the pages' definitions):
+//   softmax forward  y_j = exp(x_j - m) / d, m = max_j x_j, d = sum_j exp(x_j - m)
+//                    (page "python sum function examples", kernels softmax_kernel / _softmax)
+//   softmax backward dx_j = y_j * (dy_j - sum_k y_k dy_k)
+//                    (same page, kernel _backward, block-sparse scale taken as 1)
+//   cross-entropy    loss_i = m + log d - x_{t_i}; the logits are overwritten with the gradient
+//                    (softmax - onehot(t_i)) / n, n = #targets != ignore_index; ignored rows
+//                    get zero gradient and zero loss; mean = sum_i loss_i / n
+//                    (Liger-Kernel cross_entropy.py page, liger_cross_entropy_kernel steps 1-6,
+//                    LigerCrossEntropyFunction.forward)
+//
+// Register budget: every row kernel is compiled for at least 4 waves per SIMD (128 VGPRs),
+// so a 1024-thread workgroup fits a compute unit and smaller ones can share it.
+//
+// How, on MI355X:
+//   * Row-resident kernels keep a whole row (or, for split rows, one chunk of it) in
+//     registers as raw 16-byte vectors, so the logits are read from HBM exactly once:
+//     max pass, then sum pass with that max (one exp per element, no online rescale),
+//     then the output pass. The output is exp2(x*log2e - c) with c = m*log2e + log2(d*n),
+//     which folds the division by d and by n into the exponent.
+//   * The kernels are persistent: workgroup g handles rows g, g + G, g + 2G, ... and while
+//     it writes row r it already issues the loads of row r + G into the registers it has
+//     just written out ("rolling prefetch"), so a CU keeps reading while it stores.
+//   * Rows longer than one workgroup's registers, or batches too short to fill the GPU,
+//     are split over S workgroups. Each publishes its chunk's (m_c, d_c) pair as one
+//     64-bit word; the chunks of a row combine them with the online-softmax rule
+//     (m, d) + (m_c, d_c) -> (max, d e^(m - max) + d_c e^(m_c - max)), chunks whose max
+//     is -inf being the identity. The grid is launched cooperatively so all chunk
+//     workgroups are co-resident; the wait is bounded and reports a flag if it expires.
+//   * Stream kernels (one workgroup per row, element-wise, several passes over global
+//     memory) handle anything the row-resident kernels do not: rows whose operands are
+//     not equally aligned, rows too long for the split grid.
+#include "xr_rows.h"
+
+namespace xr {
+
+// ============================================================================ cross-entropy
+// Target scan: n = #{t != ignore_index}, bad = #{t != ignore_index, t outside [0, V)}.
+// Also clears the error flags and marks every split-row (m, d) slot as unpublished.
+__global__ __launch_bounds__(kScanThreads) void xent_scan_kernel(const int64_t* __restrict__ target,
+                                                                 int64_t M, int64_t V,
+                                                                 int64_t ignore_index,
+                                                                 int32_t* __restrict__ ws_counts,
+                                                                 uint64_t* __restrict__ partials,
+                                                                 int64_t nslots) {
+  __shared__ int red[2][kScanThreads / kWave];
+  int n = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < M; i += kScanThreads) {
+    const int64_t t = target[i];
+    if (t != ignore_index) {
+      ++n;
+      if (t < 0 || t >= V) ++bad;
+    }
+  }
+  n = block_sum_int<kScanThreads>(n, red[0]);
+  bad = block_sum_int<kScanThreads>(bad, red[1]);
+  if (threadIdx.x == 0) {
+    ws_counts[0] = n;
+    ws_counts[1] = bad;
+    ws_counts[2] = 0;
+    ws_counts[3] = 0;
+  }
+  for (int64_t i = threadIdx.x; i < nslots; i += kScanThreads) partials[i] = kPartialEmpty;
+}
+
+// Mean over the row losses in a fixed order; copies the counts out.
+__global__ __launch_bounds__(kScanThreads) void xent_mean_kernel(const float* __restrict__ row_loss,
+                                                                 int64_t M,
+                                                                 const int32_t* __restrict__ ws_counts,
+                                                                 float* __restrict__ mean,
+                                                                 int32_t* __restrict__ counts_out) {
+  __shared__ float red[kScanThreads / kWave];
+  float s = 0.f;
+  for (int64_t i = threadIdx.x; i < M; i += kScanThreads) s += row_loss[i];
+  s = block_reduce<kScanThreads>(s, OpAdd(), red);
+  if (threadIdx.x == 0) {
+    const int32_t n = ws_counts[0];
+    *mean = s / (float)n;  // n == 0: 0/0 = NaN
+    if (counts_out) {
+      counts_out[0] = n;
+      counts_out[1] = ws_counts[1];
+      counts_out[2] = ws_counts[2];
+    }
+  }
+}
+
+// Row-resident fused cross-entropy; S workgroups per row (S == 1: the whole row).
+template <int D, int THREADS, int VPT, int LP>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void xent_rows_kernel(XentParams p) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int NW = THREADS / kWave;
+  __shared__ float2 red[2][NW];
+  __shared__ float bcast[2];
+  int buf = 0;
+
+  const int tid = threadIdx.x;
+  const int S = p.S;
+  const int64_t grp = blockIdx.x / S;
+  const int chunk = blockIdx.x % S;
+  const int64_t lo = (int64_t)chunk * p.chunk_vecs;
+  const int32_t n = p.ws_counts[0];
+  const float inv_n = 1.0f / (float)n;
+  const float log2n = log2f((float)n);
+
+  auto skip = [&](int64_t t) { return t == p.ignore_index || t < 0 || t >= p.V; };
+  auto row_ptr = [&](int64_t r) { return p.logits + r * p.ld_bytes; };
+
+  u32x4 v[VPT];
+  int64_t r = grp;
+  int64_t t = (r < p.M) ? p.target[r] : p.ignore_index;
+  if (r < p.M && !skip(t)) issue_loads<D, THREADS, VPT, LP>(v, Chunk<D>(row_ptr(r), p.V, lo, p.chunk_vecs));
+
+  while (r < p.M) {
+    const int64_t rn = r + p.groups;
+    const int64_t tn = (rn < p.M) ? p.target[rn] : p.ignore_index;
+    const bool pf = rn < p.M && !skip(tn);
+    const Chunk<D> c(row_ptr(r), p.V, lo, p.chunk_vecs);
+    const bool ignored = skip(t);
+
+    // The target logit, read by the thread holding its vector. Only this workgroup
+    // writes this chunk, and it does so after the barriers below.
+    const int64_t vt = c.lead + t - c.lo * EPV;  // chunk-local element index of the target
+    const bool owner = !ignored && vt >= 0 && vt < (int64_t)c.nvec * EPV &&
+                       tid == (int)(vt / EPV) % THREADS;
+    float xt = 0.f;
+    if (owner) xt = buf_load_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes));
+
+    float m = 0.f, d = 1.f, coff;
+    if (ignored) {
+      // Ignored (or out-of-range) target: the row was not loaded; with every input at
+      // -inf and c = +inf the output pass below writes exact zeros.
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) v[k] = splat(Elt<D>::kNegInfWord);
+      coff = __builtin_inff();
+    } else {
+      // (m, d) of the chunk; an all -inf chunk gives (-inf, 0).
+      const Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, c), red[buf]);
+      buf ^= 1;
+      m = st.m;
+      d = st.d;
+
+      if (S > 1) {
+        // Publish this chunk's pair, then combine the pairs of all chunks of the row in
+        // chunk order (every chunk of the row computes the same (m, d)).
+        if (tid == 0) {
+          uint64_t* slot = p.partials + r * S;
+          __hip_atomic_store(slot + chunk, pack_pair(m, d), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          float ms = kNegInf, ds = 0.f;
+          bool ok = true;
+          // One bounded wait for the whole row; after any timeout in this call no
+          // workgroup waits again (the flag is set), so the kernel always drains.
+          int budget = (__hip_atomic_load(p.ws_flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                        kFlagExchangeTimeout) ? 0 : kSpinLimit;
+          for (int q = 0; q < S && ok; ++q) {
+            uint64_t w;
+            while ((w = __hip_atomic_load(slot + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+                   kPartialEmpty) {
+              if (--budget < 0) {
+                ok = false;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+            if (!ok) break;
+            const float mc = pair_m(w), dc = pair_d(w);
+            if (mc == kNegInf) continue;
+            const float mx = fmaxf(ms, mc);
+            ds = ((ms == kNegInf) ? 0.f : ds * exp2f((ms - mx) * kLog2e)) +
+                 dc * exp2f((mc - mx) * kLog2e);
+            ms = mx;
+          }
+          if (!ok) {
+            __hip_atomic_fetch_or(p.ws_flags, kFlagExchangeTimeout, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            ms = __builtin_nanf("");
+          }
+          bcast[0] = ms;
+          bcast[1] = ds;
+        }
+        __syncthreads();
+        m = bcast[0];
+        d = bcast[1];
+      }
+      // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) is p_j / n.
+      coff = m * kLog2e + log2f(d) + log2n;
+    }
+
+    // Output pass, with the next row's loads issued into each slot once it is written out.
+    if (pf) {
+      const Chunk<D> cn(row_ptr(rn), p.V, lo, p.chunk_vecs);
+      const uint32_t off = tid * 16u;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
+        v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
+    }
+    store_partials<D, THREADS>(c, c, [coff, ignored](float x) {
+      return ignored ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
+    });
+    if (owner) {
+      // Target column: (p_t - 1)/n rounded once, stored after this thread's vector store.
+      const float pt = exp2f((xt - m) * kLog2e) / d;
+      store_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes), (pt - 1.0f) * inv_n);
+      p.row_loss[r] = m + logf(d) - xt;
+    }
+    if (ignored && chunk == 0 && tid == 0) p.row_loss[r] = 0.f;
+    r = rn;
+    t = tn;
+  }
+}
+
+// Stream fallback: one workgroup per row, element-wise, max / sum / write passes over memory.
+template <int D>
+__global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams p) {
+  __shared__ float red[2][kStreamThreads / kWave];
+  const int64_t r = blockIdx.x;
+  if (r >= p.M) return;
+  const int64_t t = p.target[r];
+  char* row = p.logits + r * p.ld_bytes;
+  const int tid = threadIdx.x;
+  auto ld = [&](int64_t j) -> float {
+    if (D == kF32) return reinterpret_cast<const float*>(row)[j];
+    return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
+  };
+  auto st = [&](int64_t j, float val) {
+    if (D == kF32) reinterpret_cast<float*>(row)[j] = val;
+    else reinterpret_cast<uint16_t*>(row)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+  };
+  if (t == p.ignore_index || t < 0 || t >= p.V) {
+    for (int64_t j = tid; j < p.V; j += kStreamThreads) st(j, 0.f);
+    if (tid == 0) p.row_loss[r] = 0.f;
+    return;
+  }
+  const int32_t n = p.ws_counts[0];
+  const float xt = ld(t);
+  float m = kNegInf;
+  for (int64_t j = tid; j < p.V; j += kStreamThreads) m = fmaxf(m, ld(j));
+  m = block_reduce<kStreamThreads>(m, OpMax(), red[0]);
+  const float mL = m * kLog2e;
+  float d = 0.f;
+  for (int64_t j = tid; j < p.V; j += kStreamThreads)
+    d += __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -mL));
+  d = block_reduce<kStreamThreads>(d, OpAdd(), red[1]);
+  // Every thread has read xt and the row before the barrier inside the reductions.
+  const float coff = mL + log2f(d) + log2f((float)n);
+  for (int64_t j = tid; j < p.V; j += kStreamThreads) {
+    const float g = (j == t) ? (exp2f((xt - m) * kLog2e) / d - 1.0f) / (float)n
+                             : __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
+    st(j, g);
+  }
+  if (tid == 0) p.row_loss[r] = m + logf(d) - xt;
+}
+
+// ============================================================================ lookup tables
+#define XR_CASE_XENT(D, T, V)                                                                  \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&xent_rows_kernel<D, T, V, kPolicyNT>)             \
+              : reinterpret_cast<const void*>(&xent_rows_kernel<D, T, V, kPolicyDefault>);
+const void* xent_rows_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_XENT, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_XENT, kBF16) }
+  return nullptr;
+}
+const void* xent_stream_kernel_ptr(int dtype) {
+  return dtype == kF32 ? reinterpret_cast<const void*>(&xent_stream_kernel<kF32>)
+                       : reinterpret_cast<const void*>(&xent_stream_kernel<kBF16>);
+}
+const void* xent_scan_kernel_ptr() { return reinterpret_cast<const void*>(&xent_scan_kernel); }
+const void* xent_mean_kernel_ptr() { return reinterpret_cast<const void*>(&xent_mean_kernel); }
+
+}  // namespace xr
