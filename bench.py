@@ -9,14 +9,22 @@ logits (made before the timed region).
 Prints one JSON line on stdout. Throughput is B_min / t, where B_min is the method's
 minimal traffic: every non-ignored row read once, every row written once, the targets read
 and the row losses written. `roofline` reports the row kernel alone, timed with HIP events
-recorded around it on its stream; `cpu_baseline` times the float64 oracle on a sample of
-the same workload on this host's cores.
+the library records around that launch on its stream; `cpu_baseline` times the float64
+oracle on the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
+                    [--workload c4|c3|c5|c2|c1]
+    python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
+
+The other workloads (c1 softmax fp32 128x1000, c2 softmax forward + backward bf16 4096^2,
+c3 cross-entropy bf16 8192x32000, c5 cross-entropy fp32 2048x256000 padded) print the same
+kind of line; small inputs are rotated through >= 1 GB of copies so no step reads data a
+previous step left in the 256 MB Infinity Cache.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
 import hashlib
 import json
@@ -34,6 +42,21 @@ COUNTERS = os.path.join(ROOT, "profiles", "xent_c4_hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "cross_entropy_reductions_amd", "csrc", f)
                   for f in ("xr_xent.hip", "xr_softmax.hip", "xr_rows.h", "xr_device.h",
                             "xr_internal.h", "xr_api.cpp")]
+ROW_KERNEL = "xent_rows_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+C4_M, C4_V, C4_KEEP = 16384, 128256, 15565
+
+DESCRIPTIONS = {
+    "c1": "softmax forward, M=128, N=1000, fp32 logits 3 N(0,1), contiguous",
+    "c2": "softmax forward + backward, M=4096, N=4096, bf16 in / fp32 accumulation, "
+          "x and dy N(0,1)",
+    "c3": "fused cross-entropy loss+grad, M=8192 tokens (B=4, T=2048), V=32000, bf16 logits "
+          "2 N(0,1), int64 targets, 10% ignore_index=-100, mean reduction",
+    "c4": "fused cross-entropy loss+grad, M=16384 tokens, V=128256, bf16 logits N(0,1) + 4 "
+          "spikes of +20 per row, int64 targets, 5% ignore_index=-100, mean reduction",
+    "c5": "fused cross-entropy loss+grad, M=2048, V=256000, fp32 logits 8 N(0,1), row stride "
+          "V+64, 1% all-equal rows, 1% half -inf rows, no ignored rows, mean reduction",
+}
 
 
 def kernel_source_hash() -> str:
@@ -94,6 +117,8 @@ class HipEvents:
 def cpu_baseline(workload: dict, rows: int) -> dict:
     """The oracle as it stands on the first `rows` rows (count, loss + gradient, mean), in
     1024-row chunks so its float64 gradient buffer stays near 1 GB."""
+    import numpy as np
+
     import oracle
 
     orc = oracle.get()
@@ -106,17 +131,50 @@ def cpu_baseline(workload: dict, rows: int) -> dict:
     for r0 in range(0, rows, 1024):
         _, loss = orc.xent_rows(x[r0:r0 + 1024], t[r0:r0 + 1024], V, n, want_grad=True)
         losses.append(loss)
-    import numpy as np
     orc.mean(np.concatenate(losses), n)
     sec = time.perf_counter() - t0
-    b = xent_bmin(rows, V, int((t != -100).sum()), 2)
+    elt = 2 if workload["dtype"] == "bf16" else 4
+    b = xent_bmin(rows, V, int((t != -100).sum()), elt)
     return {"value": round(b / sec / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle", "rows_per_s": round(rows / sec, 1), "seconds": round(sec, 3),
             "sample": f"first {rows} of {workload['M']} rows of the same workload "
-                      f"(V={V} bf16): float64 count, loss, gradient and mean, one run"}
+                      f"(V={V} {workload['dtype']}): float64 count, loss, gradient and mean, "
+                      "one run"}
 
 
-def run(args) -> dict:
+def _device_matrix(torch, a, dev):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def _timed(ev, steps, warmup, launch):
+    """Warm up, then time `steps` launches back to back, with the row kernel of each timed
+    step bracketed by its own pair of events."""
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    starts = [ev.create() for _ in range(steps)]
+    stops = [ev.create() for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        xr.set_profile_events(starts[i], stops[i])
+        launch(warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    xr.set_profile_events(None, None)
+    ms = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+    for e in starts + stops:
+        ev.destroy(e)
+    return wall, ms
+
+
+def run_xent(args, name: str) -> dict:
     import torch
 
     import cross_entropy_reductions_amd as xr
@@ -125,14 +183,14 @@ def run(args) -> dict:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
-    w = synth.xent_c4()
+    w = synth.WORKLOADS[name]()
     M, V = w["M"], w["N"]
     t = torch.from_numpy(w["target"]).to(dev)
-    x0 = torch.from_numpy(w["x"].view("int16")).view(torch.bfloat16).to(dev)
+    x0 = _device_matrix(torch, w["x"], dev)
     n_keep = int((w["target"] != -100).sum())
-    gen_s = time.perf_counter() - t_gen
-    print(f"[bench] workload ready in {gen_s:.1f}s: M={M} V={V} n={n_keep}", file=sys.stderr,
-          flush=True)
+    elt = 2 if w["dtype"] == "bf16" else 4
+    print(f"[bench] {name} ready in {time.perf_counter() - t_gen:.1f}s: M={M} V={V} "
+          f"n={n_keep}", file=sys.stderr, flush=True)
 
     steps, warmup = args.steps, args.warmup
     copies = [x0.clone() for _ in range(warmup + steps)]
@@ -140,66 +198,143 @@ def run(args) -> dict:
     row_loss = torch.empty(M, dtype=torch.float32, device=dev)
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     counts = torch.empty(3, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(256, xr.xent_workspace_bytes(M, V, torch.bfloat16)), dtype=torch.uint8,
-                     device=dev)
-    ev = HipEvents()
-    starts = [ev.create() for _ in range(steps)]
-    stops = [ev.create() for _ in range(steps)]
+    dt = copies[0].dtype
+    ws = torch.empty(max(256, xr.xent_workspace_bytes(M, V, dt)), dtype=torch.uint8, device=dev)
 
-    for i in range(warmup):
-        xr.xent_fwd_bwd(copies[i], t, -100, row_loss=row_loss, mean_loss=mean, counts=counts,
-                        workspace=ws)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for i in range(steps):
-        xr.set_profile_events(starts[i], stops[i])
-        xr.xent_fwd_bwd(copies[warmup + i], t, -100, row_loss=row_loss, mean_loss=mean,
+    def launch(i):
+        xr.xent_fwd_bwd(copies[i][:, :V], t, -100, row_loss=row_loss, mean_loss=mean,
                         counts=counts, workspace=ws)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    xr.set_profile_events(None, None)
-    kernel_ms = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
-    for e in starts + stops:
-        ev.destroy(e)
+
+    wall, kernel_ms = _timed(HipEvents(), steps, warmup, launch)
     c = counts.cpu().tolist()
     assert c[0] == n_keep and c[2] == 0, f"unexpected counts {c}"
+    bmin = xent_bmin(M, V, n_keep, elt)
+    p = xr.plan("xent", M, V, dt)
+    out = _line(args, name, bmin, M, wall, kernel_ms, ROW_KERNEL,
+                {"M": M, "V": V, "n_non_ignore": n_keep, "bytes_min": bmin, "path": p["path"],
+                 "threads": p["threads"], "split": p["split"], "grid": p["grid"]},
+                w["dtype"])
+    if name == "c4":
+        out["roofline"]["traffic"] = measured_traffic()
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
+    return out
 
-    bmin = xent_bmin(M, V, n_keep, 2)
-    ms_step = wall * 1e3 / steps
+
+def run_softmax(args, name: str) -> dict:
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[name]()
+    M, N = w["M"], w["N"]
+    x = _device_matrix(torch, w["x"], dev)
+    elt = x.element_size()
+    bwd = "dy" in w
+    dy = _device_matrix(torch, w["dy"], dev) if bwd else None
+    per_set = (4 if bwd else 2) * M * N * elt
+    nsets = max(2, -(-(1 << 30) // per_set))  # >= 1 GB of distinct inputs and outputs
+    xs = [x.clone() for _ in range(nsets)]
+    dys = [dy.clone() for _ in range(nsets)] if bwd else None
+    ys = [torch.empty_like(x) for _ in range(nsets)]
+    dxs = [torch.empty_like(x) for _ in range(nsets)] if bwd else None
+    ev = HipEvents()
+    bwd_events = [(ev.create(), ev.create()) for _ in range(args.warmup + args.steps)]
+
+    def launch(i):
+        j = i % nsets
+        xr.softmax_fwd(xs[j], ys[j])  # bracketed by the events _timed installs
+        if bwd:
+            xr.set_profile_events(*bwd_events[i])
+            xr.softmax_bwd(ys[j], dys[j], dxs[j])
+
+    wall, fwd_ms = _timed(ev, args.steps, args.warmup, launch)
+    bwd_ms = [ev.elapsed_ms(a, b) for a, b in bwd_events[args.warmup:]] if bwd else []
+    for a, b in bwd_events:
+        ev.destroy(a)
+        ev.destroy(b)
+    b_fwd = 2 * M * N * elt
+    b_bwd = 3 * M * N * elt if bwd else 0
+    p = xr.plan("softmax_fwd", M, N, x.dtype)
+    out = _line(args, name, b_fwd + b_bwd, M, wall, fwd_ms, "softmax_fwd_kernel",
+                {"M": M, "N": N, "bytes_min": b_fwd + b_bwd, "path": p["path"],
+                 "threads": p["threads"], "grid": p["grid"], "input_sets": nsets},
+                w["dtype"], kernel_bytes=b_fwd)
+    if bwd:
+        kavg = statistics.mean(bwd_ms)
+        out["roofline_bwd"] = {"bound": "hbm", "achieved": round(b_bwd / kavg / 1e6, 1),
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(b_bwd / kavg / 1e6 / PEAK_HBM_GBS, 4),
+                               "kernel": "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5)}
+    return out
+
+
+def _line(args, name, bmin, M, wall, kernel_ms, kernel, config, dtype, kernel_bytes=None):
+    steps = args.steps
     gbs = bmin / (wall / steps) / 1e9
     kavg = statistics.mean(kernel_ms)
-    kgbs = bmin / (kavg / 1e3) / 1e9
-    p = xr.plan("xent", M, V, torch.bfloat16)
-    out = {
-        "metric": "achieved HBM GB/s (% of peak) and rows/s for fused xent fwd+bwd, V=128256 bf16",
+    kb = bmin if kernel_bytes is None else kernel_bytes
+    kgbs = kb / (kavg / 1e3) / 1e9
+    metric = ("achieved HBM GB/s (% of peak) and rows/s for fused xent fwd+bwd, V=128256 bf16"
+              if name == "c4" else f"achieved HBM GB/s (% of peak) and rows/s, {name}")
+    return {
+        "metric": metric,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(ms_step, 4),
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "fused cross-entropy loss+grad, M=16384 tokens, V=128256, bf16 "
-                               "logits N(0,1) + 4 spikes of +20 per row, int64 targets, 5% "
-                               "ignore_index=-100, mean reduction",
-                   "M": M, "V": V, "n_non_ignore": n_keep, "bytes_min": bmin,
-                   "path": p["path"], "threads": p["threads"], "grid": p["grid"]},
+        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", **config},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(M / (wall / steps), 1),
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "xent_rows_kernel", "kernel_ms_avg": round(kavg, 4),
-                     "kernel_ms_min": round(min(kernel_ms), 4)},
+                     "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": kernel, "kernel_ms_avg": round(kavg, 5),
+                     "kernel_ms_min": round(min(kernel_ms), 5)},
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
-    return out
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the row kernel on the default workload,
+    each scaled by what the same counter reads for the runtime's device copy of the 4.2 GB
+    logit matrix (the per-step copies bench.py makes before its timed region: one known read
+    and one known write of the whole matrix)."""
+    matrix = C4_M * C4_V * 2
+
+    def per_kernel(path):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name", "")
+                key = (ROW_KERNEL if ROW_KERNEL in name else
+                       COPY_KERNEL if COPY_KERNEL in name else None)
+                if key is not None:
+                    vals.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
+        return vals
+
+    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy_f = [v for v in f[COPY_KERNEL] if v > 0.5 * matrix]
+    copy_w = [v for v in w[COPY_KERNEL] if v > 0.5 * matrix]
+    scale_f = matrix / statistics.median(copy_f)
+    scale_w = matrix / statistics.median(copy_w)
+    fetch = statistics.median(f[ROW_KERNEL]) * scale_f
+    write = statistics.median(w[ROW_KERNEL]) * scale_w
+    bmin = xent_bmin(C4_M, C4_V, C4_KEEP, 2)
+    return {"kernel": ROW_KERNEL, "kernel_source_hash": kernel_source_hash(),
+            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+            "traffic_bytes_per_launch": round(fetch + write), "bytes_min": bmin,
+            "traffic_over_bytes_min": round((fetch + write) / bmin, 4),
+            "copy_scale_fetch": round(scale_f, 4), "copy_scale_write": round(scale_w, 4),
+            "dispatches": {"row_kernel": len(f[ROW_KERNEL]), "copy": len(copy_f)}}
 
 
 def main() -> int:
@@ -209,16 +344,25 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--workload", default="c4", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               "requested).", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0 or args.steps + args.warmup > 40:
-        print("need 1 <= steps and steps + warmup <= 40 (one 4.2 GB copy of the logits per step)",
+        print("need 1 <= steps and steps + warmup <= 40 (one copy of the logits per step)",
               file=sys.stderr)
         return 2
-    print(json.dumps(run(args)), flush=True)
+    if args.workload in ("c1", "c2"):
+        out = run_softmax(args, args.workload)
+    else:
+        out = run_xent(args, args.workload)
+    print(json.dumps(out), flush=True)
     return 0
 
 

@@ -160,17 +160,24 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     return XR_OK;
   }
 
-  // Workgroups per row: enough for the row to fit, and (cross-entropy only) enough rows'
+  // Workgroups per row (cross-entropy; softmax rows stay whole): enough for the row to fit;
+  // chunks of at most ~128 KB, and at least two for rows of 32 KB and more, so that several
+  // workgroups share a compute unit and one's reductions overlap another's memory traffic
+  // (measured: 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 TB/s in two chunks); and enough
   // chunks to give every compute unit work when the batch is short.
   int64_t S = 1;
   if (op == 2) {
     const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
+    const int64_t row_bytes = nvm * 16;
+    const int64_t s_bw = row_bytes >= (32 << 10)
+                             ? std::max<int64_t>(2, (row_bytes + (128 << 10) - 1) / (128 << 10))
+                             : 1;
     int64_t s_par = 1;
     if (M > 0 && M < di.cus) {
       s_par = (di.cus + M - 1) / M;
       s_par = std::min(s_par, std::max<int64_t>(1, nvm / kMinChunkVecs));
     }
-    S = std::max(s_cap, s_par);
+    S = std::max(std::max(s_cap, s_bw), s_par);
     if (g_opt.split) S = g_opt.split;
     if (want == kPathResident && g_opt.split == 0) S = s_cap;
     if (want == kPathSplit && g_opt.split == 0) S = std::max<int64_t>(2, S);
@@ -214,6 +221,13 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     int64_t g = M;
     if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
     p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
+  } else if (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF) {
+    // One workgroup per row chunk, launched normally (measured faster than a persistent
+    // cooperative grid): the S chunks of a row have consecutive workgroup ids, and the
+    // dispatcher starts workgroups in id order, so a chunk only ever waits for chunks that
+    // are resident or about to be; the wait is bounded in any case.
+    p.path = kPathSplit;
+    p.grid = M * S;
   } else {
     p.path = kPathSplit;
     if (!di.coop) return XR_ERR_DEVICE;

@@ -147,9 +147,9 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
  *                   returns XR_ERR_SHAPE from the entry point)
  *   XR_OPT_SPLIT    workgroups per row for the split path (>= 2)
  *   XR_OPT_THREADS  workgroup size of the row-resident kernels (64 .. 1024)
- *   XR_OPT_GRID     rows held whole: 0 or -1 = one workgroup per row, k >= 1 = a persistent
- *                   grid of k workgroups per compute unit; split rows: k >= 1 caps the
- *                   cooperative grid at k workgroups per compute unit
+ *   XR_OPT_GRID     0 or -1 = one workgroup per row (or per row chunk), launched normally;
+ *                   k >= 1 = a persistent grid of k workgroups per compute unit (launched
+ *                   cooperatively for split rows)
  *   XR_OPT_LOAD_POLICY  row loads: 1 = default cache policy, 2 = non-temporal
  */
 typedef enum xr_option {

@@ -262,10 +262,13 @@ def test_xent_all_paths_agree(orc, dtype):
     x = synth.random_rows(9500, M, V, dtype=dtype, scale=3.0)
     t = synth.random_targets(9501, M, V, ignore_frac=0.1)
     outs = {}
-    for name, path, split in (("auto", 0, 0), ("resident", 1, 0), ("split2", 2, 2),
-                              ("split5", 2, 5), ("stream", 3, 0)):
+    for name, path, split, grid in (("auto", 0, 0, 0), ("resident", 1, 0, 0),
+                                    ("resident-persistent", 1, 0, 2), ("split2", 2, 2, 0),
+                                    ("split5", 2, 5, 0), ("split3-cooperative", 2, 3, 1),
+                                    ("stream", 3, 0, 0)):
         xr.set_option("path", path)
         xr.set_option("split", split)
+        xr.set_option("grid", grid)
         g, rows, mean, counts = run_xent(x, t, V)
         compare_xent(orc, x, t, V, g, rows, mean, counts, f"{dtype} {name}")
         outs[name] = g
@@ -285,12 +288,20 @@ def test_xent_workgroup_sizes(orc, threads):
 
 @pytest.mark.parametrize("grid", [1, 2, -1])
 def test_xent_grid_shapes(orc, grid):
+    """Persistent grids (rows g, g + G, ... with the next row's loads issued while the
+    current one is written) and one workgroup per row, on rows held whole and split."""
     M, V = 700, 3000
     x = synth.random_rows(9700, M, V, dtype="bf16", scale=2.0)
     t = synth.random_targets(9701, M, V, ignore_frac=0.1)
     xr.set_option("grid", grid)
     g, rows, mean, counts = run_xent(x, t, V)
     compare_xent(orc, x, t, V, g, rows, mean, counts, f"grid {grid}")
+    M, V = 300, 40000
+    x = synth.random_rows(9702, M, V, dtype="bf16", scale=2.0)
+    t = synth.random_targets(9703, M, V, ignore_frac=0.1)
+    assert xr.plan("xent", M, V, torch.bfloat16)["path"] == "split"
+    g, rows, mean, counts = run_xent(x, t, V)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"split grid {grid}")
 
 
 def test_xent_deterministic():
