@@ -20,15 +20,18 @@
 //     max pass, then sum pass with that max (one exp per element, no online rescale),
 //     then the output pass. The output is exp2(x*log2e - c) with c = m*log2e + log2(d*n),
 //     which folds the division by d and by n into the exponent.
-//   * The kernels are persistent: workgroup g handles rows g, g + G, g + 2G, ... and while
-//     it writes row r it already issues the loads of row r + G into the registers it has
-//     just written out ("rolling prefetch"), so a CU keeps reading while it stores.
-//   * Rows longer than one workgroup's registers, or batches too short to fill the GPU,
-//     are split over S workgroups. Each publishes its chunk's (m_c, d_c) pair as one
-//     64-bit word; the chunks of a row combine them with the online-softmax rule
+//   * One workgroup per row, or per row chunk, by default: the dispatcher starts a new
+//     workgroup as soon as one retires. A persistent form (workgroup g handles rows g,
+//     g + G, ... and, while it writes row r, issues the loads of row r + G into the
+//     registers it has just written out) is kept for grids set explicitly.
+//   * Long rows, and batches too short to fill the GPU, are split over S workgroups. Each
+//     publishes its chunk's (m_c, d_c) pair as one 64-bit word; the chunks of a row
+//     combine them with the online-softmax rule
 //     (m, d) + (m_c, d_c) -> (max, d e^(m - max) + d_c e^(m_c - max)), chunks whose max
-//     is -inf being the identity. The grid is launched cooperatively so all chunk
-//     workgroups are co-resident; the wait is bounded and reports a flag if it expires.
+//     is -inf being the identity. A row's chunks have consecutive workgroup ids, so in a
+//     normal launch a chunk waits only for chunks already started or next in line (a
+//     persistent grid is launched cooperatively); the wait is bounded and reports a flag
+//     if it expires.
 //   * Stream kernels (one workgroup per row, element-wise, several passes over global
 //     memory) handle anything the row-resident kernels do not: rows whose operands are
 //     not equally aligned, rows too long for the split grid.
