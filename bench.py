@@ -27,6 +27,7 @@ import argparse
 import csv
 import ctypes
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -59,11 +60,19 @@ DESCRIPTIONS = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text with comments and blank space removed, so that the hash below changes
+    with the code and not with its comments."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
