@@ -15,7 +15,11 @@ What each function computes, and the passage it follows:
   ``cross_entropy.py``: ``liger_cross_entropy_kernel`` steps 1-6 (ignore
   early-out, loss ``m + log d - x_y``, gradient ``(softmax - onehot)/n``) and
   ``LigerCrossEntropyFunction.forward`` (``n`` counts non-ignored targets, mean
-  loss ``sum(loss)/n``).
+  loss ``sum(loss)/n``). ``reduction="sum"`` / ``"none"`` and the upstream
+  gradient ``scale`` follow the definition of the loss that page links to
+  (its kernel documents only the mean).
+* ``element_mul`` -- the backward's ``element_mul`` kernel on the same page:
+  every element of a stored gradient row times the upstream gradient.
 
 Inputs are host numpy arrays holding exactly the bytes the GPU receives:
 ``uint16`` arrays carry bf16 bit patterns, ``float32`` arrays carry fp32.
@@ -40,6 +44,7 @@ SOURCE = os.path.join(_HERE, "xr_oracle.c")
 LIBRARY = os.path.join(_HERE, "libxr_oracle.so")
 
 F32, BF16 = 0, 1
+REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
 _c_i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -70,6 +75,13 @@ class Oracle:
         lib.xro_xent_rows.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int,
                                       _c_i64, _p, _p]
         lib.xro_xent_rows.restype = None
+        lib.xro_xent_rows_ex.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                         ctypes.c_int, _c_i64, _p, _c_i64, _p, _p]
+        lib.xro_xent_rows_ex.restype = None
+        lib.xro_sum.argtypes = [_p, _c_i64]
+        lib.xro_sum.restype = ctypes.c_double
+        lib.xro_element_mul.argtypes = [_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _p, _c_i64, _p]
+        lib.xro_element_mul.restype = None
         lib.xro_mean.argtypes = [_p, _c_i64, _c_i64]
         lib.xro_mean.restype = ctypes.c_double
         lib.xro_num_threads.argtypes = []
@@ -131,9 +143,24 @@ class Oracle:
                                 counts.ctypes.data)
         return int(counts[0]), int(counts[1])
 
+    @staticmethod
+    def _scale(scale, M: int):
+        """(array, stride) of an upstream gradient: None, a number, or one value per row."""
+        if scale is None:
+            return None, 0
+        a = np.ascontiguousarray(np.atleast_1d(np.asarray(scale, dtype=np.float64)))
+        if a.ndim != 1 or a.shape[0] not in (1, M):
+            raise ValueError("scale must be a number or hold one value per row")
+        return a, (1 if a.shape[0] == M and M != 1 else 0)
+
     def xent_rows(self, logits: np.ndarray, target: np.ndarray, V: int, n: int,
-                  ignore_index: int = -100, rows=None, want_grad: bool = True):
-        """(grad [len(rows), V] or None, loss [len(rows)]) for the given rows."""
+                  ignore_index: int = -100, rows=None, want_grad: bool = True,
+                  reduction: str = "mean", scale=None):
+        """(grad [len(rows), V] or None, loss [len(rows)]) for the given rows.
+
+        reduction selects whose gradient is written (mean: of sum(loss)/n, sum: of
+        sum(loss), none: of each row's loss); scale is the upstream gradient (a number, or
+        one value per row of ``logits``), None meaning 1."""
         ptr, ld, M, code = self._matrix(logits)
         if not 0 < V <= logits.shape[1]:
             raise ValueError("V out of range")
@@ -147,24 +174,49 @@ class Oracle:
             if ridx.size and (ridx.min() < 0 or ridx.max() >= M):
                 raise ValueError("row index out of range")
             nr = ridx.shape[0]
+        sc, sstride = self._scale(scale, M)
         # Outputs start as NaN, so an element the library never writes cannot pass as a value.
         grad = np.full((nr, V), np.nan, dtype=np.float64) if want_grad else None
         loss = np.full(nr, np.nan, dtype=np.float64)
-        self.lib.xro_xent_rows(ptr, ld, t.ctypes.data, None if ridx is None else ridx.ctypes.data,
-                               nr, int(V), int(ignore_index), code, int(n),
-                               None if grad is None else grad.ctypes.data, loss.ctypes.data)
+        self.lib.xro_xent_rows_ex(ptr, ld, t.ctypes.data,
+                                  None if ridx is None else ridx.ctypes.data, nr, int(V),
+                                  int(ignore_index), code, REDUCTIONS[reduction], int(n),
+                                  None if sc is None else sc.ctypes.data, sstride,
+                                  None if grad is None else grad.ctypes.data, loss.ctypes.data)
         return grad, loss
 
     def mean(self, loss: np.ndarray, n: int) -> float:
         lo = np.ascontiguousarray(loss, dtype=np.float64)
         return float(self.lib.xro_mean(lo.ctypes.data, lo.shape[0], int(n)))
 
+    def sum(self, loss: np.ndarray) -> float:
+        lo = np.ascontiguousarray(loss, dtype=np.float64)
+        return float(self.lib.xro_sum(lo.ctypes.data, lo.shape[0]))
+
     def xent(self, logits: np.ndarray, target: np.ndarray, V: int, ignore_index: int = -100,
-             want_grad: bool = True):
-        """(grad or None, row losses, mean loss, (n_non_ignore, n_bad))."""
+             want_grad: bool = True, reduction: str = "mean", scale=None):
+        """(grad or None, row losses, reduced loss, (n_non_ignore, n_bad)).
+
+        The reduced loss is the mean for "mean", the sum for "sum" and None for "none"."""
         n, bad = self.xent_count(target, V, ignore_index)
-        grad, loss = self.xent_rows(logits, target, V, n, ignore_index, None, want_grad)
-        return grad, loss, self.mean(loss, n), (n, bad)
+        grad, loss = self.xent_rows(logits, target, V, n, ignore_index, None, want_grad,
+                                    reduction, scale)
+        red = {"mean": lambda: self.mean(loss, n), "sum": lambda: self.sum(loss),
+               "none": lambda: None}[reduction]()
+        return grad, loss, red, (n, bad)
+
+    def element_mul(self, x: np.ndarray, scale, n_cols: int | None = None) -> np.ndarray:
+        """x[i, :V] * scale_i as float64 [M, V]; scale is a number or one value per row."""
+        ptr, ld, M, code = self._matrix(x)
+        V = x.shape[1] if n_cols is None else int(n_cols)
+        if not 0 < V <= x.shape[1]:
+            raise ValueError("n_cols out of range")
+        sc, sstride = self._scale(scale, M)
+        if sc is None:
+            raise ValueError("element_mul needs a scale")
+        out = np.full((M, V), np.nan, dtype=np.float64)
+        self.lib.xro_element_mul(ptr, ld, M, V, code, sc.ctypes.data, sstride, out.ctypes.data)
+        return out
 
 
 _default: Oracle | None = None

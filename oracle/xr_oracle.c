@@ -24,6 +24,16 @@
  *                        n counts the targets that differ from ignore_index,
  *                        zero rows (gradient and loss) for ignored targets,
  *                        and the mean of the row losses over n.
+ *   reductions and    -- the same page's kernel documents only the mean
+ *   upstream gradient    reduction; the sum and none reductions are read from
+ *                        the definition of the loss it links to: "sum" is
+ *                        sum_i loss_i, whose gradient is softmax - onehot (no
+ *                        1/n), and "none" returns the row losses, the gradient
+ *                        of row i being weighted by its own upstream value.
+ *                        `LigerCrossEntropyFunction.backward` and its
+ *                        `element_mul` kernel multiply the stored gradient by
+ *                        the upstream gradient of the loss; the forward here
+ *                        can apply that factor while it writes the gradient.
  *
  * The oracle deliberately uses the two-pass safe form (max first, then the
  * sum with that max), not the online running max/sum of the GPU path; both
@@ -53,6 +63,7 @@
 #endif
 
 enum { XRO_F32 = 0, XRO_BF16 = 1 };
+enum { XRO_MEAN = 0, XRO_SUM = 1, XRO_NONE = 2 };
 
 /* Element idx (in elements from base) of a bf16 or fp32 buffer, as double. */
 static double load_elem(const void* base, int64_t idx, int dtype) {
@@ -138,14 +149,20 @@ void xro_xent_count(const int64_t* target, int64_t M, int64_t V, int64_t ignore_
 
 /*
  * Cross-entropy loss and gradient for a list of rows.
- *   rows     : row indices into logits/target, or NULL for rows 0..nrows-1
- *   n        : the batch's non-ignored count (from xro_xent_count)
- *   grad     : [nrows][V] contiguous doubles, or NULL to skip the gradient
- *   loss     : [nrows] doubles
+ *   rows         : row indices into logits/target, or NULL for rows 0..nrows-1
+ *   reduction    : XRO_MEAN (gradient of sum_i loss_i / n), XRO_SUM (gradient of
+ *                  sum_i loss_i) or XRO_NONE (gradient of the row losses)
+ *   n            : the batch's non-ignored count (from xro_xent_count)
+ *   scale        : upstream gradient; row i's gradient is multiplied by
+ *                  scale[i * scale_stride] (stride 0: one value for every row);
+ *                  NULL means 1. Ignored rows stay exactly zero.
+ *   grad         : [nrows][V] contiguous doubles, or NULL to skip the gradient
+ *   loss         : [nrows] doubles
  */
-void xro_xent_rows(const void* logits, int64_t ld, const int64_t* target, const int64_t* rows,
-                   int64_t nrows, int64_t V, int64_t ignore_index, int dtype, int64_t n,
-                   double* grad, double* loss) {
+void xro_xent_rows_ex(const void* logits, int64_t ld, const int64_t* target, const int64_t* rows,
+                      int64_t nrows, int64_t V, int64_t ignore_index, int dtype, int reduction,
+                      int64_t n, const double* scale, int64_t scale_stride, double* grad,
+                      double* loss) {
   int64_t r;
 #pragma omp parallel for schedule(dynamic, 4)
   for (r = 0; r < nrows; ++r) {
@@ -169,11 +186,43 @@ void xro_xent_rows(const void* logits, int64_t ld, const int64_t* target, const 
     double xt = load_elem(logits, off + t, dtype);
     loss[r] = m + log(d) - xt;
     if (g) {
+      /* d(loss_i)/d(x_ij) = p_j - [j == t]; the reduction and the upstream value scale it. */
+      double w = scale ? scale[i * scale_stride] : 1.0;
+      if (reduction == XRO_MEAN) w = w / (double)n;
       for (int64_t j = 0; j < V; ++j) {
         double p = exp(load_elem(logits, off + j, dtype) - m) / d;
-        g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;
+        g[j] = w * ((j == t) ? p - 1.0 : p);
       }
     }
+  }
+}
+
+/* The mean-reduction case with upstream gradient 1 (the pages' own kernel). */
+void xro_xent_rows(const void* logits, int64_t ld, const int64_t* target, const int64_t* rows,
+                   int64_t nrows, int64_t V, int64_t ignore_index, int dtype, int64_t n,
+                   double* grad, double* loss) {
+  xro_xent_rows_ex(logits, ld, target, rows, nrows, V, ignore_index, dtype, XRO_MEAN, n, NULL, 0,
+                   grad, loss);
+}
+
+/* sum_i loss_i, left to right in row order. */
+double xro_sum(const double* loss, int64_t M) {
+  double s = 0.0;
+  for (int64_t i = 0; i < M; ++i) s += loss[i];
+  return s;
+}
+
+/*
+ * The backward's `element_mul`: out[i][j] = x[i][j] * scale[i * scale_stride] for the V
+ * columns of each row of x (row stride ld, read in dtype); out is [M][V] contiguous doubles.
+ */
+void xro_element_mul(const void* x, int64_t ld, int64_t M, int64_t V, int dtype,
+                     const double* scale, int64_t scale_stride, double* out) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) {
+    double w = scale[i * scale_stride];
+    for (int64_t j = 0; j < V; ++j) out[i * V + j] = load_elem(x, i * ld + j, dtype) * w;
   }
 }
 

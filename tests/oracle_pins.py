@@ -290,9 +290,100 @@ def pin_xent_row_subset_and_padding(o):
     rows = np.array([19, 0, 7, 7, 13])
     g_sub, l_sub = o.xent_rows(x, t, 300, n, rows=rows)
     assert np.array_equal(g_sub, g_all[rows]) and np.array_equal(l_sub, l_all[rows])
+    # a per-row upstream gradient belongs to the row, not to its place in the list
+    s = np.arange(1.0, 21.0)
+    g_none, _, _, _ = o.xent(x, t, 300, reduction="none", scale=s)
+    g_sub, _ = o.xent_rows(x, t, 300, n, rows=rows, reduction="none", scale=s)
+    assert np.array_equal(g_sub, g_none[rows])
     dense = np.ascontiguousarray(x[:, :300])
     g_d, l_d, _, _ = o.xent(dense, t, 300)
     assert np.array_equal(g_d, g_all) and np.array_equal(l_d, l_all)
+
+
+# ------------------------------------------------------- reductions and upstream gradient
+def pin_xent_reductions_finite_differences(o):
+    """Each reduction's gradient, times its upstream value, is the derivative of that loss."""
+    M, V = 5, 7
+    x = _grid_rows(16, M, V, 1.0 / 4, -2.0, 2.0)
+    t = np.array([3, -100, 0, 6, 2], dtype=np.int64)
+    s = np.array([0.5, -2.0, 3.0, 1.25, -0.75])
+    n = 4
+    cases = [("none", s, lambda loss: float(np.dot(s, loss))),
+             ("sum", -1.5, lambda loss: -1.5 * math.fsum(loss.tolist())),
+             ("mean", 2.5, lambda loss: 2.5 * math.fsum(loss.tolist()) / n)]
+    h = 2.0 ** -14
+    for reduction, scale, objective in cases:
+        grad, _, _, (nn, _) = o.xent(x, t, V, reduction=reduction, scale=scale)
+        assert nn == n
+        for i in range(M):
+            for j in range(V):
+                xp, xm = x.copy(), x.copy()
+                xp[i, j] += np.float32(h)
+                xm[i, j] -= np.float32(h)
+                fp = objective(o.xent(xp, t, V, want_grad=False)[1])
+                fm = objective(o.xent(xm, t, V, want_grad=False)[1])
+                fd = (fp - fm) / (2 * h)
+                assert abs(fd - grad[i, j]) <= 1e-8, f"{reduction}: gradient vs finite differences at ({i},{j})"
+
+
+def pin_xent_reductions_match_torch(o):
+    import torch
+    import torch.nn.functional as F
+    M, V = 11, 300
+    x = synth.random_rows(1300, M, V, dtype="bf16", scale=3.0)
+    t = synth.random_targets(1301, M, V, ignore_frac=0.3)
+    s = synth.random_rows(1302, 1, M, dtype="f32", scale=2.0)[0].astype(np.float64)
+    xt = torch.from_numpy(decode(x))
+    tt = torch.from_numpy(t)
+    # none: upstream gradient s_i on row i
+    a = xt.clone().requires_grad_(True)
+    ref = F.cross_entropy(a, tt, reduction="none")
+    (ref * torch.from_numpy(s)).sum().backward()
+    grad, loss, red, _ = o.xent(x, t, V, reduction="none", scale=s)
+    assert red is None
+    assert np.max(np.abs(loss - ref.detach().numpy())) <= 1e-12, "none: row losses vs torch"
+    assert np.max(np.abs(grad - a.grad.numpy())) <= 1e-14, "none: gradient vs torch autograd"
+    # sum: one upstream value for the scalar
+    b = xt.clone().requires_grad_(True)
+    ref = F.cross_entropy(b, tt, reduction="sum")
+    (ref * -0.625).backward()
+    grad, loss, red, _ = o.xent(x, t, V, reduction="sum", scale=-0.625)
+    assert abs(red - ref.item()) <= 1e-13 * abs(ref.item()), "sum: loss vs torch"
+    assert np.max(np.abs(grad - b.grad.numpy())) <= 1e-14, "sum: gradient vs torch autograd"
+    # mean with an upstream value: torch's mean loss scaled
+    c = xt.clone().requires_grad_(True)
+    ref = F.cross_entropy(c, tt, reduction="mean")
+    (ref * 3.0).backward()
+    grad, _, red, _ = o.xent(x, t, V, reduction="mean", scale=3.0)
+    assert abs(red - ref.item()) <= 1e-13 * abs(ref.item()), "mean: loss vs torch"
+    assert np.max(np.abs(grad - c.grad.numpy())) <= 1e-14, "mean: gradient vs torch autograd"
+
+
+def pin_xent_sum_is_exact_sum(o):
+    t = synth.random_targets(1400, 700, 90, ignore_frac=0.2)
+    x = synth.random_rows(1401, 700, 90, dtype="f32", scale=5.0)
+    _, loss, red, (n, _) = o.xent(x, t, 90, reduction="sum", want_grad=False)
+    assert abs(red - math.fsum(loss.tolist())) <= 1e-12 * abs(red), "sum = fsum(row losses)"
+    _, _, mean, _ = o.xent(x, t, 90, want_grad=False)
+    assert abs(mean * n - red) <= 1e-12 * abs(red), "sum = n * mean"
+    assert o.sum(np.zeros(0)) == 0.0
+
+
+def pin_element_mul_products(o):
+    """Products with scales of few significant bits are exact in float64, so they must match
+    the decoded inputs times the scale bit for bit; padding columns are never read."""
+    M, V, ld = 6, 257, 300
+    for dtype in ("bf16", "f32"):
+        x = synth.random_rows(1500, M, V, ld=ld, dtype=dtype, scale=4.0)
+        xd = decode(x)[:, :V]
+        rows = np.array([2.0, 0.5, -1.0, 1.0, 0.0, -3.0])
+        out = o.element_mul(x, rows, n_cols=V)
+        assert np.array_equal(out, xd * rows[:, None]), f"{dtype}: per-row products"
+        assert np.array_equal(out[3], xd[3]) and np.array_equal(out[2], -xd[2])
+        assert np.all(out[4] == 0.0)
+        out = o.element_mul(x, 0.25, n_cols=V)
+        assert np.array_equal(out, xd * 0.25), f"{dtype}: one scale for every row"
+        assert np.all(np.isfinite(out)), "padding (NaN) must never be read"
 
 
 # --------------------------------------------------------------------------- worked examples
@@ -317,6 +408,25 @@ def pin_golden_worked_examples(o):
         assert abs(mean - closed_form(case["mean"])) <= 1e-15, case["name"]
         want = np.array([[closed_form(v) for v in r] for r in case["grad"]])
         assert np.max(np.abs(grad - want)) <= 1e-15, case["name"]
+    for case in gold["xent_reduced"]:
+        x = as_input(case["x"], case["dtype"])
+        t = np.array(case["target"], dtype=np.int64)
+        V = x.shape[1]
+        grad, loss, red, (n, bad) = o.xent(x, t, V, ignore_index=case["ignore_index"],
+                                           reduction=case["reduction"], scale=case["scale"])
+        assert n == case["n"] and bad == 0, case["name"]
+        assert np.max(np.abs(loss - [closed_form(v) for v in case["loss"]])) <= 1e-15, case["name"]
+        if case["reduced"] is None:
+            assert red is None, case["name"]
+        else:
+            assert abs(red - closed_form(case["reduced"])) <= 1e-15, case["name"]
+        want = np.array([[closed_form(v) for v in r] for r in case["grad"]])
+        assert np.max(np.abs(grad - want)) <= 1e-15, case["name"]
+    for case in gold["element_mul"]:
+        x = as_input(case["x"], case["dtype"])
+        out = o.element_mul(x, case["scale"], n_cols=case["n_cols"])
+        want = np.array([[closed_form(v) for v in r] for r in case["out"]])
+        assert np.array_equal(out, want), case["name"]
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -34,12 +34,31 @@ MUTANTS = {
     "loss drops log d": ("loss[r] = m + log(d) - xt;", "loss[r] = m - xt;"),
     "target logit read from row 0": ("double xt = load_elem(logits, off + t, dtype);",
                                      "double xt = load_elem(logits, t, dtype);"),
-    "gradient not divided by n": ("g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;",
-                                  "g[j] = (j == t) ? (p - 1.0) / (double)n : p;"),
-    "onehot at the wrong column": ("g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;",
-                                   "g[j] = (j == t + 1) ? (p - 1.0) / (double)n : p / (double)n;"),
-    "onehot added instead of subtracted": ("g[j] = (j == t) ? (p - 1.0) / (double)n : p / (double)n;",
-                                           "g[j] = (j == t) ? (p + 1.0) / (double)n : p / (double)n;"),
+    "gradient not divided by n": ("if (reduction == XRO_MEAN) w = w / (double)n;",
+                                  "if (reduction == XRO_MEAN) w = w;"),
+    "onehot at the wrong column": ("g[j] = w * ((j == t) ? p - 1.0 : p);",
+                                   "g[j] = w * ((j == t + 1) ? p - 1.0 : p);"),
+    "onehot added instead of subtracted": ("g[j] = w * ((j == t) ? p - 1.0 : p);",
+                                           "g[j] = w * ((j == t) ? p + 1.0 : p);"),
+    "upstream gradient ignored": ("double w = scale ? scale[i * scale_stride] : 1.0;",
+                                  "double w = 1.0;"),
+    "upstream gradient of row 0 for every row": ("double w = scale ? scale[i * scale_stride] : 1.0;",
+                                                 "double w = scale ? scale[0] : 1.0;"),
+    "upstream gradient indexed by list position": (
+        "double w = scale ? scale[i * scale_stride] : 1.0;",
+        "double w = scale ? scale[r * scale_stride] : 1.0;"),
+    "sum reduction divides by n": ("if (reduction == XRO_MEAN) w = w / (double)n;",
+                                   "if (reduction != XRO_NONE) w = w / (double)n;"),
+    "none reduction divides by n": ("if (reduction == XRO_MEAN) w = w / (double)n;",
+                                    "if (reduction != XRO_SUM) w = w / (double)n;"),
+    "sum skips the first loss": ("for (int64_t i = 0; i < M; ++i) s += loss[i];\n  return s;",
+                                 "for (int64_t i = 1; i < M; ++i) s += loss[i];\n  return s;"),
+    "element_mul ignores the row stride": ("out[i * V + j] = load_elem(x, i * ld + j, dtype) * w;",
+                                           "out[i * V + j] = load_elem(x, i * V + j, dtype) * w;"),
+    "element_mul scales by row 0's value": ("double w = scale[i * scale_stride];",
+                                            "double w = scale[0];"),
+    "element_mul adds the scale": ("out[i * V + j] = load_elem(x, i * ld + j, dtype) * w;",
+                                   "out[i * V + j] = load_elem(x, i * ld + j, dtype) + w;"),
     "ignored rows keep stale gradient": ("        for (int64_t j = 0; j < V; ++j) g[j] = 0.0;\n      continue;",
                                          "        for (int64_t j = 0; j < V; ++j) (void)g;\n      continue;"),
     "ignored rows counted in n": ("    if (target[i] == ignore_index) continue;\n    ++n;",
