@@ -13,13 +13,17 @@ the library records around that launch on its stream; `cpu_baseline` times the f
 oracle on the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
-                    [--workload c4|c3|c5|c2|c1]
+                    [--workload c4|c3|c5|c2|c1|c4-mul] [--reduction mean|sum|none]
+                    [--grad-scale S]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
 
 The other workloads (c1 softmax fp32 128x1000, c2 softmax forward + backward bf16 4096^2,
 c3 cross-entropy bf16 8192x32000, c5 cross-entropy fp32 2048x256000 padded) print the same
 kind of line; small inputs are rotated through >= 1 GB of copies so no step reads data a
-previous step left in the 256 MB Infinity Cache.
+previous step left in the 256 MB Infinity Cache. `--reduction` / `--grad-scale` run the
+cross-entropy workloads with another reduction or an upstream gradient folded into the
+gradient write; `c4-mul` times the backward's element_mul (the stored gradient times an
+upstream gradient of 0.5) over the 16384 x 128256 bf16 matrix.
 """
 from __future__ import annotations
 
@@ -48,6 +52,8 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 C4_M, C4_V, C4_KEEP = 16384, 128256, 15565
 
 DESCRIPTIONS = {
+    "c4-mul": "element_mul (stored gradient x upstream gradient 0.5, in place), M=16384, "
+              "V=128256, bf16",
     "c1": "softmax forward, M=128, N=1000, fp32 logits 3 N(0,1), contiguous",
     "c2": "softmax forward + backward, M=4096, N=4096, bf16 in / fp32 accumulation, "
           "x and dy N(0,1)",
@@ -210,9 +216,14 @@ def run_xent(args, name: str) -> dict:
     dt = copies[0].dtype
     ws = torch.empty(max(256, xr.xent_workspace_bytes(M, V, dt)), dtype=torch.uint8, device=dev)
 
+    scale = None
+    if args.grad_scale is not None:
+        scale = torch.tensor([args.grad_scale], dtype=torch.float32, device=dev)
+
     def launch(i):
         xr.xent_fwd_bwd(copies[i][:, :V], t, -100, row_loss=row_loss, mean_loss=mean,
-                        counts=counts, workspace=ws)
+                        counts=counts, workspace=ws, reduction=args.reduction,
+                        grad_scale=scale)
 
     wall, kernel_ms = _timed(HipEvents(), steps, warmup, launch)
     c = counts.cpu().tolist()
@@ -221,12 +232,40 @@ def run_xent(args, name: str) -> dict:
     p = xr.plan("xent", M, V, dt)
     out = _line(args, name, bmin, M, wall, kernel_ms, ROW_KERNEL,
                 {"M": M, "V": V, "n_non_ignore": n_keep, "bytes_min": bmin, "path": p["path"],
-                 "threads": p["threads"], "split": p["split"], "grid": p["grid"]},
+                 "threads": p["threads"], "split": p["split"], "grid": p["grid"],
+                 "reduction": args.reduction, "grad_scale": args.grad_scale},
                 w["dtype"])
-    if name == "c4":
+    if name == "c4" and args.reduction == "mean" and args.grad_scale is None:
         out["roofline"]["traffic"] = measured_traffic()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
+    return out
+
+
+def run_element_mul(args, name: str) -> dict:
+    """The backward's element_mul over the c4 matrix: every row read and written once."""
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.xent_c4()
+    M, V = w["M"], w["N"]
+    x0 = _device_matrix(torch, w["x"], dev)
+    copies = [x0.clone() for _ in range(args.warmup + args.steps)]
+    del x0
+    scale = torch.tensor([0.5], dtype=torch.float32, device=dev)
+
+    def launch(i):
+        xr.element_mul(copies[i], scale)
+
+    wall, kernel_ms = _timed(HipEvents(), args.steps, args.warmup, launch)
+    bmin = 2 * M * V * 2 + 4
+    out = _line(args, name, bmin, M, wall, kernel_ms, "element_mul_kernel",
+                {"M": M, "V": V, "bytes_min": bmin, "threads": 256, "vec_per_thread": 8},
+                "bf16")
     return out
 
 
@@ -354,6 +393,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--workload", default="c4", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--reduction", default="mean", choices=["mean", "sum", "none"])
+    ap.add_argument("--grad-scale", type=float, default=None,
+                    help="upstream gradient folded into the cross-entropy gradient write")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.summarize_counters:
@@ -369,6 +411,8 @@ def main() -> int:
         return 2
     if args.workload in ("c1", "c2"):
         out = run_softmax(args, args.workload)
+    elif args.workload == "c4-mul":
+        out = run_element_mul(args, args.workload)
     else:
         out = run_xent(args, args.workload)
     print(json.dumps(out), flush=True)

@@ -3,8 +3,12 @@
 A thin ctypes binding over ``libxr.so`` (``include/xr.h``): every function here
 checks and marshals its torch tensors into the C ABI call of the same name
 (``softmax_fwd`` -> ``xr_softmax_fwd``, ``softmax_bwd`` -> ``xr_softmax_bwd``,
-``xent_fwd_bwd`` -> ``xr_xent_fwd_bwd``, ...). All of the computation runs in the
-library's HIP kernels; PyTorch only provides device memory and the current stream.
+``xent_fwd_bwd`` -> ``xr_xent_fwd_bwd_ex``, ``element_mul`` -> ``xr_element_mul``, ...).
+All of the computation runs in the library's HIP kernels; PyTorch only provides device
+memory and the current stream. ``CrossEntropyFunction`` / ``cross_entropy`` wrap the
+fused cross-entropy as a ``torch.autograd.Function`` the way the Liger-Kernel
+``cross_entropy.py`` page's ``LigerCrossEntropyFunction`` does: the forward leaves the
+gradient in the logits' memory, the backward scales it by the upstream gradient.
 
 There is no fallback: importing this package raises if ``libxr.so`` has not been
 built (``python cross_entropy_reductions_amd/build.py``), and every call raises on a
@@ -37,6 +41,11 @@ lib.xr_xent_workspace_bytes.restype = _sz
 lib.xr_xent_fwd_bwd.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p, _p, _p, _p,
                                 _sz, _p]
 lib.xr_xent_fwd_bwd.restype = ctypes.c_int
+lib.xr_xent_fwd_bwd_ex.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                   _p, _i64, _p, _p, _p, _p, _sz, _p]
+lib.xr_xent_fwd_bwd_ex.restype = ctypes.c_int
+lib.xr_element_mul.argtypes = [_p, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p]
+lib.xr_element_mul.restype = ctypes.c_int
 lib.xr_status_string.argtypes = [ctypes.c_int]
 lib.xr_status_string.restype = ctypes.c_char_p
 lib.xr_version.argtypes = []
@@ -57,14 +66,15 @@ lib.xr_set_profile_events.restype = ctypes.c_int
 
 # Names exported by include/xr.h (checked against the library by the tests).
 C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_xent_workspace_bytes", "xr_xent_fwd_bwd",
-             "xr_status_string", "xr_version", "xr_plan", "xr_set_option",
-             "xr_set_profile_events")
+             "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_status_string", "xr_version",
+             "xr_plan", "xr_set_option", "xr_set_profile_events")
 
 F32, BF16 = 0, 1
 OK = 0
 PATHS = {1: "resident", 2: "split", 3: "stream"}
 OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2}
 OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4, "load_policy": 5}
+REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -145,42 +155,111 @@ def xent_workspace_bytes(M: int, V: int, dtype: torch.dtype) -> int:
     return int(lib.xr_xent_workspace_bytes(int(M), int(V), _DTYPES[dtype]))
 
 
+def _scale_arg(scale, M: int, dev, name: str):
+    """(pointer, stride) of an upstream-gradient argument: None, a number, or a float32
+    device tensor holding one value (any shape with one element) or one value per row."""
+    if scale is None:
+        return None, 0, None
+    if not isinstance(scale, torch.Tensor):
+        scale = torch.tensor([float(scale)], dtype=torch.float32, device=dev)
+    if scale.dtype != torch.float32 or scale.device != dev:
+        raise TypeError(f"{name} must be a float32 tensor on the logits' device")
+    if scale.numel() == 1:
+        return scale.data_ptr(), 0, scale
+    if scale.dim() != 1 or scale.shape[0] != M:
+        raise ValueError(f"{name} must hold one value, or one value per row")
+    return scale.data_ptr(), scale.stride(0), scale
+
+
 def xent_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100, *,
+                 reduction: str = "mean", grad_scale=None,
                  row_loss: torch.Tensor | None = None, mean_loss: torch.Tensor | None = None,
                  counts: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  stream=None):
-    """Fused cross-entropy: overwrites ``logits`` with the gradient of the mean loss.
+    """Fused cross-entropy: overwrites ``logits`` with the gradient of the reduced loss.
 
-    Returns ``(mean_loss, row_loss, counts)``: a 1-element fp32 tensor, the fp32 row
-    losses and int32 ``[n_non_ignore, n_bad_target, error_flags]``, all on the device
-    (nothing is synchronised).
+    ``reduction`` is "mean" (the pages' kernel), "sum" or "none"; ``grad_scale`` is the
+    upstream gradient folded into the gradient write (None for 1, a number, or a float32
+    device tensor of one value or one value per row). Returns ``(loss, row_loss, counts)``:
+    the reduced loss as a 1-element fp32 tensor (the row losses themselves for "none"),
+    the fp32 row losses and int32 ``[n_non_ignore, n_bad_target, error_flags]``, all on the
+    device (nothing is synchronised).
     """
     pl, ld, M, V, dt = _matrix(logits, "logits")
     dev = logits.device
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
     if not isinstance(target, torch.Tensor) or target.dtype != torch.int64 or target.device != dev:
         raise TypeError("target must be an int64 tensor on the logits' device")
     if target.dim() != 1 or target.shape[0] != M or (M > 1 and target.stride(0) != 1):
         raise ValueError("target must be a contiguous 1-D tensor of one entry per row")
     if row_loss is None:
         row_loss = torch.empty(M, dtype=torch.float32, device=dev)
-    if mean_loss is None:
+    if mean_loss is None and reduction != "none":
         mean_loss = torch.empty(1, dtype=torch.float32, device=dev)
     if counts is None:
         counts = torch.empty(3, dtype=torch.int32, device=dev)
-    for t, name, dtp, n in ((row_loss, "row_loss", torch.float32, M),
-                            (mean_loss, "mean_loss", torch.float32, 1),
-                            (counts, "counts", torch.int32, 3)):
+    outs = [(row_loss, "row_loss", torch.float32, M), (counts, "counts", torch.int32, 3)]
+    if reduction != "none":
+        outs.append((mean_loss, "mean_loss", torch.float32, 1))
+    for t, name, dtp, n in outs:
         if t.dtype != dtp or t.device != dev or t.numel() < n or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dtp} tensor of >= {n} entries")
+    ps, sstride, _keep = _scale_arg(grad_scale, M, dev, "grad_scale")
     need = xent_workspace_bytes(M, V, logits.dtype) if M >= 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("xr_xent_fwd_bwd",
-           lib.xr_xent_fwd_bwd(pl, ld, target.data_ptr(), M, V, int(ignore_index), dt,
-                               row_loss.data_ptr(), mean_loss.data_ptr(), counts.data_ptr(),
-                               workspace.data_ptr(), ws_bytes, _stream(logits, stream)))
-    return mean_loss, row_loss, counts
+    _check("xr_xent_fwd_bwd_ex",
+           lib.xr_xent_fwd_bwd_ex(pl, ld, target.data_ptr(), M, V, int(ignore_index), dt,
+                                  REDUCTIONS[reduction], ps, sstride, row_loss.data_ptr(),
+                                  None if reduction == "none" else mean_loss.data_ptr(),
+                                  counts.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                  _stream(logits, stream)))
+    return (row_loss if reduction == "none" else mean_loss), row_loss, counts
+
+
+def element_mul(x: torch.Tensor, grad_output, *, stream=None) -> torch.Tensor:
+    """x[i, :] *= grad_output[i] in place (one value for all rows, or one per row; rows
+    whose value is exactly 1.0 are left untouched without being read). Returns x."""
+    px, ld, M, N, dt = _matrix(x, "x")
+    pg, gstride, _keep = _scale_arg(grad_output, M, x.device, "grad_output")
+    if pg is None:
+        raise ValueError("grad_output is required")
+    _check("xr_element_mul", lib.xr_element_mul(px, ld, M, N, dt, pg, gstride, _stream(x, stream)))
+    return x
+
+
+class CrossEntropyFunction(torch.autograd.Function):
+    """Cross-entropy whose forward computes the loss and, in the same pass, the gradient,
+    stored in the logits' own memory (the logits are overwritten); the backward multiplies
+    that stored gradient by the upstream gradient (``element_mul``; skipped on the device
+    for rows whose upstream value is exactly 1.0). As on the Liger-Kernel page, the logits
+    tensor passed in must not be needed afterwards by anything else."""
+
+    @staticmethod
+    def forward(ctx, logits, target, ignore_index=-100, reduction="mean"):
+        loss, _, _ = xent_fwd_bwd(logits, target, ignore_index, reduction=reduction)
+        ctx.reduction = reduction
+        ctx.save_for_backward(logits.detach())
+        return loss.reshape(()) if reduction != "none" else loss
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        (grad,) = ctx.saved_tensors
+        g = grad_output
+        if g.dtype != torch.float32:
+            g = g.float()
+        if g.dim() > 1 or (g.dim() == 1 and g.shape[0] != grad.shape[0]):
+            raise ValueError("unexpected upstream gradient shape")
+        element_mul(grad, g.reshape(-1) if g.dim() == 0 else g)
+        return grad, None, None, None
+
+
+def cross_entropy(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
+                  reduction: str = "mean") -> torch.Tensor:
+    """Autograd-aware fused cross-entropy (``CrossEntropyFunction``); logits are consumed."""
+    return CrossEntropyFunction.apply(logits, target, ignore_index, reduction)
 
 
 def plan(op: str, M: int, N: int, dtype: torch.dtype, aligned: int = 2) -> dict:

@@ -18,7 +18,7 @@
 namespace xr {
 namespace {
 
-constexpr int32_t kVersion = 10000;  // 1.0.0
+constexpr int32_t kVersion = 10100;  // 1.1.0
 constexpr int64_t kMinChunkVecs = 256;
 
 // ----------------------------------------------------------------------------- options
@@ -286,6 +286,7 @@ const char* xr_status_string(xr_status_t s) {
     case XR_ERR_DEVICE: return "no usable HIP device";
     case XR_ERR_LAUNCH: return "kernel launch failed";
     case XR_ERR_OPTION: return "unknown option or value";
+    case XR_ERR_VALUE: return "invalid argument value";
   }
   return "unknown status";
 }
@@ -393,19 +394,28 @@ size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype) {
   return xent_ws_bytes(p, M);
 }
 
-xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int64_t M,
-                            int64_t V, int64_t ignore_index, xr_dtype_t dtype, float* row_loss,
-                            float* mean_loss, int32_t* counts, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, int64_t M,
+                               int64_t V, int64_t ignore_index, xr_dtype_t dtype,
+                               xr_reduction_t reduction, const float* grad_scale,
+                               int64_t grad_scale_stride, float* row_loss, float* loss,
+                               int32_t* counts, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (reduction != XR_REDUCTION_MEAN && reduction != XR_REDUCTION_SUM &&
+      reduction != XR_REDUCTION_NONE)
+    return XR_ERR_VALUE;
+  if (grad_scale_stride < 0) return XR_ERR_VALUE;
   if (M < 0 || V < 1) return XR_ERR_SHAPE;
   if (ld < V) return XR_ERR_STRIDE;
-  if (!mean_loss || !workspace) return XR_ERR_NULL;
+  if (reduction != XR_REDUCTION_NONE && !loss) return XR_ERR_NULL;
+  if (reduction == XR_REDUCTION_NONE) loss = nullptr;
+  if (!workspace) return XR_ERR_NULL;
   if (M > 0 && (!logits || !target || !row_loss)) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if ((logits && !aligned_to(logits, eb)) || (target && !aligned_to(target, 8)) ||
-      (row_loss && !aligned_to(row_loss, 4)) || !aligned_to(mean_loss, 4) ||
-      (counts && !aligned_to(counts, 4)) || !aligned_to(workspace, 8))
+      (row_loss && !aligned_to(row_loss, 4)) || (loss && !aligned_to(loss, 4)) ||
+      (counts && !aligned_to(counts, 4)) || (grad_scale && !aligned_to(grad_scale, 4)) ||
+      !aligned_to(workspace, 8))
     return XR_ERR_ALIGN;
   Plan p;
   const bool on16 = logits == nullptr || rows_on_16(logits, ld, M, eb);
@@ -428,7 +438,8 @@ xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int
   if (M > 0) {
     XentParams prm{static_cast<char*>(logits), ld * eb, target, M, V, ignore_index, row_loss,
                    ws_counts, ws_counts + 2, partials, p.chunk_vecs, p.S,
-                   (int)(p.path == kPathSplit ? p.grid / p.S : p.grid)};
+                   (int)(p.path == kPathSplit ? p.grid / p.S : p.grid), (int)reduction,
+                   grad_scale, grad_scale_stride};
     if (xr_status_t st = launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads))
       return st;
   }
@@ -436,11 +447,59 @@ xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int
     const float* rl = row_loss;
     int64_t mm = M;
     const int32_t* wc = ws_counts;
-    void* args[] = {&rl, &mm, &wc, &mean_loss, &counts};
+    int red = (int)reduction;
+    void* args[] = {&rl, &mm, &wc, &loss, &counts, &red};
     if (hipLaunchKernel(xent_mean_kernel_ptr(), dim3(1), dim3(kScanThreads), args, 0, s) != hipSuccess)
       return XR_ERR_LAUNCH;
   }
   return XR_OK;
+}
+
+xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int64_t M,
+                            int64_t V, int64_t ignore_index, xr_dtype_t dtype, float* row_loss,
+                            float* mean_loss, int32_t* counts, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return xr_xent_fwd_bwd_ex(logits, ld, target, M, V, ignore_index, dtype, XR_REDUCTION_MEAN,
+                            nullptr, 0, row_loss, mean_loss, counts, workspace, workspace_bytes,
+                            stream);
+}
+
+xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t dtype,
+                           const float* grad_output, int64_t grad_output_stride, void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (grad_output_stride < 0) return XR_ERR_VALUE;
+  if (M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (ld < N) return XR_ERR_STRIDE;
+  if (M == 0) return XR_OK;
+  if (!x || !grad_output) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if (!aligned_to(x, eb) || !aligned_to(grad_output, 4)) return XR_ERR_ALIGN;
+  {
+    // grad_output must not lie inside the matrix's span
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x);
+    const uintptr_t a1 = a0 + (uintptr_t)((M - 1) * ld + N) * (uintptr_t)eb;
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_output);
+    const uintptr_t g1 = g0 + (uintptr_t)((M - 1) * grad_output_stride + 1) * 4u;
+    if (g0 < a1 && a0 < g1) return XR_ERR_ALIAS;
+  }
+  // Vectors a row spans (one more when it does not start on a 16-byte boundary).
+  const int64_t epv = 16 / eb;
+  const int64_t nvm = (N + epv - 1) / epv + ((reinterpret_cast<uintptr_t>(x) & 15u) ||
+                                             ((ld * eb) & 15) ? 1 : 0);
+  const int64_t cv = (int64_t)kMulThreads * kMulVpt;
+  const int64_t chunks = (nvm + cv - 1) / cv;
+  if (M > INT64_MAX / chunks) return XR_ERR_SHAPE;
+  const int64_t total = M * chunks;
+  // One workgroup per row chunk, up to the grid limit; the kernel strides past it.
+  const int64_t grid = std::min<int64_t>(total, 0x7FFFFFFF);
+  bool nt = g_opt.load_policy == 0 ? true : g_opt.load_policy == 2;
+  const void* kern = element_mul_kernel_ptr(dtype, nt);
+  ElementMulParams prm{static_cast<char*>(x), ld * eb, M, N, grad_output, grad_output_stride,
+                       cv, chunks};
+  Plan p;
+  p.kernel = kern;
+  p.grid = grid;
+  return launch(p, &prm, static_cast<hipStream_t>(stream), kMulThreads);
 }
 
 }  // extern "C"

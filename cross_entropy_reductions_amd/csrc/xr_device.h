@@ -29,11 +29,13 @@ template <> struct Elt<kF32> {
   static constexpr int kBytes = 4;
   static constexpr int kPerVec = 4;
   static constexpr uint32_t kNegInfWord = 0xFF800000u;
+  static constexpr uint32_t kSignWord = 0x80000000u;  // sign bit of every element of a word
 };
 template <> struct Elt<kBF16> {
   static constexpr int kBytes = 2;
   static constexpr int kPerVec = 8;
   static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
+  static constexpr uint32_t kSignWord = 0x80008000u;
 };
 
 __device__ __forceinline__ float as_f32(uint32_t b) { return __builtin_bit_cast(float, b); }

@@ -18,6 +18,9 @@ constexpr uint64_t kPartialEmpty = ~0ull;
 
 enum Path : int { kPathAuto = 0, kPathResident = 1, kPathSplit = 2, kPathStream = 3 };
 
+// Loss reductions (the values of xr_reduction_t).
+enum Reduction : int { kReduceMean = 0, kReduceSum = 1, kReduceNone = 2 };
+
 struct XentParams {
   char* logits;           // row 0 of the logits (overwritten by the gradient)
   int64_t ld_bytes;       // row pitch in bytes
@@ -30,6 +33,21 @@ struct XentParams {
   int64_t chunk_vecs;     // 16-byte vectors per chunk (the whole row when S == 1)
   int S;                  // workgroups per row
   int groups;             // row groups in the grid; grid = groups * S
+  int reduction;          // Reduction: the mean divides the gradient by n
+  const float* gscale;    // upstream gradient, row i at gscale[i * gstride]; nullptr = 1
+  int64_t gstride;
+};
+
+// Rows x[i, 0:V) scaled in place by scale[i * sstride]; chunk_vecs 16-byte vectors per
+// workgroup, `chunks` workgroups per row.
+struct ElementMulParams {
+  char* x;
+  int64_t ld_bytes;
+  int64_t M, V;
+  const float* scale;
+  int64_t sstride;
+  int64_t chunk_vecs;
+  int64_t chunks;
 };
 
 struct SoftmaxFwdParams {
@@ -66,10 +84,14 @@ const void* softmax_fwd_stream_kernel_ptr(int dtype);
 const void* softmax_bwd_stream_kernel_ptr(int dtype);
 const void* xent_scan_kernel_ptr();
 const void* xent_mean_kernel_ptr();
+const void* element_mul_kernel_ptr(int dtype, bool nt_loads);
 
 // Workgroup size of the stream, scan and mean kernels.
 constexpr int kStreamThreads = 256;
 constexpr int kScanThreads = 1024;
+// element_mul: workgroup size and 16-byte vectors per thread.
+constexpr int kMulThreads = 256;
+constexpr int kMulVpt = 8;
 
 // Shapes available to the row-resident kernels, smallest capacity first.
 constexpr int kNumFwdShapes = 7;

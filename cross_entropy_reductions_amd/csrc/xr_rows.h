@@ -163,14 +163,26 @@ __device__ __forceinline__ Stats thread_stats(u32x4 (&v)[VPT], const Chunk<D>& c
   return {m, d};
 }
 
-// exp2(x*log2e - coff) for every element of one slot, in the element type.
+// exp2(x*log2e - coff) for every element of one slot, in the element type, XOR-ed with
+// `sign` (0, or Elt<D>::kSignWord to negate every result: a negative upstream gradient).
 template <int D>
-__device__ __forceinline__ u32x4 exp_slot(u32x4 v, float coff) {
+__device__ __forceinline__ u32x4 exp_slot(u32x4 v, float coff, uint32_t sign = 0) {
   pin_slot<D>(v);
   OutVec<D> o;
 #pragma unroll
   for (int e = 0; e < Elt<D>::kPerVec; ++e)
     o.v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(v, e), kLog2e, -coff));
+  return o.bits() ^ splat(sign);
+}
+
+// x * s for every element of one slot, in the element type (fp32 product, one rounding to
+// bf16 for bf16 rows).
+template <int D>
+__device__ __forceinline__ u32x4 mul_slot(u32x4 v, float s) {
+  pin_slot<D>(v);
+  OutVec<D> o;
+#pragma unroll
+  for (int e = 0; e < Elt<D>::kPerVec; ++e) o.v[e] = elem<D>(v, e) * s;
   return o.bits();
 }
 

@@ -9,7 +9,10 @@
 //                    (softmax - onehot(t_i)) / n, n = #targets != ignore_index; ignored rows
 //                    get zero gradient and zero loss; mean = sum_i loss_i / n
 //                    (Liger-Kernel cross_entropy.py page, liger_cross_entropy_kernel steps 1-6,
-//                    LigerCrossEntropyFunction.forward)
+//                    LigerCrossEntropyFunction.forward). The sum reduction drops the 1/n,
+//                    the none reduction keeps the row losses; an upstream gradient s_i
+//                    multiplies row i's gradient as it is written (what the same page's
+//                    backward does afterwards with element_mul, which is also here).
 //
 // Register budget: every row kernel is compiled for at least 4 waves per SIMD (128 VGPRs),
 // so a 1024-thread workgroup fits a compute unit and smaller ones can share it.
@@ -68,19 +71,20 @@ __global__ __launch_bounds__(kScanThreads) void xent_scan_kernel(const int64_t* 
   for (int64_t i = threadIdx.x; i < nslots; i += kScanThreads) partials[i] = kPartialEmpty;
 }
 
-// Mean over the row losses in a fixed order; copies the counts out.
+// Sum (or mean) of the row losses in a fixed order; copies the counts out.
 __global__ __launch_bounds__(kScanThreads) void xent_mean_kernel(const float* __restrict__ row_loss,
                                                                  int64_t M,
                                                                  const int32_t* __restrict__ ws_counts,
                                                                  float* __restrict__ mean,
-                                                                 int32_t* __restrict__ counts_out) {
+                                                                 int32_t* __restrict__ counts_out,
+                                                                 int reduction) {
   __shared__ float red[kScanThreads / kWave];
   float s = 0.f;
   for (int64_t i = threadIdx.x; i < M; i += kScanThreads) s += row_loss[i];
   s = block_reduce<kScanThreads>(s, OpAdd(), red);
   if (threadIdx.x == 0) {
     const int32_t n = ws_counts[0];
-    *mean = s / (float)n;  // n == 0: 0/0 = NaN
+    if (mean) *mean = reduction == kReduceMean ? s / (float)n : s;  // n == 0: 0/0 = NaN
     if (counts_out) {
       counts_out[0] = n;
       counts_out[1] = ws_counts[1];
@@ -104,8 +108,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int chunk = blockIdx.x % S;
   const int64_t lo = (int64_t)chunk * p.chunk_vecs;
   const int32_t n = p.ws_counts[0];
-  const float inv_n = 1.0f / (float)n;
-  const float log2n = log2f((float)n);
+  const bool mean = p.reduction == kReduceMean;
+  const float inv_n = mean ? 1.0f / (float)n : 1.0f;
+  const float log2n = mean ? log2f((float)n) : 0.0f;
 
   auto skip = [&](int64_t t) { return t == p.ignore_index || t < 0 || t >= p.V; };
   auto row_ptr = [&](int64_t r) { return p.logits + r * p.ld_bytes; };
@@ -121,6 +126,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     const bool pf = rn < p.M && !skip(tn);
     const Chunk<D> c(row_ptr(r), p.V, lo, p.chunk_vecs);
     const bool ignored = skip(t);
+    // Upstream gradient of this row's loss (1 when none is given).
+    const float sc = p.gscale ? p.gscale[r * p.gstride] : 1.0f;
+    bool neg = false;
 
     // The target logit, read by the thread holding its vector. Only this workgroup
     // writes this chunk, and it does so after the barriers below.
@@ -187,30 +195,35 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
         m = bcast[0];
         d = bcast[1];
       }
-      // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) is p_j / n.
-      coff = m * kLog2e + log2f(d) + log2n;
+      // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) - log2|s| is
+      // |s| p_j / n (n = 1 unless the reduction is the mean); the sign of s is applied to
+      // the result bits.
+      coff = m * kLog2e + log2f(d) + log2n - log2f(fabsf(sc));
+      neg = __builtin_signbit(sc) != 0;
     }
 
     // Output pass, with the next row's loads issued into each slot once it is written out.
+    const uint32_t sign = neg ? Elt<D>::kSignWord : 0u;
     if (pf) {
       const Chunk<D> cn(row_ptr(rn), p.V, lo, p.chunk_vecs);
       const uint32_t off = tid * 16u;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
+        store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff, sign));
         v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff));
+      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff, sign));
     }
-    store_partials<D, THREADS>(c, c, [coff, ignored](float x) {
-      return ignored ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
+    store_partials<D, THREADS>(c, c, [coff, ignored, neg](float x) {
+      const float g = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
+      return ignored ? 0.f : (neg ? -g : g);
     });
     if (owner) {
-      // Target column: (p_t - 1)/n rounded once, stored after this thread's vector store.
+      // Target column: s (p_t - 1)/n, stored after this thread's vector store.
       const float pt = exp2f((xt - m) * kLog2e) / d;
-      store_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes), (pt - 1.0f) * inv_n);
+      store_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes), (pt - 1.0f) * inv_n * sc);
       p.row_loss[r] = m + logf(d) - xt;
     }
     if (ignored && chunk == 0 && tid == 0) p.row_loss[r] = 0.f;
@@ -241,7 +254,9 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams 
     if (tid == 0) p.row_loss[r] = 0.f;
     return;
   }
-  const int32_t n = p.ws_counts[0];
+  const int32_t n = p.reduction == kReduceMean ? p.ws_counts[0] : 1;
+  const float sc = p.gscale ? p.gscale[r * p.gstride] : 1.0f;
+  const bool neg = __builtin_signbit(sc) != 0;
   const float xt = ld(t);
   float m = kNegInf;
   for (int64_t j = tid; j < p.V; j += kStreamThreads) m = fmaxf(m, ld(j));
@@ -252,13 +267,41 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams 
     d += __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -mL));
   d = block_reduce<kStreamThreads>(d, OpAdd(), red[1]);
   // Every thread has read xt and the row before the barrier inside the reductions.
-  const float coff = mL + log2f(d) + log2f((float)n);
+  const float coff = mL + log2f(d) + log2f((float)n) - log2f(fabsf(sc));
   for (int64_t j = tid; j < p.V; j += kStreamThreads) {
-    const float g = (j == t) ? (exp2f((xt - m) * kLog2e) / d - 1.0f) / (float)n
-                             : __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
+    float g;
+    if (j == t) {
+      g = (exp2f((xt - m) * kLog2e) / d - 1.0f) / (float)n * sc;
+    } else {
+      g = __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
+      if (neg) g = -g;
+    }
     st(j, g);
   }
   if (tid == 0) p.row_loss[r] = m + logf(d) - xt;
+}
+
+// ============================================================================ element_mul
+// The backward's scaling of a stored gradient by the upstream gradient, in place:
+// x[i, 0:V) *= scale[i * sstride] (Liger-Kernel cross_entropy.py page, element_mul and
+// LigerCrossEntropyFunction.backward). A row whose scale is exactly 1 is neither read nor
+// written, which is what the page's skip of a unit upstream gradient amounts to, decided
+// here on the device with no host synchronisation. Workgroup b handles chunk b % chunks of
+// row b / chunks; 16-byte vectors, head / tail elements of unaligned rows element-wise.
+template <int D, int LP>
+__global__ __launch_bounds__(kMulThreads) void element_mul_kernel(ElementMulParams p) {
+  const int64_t total = p.M * p.chunks;
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    const int64_t r = b / p.chunks;
+    const float sc = p.scale[r * p.sstride];
+    if (sc == 1.0f) continue;
+    const Chunk<D> c(p.x + r * p.ld_bytes, p.V, (b - r * p.chunks) * p.chunk_vecs, p.chunk_vecs);
+    u32x4 v[kMulVpt];
+    issue_loads<D, kMulThreads, kMulVpt, LP>(v, c);
+#pragma unroll
+    for (int k = 0; k < kMulVpt; ++k) store_slot<D, kMulThreads>(c, k, mul_slot<D>(v[k], sc));
+    store_partials<D, kMulThreads>(c, c, [sc](float x) { return x * sc; });
+  }
 }
 
 // ============================================================================ lookup tables
@@ -277,5 +320,12 @@ const void* xent_stream_kernel_ptr(int dtype) {
 }
 const void* xent_scan_kernel_ptr() { return reinterpret_cast<const void*>(&xent_scan_kernel); }
 const void* xent_mean_kernel_ptr() { return reinterpret_cast<const void*>(&xent_mean_kernel); }
+const void* element_mul_kernel_ptr(int dtype, bool nt) {
+  if (dtype == kF32)
+    return nt ? reinterpret_cast<const void*>(&element_mul_kernel<kF32, kPolicyNT>)
+              : reinterpret_cast<const void*>(&element_mul_kernel<kF32, kPolicyDefault>);
+  return nt ? reinterpret_cast<const void*>(&element_mul_kernel<kBF16, kPolicyNT>)
+            : reinterpret_cast<const void*>(&element_mul_kernel<kBF16, kPolicyDefault>);
+}
 
 }  // namespace xr

@@ -46,7 +46,8 @@ typedef enum xr_status {
   XR_ERR_ALIGN = 7,     /* a tensor pointer is not aligned to its element size */
   XR_ERR_DEVICE = 8,    /* no usable HIP device, or a device query failed */
   XR_ERR_LAUNCH = 9,    /* a kernel launch failed (the HIP error is reported by HIP) */
-  XR_ERR_OPTION = 10    /* unknown option or value in xr_set_option() */
+  XR_ERR_OPTION = 10,   /* unknown option or value in xr_set_option() */
+  XR_ERR_VALUE = 11     /* an argument has an invalid value (reduction, negative stride) */
 } xr_status_t;
 
 /*
@@ -109,6 +110,58 @@ xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int
                             int64_t V, int64_t ignore_index, xr_dtype_t dtype, float* row_loss,
                             float* mean_loss, int32_t* counts, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Loss reductions of xr_xent_fwd_bwd_ex(). */
+typedef enum {
+  XR_REDUCTION_MEAN = 0, /* sum_i row_loss[i] / n: the pages' kernel */
+  XR_REDUCTION_SUM = 1,  /* sum_i row_loss[i] */
+  XR_REDUCTION_NONE = 2  /* the row losses themselves */
+} xr_reduction_t;
+
+/*
+ * xr_xent_fwd_bwd() with a choice of reduction and the upstream gradient folded into the
+ * gradient write. The Liger-Kernel `cross_entropy.py` kernel documents the mean reduction
+ * only; the sum and none reductions are those of the loss definition its docstring links
+ * to. `LigerCrossEntropyFunction.backward` multiplies the stored gradient by the upstream
+ * gradient in a second pass (`element_mul`); a caller that knows that gradient before the
+ * forward (a loss scale, a per-token weight) passes it here and saves the pass:
+ *   logits[i, j] <- s_i * (softmax(logits[i, :])_j - [j == t_i]) / n_r   (0 for ignored rows)
+ *   with n_r = n for XR_REDUCTION_MEAN and 1 otherwise, s_i = grad_scale[i * grad_scale_stride]
+ *   (s_i = 1 when grad_scale is NULL).
+ *   reduction          an xr_reduction_t; anything else returns XR_ERR_VALUE
+ *   grad_scale         fp32, device, or NULL; grad_scale_stride >= 0 (0: one value for all
+ *                      rows, the usual case for the mean and sum; 1: one value per row,
+ *                      the none reduction's upstream gradient); negative returns XR_ERR_VALUE
+ *   loss               fp32 [1], device: the mean (XR_REDUCTION_MEAN, NaN when n == 0) or
+ *                      the sum (XR_REDUCTION_SUM, 0 when M == 0); required for those two,
+ *                      ignored and may be NULL for XR_REDUCTION_NONE
+ *   row_loss           fp32 [M], device, required: the unscaled row losses (0 for ignored rows)
+ * Everything else is as in xr_xent_fwd_bwd(), which equals this call with
+ * XR_REDUCTION_MEAN and grad_scale NULL.
+ */
+xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, int64_t M,
+                               int64_t V, int64_t ignore_index, xr_dtype_t dtype,
+                               xr_reduction_t reduction, const float* grad_scale,
+                               int64_t grad_scale_stride, float* row_loss, float* loss,
+                               int32_t* counts, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The backward's scaling of a stored cross-entropy gradient by the upstream gradient, in
+ * place (Liger-Kernel `cross_entropy.py`: `element_mul`, called by
+ * `LigerCrossEntropyFunction.backward`):
+ *   x[i, j] <- x[i, j] * grad_output[i * grad_output_stride]   for j < N
+ * computed in fp32 and rounded once to dtype. A row whose factor is exactly 1.0 is neither
+ * read nor written: the page skips the multiplication for a unit upstream gradient after a
+ * host-side comparison, which this decides on the device, with no synchronisation.
+ *   x, ld              [M, N] of dtype, device, modified in place; columns [N, ld) untouched
+ *   grad_output        fp32, device, required; grad_output_stride >= 0 (0: one factor for
+ *                      every row, a scalar loss's upstream gradient; 1: one per row)
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1
+ * grad_output must not overlap x.
+ */
+xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t dtype,
+                           const float* grad_output, int64_t grad_output_stride, void* stream);
 
 /* Static, human-readable text for a status code (host). */
 const char* xr_status_string(xr_status_t status);

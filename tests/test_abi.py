@@ -37,14 +37,14 @@ def test_library_exports_every_declared_symbol(xr):
 
 def test_status_strings_and_version(xr):
     assert xr.status_string(0) == "ok"
-    for code in range(1, 11):
+    for code in range(1, 12):
         assert xr.status_string(code) != "unknown status"
     assert xr.status_string(99) == "unknown status"
-    assert xr.version() == 10000
+    assert xr.version() == 10100
 
 
 XR_OK, XR_ERR_NULL, XR_ERR_SHAPE, XR_ERR_STRIDE, XR_ERR_DTYPE, XR_ERR_ALIAS = 0, 1, 2, 3, 4, 5
-XR_ERR_ALIGN, XR_ERR_OPTION = 7, 10
+XR_ERR_ALIGN, XR_ERR_OPTION, XR_ERR_VALUE = 7, 10, 11
 
 
 def test_softmax_argument_errors(xr):
@@ -88,6 +88,39 @@ def test_xent_argument_errors(xr):
     assert f(L, 8, None, 2, 8, -100, 0, R, Mn, None, W, 4096, None) == XR_ERR_NULL
     assert f(L, 8, ctypes.c_void_p(0x20004), 2, 8, -100, 0, R, Mn, None, W, 4096, None) == XR_ERR_ALIGN
     assert f(ctypes.c_void_p(0x10002), 8, T, 2, 8, -100, 0, R, Mn, None, W, 4096, None) == XR_ERR_ALIGN
+
+
+def test_xent_ex_argument_errors(xr):
+    f = xr.lib.xr_xent_fwd_bwd_ex
+    L, T, R, Mn, W, S = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000,
+                                                       0x50000, 0x60000))
+    assert f(L, 8, T, 2, 8, -100, 0, 3, None, 0, R, Mn, None, W, 4096, None) == XR_ERR_VALUE
+    assert f(L, 8, T, 2, 8, -100, 0, -1, None, 0, R, Mn, None, W, 4096, None) == XR_ERR_VALUE
+    assert f(L, 8, T, 2, 8, -100, 0, 0, S, -1, R, Mn, None, W, 4096, None) == XR_ERR_VALUE
+    assert f(L, 8, T, 2, 8, -100, 5, 0, None, 0, R, Mn, None, W, 4096, None) == XR_ERR_DTYPE
+    # mean and sum need the loss output; none does not
+    assert f(L, 8, T, 2, 8, -100, 0, 0, None, 0, R, None, None, W, 4096, None) == XR_ERR_NULL
+    assert f(L, 8, T, 2, 8, -100, 0, 1, None, 0, R, None, None, W, 4096, None) == XR_ERR_NULL
+    assert f(L, 8, T, 2, 8, -100, 0, 2, None, 0, None, None, None, W, 4096, None) == XR_ERR_NULL
+    assert f(L, 8, T, 2, 8, -100, 0, 2, ctypes.c_void_p(0x60002), 1, R, None, None, W, 4096,
+             None) == XR_ERR_ALIGN
+
+
+def test_element_mul_argument_errors(xr):
+    f = xr.lib.xr_element_mul
+    X, G = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x90000)
+    assert f(X, 8, 4, 8, 2, G, 0, None) == XR_ERR_DTYPE
+    assert f(X, 8, 4, 8, 0, G, -1, None) == XR_ERR_VALUE
+    assert f(X, 8, -1, 8, 0, G, 0, None) == XR_ERR_SHAPE
+    assert f(X, 8, 4, 0, 0, G, 0, None) == XR_ERR_SHAPE
+    assert f(X, 7, 4, 8, 0, G, 0, None) == XR_ERR_STRIDE
+    assert f(None, 8, 4, 8, 0, G, 0, None) == XR_ERR_NULL
+    assert f(X, 8, 4, 8, 0, None, 0, None) == XR_ERR_NULL
+    assert f(ctypes.c_void_p(0x10001), 8, 4, 8, 1, G, 0, None) == XR_ERR_ALIGN
+    assert f(X, 8, 4, 8, 0, ctypes.c_void_p(0x90002), 0, None) == XR_ERR_ALIGN
+    # the factors may not lie inside the matrix they scale
+    assert f(X, 8, 4, 8, 0, ctypes.c_void_p(0x10010), 0, None) == XR_ERR_ALIAS
+    assert f(X, 8, 0, 8, 0, None, 0, None) == XR_OK  # M == 0: nothing to do
 
 
 def test_options(xr):
