@@ -90,8 +90,14 @@ const void* element_mul_kernel_ptr(int dtype, bool nt_loads);
 constexpr int kStreamThreads = 256;
 constexpr int kScanThreads = 1024;
 // element_mul: workgroup size and 16-byte vectors per thread.
-constexpr int kMulThreads = 256;
-constexpr int kMulVpt = 8;
+#ifndef XR_MUL_THREADS
+#define XR_MUL_THREADS 1024
+#endif
+#ifndef XR_MUL_VPT
+#define XR_MUL_VPT 8
+#endif
+constexpr int kMulThreads = XR_MUL_THREADS;
+constexpr int kMulVpt = XR_MUL_VPT;
 
 // Shapes available to the row-resident kernels, smallest capacity first.
 constexpr int kNumFwdShapes = 7;

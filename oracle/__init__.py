@@ -11,6 +11,8 @@ What each function computes, and the passage it follows:
   examples", Triton kernels ``softmax_kernel`` / ``_softmax``).
 * ``softmax_bwd`` -- ``dx = y * (dy - sum(y * dy))`` per row (same page,
   kernel ``_backward``, block-sparse scale taken as 1).
+* ``nll_fwd`` -- negative log-softmax rows and the loss gathered at one index
+  per row, as stored in the output type (same page, kernel ``_forward``).
 * ``xent_count``, ``xent_rows``, ``mean``, ``xent`` -- Liger-Kernel
   ``cross_entropy.py``: ``liger_cross_entropy_kernel`` steps 1-6 (ignore
   early-out, loss ``m + log d - x_y``, gradient ``(softmax - onehot)/n``) and
@@ -70,6 +72,8 @@ class Oracle:
         lib.xro_softmax_fwd.restype = None
         lib.xro_softmax_bwd.argtypes = [_p, _c_i64, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _p]
         lib.xro_softmax_bwd.restype = None
+        lib.xro_nll_fwd.argtypes = [_p, _c_i64, _p, _c_i64, _c_i64, ctypes.c_int, _p, _p]
+        lib.xro_nll_fwd.restype = None
         lib.xro_xent_count.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p]
         lib.xro_xent_count.restype = None
         lib.xro_xent_rows.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int,
@@ -135,6 +139,22 @@ class Oracle:
         dx = np.full((M, N), np.nan, dtype=np.float64)
         self.lib.xro_softmax_bwd(py, ldy, pd, ldd, M, N, code, dx.ctypes.data)
         return dx
+
+    def nll_fwd(self, x: np.ndarray, idx: np.ndarray, n_cols: int | None = None):
+        """(-log softmax rows [M, N] as float64, loss [M]: the output element at idx[i] rounded
+        to x's type, NaN where idx[i] is outside [0, N))."""
+        ptr, ld, M, code = self._matrix(x)
+        N = x.shape[1] if n_cols is None else int(n_cols)
+        if not 0 < N <= x.shape[1]:
+            raise ValueError("n_cols out of range")
+        ix = np.ascontiguousarray(idx, dtype=np.int64)
+        if ix.shape != (M,):
+            raise ValueError("idx must hold one index per row")
+        out = np.full((M, N), np.nan, dtype=np.float64)
+        loss = np.full(M, np.nan, dtype=np.float64)
+        self.lib.xro_nll_fwd(ptr, ld, ix.ctypes.data, M, N, code, out.ctypes.data,
+                             loss.ctypes.data)
+        return out, loss
 
     def xent_count(self, target: np.ndarray, V: int, ignore_index: int = -100):
         t = np.ascontiguousarray(target, dtype=np.int64)

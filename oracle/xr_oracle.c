@@ -17,6 +17,12 @@
  *   softmax backward  -- the fused softmax backward of the `_backward` kernel
  *                        on the same page, with its block-sparse scale taken
  *                        as 1: dx_j = y_j * (dy_j - sum_k y_k * dy_k).
+ *   negative log-softmax with a gathered loss -- the Triton kernel `_forward`
+ *                        on the same page: each output element is
+ *                        log(sum_k exp(x_k - m)) - (x_j - m) = -log p_j, and
+ *                        the row's loss is the output element at the row's
+ *                        index as stored (the kernel reads it back from the
+ *                        output), i.e. rounded to the output type.
  *   cross-entropy     -- Liger-Kernel `cross_entropy.py`,
  *                        `liger_cross_entropy_kernel` steps 1-6 and
  *                        `LigerCrossEntropyFunction.forward`: per-row loss
@@ -131,6 +137,41 @@ void xro_softmax_bwd(const void* y, int64_t ld_y, const void* dy, int64_t ld_dy,
       s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_dy + j, dtype);
     for (int64_t j = 0; j < N; ++j)
       dx[i * N + j] = load_elem(y, i * ld_y + j, dtype) * (load_elem(dy, i * ld_dy + j, dtype) - s);
+  }
+}
+
+/*
+ * v rounded to the nearest value of the element type, ties to even: fp32 by the C
+ * conversion (round to nearest even), bf16 by keeping 8 significant bits of v with
+ * nearbyint (the default rounding mode: to nearest, ties to even). Finite, normal v only.
+ */
+static double round_to_dtype(double v, int dtype) {
+  if (dtype == XRO_F32) return (double)(float)v;
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  double f = frexp(v, &e); /* v = f * 2^e, 0.5 <= |f| < 1 */
+  return ldexp(nearbyint(ldexp(f, 8)), e - 8);
+}
+
+/*
+ * out[M][N] (contiguous doubles) = -log softmax of each row of x (row stride ld_x);
+ * loss[i] = out[i][idx[i]] rounded to dtype, NaN when idx[i] lies outside [0, N).
+ */
+void xro_nll_fwd(const void* x, int64_t ld_x, const int64_t* idx, int64_t M, int64_t N,
+                 int dtype, double* out, double* loss) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j) {
+      double v = load_elem(x, i * ld_x + j, dtype);
+      if (v > m) m = v;
+    }
+    double d = 0.0;
+    for (int64_t j = 0; j < N; ++j) d += exp(load_elem(x, i * ld_x + j, dtype) - m);
+    double lse = log(d);
+    for (int64_t j = 0; j < N; ++j) out[i * N + j] = lse - (load_elem(x, i * ld_x + j, dtype) - m);
+    loss[i] = (idx[i] >= 0 && idx[i] < N) ? round_to_dtype(out[i * N + idx[i]], dtype) : NAN;
   }
 }
 

@@ -27,7 +27,8 @@ import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                       "worked_examples.json")
-_MATH = {"log": math.log, "exp": math.exp, "inf": math.inf, "__builtins__": {}}
+_MATH = {"log": math.log, "exp": math.exp, "inf": math.inf, "nan": math.nan,
+         "__builtins__": {}}
 
 
 def closed_form(expr) -> float:
@@ -300,6 +301,70 @@ def pin_xent_row_subset_and_padding(o):
     assert np.array_equal(g_d, g_all) and np.array_equal(l_d, l_all)
 
 
+# --------------------------------------------------------------------------- negative log-softmax
+def _nearest_bf16(v: float) -> float:
+    """The bf16 value nearest to v (ties to even), by exact rational arithmetic."""
+    from fractions import Fraction
+    if v == 0.0 or not math.isfinite(v):
+        return v
+    q = Fraction(v)
+    e = math.frexp(v)[1]  # v = f 2^e, 0.5 <= |f| < 1: 8 significant bits are steps of 2^(e-8)
+    step = Fraction(2) ** (e - 8)
+    k = q / step
+    lo = math.floor(k)
+    rem = k - lo
+    n = lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
+    return float(n * step)
+
+
+def pin_nll_uniform_and_two_columns(o):
+    for N in (4, 1000, 128256):
+        x = np.full((2, N), 0.75, dtype=np.float32)
+        out, loss = o.nll_fwd(x, np.array([0, N - 1]))
+        assert np.max(np.abs(out - math.log(N))) <= 1e-12 * math.log(N), "uniform row: log N"
+    a = 3.0
+    x = np.array([[0.0, a], [a, 0.0]], dtype=np.float32)
+    out, loss = o.nll_fwd(x, np.array([1, 1]))
+    l1 = math.log1p(math.exp(a))
+    want = np.array([[l1, l1 - a], [l1 - a, l1]])
+    assert np.max(np.abs(out - want)) <= 1e-14, "two columns: softplus"
+    assert loss[0] == float(np.float32(l1 - a)) and loss[1] == float(np.float32(l1))
+
+
+def pin_nll_matches_torch(o):
+    import torch
+    for seed, (M, N, dtype, scale) in enumerate([(9, 1000, "f32", 4.0), (6, 777, "bf16", 3.0)]):
+        x = synth.random_rows(1600 + seed, M, N, dtype=dtype, scale=scale)
+        idx = synth.random_targets(1650 + seed, M, N)
+        out, loss = o.nll_fwd(x, idx)
+        ref = -torch.log_softmax(torch.from_numpy(decode(x)), dim=1).numpy()
+        assert np.max(np.abs(out - ref)) <= 1e-12, "-log_softmax vs torch"
+        assert np.all(out >= 0.0)
+        p = np.exp(-out)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) <= 1e-12, "exp(-out) rows sum to 1"
+
+
+def pin_nll_loss_is_the_stored_element(o):
+    """The loss is the output at the row's index rounded to the element type (checked with
+    an independent exact rounding), NaN for an index outside the row; padding is never read."""
+    M, N, ld = 40, 300, 320
+    for dtype in ("f32", "bf16"):
+        x = synth.random_rows(1700, M, N, ld=ld, dtype=dtype, scale=3.0, pad_nan=True)
+        idx = synth.random_targets(1701, M, N)
+        idx[0] = N
+        idx[1] = -1
+        out, loss = o.nll_fwd(x, idx, n_cols=N)
+        assert np.all(np.isfinite(out)), "padding (NaN) must never be read"
+        assert math.isnan(loss[0]) and math.isnan(loss[1]), "index outside the row: NaN"
+        for i in range(2, M):
+            v = out[i, idx[i]]
+            want = float(np.float32(v)) if dtype == "f32" else _nearest_bf16(v)
+            assert loss[i] == want, f"{dtype} row {i}: loss {loss[i]!r} vs stored {want!r}"
+        dense = np.ascontiguousarray(x[:, :N])
+        out_d, loss_d = o.nll_fwd(dense, idx)
+        assert np.array_equal(out_d, out)
+
+
 # ------------------------------------------------------- reductions and upstream gradient
 def pin_xent_reductions_finite_differences(o):
     """Each reduction's gradient, times its upstream value, is the derivative of that loss."""
@@ -427,6 +492,17 @@ def pin_golden_worked_examples(o):
         out = o.element_mul(x, case["scale"], n_cols=case["n_cols"])
         want = np.array([[closed_form(v) for v in r] for r in case["out"]])
         assert np.array_equal(out, want), case["name"]
+    for case in gold["nll_fwd"]:
+        x = as_input(case["x"], case["dtype"])
+        out, loss = o.nll_fwd(x, np.array(case["idx"], dtype=np.int64))
+        want = np.array([[closed_form(v) for v in r] for r in case["out"]])
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(out), fin), case["name"]
+        assert np.max(np.abs(out[fin] - want[fin])) <= 1e-14 and np.all(out[~fin] == want[~fin]), case["name"]
+        wl = np.array([closed_form(v) for v in case["loss"]])
+        assert np.array_equal(np.isnan(loss), np.isnan(wl)), case["name"]
+        ok = ~np.isnan(wl)
+        assert np.max(np.abs(loss[ok] - wl[ok])) <= 2e-7 * np.max(np.abs(wl[ok])), case["name"]
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

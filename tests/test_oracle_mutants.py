@@ -57,6 +57,20 @@ MUTANTS = {
                                            "out[i * V + j] = load_elem(x, i * V + j, dtype) * w;"),
     "element_mul scales by row 0's value": ("double w = scale[i * scale_stride];",
                                             "double w = scale[0];"),
+    "nll drops log d": ("out[i * N + j] = lse - (load_elem(x, i * ld_x + j, dtype) - m);",
+                        "out[i * N + j] = 0.0 - (load_elem(x, i * ld_x + j, dtype) - m);"),
+    "nll adds the logit": ("out[i * N + j] = lse - (load_elem(x, i * ld_x + j, dtype) - m);",
+                           "out[i * N + j] = lse + (load_elem(x, i * ld_x + j, dtype) - m);"),
+    "nll ignores the row stride": ("out[i * N + j] = lse - (load_elem(x, i * ld_x + j, dtype) - m);",
+                                   "out[i * N + j] = lse - (load_elem(x, i * N + j, dtype) - m);"),
+    "nll loss read at the next column": ("round_to_dtype(out[i * N + idx[i]], dtype)",
+                                         "round_to_dtype(out[i * N + (idx[i] + 1) % N], dtype)"),
+    "nll loss not rounded": ("round_to_dtype(out[i * N + idx[i]], dtype)", "out[i * N + idx[i]]"),
+    "bf16 rounding keeps 9 bits": ("return ldexp(nearbyint(ldexp(f, 8)), e - 8);",
+                                   "return ldexp(nearbyint(ldexp(f, 9)), e - 9);"),
+    "bf16 rounding truncates": ("return ldexp(nearbyint(ldexp(f, 8)), e - 8);",
+                                "return ldexp(trunc(ldexp(f, 8)), e - 8);"),
+    "nll accepts an index equal to N": ("(idx[i] >= 0 && idx[i] < N)", "(idx[i] >= 0 && idx[i] <= N)"),
     "element_mul adds the scale": ("out[i * V + j] = load_elem(x, i * ld + j, dtype) * w;",
                                    "out[i * V + j] = load_elem(x, i * ld + j, dtype) + w;"),
     "ignored rows keep stale gradient": ("        for (int64_t j = 0; j < V; ++j) g[j] = 0.0;\n      continue;",
