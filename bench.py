@@ -13,7 +13,7 @@ the library records around that launch on its stream; `cpu_baseline` times the f
 oracle on the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
-                    [--workload c4|c3|c5|c2|c1|c4-mul] [--reduction mean|sum|none]
+                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll] [--reduction mean|sum|none]
                     [--grad-scale S]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
 
@@ -23,7 +23,8 @@ kind of line; small inputs are rotated through >= 1 GB of copies so no step read
 previous step left in the 256 MB Infinity Cache. `--reduction` / `--grad-scale` run the
 cross-entropy workloads with another reduction or an upstream gradient folded into the
 gradient write; `c4-mul` times the backward's element_mul (the stored gradient times an
-upstream gradient of 0.5) over the 16384 x 128256 bf16 matrix.
+upstream gradient of 0.5) over the 16384 x 128256 bf16 matrix; `c4-nll` the negative
+log-softmax forward with a gathered loss over the same matrix, into a separate output.
 """
 from __future__ import annotations
 
@@ -52,6 +53,8 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 C4_M, C4_V, C4_KEEP = 16384, 128256, 15565
 
 DESCRIPTIONS = {
+    "c4-nll": "negative log-softmax forward + loss gathered at each row's target, M=16384, "
+              "N=128256, bf16 logits in, bf16 -log p out (separate buffer), fp32 losses",
     "c4-mul": "element_mul (stored gradient x upstream gradient 0.5, in place), M=16384, "
               "V=128256, bf16",
     "c1": "softmax forward, M=128, N=1000, fp32 logits 3 N(0,1), contiguous",
@@ -269,6 +272,33 @@ def run_element_mul(args, name: str) -> dict:
     return out
 
 
+def run_nll(args, name: str) -> dict:
+    """-log softmax of the c4 logits into a separate output, plus the gathered losses."""
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.xent_c4()
+    M, N = w["M"], w["N"]
+    x = _device_matrix(torch, w["x"], dev)
+    idx = torch.from_numpy(w["target"]).clamp(min=0).to(dev)
+    out = torch.empty_like(x)
+    loss = torch.empty(M, dtype=torch.float32, device=dev)
+
+    def launch(i):
+        xr.nll_fwd(x, idx, out, loss)
+
+    wall, kernel_ms = _timed(HipEvents(), args.steps, args.warmup, launch)
+    bmin = 2 * M * N * 2 + 12 * M
+    p = xr.plan("nll_fwd", M, N, x.dtype)
+    return _line(args, name, bmin, M, wall, kernel_ms, "softmax_fwd_kernel (negative log)",
+                 {"M": M, "N": N, "bytes_min": bmin, "path": p["path"], "threads": p["threads"],
+                  "vec_per_thread": p["vec_per_thread"], "grid": p["grid"]}, "bf16")
+
+
 def run_softmax(args, name: str) -> dict:
     import torch
 
@@ -413,6 +443,8 @@ def main() -> int:
         out = run_softmax(args, args.workload)
     elif args.workload == "c4-mul":
         out = run_element_mul(args, args.workload)
+    elif args.workload == "c4-nll":
+        out = run_nll(args, args.workload)
     else:
         out = run_xent(args, args.workload)
     print(json.dumps(out), flush=True)

@@ -3,6 +3,7 @@
 A thin ctypes binding over ``libxr.so`` (``include/xr.h``): every function here
 checks and marshals its torch tensors into the C ABI call of the same name
 (``softmax_fwd`` -> ``xr_softmax_fwd``, ``softmax_bwd`` -> ``xr_softmax_bwd``,
+``nll_fwd`` -> ``xr_nll_fwd``,
 ``xent_fwd_bwd`` -> ``xr_xent_fwd_bwd_ex``, ``element_mul`` -> ``xr_element_mul``, ...).
 All of the computation runs in the library's HIP kernels; PyTorch only provides device
 memory and the current stream. ``CrossEntropyFunction`` / ``cross_entropy`` wrap the
@@ -36,6 +37,8 @@ lib.xr_softmax_fwd.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p]
 lib.xr_softmax_fwd.restype = ctypes.c_int
 lib.xr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p]
 lib.xr_softmax_bwd.restype = ctypes.c_int
+lib.xr_nll_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, ctypes.c_int, _p]
+lib.xr_nll_fwd.restype = ctypes.c_int
 lib.xr_xent_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
 lib.xr_xent_workspace_bytes.restype = _sz
 lib.xr_xent_fwd_bwd.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p, _p, _p, _p,
@@ -65,14 +68,15 @@ lib.xr_set_profile_events.argtypes = [_p, _p]
 lib.xr_set_profile_events.restype = ctypes.c_int
 
 # Names exported by include/xr.h (checked against the library by the tests).
-C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_xent_workspace_bytes", "xr_xent_fwd_bwd",
+C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_nll_fwd", "xr_xent_workspace_bytes",
+             "xr_xent_fwd_bwd",
              "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_status_string", "xr_version",
              "xr_plan", "xr_set_option", "xr_set_profile_events")
 
 F32, BF16 = 0, 1
 OK = 0
 PATHS = {1: "resident", 2: "split", 3: "stream"}
-OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2}
+OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2, "nll_fwd": 3}
 OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4, "load_policy": 5}
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
@@ -148,6 +152,30 @@ def softmax_bwd(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = No
     _check("xr_softmax_bwd",
            lib.xr_softmax_bwd(px, ldx, py, ldy, pd, ldd, M, N, dt, _stream(y, stream)))
     return out
+
+
+def nll_fwd(x: torch.Tensor, idx: torch.Tensor, out: torch.Tensor | None = None,
+            loss: torch.Tensor | None = None, *, stream=None):
+    """-log softmax of each row of x into ``out`` (new, or x itself), and the fp32 loss
+    ``out[i, idx[i]]`` as stored (NaN for an index outside the row). Returns (out, loss)."""
+    px, ldx, M, N, dt = _matrix(x, "x")
+    if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int64 or idx.device != x.device:
+        raise TypeError("idx must be an int64 tensor on x's device")
+    if idx.dim() != 1 or idx.shape[0] != M or (M > 1 and idx.stride(0) != 1):
+        raise ValueError("idx must be a contiguous 1-D tensor of one entry per row")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    po, ldo, M2, N2, dt2 = _matrix(out, "out")
+    if (M2, N2, dt2) != (M, N, dt) or out.device != x.device:
+        raise ValueError("out must match x in shape, dtype and device")
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=x.device)
+    if loss.dtype != torch.float32 or loss.device != x.device or loss.numel() < M or \
+            not loss.is_contiguous():
+        raise ValueError("loss must be a contiguous float32 tensor of one entry per row")
+    _check("xr_nll_fwd", lib.xr_nll_fwd(po, ldo, px, ldx, idx.data_ptr(), loss.data_ptr(), M, N,
+                                        dt, _stream(x, stream)))
+    return out, loss
 
 
 def xent_workspace_bytes(M: int, V: int, dtype: torch.dtype) -> int:

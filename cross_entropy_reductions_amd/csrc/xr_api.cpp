@@ -98,6 +98,15 @@ bool overlaps(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M,
   const uintptr_t b1 = b0 + (uintptr_t)(((M - 1) * ldb + n) * eb);
   return a0 < b1 && b0 < a1;
 }
+// Byte spans [a, a + abytes) and [b, b + bbytes) intersect.
+bool spans_overlap(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return abytes && bbytes && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+// Bytes from the first element of an [M, n] matrix of row stride ld to past its last element.
+uint64_t matrix_span(int64_t M, int64_t ld, int64_t n, int eb) {
+  return M > 0 ? (uint64_t)((M - 1) * ld + n) * (uint64_t)eb : 0;
+}
 bool bad_alias(const void* out, int64_t ldo, const void* in, int64_t ldi, int64_t M, int64_t n,
                int eb) {
   if (out == in && ldo == ldi) return false;  // exactly in place
@@ -135,15 +144,33 @@ bool rows_on_16(const void* p, int64_t ld, int64_t M, int eb) {
   return aligned_to(p, 16) && (M <= 1 || ((ld * eb) % 16) == 0);
 }
 
-// op: 0 softmax fwd, 1 softmax bwd, 2 cross-entropy. `aligned`: every operand row has the
-// same address modulo 16; `on16`: moreover every row starts on a 16-byte boundary (then a
-// row touches exactly ceil(N / elements-per-vector) vectors).
+const void* stream_kernel(int op, xr_dtype_t dt) {
+  switch (op) {
+    case kOpSoftmaxFwd: return softmax_fwd_stream_kernel_ptr(dt);
+    case kOpSoftmaxBwd: return softmax_bwd_stream_kernel_ptr(dt);
+    case kOpNllFwd: return nll_fwd_stream_kernel_ptr(dt);
+    default: return xent_stream_kernel_ptr(dt);
+  }
+}
+
+const void* row_kernel(int op, xr_dtype_t dt, Shape sh, bool nt) {
+  switch (op) {
+    case kOpSoftmaxFwd: return softmax_fwd_kernel_ptr(dt, sh, nt);
+    case kOpSoftmaxBwd: return softmax_bwd_kernel_ptr(dt, sh, nt);
+    case kOpNllFwd: return nll_fwd_kernel_ptr(dt, sh, nt);
+    default: return xent_rows_kernel_ptr(dt, sh, nt);
+  }
+}
+
+// op: an Op (softmax fwd / bwd, cross-entropy, negative log-softmax fwd). `aligned`: every
+// operand row has the same address modulo 16; `on16`: moreover every row starts on a
+// 16-byte boundary (then a row touches exactly ceil(N / elements-per-vector) vectors).
 xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned, bool on16,
                       Plan* plan) {
   int dev = 0;
   DeviceInfo di;
   if (xr_status_t st = device_info(&dev, &di)) return st;
-  const bool bwd = op == 1;
+  const bool bwd = op == kOpSoftmaxBwd;
   const Shape* menu = bwd ? kBwdShapes : kFwdShapes;
   const int nmenu = bwd ? kNumBwdShapes : kNumFwdShapes;
   const int64_t nvm = on16 ? (N + elts_per_vec(dt) - 1) / elts_per_vec(dt) : row_vecs_max(N, dt);
@@ -154,8 +181,7 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   const int64_t want = g_opt.path;
   if (want == kPathStream || !aligned) {
     if (want && want != kPathStream) return XR_ERR_SHAPE;
-    p.kernel = op == 0 ? softmax_fwd_stream_kernel_ptr(dt)
-                       : op == 1 ? softmax_bwd_stream_kernel_ptr(dt) : xent_stream_kernel_ptr(dt);
+    p.kernel = stream_kernel(op, dt);
     *plan = p;
     return XR_OK;
   }
@@ -166,7 +192,7 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   // (measured: 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 TB/s in two chunks); and enough
   // chunks to give every compute unit work when the batch is short.
   int64_t S = 1;
-  if (op == 2) {
+  if (op == kOpXent) {
     const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
     const int64_t row_bytes = nvm * 16;
     const int64_t s_bw = row_bytes >= (32 << 10)
@@ -185,7 +211,7 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     if (want == kPathSplit && S < 2) return XR_ERR_SHAPE;
   } else if (nvm > cap_max || want == kPathSplit) {
     if (want == kPathResident || want == kPathSplit) return XR_ERR_SHAPE;
-    p.kernel = op == 0 ? softmax_fwd_stream_kernel_ptr(dt) : softmax_bwd_stream_kernel_ptr(dt);
+    p.kernel = stream_kernel(op, dt);
     *plan = p;
     return XR_OK;
   }
@@ -194,8 +220,7 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   const Shape* sh = pick_shape(menu, nmenu, chunk);
   if (!sh) {
     if (want) return XR_ERR_SHAPE;
-    p.kernel = op == 0 ? softmax_fwd_stream_kernel_ptr(dt)
-                       : op == 1 ? softmax_bwd_stream_kernel_ptr(dt) : xent_stream_kernel_ptr(dt);
+    p.kernel = stream_kernel(op, dt);
     *plan = p;
     return XR_OK;
   }
@@ -206,9 +231,7 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   // faster with the default policy (the cross-entropy over a 128256-wide bf16 vocabulary).
   bool nt_loads = !(S == 1 && nvm * 16 >= (128 << 10));
   if (g_opt.load_policy) nt_loads = g_opt.load_policy == 2;
-  p.kernel = op == 0 ? softmax_fwd_kernel_ptr(dt, *sh, nt_loads)
-                     : op == 1 ? softmax_bwd_kernel_ptr(dt, *sh, nt_loads)
-                               : xent_rows_kernel_ptr(dt, *sh, nt_loads);
+  p.kernel = row_kernel(op, dt, *sh, nt_loads);
   if (!p.kernel) return XR_ERR_SHAPE;
   const int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
   if (per_cu <= 0) return XR_ERR_DEVICE;
@@ -331,7 +354,7 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
                     xr_plan_t* out) {
   if (!out) return XR_ERR_NULL;
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
-  if (op < 0 || op > 2 || M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (op < 0 || op > 3 || M < 0 || N < 1) return XR_ERR_SHAPE;
   Plan p;
   if (xr_status_t st = make_plan(op, M, N, dtype, op == 2 ? true : aligned != 0, aligned == 2, &p))
     return st;
@@ -359,7 +382,37 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
   const bool on16 = rows_on_16(x, ld_x, M, eb) && rows_on_16(y, ld_y, M, eb);
   if (xr_status_t st = make_plan(0, M, N, dtype, same_lead(x, ld_x, y, ld_y, eb), on16, &p))
     return st;
-  SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N};
+  SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N,
+                       nullptr, nullptr};
+  return launch(p, &prm, static_cast<hipStream_t>(stream),
+                p.path == kPathStream ? kStreamThreads : p.shape.threads);
+}
+
+xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
+                       const int64_t* idx, float* loss, int64_t M, int64_t N, xr_dtype_t dtype,
+                       void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (ld_x < N || ld_out < N) return XR_ERR_STRIDE;
+  if (M == 0) return XR_OK;
+  if (!x || !out || !idx || !loss) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if (!aligned_to(x, eb) || !aligned_to(out, eb) || !aligned_to(idx, 8) || !aligned_to(loss, 4))
+    return XR_ERR_ALIGN;
+  if (bad_alias(out, ld_out, x, ld_x, M, N, eb)) return XR_ERR_ALIAS;
+  // idx and loss must lie outside both matrices
+  const uint64_t out_span = matrix_span(M, ld_out, N, eb);
+  if (spans_overlap(out, out_span, idx, (uint64_t)M * 8) ||
+      spans_overlap(out, out_span, loss, (uint64_t)M * 4) ||
+      spans_overlap(x, matrix_span(M, ld_x, N, eb), loss, (uint64_t)M * 4) ||
+      spans_overlap(idx, (uint64_t)M * 8, loss, (uint64_t)M * 4))
+    return XR_ERR_ALIAS;
+  Plan p;
+  const bool on16 = rows_on_16(x, ld_x, M, eb) && rows_on_16(out, ld_out, M, eb);
+  if (xr_status_t st = make_plan(kOpNllFwd, M, N, dtype, same_lead(x, ld_x, out, ld_out, eb), on16, &p))
+    return st;
+  SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(out), ld_out * eb,
+                       M, N, idx, loss};
   return launch(p, &prm, static_cast<hipStream_t>(stream),
                 p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }

@@ -57,6 +57,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// v rounded to the element type (as a store of v would leave it), widened back to fp32.
+template <int D> __device__ __forceinline__ float round_elem(float v) {
+  if (D == kF32) return v;
+  return as_f32(pack_bf16x2(v, 0.f) << 16);
+}
+
 // A vector of kPerVec fp32 results stored back in the element type.
 template <int D> struct OutVec;
 template <> struct OutVec<kF32> {

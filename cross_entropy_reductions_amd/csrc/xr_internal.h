@@ -56,7 +56,12 @@ struct SoftmaxFwdParams {
   char* y;
   int64_t ldy_bytes;
   int64_t M, N;
+  const int64_t* idx;  // negative log-softmax only: the index gathered into loss[] per row
+  float* loss;
 };
+
+// Operations of the row kernels (also the `op` argument of xr_plan).
+enum Op : int { kOpSoftmaxFwd = 0, kOpSoftmaxBwd = 1, kOpXent = 2, kOpNllFwd = 3 };
 
 struct SoftmaxBwdParams {
   const char* y;
@@ -78,9 +83,11 @@ struct Shape {
 // the instantiation whose row loads carry the non-temporal hint.
 const void* xent_rows_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* xent_stream_kernel_ptr(int dtype);
 const void* softmax_fwd_stream_kernel_ptr(int dtype);
+const void* nll_fwd_stream_kernel_ptr(int dtype);
 const void* softmax_bwd_stream_kernel_ptr(int dtype);
 const void* xent_scan_kernel_ptr();
 const void* xent_mean_kernel_ptr();

@@ -1,5 +1,8 @@
 // xr_softmax.hip -- softmax forward and backward kernels for gfx950 (the row-kernel design
-// is described at the top of xr_xent.hip).
+// is described at the top of xr_xent.hip), and the negative log-softmax forward with a
+// gathered loss (page "python sum function examples", Triton kernel _forward): the same
+// row pass, writing log d - (x - m) = -log p instead of p, and loss[i] = the written
+// element at idx[i].
 #include "xr_rows.h"
 
 namespace xr {
@@ -9,9 +12,23 @@ const Shape kFwdShapes[kNumFwdShapes] = {{64, 4},   {64, 8},   {64, 16},  {128, 
 const Shape kBwdShapes[kNumBwdShapes] = {{64, 4},  {64, 8},   {128, 8},
                                          {256, 8}, {512, 8}, {1024, 8}};
 
+// (m + log d) - x for every element of one slot, in the element type: -log p.
+template <int D>
+__device__ __forceinline__ u32x4 nll_slot(u32x4 v, float c) {
+  pin(v);  // fp32 too: the subtraction is cheap enough that, unpinned, the compiler computes
+           // every slot's result at once and spills
+  OutVec<D> o;
+#pragma unroll
+  for (int e = 0; e < Elt<D>::kPerVec; ++e) o.v[e] = c - elem<D>(v, e);
+  return o.bits();
+}
+
 // ============================================================================ softmax forward
-template <int D, int THREADS, int VPT, int LP>
+// NLL = false: y = softmax(x). NLL = true: y = -log softmax(x) and loss[r] = y[r, idx[r]] as
+// stored (NaN when idx[r] lies outside the row).
+template <int D, int THREADS, int VPT, int LP, bool NLL>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_fwd_kernel(SoftmaxFwdParams p) {
+  constexpr int EPV = Elt<D>::kPerVec;
   constexpr int NW = THREADS / kWave;
   __shared__ float2 red[2][NW];
   int buf = 0;
@@ -25,29 +42,46 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     const int64_t rn = r + G;
     const Chunk<D> cx(p.x + r * p.ldx_bytes, p.N, 0, cv);
     const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);  // same lead as cx (host-checked)
+    // NLL: the gathered element, read by the thread holding its vector before any store of
+    // this row (y may be exactly x).
+    int64_t vi = -1;
+    bool owner = false;
+    float xi = 0.f;
+    if (NLL) {
+      const int64_t ix = p.idx[r];
+      if (ix >= 0 && ix < p.N) vi = cx.lead + ix;
+      owner = vi >= 0 && (int)threadIdx.x == (int)((vi / EPV) % THREADS);
+      if (owner) xi = buf_load_elem<D>(cx.rsrc, (uint32_t)(vi * Elt<D>::kBytes));
+    }
     const Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red[buf]);
     buf ^= 1;
-    const float coff = st.m * kLog2e + log2f(st.d);
+    // softmax: exp2(x*log2e - coff), coff = m*log2e + log2 d.  NLL: c - x, c = m + log d.
+    const float coff = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
+    auto out_slot = [coff](u32x4 x) { return NLL ? nll_slot<D>(x, coff) : exp_slot<D>(x, coff); };
     if (rn < p.M) {
       const Chunk<D> cn(p.x + rn * p.ldx_bytes, p.N, 0, cv);
       const uint32_t off = threadIdx.x * 16u;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        store_slot<D, THREADS>(cy, k, exp_slot<D>(v[k], coff));
+        store_slot<D, THREADS>(cy, k, out_slot(v[k]));
         v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(cy, k, exp_slot<D>(v[k], coff));
+      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(cy, k, out_slot(v[k]));
     }
     store_partials<D, THREADS>(cy, cx, [coff](float x) {
-      return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
+      return NLL ? coff - x : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
     });
+    if (NLL) {
+      if (owner) p.loss[r] = round_elem<D>(coff - xi);
+      else if (vi < 0 && threadIdx.x == 0) p.loss[r] = __builtin_nanf("");
+    }
     r = rn;
   }
 }
 
-template <int D>
+template <int D, bool NLL>
 __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(SoftmaxFwdParams p) {
   __shared__ float red[2][kStreamThreads / kWave];
   const int64_t r = blockIdx.x;
@@ -59,6 +93,10 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
     if (D == kF32) return reinterpret_cast<const float*>(row)[j];
     return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
   };
+  // NLL: the gathered element, read before the barriers below (y may be exactly x).
+  const int64_t ix = NLL ? p.idx[r] : -1;
+  const bool in_row = ix >= 0 && ix < p.N;
+  const float xi = (NLL && tid == 0 && in_row) ? ld(ix) : 0.f;
   float m = kNegInf;
   for (int64_t j = tid; j < p.N; j += kStreamThreads) m = fmaxf(m, ld(j));
   m = block_reduce<kStreamThreads>(m, OpMax(), red[0]);
@@ -69,12 +107,13 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
   d = block_reduce<kStreamThreads>(d, OpAdd(), red[1]);
   // In place (y == x) is safe: every element's output depends only on itself and (m, d),
   // and all reads of the max / sum passes finished before the barrier above.
-  const float coff = mL + log2f(d);
+  const float coff = NLL ? m + logf(d) : mL + log2f(d);
   for (int64_t j = tid; j < p.N; j += kStreamThreads) {
-    const float val = __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
+    const float val = NLL ? coff - ld(j) : __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
     if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
     else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
   }
+  if (NLL && tid == 0) p.loss[r] = in_row ? round_elem<D>(coff - xi) : __builtin_nanf("");
 }
 
 // ============================================================================ softmax backward
@@ -178,8 +217,12 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream_kernel(Soft
 // ============================================================================ lookup tables
 #define XR_CASE_SFWD(D, T, V)                                                                  \
   if (s.threads == T && s.vpt == V)                                                              \
-    return lp ? reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyNT>)           \
-              : reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyDefault>);
+    return lp ? reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyNT, false>)    \
+              : reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyDefault, false>);
+#define XR_CASE_NLL(D, T, V)                                                                   \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyNT, true>)     \
+              : reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyDefault, true>);
 #define XR_CASE_SBWD(D, T, V)                                                                  \
   if (s.threads == T && s.vpt == V)                                                              \
     return lp ? reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyNT>)           \
@@ -190,14 +233,23 @@ const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
   if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_SFWD, kBF16) }
   return nullptr;
 }
+const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_NLL, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_NLL, kBF16) }
+  return nullptr;
+}
 const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool lp) {
   if (dtype == kF32) { XR_SHAPES_BWD(XR_CASE_SBWD, kF32) }
   if (dtype == kBF16) { XR_SHAPES_BWD(XR_CASE_SBWD, kBF16) }
   return nullptr;
 }
 const void* softmax_fwd_stream_kernel_ptr(int dtype) {
-  return dtype == kF32 ? reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kF32>)
-                       : reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kBF16>);
+  return dtype == kF32 ? reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kF32, false>)
+                       : reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kBF16, false>);
+}
+const void* nll_fwd_stream_kernel_ptr(int dtype) {
+  return dtype == kF32 ? reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kF32, true>)
+                       : reinterpret_cast<const void*>(&softmax_fwd_stream_kernel<kBF16, true>);
 }
 const void* softmax_bwd_stream_kernel_ptr(int dtype) {
   return dtype == kF32 ? reinterpret_cast<const void*>(&softmax_bwd_stream_kernel<kF32>)

@@ -77,6 +77,22 @@ xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y,
                            int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream);
 
 /*
+ * Negative log-softmax forward with the loss gathered at one index per row (the Triton
+ * kernel `_forward` on the page "python sum function examples"):
+ *   out[i, j] = log d_i - (x[i, j] - m_i)   (= -log softmax(x[i, :])_j; +inf where x is -inf)
+ *   loss[i]   = out[i, idx[i]] as stored, i.e. rounded to dtype (the page reads the loss back
+ *               from the output), widened to fp32; NaN when idx[i] lies outside [0, N)
+ *   out, ld_out  output [M, N] of dtype; may be exactly x (in place)
+ *   x, ld_x      input [M, N] of dtype
+ *   idx          int64 [M], device;  loss  fp32 [M], device
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1
+ * idx and loss must not overlap the matrices or each other (XR_ERR_ALIAS).
+ */
+xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
+                       const int64_t* idx, float* loss, int64_t M, int64_t N, xr_dtype_t dtype,
+                       void* stream);
+
+/*
  * Bytes of device workspace xr_xent_fwd_bwd() needs for these sizes on the current device
  * (host query; 0 if the sizes are invalid). The caller owns the workspace; its contents
  * need no initialisation and are scratch between calls.
@@ -174,7 +190,8 @@ int32_t xr_version(void);
  * (a row or a row chunk per workgroup, held in registers: one read of the input),
  * 2 = split row (S > 1 workgroups per row exchanging (max, sum) pairs), 3 = stream
  * (one workgroup per row, several passes over global memory).
- * op: 0 = softmax forward, 1 = softmax backward, 2 = cross-entropy.
+ * op: 0 = softmax forward, 1 = softmax backward, 2 = cross-entropy, 3 = negative
+ * log-softmax forward.
  * aligned: 0 = the operand rows sit at different addresses modulo 16 bytes (stream path),
  * 1 = they share their address modulo 16 (rows may start anywhere), 2 = moreover every row
  * starts on a 16-byte boundary (the usual contiguous tensors). The cross-entropy has one

@@ -136,5 +136,21 @@ def test_options(xr):
 def test_plan_argument_errors(xr):
     out = xr.XrPlan()
     assert xr.lib.xr_plan(0, 4, 8, 0, 1, None) == XR_ERR_NULL
-    assert xr.lib.xr_plan(3, 4, 8, 0, 1, ctypes.byref(out)) == XR_ERR_SHAPE
+    assert xr.lib.xr_plan(4, 4, 8, 0, 1, ctypes.byref(out)) == XR_ERR_SHAPE
     assert xr.lib.xr_plan(0, 4, 8, 5, 1, ctypes.byref(out)) == XR_ERR_DTYPE
+
+
+def test_nll_argument_errors(xr):
+    f = xr.lib.xr_nll_fwd
+    Y, X, I, L = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000))
+    assert f(Y, 8, X, 8, I, L, 4, 8, 2, None) == XR_ERR_DTYPE
+    assert f(Y, 8, X, 8, I, L, -1, 8, 0, None) == XR_ERR_SHAPE
+    assert f(Y, 7, X, 8, I, L, 4, 8, 0, None) == XR_ERR_STRIDE
+    assert f(Y, 8, X, 8, None, L, 4, 8, 0, None) == XR_ERR_NULL
+    assert f(Y, 8, X, 8, I, None, 4, 8, 0, None) == XR_ERR_NULL
+    assert f(Y, 8, X, 8, ctypes.c_void_p(0x30004), L, 4, 8, 0, None) == XR_ERR_ALIGN
+    assert f(ctypes.c_void_p(0x10010), 8, ctypes.c_void_p(0x10000), 8, I, L, 4, 8, 0, None) == XR_ERR_ALIAS
+    # the losses may not land inside the output or the input
+    assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x10010), 4, 8, 0, None) == XR_ERR_ALIAS
+    assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x20010), 4, 8, 0, None) == XR_ERR_ALIAS
+    assert f(Y, 8, X, 8, I, L, 0, 8, 0, None) == XR_OK
