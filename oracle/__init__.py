@@ -13,6 +13,10 @@ What each function computes, and the passage it follows:
   kernel ``_backward``, block-sparse scale taken as 1).
 * ``nll_fwd`` -- negative log-softmax rows and the loss gathered at one index
   per row, as stored in the output type (same page, kernel ``_forward``).
+* ``layernorm_fwd``, ``layernorm_bwd`` -- layer norm (the Triton LayerNorm
+  tutorial page, from its prose and the paper it cites; its code is cut off):
+  y = (x - mean) * rstd * w + b per row, and the derivative of that definition,
+  dw and db summed over the rows.
 * ``xent_count``, ``xent_rows``, ``mean``, ``xent`` -- Liger-Kernel
   ``cross_entropy.py``: ``liger_cross_entropy_kernel`` steps 1-6 (ignore
   early-out, loss ``m + log d - x_y``, gradient ``(softmax - onehot)/n``) and
@@ -74,6 +78,12 @@ class Oracle:
         lib.xro_softmax_bwd.restype = None
         lib.xro_nll_fwd.argtypes = [_p, _c_i64, _p, _c_i64, _c_i64, ctypes.c_int, _p, _p]
         lib.xro_nll_fwd.restype = None
+        lib.xro_layernorm_fwd.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, ctypes.c_double,
+                                          ctypes.c_int, _p, _p, _p]
+        lib.xro_layernorm_fwd.restype = None
+        lib.xro_layernorm_bwd.argtypes = [_p, _c_i64, _p, _c_i64, _p, _c_i64, _c_i64,
+                                          ctypes.c_double, ctypes.c_int, _p, _p, _p]
+        lib.xro_layernorm_bwd.restype = None
         lib.xro_xent_count.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p]
         lib.xro_xent_count.restype = None
         lib.xro_xent_rows.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, _c_i64, ctypes.c_int,
@@ -155,6 +165,47 @@ class Oracle:
         self.lib.xro_nll_fwd(ptr, ld, ix.ctypes.data, M, N, code, out.ctypes.data,
                              loss.ctypes.data)
         return out, loss
+
+    def _vector(self, a: np.ndarray, code: int, N: int, name: str) -> np.ndarray:
+        a = np.ascontiguousarray(a)
+        if a.ndim != 1 or a.shape[0] < N or (BF16 if a.dtype == np.uint16 else F32) != code or \
+                a.dtype not in (np.uint16, np.float32):
+            raise ValueError(f"{name} must be a 1-D array of >= N entries in x's type")
+        return a
+
+    def layernorm_fwd(self, x: np.ndarray, w: np.ndarray, b: np.ndarray, eps: float,
+                      n_cols: int | None = None):
+        """(y [M, N], mean [M], rstd [M]) as float64."""
+        ptr, ld, M, code = self._matrix(x)
+        N = x.shape[1] if n_cols is None else int(n_cols)
+        if not 0 < N <= x.shape[1]:
+            raise ValueError("n_cols out of range")
+        w = self._vector(w, code, N, "w")
+        b = self._vector(b, code, N, "b")
+        y = np.full((M, N), np.nan, dtype=np.float64)
+        mean = np.full(M, np.nan, dtype=np.float64)
+        rstd = np.full(M, np.nan, dtype=np.float64)
+        self.lib.xro_layernorm_fwd(ptr, ld, w.ctypes.data, b.ctypes.data, M, N, float(eps), code,
+                                   y.ctypes.data, mean.ctypes.data, rstd.ctypes.data)
+        return y, mean, rstd
+
+    def layernorm_bwd(self, dy: np.ndarray, x: np.ndarray, w: np.ndarray, eps: float,
+                      n_cols: int | None = None):
+        """(dx [M, N], dw [N], db [N]) as float64."""
+        pd, ldd, M, code = self._matrix(dy)
+        px, ldx, M2, code2 = self._matrix(x)
+        if M != M2 or code != code2:
+            raise ValueError("dy and x must have the same rows and type")
+        N = x.shape[1] if n_cols is None else int(n_cols)
+        if not 0 < N <= min(x.shape[1], dy.shape[1]):
+            raise ValueError("n_cols out of range")
+        w = self._vector(w, code, N, "w")
+        dx = np.full((M, N), np.nan, dtype=np.float64)
+        dw = np.full(N, np.nan, dtype=np.float64)
+        db = np.full(N, np.nan, dtype=np.float64)
+        self.lib.xro_layernorm_bwd(pd, ldd, px, ldx, w.ctypes.data, M, N, float(eps), code,
+                                   dx.ctypes.data, dw.ctypes.data, db.ctypes.data)
+        return dx, dw, db
 
     def xent_count(self, target: np.ndarray, V: int, ignore_index: int = -100):
         t = np.ascontiguousarray(target, dtype=np.int64)

@@ -23,6 +23,14 @@
  *                        the row's loss is the output element at the row's
  *                        index as stored (the kernel reads it back from the
  *                        output), i.e. rounded to the output type.
+ *   layer norm        -- the Triton LayerNorm tutorial page (translated; its code is
+ *                        cut off, so the definitions come from its prose and the
+ *                        cited paper, Ba, Kiros & Hinton 2016): per row, mean
+ *                        and variance over the N features, rstd = 1/sqrt(var +
+ *                        eps), y = (x - mean) * rstd * w + b; the backward is the
+ *                        derivative of that definition, with dw and db summed
+ *                        over all rows (the page's two-stage reduction reaches
+ *                        the same sums).
  *   cross-entropy     -- Liger-Kernel `cross_entropy.py`,
  *                        `liger_cross_entropy_kernel` steps 1-6 and
  *                        `LigerCrossEntropyFunction.forward`: per-row loss
@@ -63,6 +71,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -173,6 +182,94 @@ void xro_nll_fwd(const void* x, int64_t ld_x, const int64_t* idx, int64_t M, int
     for (int64_t j = 0; j < N; ++j) out[i * N + j] = lse - (load_elem(x, i * ld_x + j, dtype) - m);
     loss[i] = (idx[i] >= 0 && idx[i] < N) ? round_to_dtype(out[i * N + idx[i]], dtype) : NAN;
   }
+}
+
+/*
+ * Layer norm forward. x [M, N] (row stride ld_x), w and b [N], all in dtype.
+ * y [M][N] contiguous doubles; mean [M], rstd [M] doubles.
+ *   mean_i = (1/N) sum_j x_ij,  var_i = (1/N) sum_j (x_ij - mean_i)^2,
+ *   rstd_i = 1 / sqrt(var_i + eps),  y_ij = (x_ij - mean_i) * rstd_i * w_j + b_j
+ */
+void xro_layernorm_fwd(const void* x, int64_t ld_x, const void* w, const void* b, int64_t M,
+                       int64_t N, double eps, int dtype, double* y, double* mean, double* rstd) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) {
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j) s += load_elem(x, i * ld_x + j, dtype);
+    double mu = s / (double)N;
+    double v = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      double c = load_elem(x, i * ld_x + j, dtype) - mu;
+      v += c * c;
+    }
+    double r = 1.0 / sqrt(v / (double)N + eps);
+    mean[i] = mu;
+    rstd[i] = r;
+    for (int64_t j = 0; j < N; ++j)
+      y[i * N + j] = (load_elem(x, i * ld_x + j, dtype) - mu) * r * load_elem(w, j, dtype) +
+                     load_elem(b, j, dtype);
+  }
+}
+
+/*
+ * Layer norm backward: the derivative of xro_layernorm_fwd's y with respect to x, w and b,
+ * contracted with dy [M, N] (row stride ld_dy). mean and rstd are recomputed from x in
+ * double. With xhat_ij = (x_ij - mean_i) * rstd_i and g_ij = w_j * dy_ij:
+ *   dx_ij = rstd_i * (g_ij - (xhat_ij * c1_i + c2_i)),
+ *       c1_i = (1/N) sum_j xhat_ij g_ij,  c2_i = (1/N) sum_j g_ij
+ *   dw_j = sum_i dy_ij xhat_ij,  db_j = sum_i dy_ij      (sums in row order)
+ * dx [M][N] contiguous doubles, dw [N], db [N] doubles.
+ */
+void xro_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
+                       int64_t M, int64_t N, double eps, int dtype, double* dx, double* dw,
+                       double* db) {
+  double* mu = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  double* rs = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) {
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j) s += load_elem(x, i * ld_x + j, dtype);
+    double m = s / (double)N;
+    double v = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      double c = load_elem(x, i * ld_x + j, dtype) - m;
+      v += c * c;
+    }
+    double r = 1.0 / sqrt(v / (double)N + eps);
+    mu[i] = m;
+    rs[i] = r;
+    double c1 = 0.0, c2 = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      double xh = (load_elem(x, i * ld_x + j, dtype) - m) * r;
+      double g = load_elem(w, j, dtype) * load_elem(dy, i * ld_dy + j, dtype);
+      c1 += xh * g;
+      c2 += g;
+    }
+    c1 /= (double)N;
+    c2 /= (double)N;
+    for (int64_t j = 0; j < N; ++j) {
+      double xh = (load_elem(x, i * ld_x + j, dtype) - m) * r;
+      double g = load_elem(w, j, dtype) * load_elem(dy, i * ld_dy + j, dtype);
+      dx[i * N + j] = r * (g - (xh * c1 + c2));
+    }
+  }
+  /* dw and db: column sums over the rows, in row order */
+  int64_t j;
+#pragma omp parallel for schedule(static)
+  for (j = 0; j < N; ++j) {
+    double sw = 0.0, sb = 0.0;
+    for (int64_t r = 0; r < M; ++r) {
+      double d = load_elem(dy, r * ld_dy + j, dtype);
+      sw += d * ((load_elem(x, r * ld_x + j, dtype) - mu[r]) * rs[r]);
+      sb += d;
+    }
+    dw[j] = sw;
+    db[j] = sb;
+  }
+  free(mu);
+  free(rs);
 }
 
 /* counts[0] = #{i : t_i != ignore_index}; counts[1] = those among them outside [0, V). */

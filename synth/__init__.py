@@ -174,6 +174,30 @@ def xent_c5(M: int = 2048, V: int = 256000, pad: int = 64, seed: int = 1005) -> 
             "half_inf_rows": np.sort(half_inf_rows)}
 
 
+def layernorm_ln(M: int = 16384, N: int = 8192, seed: int = 1006, dtype: str = "bf16") -> dict:
+    """Layer norm forward + backward inputs: token rows of an 8192-wide hidden state.
+
+    x = 2 N(0,1) + a per-row offset N(0,1) (rows do not have mean 0), w = 1 + 0.1 N(0,1),
+    b = 0.1 N(0,1), dy = N(0,1) (seed + 100), eps = 1e-5."""
+    shape_dt = np.uint16 if dtype == "bf16" else np.float32
+    conv = bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a)
+
+    def rows_x(rng, rows):
+        a = _normal(rng, (rows, N), 2.0)
+        a += _normal(rng, (rows, 1), 1.0)
+        return conv(a)
+
+    x = np.empty((M, N), dtype=shape_dt)
+    dy = np.empty((M, N), dtype=shape_dt)
+    _fill_chunks(x, N, seed, rows_x)
+    _fill_chunks(dy, N, seed + 100, lambda rng, rows: conv(_normal(rng, (rows, N), 1.0)))
+    rng = np.random.Generator(np.random.PCG64(seed + 200))
+    w = conv(1.0 + _normal(rng, (N,), 0.1))
+    b = conv(_normal(rng, (N,), 0.1))
+    return {"op": "layernorm", "M": M, "N": N, "dtype": dtype, "x": x, "dy": dy, "w": w, "b": b,
+            "eps": 1e-5, "seed": seed}
+
+
 WORKLOADS = {"c1": softmax_c1, "c2": softmax_c2, "c3": xent_c3, "c4": xent_c4, "c5": xent_c5}
 
 

@@ -27,8 +27,8 @@ import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                       "worked_examples.json")
-_MATH = {"log": math.log, "exp": math.exp, "inf": math.inf, "nan": math.nan,
-         "__builtins__": {}}
+_MATH = {"log": math.log, "exp": math.exp, "sqrt": math.sqrt, "inf": math.inf,
+         "nan": math.nan, "__builtins__": {}}
 
 
 def closed_form(expr) -> float:
@@ -365,6 +365,100 @@ def pin_nll_loss_is_the_stored_element(o):
         assert np.array_equal(out_d, out)
 
 
+# --------------------------------------------------------------------------- layer norm
+def _ln_inputs(seed, M, N, dtype, ld=None, scale=2.0):
+    x = synth.random_rows(seed, M, N, ld=ld, dtype=dtype, scale=scale, pad_nan=ld is not None)
+    wb = synth.random_rows(seed + 1, 2, N, dtype=dtype, scale=1.0)
+    return x, np.ascontiguousarray(wb[0]), np.ascontiguousarray(wb[1])
+
+
+def pin_layernorm_matches_torch(o):
+    import torch
+    import torch.nn.functional as F
+    for seed, (M, N, dtype, eps, ld) in enumerate([(9, 1000, "f32", 1e-5, None),
+                                                   (7, 513, "bf16", 1e-6, 520),
+                                                   (5, 64, "f32", 0.5, 70)]):
+        x, w, b = _ln_inputs(1800 + 10 * seed, M, N, dtype, ld)
+        dy = synth.random_rows(1805 + 10 * seed, M, N, dtype=dtype, scale=1.0)
+        y, mean, rstd = o.layernorm_fwd(x, w, b, eps, n_cols=N)
+        dx, dw, db = o.layernorm_bwd(dy, x, w, eps, n_cols=N)
+        xt = torch.from_numpy(decode(x)[:, :N]).requires_grad_(True)
+        wt = torch.from_numpy(decode(w)).requires_grad_(True)
+        bt = torch.from_numpy(decode(b)).requires_grad_(True)
+        ref = F.layer_norm(xt, (N,), wt, bt, eps)
+        ref.backward(torch.from_numpy(decode(dy)))
+        assert np.max(np.abs(y - ref.detach().numpy())) <= 1e-12, "y vs torch layer_norm"
+        assert np.max(np.abs(dx - xt.grad.numpy())) <= 1e-12, "dx vs torch autograd"
+        assert np.max(np.abs(dw - wt.grad.numpy())) <= 1e-12, "dw vs torch autograd"
+        assert np.max(np.abs(db - bt.grad.numpy())) <= 1e-12, "db vs torch autograd"
+        xd = decode(x)[:, :N]
+        assert np.max(np.abs(mean - xd.mean(axis=1))) <= 1e-12
+        assert np.max(np.abs(rstd - 1 / np.sqrt(xd.var(axis=1) + eps))) <= 1e-9 * np.max(rstd)
+
+
+def pin_layernorm_invariants(o):
+    """With w = 1 and b = 0 every output row has mean 0 and mean square var / (var + eps);
+    constant rows give y = b exactly and rstd = 1/sqrt(eps); the backward of w = 1 rows sums
+    to 0 (and with eps = 0 is orthogonal to xhat); db is the exact column sum of dy."""
+    M, N, eps = 6, 300, 1e-3
+    x, _, b = _ln_inputs(1900, M, N, "f32", scale=3.0)
+    ones = np.ones(N, dtype=np.float32)
+    zeros = np.zeros(N, dtype=np.float32)
+    y, mean, rstd = o.layernorm_fwd(x, ones, zeros, eps)
+    var = decode(x).var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) <= 1e-12
+    assert np.max(np.abs((y ** 2).mean(axis=1) - var / (var + eps))) <= 1e-12
+    c = np.full((2, N), 1.25, dtype=np.float32)
+    yc, mc, rc = o.layernorm_fwd(c, ones, b, eps)
+    assert np.all(yc == decode(b)[None, :]) and np.all(mc == 1.25)
+    assert np.all(rc == 1.0 / math.sqrt(eps))
+    dy = synth.random_rows(1901, M, N, dtype="f32", scale=1.0)
+    dx, dw, db = o.layernorm_bwd(dy, x, ones, eps)
+    xhat = (decode(x) - mean[:, None]) * rstd[:, None]
+    assert np.max(np.abs(dx.sum(axis=1))) <= 1e-11, "w = 1: dx rows sum to 0"
+    # with eps = 0 the output is scale invariant in x - mean: dx is orthogonal to xhat
+    dx0, _, _ = o.layernorm_bwd(dy, x, ones, 0.0)
+    _, m0, r0 = o.layernorm_fwd(x, ones, zeros, 0.0)
+    xhat0 = (decode(x) - m0[:, None]) * r0[:, None]
+    assert np.max(np.abs((dx0 * xhat0).sum(axis=1))) <= 1e-11, "eps = 0: dx orthogonal to xhat"
+    assert all(db[j] == math.fsum(decode(dy)[:, j].tolist()) or
+               abs(db[j] - math.fsum(decode(dy)[:, j].tolist())) <= 1e-14 for j in range(N))
+    assert np.max(np.abs(dw - (decode(dy) * xhat).sum(axis=0))) <= 1e-12
+
+
+def pin_layernorm_finite_differences(o):
+    """The backward is the derivative of the forward: central differences of
+    sum(g * y) with respect to every x, w and b element."""
+    M, N, eps = 3, 5, 0.125
+    x = _grid_rows(1950, M, N, 1.0 / 4, -2.0, 2.0)
+    wb = _grid_rows(1951, 2, N, 1.0 / 4, -1.5, 1.5)
+    w, b = np.ascontiguousarray(wb[0]), np.ascontiguousarray(wb[1])
+    g = _grid_rows(1952, M, N, 1.0 / 8, -1.0, 1.0)
+    dx, dw, db = o.layernorm_bwd(g, x, w, eps)
+    h = 2.0 ** -14
+    gd = g.astype(np.float64)
+
+    def obj(xx, ww, bb):
+        return float((o.layernorm_fwd(xx, ww, bb, eps)[0] * gd).sum())
+
+    for i in range(M):
+        for j in range(N):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += np.float32(h)
+            xm[i, j] -= np.float32(h)
+            fd = (obj(xp, w, b) - obj(xm, w, b)) / (2 * h)
+            assert abs(fd - dx[i, j]) <= 1e-7, f"dx vs finite differences at ({i},{j})"
+    for j in range(N):
+        wp, wm = w.copy(), w.copy()
+        wp[j] += np.float32(h)
+        wm[j] -= np.float32(h)
+        assert abs((obj(x, wp, b) - obj(x, wm, b)) / (2 * h) - dw[j]) <= 1e-7, f"dw {j}"
+        bp, bm = b.copy(), b.copy()
+        bp[j] += np.float32(h)
+        bm[j] -= np.float32(h)
+        assert abs((obj(x, w, bp) - obj(x, w, bm)) / (2 * h) - db[j]) <= 1e-7, f"db {j}"
+
+
 # ------------------------------------------------------- reductions and upstream gradient
 def pin_xent_reductions_finite_differences(o):
     """Each reduction's gradient, times its upstream value, is the derivative of that loss."""
@@ -503,6 +597,19 @@ def pin_golden_worked_examples(o):
         assert np.array_equal(np.isnan(loss), np.isnan(wl)), case["name"]
         ok = ~np.isnan(wl)
         assert np.max(np.abs(loss[ok] - wl[ok])) <= 2e-7 * np.max(np.abs(wl[ok])), case["name"]
+    for case in gold["layernorm"]:
+        x = as_input(case["x"], case["dtype"])
+        w = as_input([case["w"]], case["dtype"])[0]
+        b = as_input([case["b"]], case["dtype"])[0]
+        dy = as_input(case["dy"], case["dtype"])
+        y, mean, rstd = o.layernorm_fwd(x, w, b, case["eps"])
+        dx, dw, db = o.layernorm_bwd(dy, x, w, case["eps"])
+        for got, key in ((y, "y"), (dx, "dx")):
+            want = np.array([[closed_form(v) for v in r] for r in case[key]])
+            assert np.max(np.abs(got - want)) <= 1e-15, f"{case['name']}: {key}"
+        for got, key in ((mean, "mean"), (rstd, "rstd"), (dw, "dw"), (db, "db")):
+            want = np.array([closed_form(v) for v in case[key]])
+            assert np.max(np.abs(got - want)) <= 1e-15, f"{case['name']}: {key}"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

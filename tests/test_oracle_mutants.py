@@ -71,6 +71,32 @@ MUTANTS = {
     "bf16 rounding truncates": ("return ldexp(nearbyint(ldexp(f, 8)), e - 8);",
                                 "return ldexp(trunc(ldexp(f, 8)), e - 8);"),
     "nll accepts an index equal to N": ("(idx[i] >= 0 && idx[i] < N)", "(idx[i] >= 0 && idx[i] <= N)"),
+    "layer norm drops eps": ("double r = 1.0 / sqrt(v / (double)N + eps);\n    mean[i] = mu;",
+                             "double r = 1.0 / sqrt(v / (double)N);\n    mean[i] = mu;"),
+    "layer norm variance over N - 1": ("double r = 1.0 / sqrt(v / (double)N + eps);\n    mean[i] = mu;",
+                                       "double r = 1.0 / sqrt(v / (double)(N - 1) + eps);\n    mean[i] = mu;"),
+    "layer norm multiplies by std": ("double r = 1.0 / sqrt(v / (double)N + eps);\n    mean[i] = mu;",
+                                     "double r = sqrt(v / (double)N + eps);\n    mean[i] = mu;"),
+    "layer norm skips the weight": ("(load_elem(x, i * ld_x + j, dtype) - mu) * r * load_elem(w, j, dtype) +",
+                                    "(load_elem(x, i * ld_x + j, dtype) - mu) * r +"),
+    "layer norm bias at the wrong column": ("                     load_elem(b, j, dtype);",
+                                            "                     load_elem(b, (j + 1) % N, dtype);"),
+    "layer norm backward drops c1": ("dx[i * N + j] = r * (g - (xh * c1 + c2));",
+                                     "dx[i * N + j] = r * (g - c2);"),
+    "layer norm backward drops c2": ("dx[i * N + j] = r * (g - (xh * c1 + c2));",
+                                     "dx[i * N + j] = r * (g - xh * c1);"),
+    "layer norm backward drops rstd": ("dx[i * N + j] = r * (g - (xh * c1 + c2));",
+                                       "dx[i * N + j] = (g - (xh * c1 + c2));"),
+    "layer norm backward c2 unweighted": ("      c1 += xh * g;\n      c2 += g;",
+                                          "      c1 += xh * g;\n      c2 += load_elem(dy, i * ld_dy + j, dtype);"),
+    "layer norm dw uses x instead of xhat": (
+        "sw += d * ((load_elem(x, r * ld_x + j, dtype) - mu[r]) * rs[r]);",
+        "sw += d * load_elem(x, r * ld_x + j, dtype);"),
+    "layer norm dw reads dy with x's stride": (
+        "double d = load_elem(dy, r * ld_dy + j, dtype);",
+        "double d = load_elem(dy, r * ld_x + j, dtype);"),
+    "layer norm db skips the last row": ("for (int64_t r = 0; r < M; ++r) {\n      double d =",
+                                         "for (int64_t r = 0; r + 1 < M; ++r) {\n      double d ="),
     "element_mul adds the scale": ("out[i * V + j] = load_elem(x, i * ld + j, dtype) * w;",
                                    "out[i * V + j] = load_elem(x, i * ld + j, dtype) + w;"),
     "ignored rows keep stale gradient": ("        for (int64_t j = 0; j < V; ++j) g[j] = 0.0;\n      continue;",
