@@ -13,7 +13,7 @@ the library records around that launch on its stream; `cpu_baseline` times the f
 oracle on the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
-                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll] [--reduction mean|sum|none]
+                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln] [--reduction mean|sum|none]
                     [--grad-scale S]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
 
@@ -24,7 +24,8 @@ previous step left in the 256 MB Infinity Cache. `--reduction` / `--grad-scale` 
 cross-entropy workloads with another reduction or an upstream gradient folded into the
 gradient write; `c4-mul` times the backward's element_mul (the stored gradient times an
 upstream gradient of 0.5) over the 16384 x 128256 bf16 matrix; `c4-nll` the negative
-log-softmax forward with a gathered loss over the same matrix, into a separate output.
+log-softmax forward with a gathered loss over the same matrix, into a separate output;
+`ln` a layer norm forward + backward (both stages) over 16384 x 8192 bf16 rows.
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 C4_M, C4_V, C4_KEEP = 16384, 128256, 15565
 
 DESCRIPTIONS = {
+    "ln": "layer norm forward + backward (dx, and dw / db in two stages), M=16384, N=8192, "
+          "bf16 x / dy / w / b, fp32 statistics and sums, eps=1e-5",
     "c4-nll": "negative log-softmax forward + loss gathered at each row's target, M=16384, "
               "N=128256, bf16 logits in, bf16 -log p out (separate buffer), fp32 losses",
     "c4-mul": "element_mul (stored gradient x upstream gradient 0.5, in place), M=16384, "
@@ -299,6 +302,61 @@ def run_nll(args, name: str) -> dict:
                   "vec_per_thread": p["vec_per_thread"], "grid": p["grid"]}, "bf16")
 
 
+def run_layernorm(args, name: str) -> dict:
+    """Forward then backward on the same rows; inputs rotated over >= 1 GB of copies."""
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.layernorm_ln()
+    M, N = wl["M"], wl["N"]
+    x = _device_matrix(torch, wl["x"], dev)
+    dy = _device_matrix(torch, wl["dy"], dev)
+    w = _device_matrix(torch, wl["w"], dev)
+    b = _device_matrix(torch, wl["b"], dev)
+    elt = x.element_size()
+    per_set = 5 * M * N * elt
+    nsets = max(2, -(-(1 << 30) // per_set))
+    xs = [x.clone() for _ in range(nsets)]
+    dys = [dy.clone() for _ in range(nsets)]
+    ys = [torch.empty_like(x) for _ in range(nsets)]
+    dxs = [torch.empty_like(x) for _ in range(nsets)]
+    mean = torch.empty(M, dtype=torch.float32, device=dev)
+    rstd = torch.empty(M, dtype=torch.float32, device=dev)
+    dw = torch.empty(N, dtype=x.dtype, device=dev)
+    db = torch.empty(N, dtype=x.dtype, device=dev)
+    ws = torch.empty(max(16, xr.layernorm_bwd_workspace_bytes(M, N, x.dtype)), dtype=torch.uint8,
+                     device=dev)
+    ev = HipEvents()
+    bwd_events = [(ev.create(), ev.create()) for _ in range(args.warmup + args.steps)]
+
+    def launch(i):
+        j = i % nsets
+        xr.layernorm_fwd(xs[j], w, b, wl["eps"], out=ys[j], mean=mean, rstd=rstd)
+        xr.set_profile_events(*bwd_events[i])
+        xr.layernorm_bwd(dys[j], xs[j], w, mean, rstd, dx=dxs[j], dw=dw, db=db, workspace=ws)
+
+    wall, fwd_ms = _timed(ev, args.steps, args.warmup, launch)
+    bwd_ms = [ev.elapsed_ms(a, b_) for a, b_ in bwd_events[args.warmup:]]
+    for a, b_ in bwd_events:
+        ev.destroy(a)
+        ev.destroy(b_)
+    b_fwd = 2 * M * N * elt + 2 * N * elt + 8 * M
+    b_bwd = 3 * M * N * elt + N * elt + 8 * M + 2 * N * elt
+    out = _line(args, name, b_fwd + b_bwd, M, wall, fwd_ms, "ln_fwd_kernel",
+                {"M": M, "N": N, "bytes_min": b_fwd + b_bwd, "input_sets": nsets,
+                 "workspace_bytes": ws.numel()}, "bf16", kernel_bytes=b_fwd)
+    kavg = statistics.mean(bwd_ms)
+    out["roofline_bwd"] = {"bound": "hbm", "achieved": round(b_bwd / kavg / 1e6, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(b_bwd / kavg / 1e6 / PEAK_HBM_GBS, 4),
+                           "kernel": "ln_bwd_kernel (stage 1)", "kernel_ms_avg": round(kavg, 5)}
+    return out
+
+
 def run_softmax(args, name: str) -> dict:
     import torch
 
@@ -445,6 +503,8 @@ def main() -> int:
         out = run_element_mul(args, args.workload)
     elif args.workload == "c4-nll":
         out = run_nll(args, args.workload)
+    elif args.workload == "ln":
+        out = run_layernorm(args, args.workload)
     else:
         out = run_xent(args, args.workload)
     print(json.dumps(out), flush=True)

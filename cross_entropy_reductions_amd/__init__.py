@@ -39,6 +39,14 @@ lib.xr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.
 lib.xr_softmax_bwd.restype = ctypes.c_int
 lib.xr_nll_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, ctypes.c_int, _p]
 lib.xr_nll_fwd.restype = ctypes.c_int
+lib.xr_layernorm_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _i64, ctypes.c_float,
+                                 ctypes.c_int, _p]
+lib.xr_layernorm_fwd.restype = ctypes.c_int
+lib.xr_layernorm_bwd_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
+lib.xr_layernorm_bwd_workspace_bytes.restype = _sz
+lib.xr_layernorm_bwd.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _p, _i64, _i64,
+                                 ctypes.c_int, _p, _sz, _p]
+lib.xr_layernorm_bwd.restype = ctypes.c_int
 lib.xr_xent_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
 lib.xr_xent_workspace_bytes.restype = _sz
 lib.xr_xent_fwd_bwd.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p, _p, _p, _p,
@@ -68,7 +76,8 @@ lib.xr_set_profile_events.argtypes = [_p, _p]
 lib.xr_set_profile_events.restype = ctypes.c_int
 
 # Names exported by include/xr.h (checked against the library by the tests).
-C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_nll_fwd", "xr_xent_workspace_bytes",
+C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_nll_fwd", "xr_layernorm_fwd",
+             "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
              "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_status_string", "xr_version",
              "xr_plan", "xr_set_option", "xr_set_profile_events")
@@ -176,6 +185,105 @@ def nll_fwd(x: torch.Tensor, idx: torch.Tensor, out: torch.Tensor | None = None,
     _check("xr_nll_fwd", lib.xr_nll_fwd(po, ldo, px, ldx, idx.data_ptr(), loss.data_ptr(), M, N,
                                         dt, _stream(x, stream)))
     return out, loss
+
+
+def _vector(t: torch.Tensor, name: str, N: int, dt: int, dev) -> int:
+    if not isinstance(t, torch.Tensor) or t.device != dev or _DTYPES.get(t.dtype) != dt:
+        raise TypeError(f"{name} must be a tensor of the input's dtype on its device")
+    if t.dim() != 1 or t.shape[0] != N or (N > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous 1-D tensor of N entries")
+    return t.data_ptr()
+
+
+def layernorm_fwd(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, eps: float = 1e-5,
+                  out: torch.Tensor | None = None, mean: torch.Tensor | None = None,
+                  rstd: torch.Tensor | None = None, *, stream=None):
+    """Layer norm of each row of x: returns (y, mean, rstd); y may be x itself."""
+    px, ldx, M, N, dt = _matrix(x, "x")
+    pw = _vector(w, "w", N, dt, x.device)
+    pb = _vector(b, "b", N, dt, x.device)
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    py, ldy, M2, N2, dt2 = _matrix(out, "out")
+    if (M2, N2, dt2) != (M, N, dt) or out.device != x.device:
+        raise ValueError("out must match x in shape, dtype and device")
+    if mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=x.device)
+    if rstd is None:
+        rstd = torch.empty(M, dtype=torch.float32, device=x.device)
+    for t, name in ((mean, "mean"), (rstd, "rstd")):
+        if t.dtype != torch.float32 or t.device != x.device or t.numel() < M or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of one entry per row")
+    _check("xr_layernorm_fwd",
+           lib.xr_layernorm_fwd(py, ldy, px, ldx, pw, pb, mean.data_ptr(), rstd.data_ptr(), M, N,
+                                float(eps), dt, _stream(x, stream)))
+    return out, mean, rstd
+
+
+def layernorm_bwd_workspace_bytes(M: int, N: int, dtype: torch.dtype) -> int:
+    return int(lib.xr_layernorm_bwd_workspace_bytes(int(M), int(N), _DTYPES[dtype]))
+
+
+def layernorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, mean: torch.Tensor,
+                  rstd: torch.Tensor, dx: torch.Tensor | None = None,
+                  dw: torch.Tensor | None = None, db: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, *, stream=None):
+    """Layer norm backward: returns (dx, dw, db); dx may be dy or x itself."""
+    pd, ldd, M, N, dt = _matrix(dy, "dy")
+    px, ldx, M2, N2, dt2 = _matrix(x, "x")
+    if (M2, N2, dt2) != (M, N, dt) or x.device != dy.device:
+        raise ValueError("x must match dy in shape, dtype and device")
+    pw = _vector(w, "w", N, dt, dy.device)
+    for t, name in ((mean, "mean"), (rstd, "rstd")):
+        if t.dtype != torch.float32 or t.device != dy.device or t.numel() < M or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of one entry per row")
+    if dx is None:
+        dx = torch.empty_like(dy, memory_format=torch.contiguous_format)
+    pdx, lddx, M3, N3, dt3 = _matrix(dx, "dx")
+    if (M3, N3, dt3) != (M, N, dt) or dx.device != dy.device:
+        raise ValueError("dx must match dy in shape, dtype and device")
+    if dw is None:
+        dw = torch.empty(N, dtype=dy.dtype, device=dy.device)
+    if db is None:
+        db = torch.empty(N, dtype=dy.dtype, device=dy.device)
+    pdw = _vector(dw, "dw", N, dt, dy.device)
+    pdb = _vector(db, "db", N, dt, dy.device)
+    need = layernorm_bwd_workspace_bytes(M, N, dy.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dy.device)
+    _check("xr_layernorm_bwd",
+           lib.xr_layernorm_bwd(pdx, lddx, pd, ldd, px, ldx, pw, mean.data_ptr(), rstd.data_ptr(),
+                                pdw, pdb, M, N, dt, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(dy, stream)))
+    return dx, dw, db
+
+
+class LayerNormFunction(torch.autograd.Function):
+    """Layer norm over the last dimension as a torch.autograd.Function (the shape of the
+    Triton LayerNorm tutorial's LayerNorm class): the forward saves x, w, mean and rstd;
+    the backward runs the two-stage dw / db reduction."""
+
+    @staticmethod
+    def forward(ctx, x, normalized_shape, weight, bias, eps=1e-5):
+        x2 = x.reshape(-1, x.shape[-1])
+        y, mean, rstd = layernorm_fwd(x2, weight, bias, eps)
+        ctx.save_for_backward(x2, weight, mean, rstd)
+        return y.reshape(x.shape)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x2, w, mean, rstd = ctx.saved_tensors
+        dy2 = dy.reshape(-1, dy.shape[-1])
+        if dy2.stride(-1) != 1:
+            dy2 = dy2.contiguous()
+        dx, dw, db = layernorm_bwd(dy2, x2, w, mean, rstd)
+        return dx.reshape(dy.shape), None, dw, db, None
+
+
+def layer_norm(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
+               eps: float = 1e-5) -> torch.Tensor:
+    """Autograd-aware layer norm over the last dimension."""
+    return LayerNormFunction.apply(x, (x.shape[-1],), weight, bias, eps)
 
 
 def xent_workspace_bytes(M: int, V: int, dtype: torch.dtype) -> int:

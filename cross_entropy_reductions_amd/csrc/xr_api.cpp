@@ -285,6 +285,57 @@ xr_status_t launch(const Plan& p, void* params, hipStream_t stream, int threads)
   return XR_OK;
 }
 
+// Layer norm launch plan. Row-resident kernels need every row of every matrix, w and b on
+// 16-byte boundaries and N * element size a multiple of 16 (`resident_ok`), and a shape of
+// the menu holding a row; anything else takes the stream kernels. Both kernels run a
+// persistent grid: the forward keeps w and b in registers across its rows, the backward
+// keeps its column sums (one partial row per workgroup, summed by the second stage).
+struct LnPlan {
+  const void* kernel = nullptr;
+  int threads = kStreamThreads;
+  int vpt = 0;
+  int64_t grid = 0;
+  bool stream = true;
+};
+constexpr int kLnBwdStreamPerCu = 4;  // stream backward: workgroups per compute unit
+
+xr_status_t make_ln_plan(bool bwd, int64_t M, int64_t N, xr_dtype_t dt, bool resident_ok,
+                         LnPlan* out) {
+  int dev = 0;
+  DeviceInfo di;
+  if (xr_status_t st = device_info(&dev, &di)) return st;
+  LnPlan p;
+  const int64_t epv = 16 / elt_bytes(dt);
+  const Shape* sh = nullptr;
+  if (resident_ok && g_opt.path != kPathStream)
+    sh = pick_shape(bwd ? kLnBwdShapes : kLnFwdShapes, bwd ? kNumLnBwdShapes : kNumLnFwdShapes,
+                    N / epv);
+  const bool nt = g_opt.load_policy ? g_opt.load_policy == 2 : true;
+  const void* rk = nullptr;
+  if (sh) rk = bwd ? ln_bwd_kernel_ptr(dt, *sh, nt) : ln_fwd_kernel_ptr(dt, *sh, nt);
+  if (!rk) {
+    if (g_opt.path == kPathResident || g_opt.path == kPathSplit) return XR_ERR_SHAPE;
+    sh = nullptr;
+  }
+  if (sh) {
+    p.kernel = rk;
+    p.threads = sh->threads;
+    p.vpt = sh->vpt;
+    p.stream = false;
+    int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
+    if (per_cu <= 0) return XR_ERR_DEVICE;
+    if (g_opt.grid > 0) per_cu = std::min<int>(per_cu, (int)g_opt.grid);
+    p.grid = std::min<int64_t>(M, (int64_t)di.cus * per_cu);
+  } else {
+    p.kernel = bwd ? ln_bwd_stream_kernel_ptr(dt) : ln_fwd_stream_kernel_ptr(dt);
+    p.grid = bwd ? std::min<int64_t>(M, (int64_t)di.cus * kLnBwdStreamPerCu) : M;
+  }
+  *out = p;
+  return XR_OK;
+}
+
+int64_t ln_pstride(int64_t N) { return (N + 3) / 4 * 4; }
+
 size_t xent_ws_bytes(const Plan& p, int64_t M) {
   return kWsPartials + (p.path == kPathSplit ? (size_t)M * (size_t)p.S * sizeof(uint64_t) : 0);
 }
@@ -415,6 +466,102 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
                        M, N, idx, loss};
   return launch(p, &prm, static_cast<hipStream_t>(stream),
                 p.path == kPathStream ? kStreamThreads : p.shape.threads);
+}
+
+xr_status_t xr_layernorm_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, const void* w,
+                             const void* b, float* mean, float* rstd, int64_t M, int64_t N,
+                             float eps, xr_dtype_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (ld_x < N || ld_y < N) return XR_ERR_STRIDE;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return XR_ERR_VALUE;
+  if (M == 0) return XR_OK;
+  if (!y || !x || !w || !b || !mean || !rstd) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if (!aligned_to(y, eb) || !aligned_to(x, eb) || !aligned_to(w, eb) || !aligned_to(b, eb) ||
+      !aligned_to(mean, 4) || !aligned_to(rstd, 4))
+    return XR_ERR_ALIGN;
+  if (bad_alias(y, ld_y, x, ld_x, M, N, eb)) return XR_ERR_ALIAS;
+  const uint64_t ys = matrix_span(M, ld_y, N, eb);
+  if (spans_overlap(y, ys, w, (uint64_t)N * eb) || spans_overlap(y, ys, b, (uint64_t)N * eb) ||
+      spans_overlap(y, ys, mean, (uint64_t)M * 4) || spans_overlap(y, ys, rstd, (uint64_t)M * 4) ||
+      spans_overlap(mean, (uint64_t)M * 4, rstd, (uint64_t)M * 4))
+    return XR_ERR_ALIAS;
+  const bool resident_ok = rows_on_16(x, ld_x, M, eb) && rows_on_16(y, ld_y, M, eb) &&
+                           aligned_to(w, 16) && aligned_to(b, 16) && (N * eb) % 16 == 0;
+  LnPlan lp;
+  if (xr_status_t st = make_ln_plan(false, M, N, dtype, resident_ok, &lp)) return st;
+  LnFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb,
+                  static_cast<const char*>(w), static_cast<const char*>(b), mean, rstd, M, N, eps};
+  Plan p;
+  p.kernel = lp.kernel;
+  p.grid = lp.grid;
+  return launch(p, &prm, static_cast<hipStream_t>(stream), lp.threads);
+}
+
+size_t xr_layernorm_bwd_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype) {
+  if (!valid_dtype(dtype) || M < 0 || N < 1) return 0;
+  // Rows may or may not qualify for the row-resident kernel: size for either plan (a plan
+  // that cannot apply under the current options needs nothing).
+  LnPlan a, b;
+  const bool ok_a = make_ln_plan(true, M, N, dtype, true, &a) == XR_OK;
+  const bool ok_b = make_ln_plan(true, M, N, dtype, false, &b) == XR_OK;
+  if (!ok_a && !ok_b) return 0;
+  const int64_t G = std::max<int64_t>(std::max(ok_a ? a.grid : 0, ok_b ? b.grid : 0), 1);
+  return (size_t)(2 * G * ln_pstride(N)) * sizeof(float);
+}
+
+xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld_dy,
+                             const void* x, int64_t ld_x, const void* w, const float* mean,
+                             const float* rstd, void* dw, void* db, int64_t M, int64_t N,
+                             xr_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (ld_dx < N || ld_dy < N || ld_x < N) return XR_ERR_STRIDE;
+  if (!w || !dw || !db || !workspace) return XR_ERR_NULL;
+  if (M > 0 && (!dx || !dy || !x || !mean || !rstd)) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  if ((dx && !aligned_to(dx, eb)) || (dy && !aligned_to(dy, eb)) || (x && !aligned_to(x, eb)) ||
+      !aligned_to(w, eb) || !aligned_to(dw, eb) || !aligned_to(db, eb) ||
+      (mean && !aligned_to(mean, 4)) || (rstd && !aligned_to(rstd, 4)) ||
+      !aligned_to(workspace, 16))
+    return XR_ERR_ALIGN;
+  if (M > 0 && (bad_alias(dx, ld_dx, dy, ld_dy, M, N, eb) || bad_alias(dx, ld_dx, x, ld_x, M, N, eb)))
+    return XR_ERR_ALIAS;
+  const uint64_t dxs = matrix_span(M, ld_dx, N, eb), vb = (uint64_t)N * eb;
+  if (spans_overlap(dx, dxs, w, vb) || spans_overlap(dx, dxs, dw, vb) ||
+      spans_overlap(dx, dxs, db, vb) || spans_overlap(dw, vb, db, vb) ||
+      spans_overlap(dx, dxs, mean, (uint64_t)M * 4) || spans_overlap(dx, dxs, rstd, (uint64_t)M * 4))
+    return XR_ERR_ALIAS;
+  const bool resident_ok = M > 0 && rows_on_16(dx, ld_dx, M, eb) && rows_on_16(dy, ld_dy, M, eb) &&
+                           rows_on_16(x, ld_x, M, eb) && aligned_to(w, 16) && (N * eb) % 16 == 0;
+  LnPlan lp;
+  if (xr_status_t st = make_ln_plan(true, M, N, dtype, resident_ok, &lp)) return st;
+  const int64_t ps = ln_pstride(N);
+  const int64_t G = lp.grid;
+  if (workspace_bytes < (size_t)(2 * std::max<int64_t>(G, 1) * ps) * sizeof(float))
+    return XR_ERR_WORKSPACE;
+  float* part_dw = static_cast<float*>(workspace);
+  float* part_db = part_dw + std::max<int64_t>(G, 1) * ps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (G > 0) {
+    LnBwdParams prm{static_cast<const char*>(dy), ld_dy * eb, static_cast<const char*>(x), ld_x * eb,
+                    static_cast<char*>(dx), ld_dx * eb, static_cast<const char*>(w), mean, rstd,
+                    part_dw, part_db, ps, M, N};
+    Plan p;
+    p.kernel = lp.kernel;
+    p.grid = G;
+    if (xr_status_t st = launch(p, &prm, s, lp.threads)) return st;
+  }
+  LnReduceParams rp{part_dw, part_db, ps, (int)G, static_cast<char*>(dw), static_cast<char*>(db), N};
+  void* args[] = {&rp};
+  const int64_t blocks = (N + kLnReduceCols - 1) / kLnReduceCols;
+  if (blocks > 0x7FFFFFFF) return XR_ERR_SHAPE;
+  if (hipLaunchKernel(ln_dwdb_kernel_ptr(dtype), dim3((unsigned)blocks), dim3(kLnReduceThreads),
+                      args, 0, s) != hipSuccess)
+    return XR_ERR_LAUNCH;
+  return XR_OK;
 }
 
 xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y, const void* dy,

@@ -60,6 +60,49 @@ struct SoftmaxFwdParams {
   float* loss;
 };
 
+// Layer norm forward: y = (x - mean) rstd w + b per row; mean and rstd saved.
+struct LnFwdParams {
+  const char* x;
+  int64_t ldx_bytes;
+  char* y;
+  int64_t ldy_bytes;
+  const char* w;
+  const char* b;
+  float* mean;
+  float* rstd;
+  int64_t M, N;
+  float eps;
+};
+
+// Layer norm backward, stage 1: dx, and per-workgroup partial column sums of dy * xhat
+// (part_dw) and dy (part_db), one row of pstride floats per workgroup of the grid.
+struct LnBwdParams {
+  const char* dy;
+  int64_t lddy_bytes;
+  const char* x;
+  int64_t ldx_bytes;
+  char* dx;
+  int64_t lddx_bytes;
+  const char* w;
+  const float* mean;
+  const float* rstd;
+  float* part_dw;
+  float* part_db;
+  int64_t pstride;
+  int64_t M, N;
+};
+
+// Layer norm backward, stage 2: dw / db = the sums of the G partial rows, in row order.
+struct LnReduceParams {
+  const float* part_dw;
+  const float* part_db;
+  int64_t pstride;
+  int G;
+  char* dw;
+  char* db;
+  int64_t N;
+};
+
 // Operations of the row kernels (also the `op` argument of xr_plan).
 enum Op : int { kOpSoftmaxFwd = 0, kOpSoftmaxBwd = 1, kOpXent = 2, kOpNllFwd = 3 };
 
@@ -93,6 +136,12 @@ const void* xent_scan_kernel_ptr();
 const void* xent_mean_kernel_ptr();
 const void* element_mul_kernel_ptr(int dtype, bool nt_loads);
 
+const void* ln_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* ln_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* ln_fwd_stream_kernel_ptr(int dtype);
+const void* ln_bwd_stream_kernel_ptr(int dtype);
+const void* ln_dwdb_kernel_ptr(int dtype);
+
 // Workgroup size of the stream, scan and mean kernels.
 constexpr int kStreamThreads = 256;
 constexpr int kScanThreads = 1024;
@@ -111,5 +160,12 @@ constexpr int kNumFwdShapes = 7;
 extern const Shape kFwdShapes[kNumFwdShapes];  // xent and softmax forward
 constexpr int kNumBwdShapes = 6;
 extern const Shape kBwdShapes[kNumBwdShapes];  // softmax backward (two row operands)
+constexpr int kNumLnFwdShapes = 7;
+extern const Shape kLnFwdShapes[kNumLnFwdShapes];  // layer norm forward (w, b resident too)
+constexpr int kNumLnBwdShapes = 7;
+extern const Shape kLnBwdShapes[kNumLnBwdShapes];  // layer norm backward (fp32 column sums too)
+// Layer norm stage-2 reduction: workgroup size, and columns per workgroup (one per lane).
+constexpr int kLnReduceThreads = 1024;
+constexpr int kLnReduceCols = 64;
 
 }  // namespace xr

@@ -93,6 +93,53 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
                        void* stream);
 
 /*
+ * Layer norm forward (the Triton LayerNorm tutorial page, translated; its code is cut off,
+ * so the definition follows its prose and the paper it cites, Ba, Kiros & Hinton 2016):
+ *   mean[i] = (1/N) sum_j x[i, j],  var_i = (1/N) sum_j (x[i, j] - mean[i])^2,
+ *   rstd[i] = 1 / sqrt(var_i + eps),  y[i, j] = (x[i, j] - mean[i]) * rstd[i] * w[j] + b[j]
+ * computed in fp32 (two passes over the row held in registers), y rounded once to dtype.
+ *   y, ld_y        output [M, N] of dtype; may be exactly x (in place)
+ *   x, ld_x        input [M, N] of dtype;  w, b  [N] of dtype, device
+ *   mean, rstd     fp32 [M], device: saved for xr_layernorm_bwd()
+ *   eps >= 0 and finite, else XR_ERR_VALUE;  M >= 0 (M == 0 enqueues nothing), N >= 1
+ * Fastest when every row, w and b start on 16-byte boundaries and N * element size is a
+ * multiple of 16 (contiguous tensors with N a multiple of 8); other layouts are accepted
+ * and run element-wise. y must not overlap w, b, mean or rstd (XR_ERR_ALIAS).
+ */
+xr_status_t xr_layernorm_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, const void* w,
+                             const void* b, float* mean, float* rstd, int64_t M, int64_t N,
+                             float eps, xr_dtype_t dtype, void* stream);
+
+/*
+ * Bytes of device workspace xr_layernorm_bwd() needs for these sizes on the current device
+ * (host query; 0 if the sizes are invalid): the partial dw / db rows of the first stage.
+ */
+size_t xr_layernorm_bwd_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype);
+
+/*
+ * Layer norm backward: the derivative of xr_layernorm_fwd()'s y, contracted with dy.
+ * With xhat = (x - mean) * rstd and g = w * dy (per row i, column j):
+ *   dx[i, j] = rstd[i] * (g[i, j] - (xhat[i, j] * c1_i + c2_i)),
+ *       c1_i = (1/N) sum_j xhat[i, j] g[i, j],  c2_i = (1/N) sum_j g[i, j]
+ *   dw[j] = sum_i dy[i, j] xhat[i, j],  db[j] = sum_i dy[i, j]
+ * The column sums run in two stages, as on the page: a persistent grid of G workgroups each
+ * sums its rows' columns into its own partial row of the workspace (no locks), then a
+ * second kernel sums the G partial rows of each column in a fixed order (deterministic for
+ * a given device and plan). All sums in fp32; dx, dw and db rounded once to dtype.
+ *   dx, ld_dx          output [M, N] of dtype; may be exactly dy or exactly x
+ *   dy, x              [M, N] of dtype (row strides ld_dy, ld_x);  w  [N] of dtype
+ *   mean, rstd         fp32 [M] from xr_layernorm_fwd()
+ *   dw, db             outputs [N] of dtype (M == 0 writes zeros)
+ *   workspace          device, 16-byte aligned, >= xr_layernorm_bwd_workspace_bytes(M, N, dtype)
+ * Outputs must not overlap each other, w, mean or rstd (XR_ERR_ALIAS).
+ */
+xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld_dy,
+                             const void* x, int64_t ld_x, const void* w, const float* mean,
+                             const float* rstd, void* dw, void* db, int64_t M, int64_t N,
+                             xr_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * Bytes of device workspace xr_xent_fwd_bwd() needs for these sizes on the current device
  * (host query; 0 if the sizes are invalid). The caller owns the workspace; its contents
  * need no initialisation and are scratch between calls.

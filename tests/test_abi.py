@@ -154,3 +154,32 @@ def test_nll_argument_errors(xr):
     assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x10010), 4, 8, 0, None) == XR_ERR_ALIAS
     assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x20010), 4, 8, 0, None) == XR_ERR_ALIAS
     assert f(Y, 8, X, 8, I, L, 0, 8, 0, None) == XR_OK
+
+
+def test_layernorm_argument_errors(xr):
+    f = xr.lib.xr_layernorm_fwd
+    Y, X, W, B, Mn, R = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000,
+                                                       0x50000, 0x60000))
+    assert f(Y, 8, X, 8, W, B, Mn, R, 4, 8, ctypes.c_float(1e-5), 2, None) == XR_ERR_DTYPE
+    assert f(Y, 8, X, 8, W, B, Mn, R, 4, 8, ctypes.c_float(-1.0), 0, None) == XR_ERR_VALUE
+    assert f(Y, 8, X, 8, W, B, Mn, R, 4, 8, ctypes.c_float(float("nan")), 0, None) == XR_ERR_VALUE
+    assert f(Y, 7, X, 8, W, B, Mn, R, 4, 8, ctypes.c_float(1e-5), 0, None) == XR_ERR_STRIDE
+    assert f(Y, 8, X, 8, None, B, Mn, R, 4, 8, ctypes.c_float(1e-5), 0, None) == XR_ERR_NULL
+    assert f(Y, 8, X, 8, W, B, Mn, ctypes.c_void_p(0x60002), 4, 8, ctypes.c_float(1e-5), 0,
+             None) == XR_ERR_ALIGN
+    assert f(Y, 8, X, 8, W, B, ctypes.c_void_p(0x10008), R, 4, 8, ctypes.c_float(1e-5), 0,
+             None) == XR_ERR_ALIAS
+    assert f(Y, 8, X, 8, W, B, Mn, R, 0, 8, ctypes.c_float(1e-5), 0, None) == XR_OK
+    g = xr.lib.xr_layernorm_bwd
+    DX, DY, DW, DB, WS = (ctypes.c_void_p(a) for a in (0x70000, 0x80000, 0x90000, 0xA0000,
+                                                        0xB0000))
+    assert g(DX, 8, DY, 8, X, 8, W, Mn, R, DW, DB, 4, 8, 3, WS, 1 << 20, None) == XR_ERR_DTYPE
+    assert g(DX, 8, DY, 7, X, 8, W, Mn, R, DW, DB, 4, 8, 0, WS, 1 << 20, None) == XR_ERR_STRIDE
+    assert g(DX, 8, DY, 8, X, 8, W, Mn, R, None, DB, 4, 8, 0, WS, 1 << 20, None) == XR_ERR_NULL
+    assert g(DX, 8, DY, 8, X, 8, W, Mn, R, DW, DB, 4, 8, 0, None, 1 << 20, None) == XR_ERR_NULL
+    assert g(DX, 8, DY, 8, X, 8, W, Mn, R, DW, DB, 4, 8, 0, ctypes.c_void_p(0xB0008), 1 << 20,
+             None) == XR_ERR_ALIGN
+    assert g(DX, 8, DY, 8, X, 8, W, Mn, R, DW, ctypes.c_void_p(0x90010), 4, 8, 0, WS, 1 << 20,
+             None) == XR_ERR_ALIAS
+    assert g(ctypes.c_void_p(0x80010), 8, DY, 8, X, 8, W, Mn, R, DW, DB, 4, 8, 0, WS, 1 << 20,
+             None) == XR_ERR_ALIAS
