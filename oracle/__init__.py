@@ -11,6 +11,8 @@ What each function computes, and the passage it follows:
   examples", Triton kernels ``softmax_kernel`` / ``_softmax``).
 * ``softmax_bwd`` -- ``dx = y * (dy - sum(y * dy))`` per row (same page,
   kernel ``_backward``, block-sparse scale taken as 1).
+* ``bsr_softmax_bwd`` -- the block-sparse softmax backward of the same page's
+  ``_backward`` kernel, rows gathered through its look-up table.
 * ``nll_fwd`` -- negative log-softmax rows and the loss gathered at one index
   per row, as stored in the output type (same page, kernel ``_forward``).
 * ``layernorm_fwd``, ``layernorm_bwd`` -- layer norm (the Triton LayerNorm
@@ -78,6 +80,9 @@ class Oracle:
         lib.xro_softmax_bwd.restype = None
         lib.xro_nll_fwd.argtypes = [_p, _c_i64, _p, _c_i64, _c_i64, ctypes.c_int, _p, _p]
         lib.xro_nll_fwd.restype = None
+        lib.xro_bsr_softmax_bwd.argtypes = [_p, _p, _c_i64, _c_i64, _p, _c_i64, _c_i64,
+                                            ctypes.c_double, ctypes.c_int, _p]
+        lib.xro_bsr_softmax_bwd.restype = None
         lib.xro_layernorm_fwd.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64, ctypes.c_double,
                                           ctypes.c_int, _p, _p, _p]
         lib.xro_layernorm_fwd.restype = None
@@ -207,6 +212,20 @@ class Oracle:
                                    dx.ctypes.data, dw.ctypes.data, db.ctypes.data)
         return dx, dw, db
 
+    def bsr_softmax_bwd(self, y: np.ndarray, dy: np.ndarray, lut: np.ndarray, n_brows: int,
+                        block: int, scale: float = 1.0) -> np.ndarray:
+        """y, dy: (Z, stride_z) arrays of blocks (uint16 bf16 bits or float32); lut: int32.
+        Returns dy as float64 with the listed rows replaced by y * (dy - sum(y dy)) * scale."""
+        py, sz, Z, code = self._matrix(y)
+        pd, sz2, Z2, code2 = self._matrix(dy)
+        if (sz, Z, code) != (sz2, Z2, code2):
+            raise ValueError("y and dy must have the same layout and type")
+        lt = np.ascontiguousarray(lut, dtype=np.int32)
+        out = _widen_bits(dy).copy()
+        self.lib.xro_bsr_softmax_bwd(py, pd, sz, Z, lt.ctypes.data, int(n_brows), int(block),
+                                     float(scale), code, out.ctypes.data)
+        return out
+
     def xent_count(self, target: np.ndarray, V: int, ignore_index: int = -100):
         t = np.ascontiguousarray(target, dtype=np.int64)
         counts = np.zeros(2, dtype=np.int64)
@@ -288,6 +307,13 @@ class Oracle:
         out = np.full((M, V), np.nan, dtype=np.float64)
         self.lib.xro_element_mul(ptr, ld, M, V, code, sc.ctypes.data, sstride, out.ctypes.data)
         return out
+
+
+def _widen_bits(a: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bits or float32 values as float64 (exact)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 _default: Oracle | None = None

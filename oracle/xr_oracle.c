@@ -17,6 +17,16 @@
  *   softmax backward  -- the fused softmax backward of the `_backward` kernel
  *                        on the same page, with its block-sparse scale taken
  *                        as 1: dx_j = y_j * (dy_j - sum_k y_k * dy_k).
+ *   block-sparse softmax backward -- the `_backward` kernel on the same page in
+ *                        full: each row of a block-sparse matrix is the row's
+ *                        segment in each of the blocks its look-up table lists;
+ *                        dx = y * (dy - sum(y * dy)) * scale along that row,
+ *                        written over dy. Table layout, as the kernel reads
+ *                        it: two words (size, offset) per block-row, then at
+ *                        word offset + 4 k the k-th block's index into the
+ *                        block storage (the other three words of an entry are
+ *                        not read). Block b of batch z holds BLOCK x BLOCK
+ *                        elements, row-major, at z * stride_z + b * BLOCK^2.
  *   negative log-softmax with a gathered loss -- the Triton kernel `_forward`
  *                        on the same page: each output element is
  *                        log(sum_k exp(x_k - m)) - (x_j - m) = -log p_j, and
@@ -270,6 +280,38 @@ void xro_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_
   }
   free(mu);
   free(rs);
+}
+
+/*
+ * Block-sparse softmax backward. y and dy hold Z batches of n_blocks blocks of block x block
+ * elements (batch z at element z * stride_z); lut as described above, for n_brows
+ * block-rows. out is a copy of dy (Z * stride_z doubles) that receives, for every row
+ * (z, block-row r, row i of the block) and every block k < size_r of its table entry list:
+ *   out[z][b_k][i][c] = y * (dy - s) * scale,   s = sum over k', c' of y * dy along the row
+ * Elements of blocks the table does not list for a row stay as in dy.
+ */
+void xro_bsr_softmax_bwd(const void* y, const void* dy, int64_t stride_z, int64_t Z,
+                         const int32_t* lut, int64_t n_brows, int64_t block, double scale,
+                         int dtype, double* out) {
+  int64_t zr;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (zr = 0; zr < Z * n_brows; ++zr) {
+    int64_t z = zr / n_brows, r = zr % n_brows;
+    int32_t size = lut[2 * r], offset = lut[2 * r + 1];
+    for (int64_t i = 0; i < block; ++i) {
+      double s = 0.0;
+      for (int32_t k = 0; k < size; ++k) {
+        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i * block;
+        for (int64_t c = 0; c < block; ++c)
+          s += load_elem(y, base + c, dtype) * load_elem(dy, base + c, dtype);
+      }
+      for (int32_t k = 0; k < size; ++k) {
+        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i * block;
+        for (int64_t c = 0; c < block; ++c)
+          out[base + c] = load_elem(y, base + c, dtype) * (load_elem(dy, base + c, dtype) - s) * scale;
+      }
+    }
+  }
 }
 
 /* counts[0] = #{i : t_i != ignore_index}; counts[1] = those among them outside [0, V). */

@@ -198,6 +198,52 @@ def layernorm_ln(M: int = 16384, N: int = 8192, seed: int = 1006, dtype: str = "
             "eps": 1e-5, "seed": seed}
 
 
+def bsr_layout(n_brows: int, local: int, stride: int) -> dict:
+    """A causal block-sparse layout and its look-up table.
+
+    Block (r, c) is present when c <= r and either r - c < local (a local window) or
+    c % stride == stride - 1 (global columns). Present blocks are numbered in row-major
+    order: that number is the block's index in the block storage. The table holds two
+    words (size, offset) per block-row, then four words per present block at word
+    `offset + 4 k`: (block index, block-row, block-column, 0); the backward reads the first."""
+    layout = np.zeros((n_brows, n_brows), dtype=bool)
+    for r in range(n_brows):
+        for c in range(r + 1):
+            layout[r, c] = (r - c < local) or (c % stride == stride - 1)
+    rows, cols = np.nonzero(layout)
+    n_blocks = rows.size
+    lut = np.zeros(2 * n_brows + 4 * n_blocks, dtype=np.int32)
+    k = 0
+    for r in range(n_brows):
+        cs = np.flatnonzero(layout[r])
+        lut[2 * r] = cs.size
+        lut[2 * r + 1] = 2 * n_brows + 4 * k
+        for c in cs:
+            lut[2 * n_brows + 4 * k: 2 * n_brows + 4 * k + 4] = (k, r, c, 0)
+            k += 1
+    return {"layout": layout, "lut": lut, "n_blocks": int(n_blocks), "n_brows": n_brows}
+
+
+def bsr_softmax(Z: int = 32, seq: int = 4096, block: int = 64, local: int = 4, stride: int = 8,
+                seed: int = 1007, dtype: str = "bf16") -> dict:
+    """Block-sparse softmax backward inputs: Z = batch x heads attention maps of seq x seq in
+    block x block blocks under bsr_layout(seq / block, local, stride). y is positive with
+    mean 1/(row length) (a softmax output's scale), dy = N(0,1) (seed + 100)."""
+    lay = bsr_layout(seq // block, local, stride)
+    per_z = lay["n_blocks"] * block * block
+    mean_len = float(lay["layout"].sum(axis=1).mean() * block)
+    shape_dt = np.uint16 if dtype == "bf16" else np.float32
+    conv = bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a)
+    y = np.empty((Z, per_z), dtype=shape_dt)
+    dy = np.empty((Z, per_z), dtype=shape_dt)
+    for z in range(Z):
+        rng = _chunk_rng(seed, z)
+        y[z] = conv(rng.random(per_z, dtype=np.float32) * np.float32(2.0 / mean_len))
+        dy[z] = conv(_normal(_chunk_rng(seed + 100, z), (per_z,), 1.0))
+    return {"op": "bsr_softmax_bwd", "Z": Z, "seq": seq, "block": block, "y": y, "dy": dy,
+            "scale": 0.125, "dtype": dtype, **lay}
+
+
 WORKLOADS = {"c1": softmax_c1, "c2": softmax_c2, "c3": xent_c3, "c4": xent_c4, "c5": xent_c5}
 
 

@@ -301,6 +301,82 @@ def pin_xent_row_subset_and_padding(o):
     assert np.array_equal(g_d, g_all) and np.array_equal(l_d, l_all)
 
 
+# --------------------------------------------------------------------------- block-sparse backward
+def _dense_from_blocks(a: np.ndarray, lay: dict, block: int) -> np.ndarray:
+    """(Z, seq, seq) float64 matrix holding each listed block at its place, zeros elsewhere."""
+    nb = lay["n_brows"]
+    Z = a.shape[0]
+    out = np.zeros((Z, nb * block, nb * block))
+    lut = lay["lut"]
+    for r in range(nb):
+        size, off = lut[2 * r], lut[2 * r + 1]
+        for k in range(size):
+            bid, br, bc = lut[off + 4 * k: off + 4 * k + 3]
+            blk = decode(a[:, bid * block * block:(bid + 1) * block * block]).reshape(Z, block, block)
+            out[:, br * block:(br + 1) * block, bc * block:(bc + 1) * block] = blk
+    return out
+
+
+def pin_bsr_softmax_bwd_dense_equivalent(o):
+    """A table listing every block of every block-row is the dense softmax backward (times
+    scale) of the matrix those blocks tile."""
+    for dtype, block in (("f32", 4), ("bf16", 8)):
+        nb = 3
+        rows, cols = np.nonzero(np.ones((nb, nb), dtype=bool))  # every block of the matrix
+        lut = np.zeros(2 * nb + 4 * rows.size, dtype=np.int32)
+        for k, (r, c) in enumerate(zip(rows, cols)):
+            lut[2 * nb + 4 * k: 2 * nb + 4 * k + 4] = (k, r, c, 0)
+        for r in range(nb):
+            lut[2 * r] = nb
+            lut[2 * r + 1] = 2 * nb + 4 * nb * r
+        lay = {"lut": lut, "n_brows": nb, "n_blocks": rows.size}
+        per_z = rows.size * block * block
+        y = synth.random_rows(2000, 2, per_z, dtype=dtype, scale=1.0)
+        dy = synth.random_rows(2001, 2, per_z, dtype=dtype, scale=1.0)
+        for scale in (1.0, 2.5):
+            out = o.bsr_softmax_bwd(y, dy, lut, nb, block, scale)
+            # dense reference through the (separately pinned) softmax backward
+            Yd = _dense_from_blocks(y, lay, block)
+            Dd = _dense_from_blocks(dy, lay, block)
+            for z in range(2):
+                ref = o.softmax_bwd(Yd[z].astype(np.float32) if dtype == "f32" else
+                                    synth.bf16_bits_from_f32(Yd[z].astype(np.float32)),
+                                    Dd[z].astype(np.float32) if dtype == "f32" else
+                                    synth.bf16_bits_from_f32(Dd[z].astype(np.float32))) * scale
+                for k, (r, c) in enumerate(zip(rows, cols)):
+                    blk = out[z, k * block * block:(k + 1) * block * block].reshape(block, block)
+                    want = ref[r * block:(r + 1) * block, c * block:(c + 1) * block]
+                    assert np.max(np.abs(blk - want)) <= 1e-14, f"{dtype} block ({r},{c}) scale {scale}"
+
+
+def pin_bsr_softmax_bwd_matches_torch_masked(o):
+    """A causal local + global layout: every listed row equals the masked dense formula
+    y * (dy - sum(y dy)) * scale computed by torch (zeros outside the layout add nothing);
+    unlisted storage is untouched; reordering a block-row's table entries changes nothing."""
+    import torch
+    import synth as sy
+    block, nb = 4, 6
+    lay = sy.bsr_layout(nb, local=2, stride=3)
+    per_z = lay["n_blocks"] * block * block
+    y = synth.random_rows(2010, 3, per_z + 16, dtype="f32", scale=1.0)  # 16 spare elements
+    dy = synth.random_rows(2011, 3, per_z + 16, dtype="f32", scale=1.0)
+    out = o.bsr_softmax_bwd(y, dy, lay["lut"], nb, block, 0.75)
+    Y = torch.from_numpy(_dense_from_blocks(y, lay, block))
+    D = torch.from_numpy(_dense_from_blocks(dy, lay, block))
+    ref = (Y * (D - (Y * D).sum(-1, keepdim=True)) * 0.75).numpy()
+    got = _dense_from_blocks(out, lay, block)
+    mask = np.kron(lay["layout"], np.ones((block, block), dtype=bool))
+    assert np.max(np.abs(got[:, mask] - ref[:, mask])) <= 1e-14, "listed rows vs torch"
+    assert np.array_equal(out[:, per_z:], decode(dy)[:, per_z:]), "storage past the blocks"
+    lut2 = lay["lut"].copy()
+    for r in range(nb):  # reverse each block-row's entry order
+        size, off = lut2[2 * r], lut2[2 * r + 1]
+        ent = lut2[off: off + 4 * size].reshape(size, 4)[::-1].copy()
+        lut2[off: off + 4 * size] = ent.reshape(-1)
+    out2 = o.bsr_softmax_bwd(y, dy, lut2, nb, block, 0.75)
+    assert np.max(np.abs(out2 - out)) <= 1e-13, "table order within a block-row (sum order only)"
+
+
 # --------------------------------------------------------------------------- negative log-softmax
 def _nearest_bf16(v: float) -> float:
     """The bf16 value nearest to v (ties to even), by exact rational arithmetic."""
@@ -610,6 +686,13 @@ def pin_golden_worked_examples(o):
         for got, key in ((mean, "mean"), (rstd, "rstd"), (dw, "dw"), (db, "db")):
             want = np.array([closed_form(v) for v in case[key]])
             assert np.max(np.abs(got - want)) <= 1e-15, f"{case['name']}: {key}"
+    for case in gold["bsr_softmax_bwd"]:
+        y = as_input(case["y"], case["dtype"])
+        dy = as_input(case["dy"], case["dtype"])
+        out = o.bsr_softmax_bwd(y, dy, np.array(case["lut"], dtype=np.int32), case["n_brows"],
+                                case["block"], case["scale"])
+        want = np.array([[closed_form(v) for v in r] for r in case["out"]])
+        assert np.max(np.abs(out - want)) <= 1e-15, case["name"]
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -97,6 +97,24 @@ MUTANTS = {
         "double d = load_elem(dy, r * ld_x + j, dtype);"),
     "layer norm db skips the last row": ("for (int64_t r = 0; r < M; ++r) {\n      double d =",
                                          "for (int64_t r = 0; r + 1 < M; ++r) {\n      double d ="),
+    "block-sparse backward drops the scale": (
+        "out[base + c] = load_elem(y, base + c, dtype) * (load_elem(dy, base + c, dtype) - s) * scale;",
+        "out[base + c] = load_elem(y, base + c, dtype) * (load_elem(dy, base + c, dtype) - s);"),
+    "block-sparse backward adds s": (
+        "out[base + c] = load_elem(y, base + c, dtype) * (load_elem(dy, base + c, dtype) - s) * scale;",
+        "out[base + c] = load_elem(y, base + c, dtype) * (load_elem(dy, base + c, dtype) + s) * scale;"),
+    "block-sparse table entries two words apart": (
+        "        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i * block;\n        for (int64_t c = 0; c < block; ++c)\n          s +=",
+        "        int64_t base = z * stride_z + (int64_t)lut[offset + 2 * k] * block * block + i * block;\n        for (int64_t c = 0; c < block; ++c)\n          s +="),
+    "block-sparse rows read as block columns": (
+        "        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i * block;\n        for (int64_t c = 0; c < block; ++c)\n          out",
+        "        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i;\n        for (int64_t c = 0; c < block; ++c)\n          out"),
+    "block-sparse sum skips the last block": (
+        "      for (int32_t k = 0; k < size; ++k) {\n        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i * block;\n        for (int64_t c = 0; c < block; ++c)\n          s +=",
+        "      for (int32_t k = 0; k + 1 < size; ++k) {\n        int64_t base = z * stride_z + (int64_t)lut[offset + 4 * k] * block * block + i * block;\n        for (int64_t c = 0; c < block; ++c)\n          s +="),
+    "block-sparse batches not offset": (
+        "    int64_t z = zr / n_brows, r = zr % n_brows;",
+        "    int64_t z = 0 * (zr / n_brows), r = zr % n_brows;"),
     "element_mul adds the scale": ("out[i * V + j] = load_elem(x, i * ld + j, dtype) * w;",
                                    "out[i * V + j] = load_elem(x, i * ld + j, dtype) + w;"),
     "ignored rows keep stale gradient": ("        for (int64_t j = 0; j < V; ++j) g[j] = 0.0;\n      continue;",
