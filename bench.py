@@ -13,7 +13,8 @@ the library records around that launch on its stream; `cpu_baseline` times the f
 oracle on the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
-                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln] [--reduction mean|sum|none]
+                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr]
+                    [--reduction mean|sum|none]
                     [--grad-scale S]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
 
@@ -25,7 +26,8 @@ cross-entropy workloads with another reduction or an upstream gradient folded in
 gradient write; `c4-mul` times the backward's element_mul (the stored gradient times an
 upstream gradient of 0.5) over the 16384 x 128256 bf16 matrix; `c4-nll` the negative
 log-softmax forward with a gathered loss over the same matrix, into a separate output;
-`ln` a layer norm forward + backward (both stages) over 16384 x 8192 bf16 rows.
+`ln` a layer norm forward + backward (both stages) over 16384 x 8192 bf16 rows; `bsr` the
+block-sparse softmax backward over 32 causal 4096 x 4096 maps of 64 x 64 bf16 blocks.
 """
 from __future__ import annotations
 
@@ -54,6 +56,9 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 C4_M, C4_V, C4_KEEP = 16384, 128256, 15565
 
 DESCRIPTIONS = {
+    "bsr": "block-sparse softmax backward through a look-up table, 32 maps of 4096 x 4096 in "
+           "64 x 64 bf16 blocks (causal: local window of 4 blocks + every 8th block column, 453 "
+           "blocks per map), in place, scale 0.125",
     "ln": "layer norm forward + backward (dx, and dw / db in two stages), M=16384, N=8192, "
           "bf16 x / dy / w / b, fp32 statistics and sums, eps=1e-5",
     "c4-nll": "negative log-softmax forward + loss gathered at each row's target, M=16384, "
@@ -357,6 +362,38 @@ def run_layernorm(args, name: str) -> dict:
     return out
 
 
+def run_bsr(args, name: str) -> dict:
+    """In-place block-sparse backward; inputs rotated over >= 1 GB of copies."""
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.bsr_softmax()
+    y = _device_matrix(torch, w["y"], dev)
+    d = _device_matrix(torch, w["dy"], dev)
+    lut = torch.from_numpy(w["lut"]).to(dev)
+    elt = y.element_size()
+    per_set = 2 * y.numel() * elt
+    nsets = max(2, -(-(1 << 30) // per_set))
+    ys = [y.clone() for _ in range(nsets)]
+    ds = [d.clone() for _ in range(nsets)]
+
+    def launch(i):
+        j = i % nsets
+        xr.bsr_softmax_bwd(ys[j], ds[j], lut, w["n_brows"], w["n_blocks"], w["block"], w["scale"])
+
+    wall, kernel_ms = _timed(HipEvents(), args.steps, args.warmup, launch)
+    listed = int(w["layout"].sum()) * w["Z"] * w["block"] ** 2
+    bmin = 3 * listed * elt + lut.numel() * 4
+    rows = w["Z"] * w["n_brows"] * w["block"]
+    return _line(args, name, bmin, rows, wall, kernel_ms, "bsr_softmax_bwd_kernel",
+                 {"Z": w["Z"], "seq": w["seq"], "block": w["block"], "n_blocks": w["n_blocks"],
+                  "bytes_min": bmin, "input_sets": nsets}, "bf16")
+
+
 def run_softmax(args, name: str) -> dict:
     import torch
 
@@ -505,6 +542,8 @@ def main() -> int:
         out = run_nll(args, args.workload)
     elif args.workload == "ln":
         out = run_layernorm(args, args.workload)
+    elif args.workload == "bsr":
+        out = run_bsr(args, args.workload)
     else:
         out = run_xent(args, args.workload)
     print(json.dumps(out), flush=True)

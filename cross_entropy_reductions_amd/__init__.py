@@ -39,6 +39,9 @@ lib.xr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.
 lib.xr_softmax_bwd.restype = ctypes.c_int
 lib.xr_nll_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, ctypes.c_int, _p]
 lib.xr_nll_fwd.restype = ctypes.c_int
+lib.xr_bsr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i32,
+                                   ctypes.c_float, ctypes.c_int, _p]
+lib.xr_bsr_softmax_bwd.restype = ctypes.c_int
 lib.xr_layernorm_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _i64, ctypes.c_float,
                                  ctypes.c_int, _p]
 lib.xr_layernorm_fwd.restype = ctypes.c_int
@@ -76,7 +79,8 @@ lib.xr_set_profile_events.argtypes = [_p, _p]
 lib.xr_set_profile_events.restype = ctypes.c_int
 
 # Names exported by include/xr.h (checked against the library by the tests).
-C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_nll_fwd", "xr_layernorm_fwd",
+C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_bsr_softmax_bwd", "xr_nll_fwd",
+             "xr_layernorm_fwd",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
              "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_status_string", "xr_version",
@@ -161,6 +165,34 @@ def softmax_bwd(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = No
     _check("xr_softmax_bwd",
            lib.xr_softmax_bwd(px, ldx, py, ldy, pd, ldd, M, N, dt, _stream(y, stream)))
     return out
+
+
+def bsr_softmax_bwd(y: torch.Tensor, dx: torch.Tensor, lut: torch.Tensor, n_brows: int,
+                    n_blocks: int, block: int, scale: float = 1.0, *, stream=None) -> torch.Tensor:
+    """Block-sparse softmax backward in place: dx (Z, stride) holds the incoming gradient and
+    receives y * (dx - sum(y * dx)) * scale along every table row (see xr_bsr_softmax_bwd
+    in include/xr.h for the table layout). Returns dx."""
+    for t, name in ((y, "y"), (dx, "dx")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 2 or t.dtype not in _DTYPES:
+            raise TypeError(f"{name} must be a 2-D float32 or bfloat16 device tensor (Z, stride)")
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit stride along its last dimension")
+    if y.dtype != dx.dtype or y.device != dx.device or y.shape[0] != dx.shape[0]:
+        raise ValueError("y and dx must share dtype, device and batch count")
+    if not isinstance(lut, torch.Tensor) or lut.dtype != torch.int32 or lut.device != dx.device \
+            or lut.dim() != 1 or not lut.is_contiguous():
+        raise TypeError("lut must be a contiguous 1-D int32 tensor on dx's device")
+    per = int(n_blocks) * int(block) * int(block)
+    if y.shape[1] < per or dx.shape[1] < per:
+        raise ValueError("y and dx rows must hold n_blocks * block^2 elements")
+    Z = dx.shape[0]
+    sy = y.stride(0) if Z > 1 else y.shape[1]
+    sd = dx.stride(0) if Z > 1 else dx.shape[1]
+    _check("xr_bsr_softmax_bwd",
+           lib.xr_bsr_softmax_bwd(y.data_ptr(), sy, dx.data_ptr(), sd, Z, lut.data_ptr(),
+                                  lut.numel(), int(n_brows), int(n_blocks), int(block),
+                                  float(scale), _DTYPES[dx.dtype], _stream(dx, stream)))
+    return dx
 
 
 def nll_fwd(x: torch.Tensor, idx: torch.Tensor, out: torch.Tensor | None = None,

@@ -564,6 +564,46 @@ xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld
   return XR_OK;
 }
 
+xr_status_t xr_bsr_softmax_bwd(const void* y, int64_t stride_zy, void* dx, int64_t stride_zdx,
+                               int64_t Z, const int32_t* lut, int64_t lut_len, int64_t n_brows,
+                               int64_t n_blocks, int32_t block, float scale, xr_dtype_t dtype,
+                               void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  const int eb = elt_bytes(dtype);
+  const int epv = 16 / eb;
+  if (Z < 0 || n_brows < 0 || n_blocks < 0 || block < epv || block > 64 * epv ||
+      (block & (block - 1)) != 0)
+    return XR_ERR_SHAPE;
+  if (!(scale == scale)) return XR_ERR_VALUE;
+  const uint64_t batch_bytes = (uint64_t)n_blocks * (uint64_t)block * (uint64_t)block * eb;
+  if (batch_bytes >= (1ull << 31)) return XR_ERR_SHAPE;
+  if (lut_len < 2 * n_brows || lut_len >= (1ll << 29)) return XR_ERR_SHAPE;
+  if (stride_zy < n_blocks * block * block || stride_zdx < n_blocks * block * block)
+    return XR_ERR_STRIDE;
+  if (Z == 0 || n_brows == 0 || n_blocks == 0) return XR_OK;
+  if (!y || !dx || !lut) return XR_ERR_NULL;
+  if (!aligned_to(y, 16) || !aligned_to(dx, 16) || !aligned_to(lut, 4) ||
+      (stride_zy * eb) % 16 != 0 || (stride_zdx * eb) % 16 != 0)
+    return XR_ERR_ALIGN;
+  // y may be exactly dx; otherwise the two must not overlap, nor may the table
+  const uint64_t ys = (uint64_t)((Z - 1) * stride_zy) * eb + batch_bytes;
+  const uint64_t ds = (uint64_t)((Z - 1) * stride_zdx) * eb + batch_bytes;
+  if (!(y == dx && stride_zy == stride_zdx) && spans_overlap(y, ys, dx, ds)) return XR_ERR_ALIAS;
+  if (spans_overlap(dx, ds, lut, (uint64_t)lut_len * 4)) return XR_ERR_ALIAS;
+  const int tpr = block / epv;
+  const int rows = std::min<int>(block, std::max(1, kBsrThreads / tpr));
+  const int chunks = (block + rows - 1) / rows;
+  const int64_t grid = Z * n_brows * chunks;
+  if (grid > 0x7FFFFFFF) return XR_ERR_SHAPE;
+  BsrParams prm{static_cast<const char*>(y), stride_zy * eb, static_cast<char*>(dx),
+                stride_zdx * eb, lut, lut_len, n_brows, (int32_t)n_blocks,
+                (uint32_t)batch_bytes, block, rows, chunks, scale};
+  Plan p;
+  p.kernel = bsr_softmax_bwd_kernel_ptr(dtype);
+  p.grid = grid;
+  return launch(p, &prm, static_cast<hipStream_t>(stream), kBsrThreads);
+}
+
 xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y, const void* dy,
                            int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream) {
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;

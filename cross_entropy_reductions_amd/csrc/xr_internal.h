@@ -103,6 +103,24 @@ struct LnReduceParams {
   int64_t N;
 };
 
+// Block-sparse softmax backward (see xr_bsr.hip): workgroup b handles rows
+// [rc * rows_per_wg, ...) of block-row br of batch z, b = (z * n_brows + br) * row_chunks + rc.
+struct BsrParams {
+  const char* y;
+  int64_t ldy_bytes;   // batch stride of y
+  char* dx;
+  int64_t lddx_bytes;  // batch stride of dx
+  const int32_t* lut;
+  int64_t lut_len;     // words
+  int64_t n_brows;
+  int32_t n_blocks;    // blocks stored per batch
+  uint32_t batch_bytes;  // n_blocks * block^2 * element size (< 2^31)
+  int32_t block;
+  int32_t rows_per_wg;
+  int32_t row_chunks;  // ceil(block / rows_per_wg)
+  float scale;
+};
+
 // Operations of the row kernels (also the `op` argument of xr_plan).
 enum Op : int { kOpSoftmaxFwd = 0, kOpSoftmaxBwd = 1, kOpXent = 2, kOpNllFwd = 3 };
 
@@ -141,6 +159,11 @@ const void* ln_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* ln_fwd_stream_kernel_ptr(int dtype);
 const void* ln_bwd_stream_kernel_ptr(int dtype);
 const void* ln_dwdb_kernel_ptr(int dtype);
+
+const void* bsr_softmax_bwd_kernel_ptr(int dtype);
+// Block-sparse backward: workgroup size, and listed blocks per row held in registers.
+constexpr int kBsrThreads = 256;
+constexpr int kBsrResident = 12;
 
 // Workgroup size of the stream, scan and mean kernels.
 constexpr int kStreamThreads = 256;

@@ -77,6 +77,29 @@ xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y,
                            int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream);
 
 /*
+ * Block-sparse softmax backward through a look-up table (the Triton kernel `_backward` on
+ * the page "python sum function examples"). y (the softmax output) and dx (the incoming
+ * gradient on entry, the result on return, as on the page) hold Z batches of n_blocks
+ * blocks of block x block elements, row-major within a block, block b of batch z at element
+ * z * stride_z + b * block^2 (stride_zy for y, stride_zdx for dx). Row i of block-row r is
+ * row i of every block the table lists for r, in table order; along it
+ *   dx <- y * (dx - sum(y * dx)) * scale          (fp32 arithmetic, one rounding to dtype)
+ * Table (int32, device, lut_len words), as that kernel reads it: words 2 r and 2 r + 1 are
+ * the number of listed blocks and the word offset of the list for block-row r; the k-th
+ * listed block's index is word offset + 4 k (the other three words of an entry are not
+ * read). A list that runs past the table is cut at its end; a block index outside
+ * [0, n_blocks) reads as zeros and is not written. A block listed for several block-rows
+ * gives unspecified results (as on the page).
+ *   block: a power of two, 8..512 for bf16, 4..256 for fp32;  Z, n_brows, n_blocks >= 0
+ *   y, dx 16-byte aligned, stride_z * element size a multiple of 16; one batch's blocks
+ *   under 2 GiB; y may be exactly dx, otherwise no overlap (nor with the table).
+ */
+xr_status_t xr_bsr_softmax_bwd(const void* y, int64_t stride_zy, void* dx, int64_t stride_zdx,
+                               int64_t Z, const int32_t* lut, int64_t lut_len, int64_t n_brows,
+                               int64_t n_blocks, int32_t block, float scale, xr_dtype_t dtype,
+                               void* stream);
+
+/*
  * Negative log-softmax forward with the loss gathered at one index per row (the Triton
  * kernel `_forward` on the page "python sum function examples"):
  *   out[i, j] = log d_i - (x[i, j] - m_i)   (= -log softmax(x[i, :])_j; +inf where x is -inf)

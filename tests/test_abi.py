@@ -183,3 +183,20 @@ def test_layernorm_argument_errors(xr):
              None) == XR_ERR_ALIAS
     assert g(ctypes.c_void_p(0x80010), 8, DY, 8, X, 8, W, Mn, R, DW, DB, 4, 8, 0, WS, 1 << 20,
              None) == XR_ERR_ALIAS
+
+
+def test_bsr_argument_errors(xr):
+    f = xr.lib.xr_bsr_softmax_bwd
+    Y, D, L = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000))
+    one = ctypes.c_float(1.0)
+    assert f(Y, 4096, D, 4096, 2, L, 20, 4, 4, 32, one, 2, None) == XR_ERR_DTYPE
+    assert f(Y, 4096, D, 4096, 2, L, 20, 4, 4, 48, one, 0, None) == XR_ERR_SHAPE  # not a power of 2
+    assert f(Y, 4096, D, 4096, 2, L, 20, 4, 4, 2, one, 1, None) == XR_ERR_SHAPE   # below a vector
+    assert f(Y, 4096, D, 4096, 2, L, 7, 4, 4, 32, one, 0, None) == XR_ERR_SHAPE   # table too short
+    assert f(Y, 4095, D, 4096, 2, L, 20, 4, 4, 32, one, 0, None) == XR_ERR_STRIDE
+    assert f(Y, 4096, D, 4096, 2, L, 20, 4, 4, 32, ctypes.c_float(float("nan")), 0, None) == XR_ERR_VALUE
+    assert f(None, 4096, D, 4096, 2, L, 20, 4, 4, 32, one, 0, None) == XR_ERR_NULL
+    assert f(ctypes.c_void_p(0x100008), 4096, D, 4096, 2, L, 20, 4, 4, 32, one, 0, None) == XR_ERR_ALIGN
+    assert f(Y, 4096, ctypes.c_void_p(0x100000 + 4096), 4096, 2, L, 20, 4, 4, 32, one, 0,
+             None) == XR_ERR_ALIAS
+    assert f(Y, 4096, D, 4096, 0, L, 20, 4, 4, 32, one, 0, None) == XR_OK
