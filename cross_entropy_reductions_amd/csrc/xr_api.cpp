@@ -187,16 +187,18 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   }
 
   // Workgroups per row (cross-entropy; softmax rows stay whole): enough for the row to fit;
-  // chunks of at most ~128 KB, and at least two for rows of 32 KB and more, so that several
-  // workgroups share a compute unit and one's reductions overlap another's memory traffic
-  // (measured: 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 TB/s in two chunks); and enough
-  // chunks to give every compute unit work when the batch is short.
+  // rows of 32 KB and more in several chunks, so that several workgroups share a compute
+  // unit and one's reductions overlap another's memory traffic: ~16 KB chunks (one wave
+  // each) up to 64 KB rows, ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s
+  // in two chunks, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 in two chunks,
+  // 6.0 in eight); and enough chunks to give every compute unit work when the batch is short.
   int64_t S = 1;
   if (op == kOpXent) {
     const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
     const int64_t row_bytes = nvm * 16;
+    const int64_t chunk_bytes = row_bytes <= (64 << 10) ? (16 << 10) : (128 << 10);
     const int64_t s_bw = row_bytes >= (32 << 10)
-                             ? std::max<int64_t>(2, (row_bytes + (128 << 10) - 1) / (128 << 10))
+                             ? std::max<int64_t>(2, (row_bytes + chunk_bytes - 1) / chunk_bytes)
                              : 1;
     int64_t s_par = 1;
     if (M > 0 && M < di.cus) {
@@ -672,7 +674,10 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
     const int64_t* tgt = target;
     int64_t mm = M, vv = V, ii = ignore_index;
     void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, &partials, const_cast<int64_t*>(&nslots)};
-    if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3(1), dim3(kScanThreads), args, 0, s) != hipSuccess)
+    // one workgroup counts; the slot fill is spread over up to 64 (8 KB of slots each)
+    const int64_t fill_groups = std::min<int64_t>(64, std::max<int64_t>(1, nslots / 1024));
+    if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),
+                        args, 0, s) != hipSuccess)
       return XR_ERR_LAUNCH;
   }
   if (M > 0) {

@@ -43,8 +43,9 @@
 namespace xr {
 
 // ============================================================================ cross-entropy
-// Target scan: n = #{t != ignore_index}, bad = #{t != ignore_index, t outside [0, V)}.
-// Also clears the error flags and marks every split-row (m, d) slot as unpublished.
+// Target scan: n = #{t != ignore_index}, bad = #{t != ignore_index, t outside [0, V)},
+// counted by workgroup 0 (16-byte loads, two targets each, all issued before the sums);
+// every workgroup marks its share of the split-row (m, d) slots as unpublished.
 __global__ __launch_bounds__(kScanThreads) void xent_scan_kernel(const int64_t* __restrict__ target,
                                                                  int64_t M, int64_t V,
                                                                  int64_t ignore_index,
@@ -52,26 +53,48 @@ __global__ __launch_bounds__(kScanThreads) void xent_scan_kernel(const int64_t* 
                                                                  uint64_t* __restrict__ partials,
                                                                  int64_t nslots) {
   __shared__ int red[2][kScanThreads / kWave];
-  int n = 0, bad = 0;
-  for (int64_t i = threadIdx.x; i < M; i += kScanThreads) {
-    const int64_t t = target[i];
-    if (t != ignore_index) {
-      ++n;
-      if (t < 0 || t >= V) ++bad;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    int n = 0, bad = 0;
+    auto count = [&](int64_t t) {
+      if (t != ignore_index) {
+        ++n;
+        if (t < 0 || t >= V) ++bad;
+      }
+    };
+    const bool vec = (reinterpret_cast<uintptr_t>(target) & 15u) == 0;
+    const int64_t pairs = vec ? M / 2 : 0;
+    constexpr int U = 8;  // pairs per thread per round, loaded together
+    for (int64_t base = 0; base < pairs; base += (int64_t)U * kScanThreads) {
+      longlong2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * kScanThreads + tid;
+        v[u] = i < pairs ? reinterpret_cast<const longlong2*>(target)[i] : make_longlong2(ignore_index, ignore_index);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        count(v[u].x);
+        count(v[u].y);
+      }
+    }
+    for (int64_t i = 2 * pairs + tid; i < M; i += kScanThreads) count(target[i]);
+    n = block_sum_int<kScanThreads>(n, red[0]);
+    bad = block_sum_int<kScanThreads>(bad, red[1]);
+    if (tid == 0) {
+      ws_counts[0] = n;
+      ws_counts[1] = bad;
+      ws_counts[2] = 0;
+      ws_counts[3] = 0;
     }
   }
-  n = block_sum_int<kScanThreads>(n, red[0]);
-  bad = block_sum_int<kScanThreads>(bad, red[1]);
-  if (threadIdx.x == 0) {
-    ws_counts[0] = n;
-    ws_counts[1] = bad;
-    ws_counts[2] = 0;
-    ws_counts[3] = 0;
-  }
-  for (int64_t i = threadIdx.x; i < nslots; i += kScanThreads) partials[i] = kPartialEmpty;
+  for (int64_t i = (int64_t)blockIdx.x * kScanThreads + tid; i < nslots;
+       i += (int64_t)gridDim.x * kScanThreads)
+    partials[i] = kPartialEmpty;
 }
 
-// Sum (or mean) of the row losses in a fixed order; copies the counts out.
+// Sum (or mean) of the row losses in a fixed order (16-byte loads issued together, then a
+// fixed tree); copies the counts out.
 __global__ __launch_bounds__(kScanThreads) void xent_mean_kernel(const float* __restrict__ row_loss,
                                                                  int64_t M,
                                                                  const int32_t* __restrict__ ws_counts,
@@ -79,10 +102,24 @@ __global__ __launch_bounds__(kScanThreads) void xent_mean_kernel(const float* __
                                                                  int32_t* __restrict__ counts_out,
                                                                  int reduction) {
   __shared__ float red[kScanThreads / kWave];
+  const int tid = threadIdx.x;
   float s = 0.f;
-  for (int64_t i = threadIdx.x; i < M; i += kScanThreads) s += row_loss[i];
+  const bool vec = (reinterpret_cast<uintptr_t>(row_loss) & 15u) == 0;
+  const int64_t quads = vec ? M / 4 : 0;
+  constexpr int U = 8;
+  for (int64_t base = 0; base < quads; base += (int64_t)U * kScanThreads) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * kScanThreads + tid;
+      v[u] = i < quads ? reinterpret_cast<const float4*>(row_loss)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+  }
+  for (int64_t i = 4 * quads + tid; i < M; i += kScanThreads) s += row_loss[i];
   s = block_reduce<kScanThreads>(s, OpAdd(), red);
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int32_t n = ws_counts[0];
     if (mean) *mean = reduction == kReduceMean ? s / (float)n : s;  // n == 0: 0/0 = NaN
     if (counts_out) {
