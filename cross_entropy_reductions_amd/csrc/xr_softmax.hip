@@ -160,8 +160,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     for (int k = 0; k < VPT; ++k) {
       OutVec<D> o;
       u32x4 a = vy[k], b = vd[k];
-      pin_slot<D>(a);
-      pin_slot<D>(b);
+      pin(a);  // fp32 too: unpinned, the fp32 shapes with 8 vectors per thread spill
+      pin(b);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
       store_slot<D, THREADS>(cx, k, o.bits());
