@@ -295,16 +295,19 @@ def run_nll(args, name: str) -> dict:
     idx = torch.from_numpy(w["target"]).clamp(min=0).to(dev)
     out = torch.empty_like(x)
     loss = torch.empty(M, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, int(xr.lib.xr_nll_fwd_workspace_bytes(M, N, xr.BF16))),
+                     dtype=torch.uint8, device=dev)
 
     def launch(i):
-        xr.nll_fwd(x, idx, out, loss)
+        xr.nll_fwd(x, idx, out, loss, workspace=ws)
 
     wall, kernel_ms = _timed(HipEvents(), args.steps, args.warmup, launch)
     bmin = 2 * M * N * 2 + 12 * M
     p = xr.plan("nll_fwd", M, N, x.dtype)
     return _line(args, name, bmin, M, wall, kernel_ms, "softmax_fwd_kernel (negative log)",
                  {"M": M, "N": N, "bytes_min": bmin, "path": p["path"], "threads": p["threads"],
-                  "vec_per_thread": p["vec_per_thread"], "grid": p["grid"]}, "bf16")
+                  "vec_per_thread": p["vec_per_thread"], "split": p["split"], "grid": p["grid"]},
+                 "bf16")
 
 
 def run_layernorm(args, name: str) -> dict:

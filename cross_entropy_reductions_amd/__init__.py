@@ -37,7 +37,9 @@ lib.xr_softmax_fwd.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p]
 lib.xr_softmax_fwd.restype = ctypes.c_int
 lib.xr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p]
 lib.xr_softmax_bwd.restype = ctypes.c_int
-lib.xr_nll_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, ctypes.c_int, _p]
+lib.xr_nll_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, ctypes.c_int, _p, _sz, _p]
+lib.xr_nll_fwd_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
+lib.xr_nll_fwd_workspace_bytes.restype = _sz
 lib.xr_nll_fwd.restype = ctypes.c_int
 lib.xr_bsr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i32,
                                    ctypes.c_float, ctypes.c_int, _p]
@@ -80,6 +82,7 @@ lib.xr_set_profile_events.restype = ctypes.c_int
 
 # Names exported by include/xr.h (checked against the library by the tests).
 C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_bsr_softmax_bwd", "xr_nll_fwd",
+             "xr_nll_fwd_workspace_bytes",
              "xr_layernorm_fwd",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
@@ -196,9 +199,11 @@ def bsr_softmax_bwd(y: torch.Tensor, dx: torch.Tensor, lut: torch.Tensor, n_brow
 
 
 def nll_fwd(x: torch.Tensor, idx: torch.Tensor, out: torch.Tensor | None = None,
-            loss: torch.Tensor | None = None, *, stream=None):
+            loss: torch.Tensor | None = None, *, workspace: torch.Tensor | None = None,
+            stream=None):
     """-log softmax of each row of x into ``out`` (new, or x itself), and the fp32 loss
-    ``out[i, idx[i]]`` as stored (NaN for an index outside the row). Returns (out, loss)."""
+    ``out[i, idx[i]]`` as stored (NaN for an index outside the row). Returns (out, loss).
+    A workspace (allocated here when not given) lets long rows be split over workgroups."""
     px, ldx, M, N, dt = _matrix(x, "x")
     if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int64 or idx.device != x.device:
         raise TypeError("idx must be an int64 tensor on x's device")
@@ -214,8 +219,13 @@ def nll_fwd(x: torch.Tensor, idx: torch.Tensor, out: torch.Tensor | None = None,
     if loss.dtype != torch.float32 or loss.device != x.device or loss.numel() < M or \
             not loss.is_contiguous():
         raise ValueError("loss must be a contiguous float32 tensor of one entry per row")
+    if workspace is None:
+        need = int(lib.xr_nll_fwd_workspace_bytes(M, N, dt)) if M > 0 else 0
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _check("xr_nll_fwd", lib.xr_nll_fwd(po, ldo, px, ldx, idx.data_ptr(), loss.data_ptr(), M, N,
-                                        dt, _stream(x, stream)))
+                                        dt, workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(x, stream)))
     return out, loss
 
 

@@ -166,7 +166,7 @@ const void* row_kernel(int op, xr_dtype_t dt, Shape sh, bool nt) {
 // operand row has the same address modulo 16; `on16`: moreover every row starts on a
 // 16-byte boundary (then a row touches exactly ceil(N / elements-per-vector) vectors).
 xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned, bool on16,
-                      Plan* plan) {
+                      Plan* plan, bool can_split = false) {
   int dev = 0;
   DeviceInfo di;
   if (xr_status_t st = device_info(&dev, &di)) return st;
@@ -186,14 +186,15 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     return XR_OK;
   }
 
-  // Workgroups per row (cross-entropy; softmax rows stay whole): enough for the row to fit;
+  // Workgroups per row (cross-entropy, and the negative log-softmax when it has a workspace
+  // for the exchange; softmax rows stay whole): enough for the row to fit;
   // rows of 32 KB and more in several chunks, so that several workgroups share a compute
   // unit and one's reductions overlap another's memory traffic: ~16 KB chunks (one wave
   // each) up to 64 KB rows, ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s
   // in two chunks, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 in two chunks,
   // 6.0 in eight); and enough chunks to give every compute unit work when the batch is short.
   int64_t S = 1;
-  if (op == kOpXent) {
+  if (op == kOpXent || (op == kOpNllFwd && can_split)) {
     const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
     const int64_t row_bytes = nvm * 16;
     const int64_t chunk_bytes = row_bytes <= (64 << 10) ? (16 << 10) : (128 << 10);
@@ -233,7 +234,8 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   // faster with the default policy (the cross-entropy over a 128256-wide bf16 vocabulary).
   bool nt_loads = !(S == 1 && nvm * 16 >= (128 << 10));
   if (g_opt.load_policy) nt_loads = g_opt.load_policy == 2;
-  p.kernel = row_kernel(op, dt, *sh, nt_loads);
+  const bool nll_split = op == kOpNllFwd && S > 1;
+  p.kernel = nll_split ? nll_split_kernel_ptr(dt, *sh, nt_loads) : row_kernel(op, dt, *sh, nt_loads);
   if (!p.kernel) return XR_ERR_SHAPE;
   const int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
   if (per_cu <= 0) return XR_ERR_DEVICE;
@@ -246,7 +248,15 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     int64_t g = M;
     if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
     p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
-  } else if (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF) {
+  } else if (nll_split || (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF)) {
+    if (M * S > 0x7FFFFFFF) {  // (the negative log-softmax has no persistent split form)
+      if (want) return XR_ERR_SHAPE;
+      Plan q;
+      q.grid = M;
+      q.kernel = stream_kernel(op, dt);
+      *plan = q;
+      return XR_OK;
+    }
     // One workgroup per row chunk, launched normally (measured faster than a persistent
     // cooperative grid): the S chunks of a row have consecutive workgroup ids, and the
     // dispatcher starts workgroups in id order, so a chunk only ever waits for chunks that
@@ -409,7 +419,8 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
   if (op < 0 || op > 3 || M < 0 || N < 1) return XR_ERR_SHAPE;
   Plan p;
-  if (xr_status_t st = make_plan(op, M, N, dtype, op == 2 ? true : aligned != 0, aligned == 2, &p))
+  if (xr_status_t st = make_plan(op, M, N, dtype, op == 2 ? true : aligned != 0, aligned == 2, &p,
+                                 op == kOpNllFwd))
     return st;
   out->path = p.path;
   out->threads = p.path == kPathStream ? kStreamThreads : p.shape.threads;
@@ -436,14 +447,21 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
   if (xr_status_t st = make_plan(0, M, N, dtype, same_lead(x, ld_x, y, ld_y, eb), on16, &p))
     return st;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N,
-                       nullptr, nullptr};
+                       nullptr, nullptr, 1, 0, nullptr, nullptr};
   return launch(p, &prm, static_cast<hipStream_t>(stream),
                 p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
 
+size_t xr_nll_fwd_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype) {
+  if (!valid_dtype(dtype) || M < 0 || N < 1) return 0;
+  Plan p;
+  if (make_plan(kOpNllFwd, M, N, dtype, true, false, &p, true) != XR_OK) return 0;
+  return xent_ws_bytes(p, M);
+}
+
 xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
                        const int64_t* idx, float* loss, int64_t M, int64_t N, xr_dtype_t dtype,
-                       void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_x < N || ld_out < N) return XR_ERR_STRIDE;
@@ -460,14 +478,34 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
       spans_overlap(x, matrix_span(M, ld_x, N, eb), loss, (uint64_t)M * 4) ||
       spans_overlap(idx, (uint64_t)M * 8, loss, (uint64_t)M * 4))
     return XR_ERR_ALIAS;
+  if (workspace && !aligned_to(workspace, 8)) return XR_ERR_ALIGN;
   Plan p;
   const bool on16 = rows_on_16(x, ld_x, M, eb) && rows_on_16(out, ld_out, M, eb);
-  if (xr_status_t st = make_plan(kOpNllFwd, M, N, dtype, same_lead(x, ld_x, out, ld_out, eb), on16, &p))
+  if (xr_status_t st = make_plan(kOpNllFwd, M, N, dtype, same_lead(x, ld_x, out, ld_out, eb), on16,
+                                 &p, workspace != nullptr))
     return st;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(out), ld_out * eb,
-                       M, N, idx, loss};
-  return launch(p, &prm, static_cast<hipStream_t>(stream),
-                p.path == kPathStream ? kStreamThreads : p.shape.threads);
+                       M, N, idx, loss, p.S, p.chunk_vecs, nullptr, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.path == kPathSplit) {
+    if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    if (spans_overlap(ws, workspace_bytes, out, matrix_span(M, ld_out, N, eb)) ||
+        spans_overlap(ws, workspace_bytes, loss, (uint64_t)M * 4))
+      return XR_ERR_ALIAS;
+    int32_t* ws_counts = reinterpret_cast<int32_t*>(ws + kWsCounts);
+    prm.partials = reinterpret_cast<uint64_t*>(ws + kWsPartials);
+    prm.flags = ws_counts + 2;
+    // clear the flags and mark every (m, d) slot unpublished (the target scan with no targets)
+    const int64_t* tgt = nullptr;
+    int64_t mm = 0, vv = N, ii = 0, nslots = M * p.S;
+    void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, &prm.partials, &nslots};
+    const int64_t fill_groups = std::min<int64_t>(64, std::max<int64_t>(1, nslots / 1024));
+    if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),
+                        args, 0, s) != hipSuccess)
+      return XR_ERR_LAUNCH;
+  }
+  return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
 
 xr_status_t xr_layernorm_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, const void* w,

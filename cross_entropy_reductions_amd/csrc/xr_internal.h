@@ -58,6 +58,12 @@ struct SoftmaxFwdParams {
   int64_t M, N;
   const int64_t* idx;  // negative log-softmax only: the index gathered into loss[] per row
   float* loss;
+  // split rows (negative log-softmax with a workspace): S workgroups per row, chunk_vecs
+  // 16-byte vectors each, exchanging (m, d) through partials[M * S]; flags as for xent
+  int S;
+  int64_t chunk_vecs;
+  uint64_t* partials;
+  int32_t* flags;
 };
 
 // Layer norm forward: y = (x - mean) rstd w + b per row; mean and rstd saved.
@@ -145,6 +151,7 @@ struct Shape {
 const void* xent_rows_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* nll_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* xent_stream_kernel_ptr(int dtype);
 const void* softmax_fwd_stream_kernel_ptr(int dtype);

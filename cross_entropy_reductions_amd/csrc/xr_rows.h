@@ -163,6 +163,50 @@ __device__ __forceinline__ Stats thread_stats(u32x4 (&v)[VPT], const Chunk<D>& c
   return {m, d};
 }
 
+// Split rows: publish this chunk's (m, d) in its slot of the row's S slots (one 64-bit
+// relaxed agent-scope store), then combine the pairs of all S chunks in chunk order, so every
+// chunk of the row gets bit-identical (m, d). Slots hold kPartialEmpty until published. The
+// wait is bounded: after kSpinLimit polls the chunk sets kFlagExchangeTimeout in *flags and
+// returns m = NaN, and once the flag is set no chunk waits again, so the grid always drains.
+// Called by every thread of the workgroup (thread 0 does the exchange; bcast is LDS).
+template <int THREADS>
+__device__ __forceinline__ Stats exchange_row_stats(Stats st, uint64_t* slots, int S, int chunk,
+                                                    int32_t* flags, float* bcast) {
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(slots + chunk, pack_pair(st.m, st.d), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    float ms = kNegInf, ds = 0.f;
+    bool ok = true;
+    int budget = (__hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                  kFlagExchangeTimeout) ? 0 : kSpinLimit;
+    for (int q = 0; q < S && ok; ++q) {
+      uint64_t w;
+      while ((w = __hip_atomic_load(slots + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+             kPartialEmpty) {
+        if (--budget < 0) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (!ok) break;
+      const float mc = pair_m(w), dc = pair_d(w);
+      if (mc == kNegInf) continue;
+      const float mx = fmaxf(ms, mc);
+      ds = ((ms == kNegInf) ? 0.f : ds * exp2f((ms - mx) * kLog2e)) + dc * exp2f((mc - mx) * kLog2e);
+      ms = mx;
+    }
+    if (!ok) {
+      __hip_atomic_fetch_or(flags, kFlagExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ms = __builtin_nanf("");
+    }
+    bcast[0] = ms;
+    bcast[1] = ds;
+  }
+  __syncthreads();
+  return {bcast[0], bcast[1]};
+}
+
 // exp2(x*log2e - coff) for every element of one slot, in the element type, XOR-ed with
 // `sign` (0, or Elt<D>::kSignWord to negate every result: a negative upstream gradient).
 template <int D>

@@ -81,6 +81,44 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+// Negative log-softmax over split rows: workgroup b handles chunk b % S of row b / S (rows
+// too long for one workgroup to keep several per compute unit). The chunks exchange their
+// (m, d) pairs as the cross-entropy's split rows do; the chunk holding idx writes the loss.
+template <int D, int THREADS, int VPT, int LP>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void nll_split_kernel(SoftmaxFwdParams p) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int NW = THREADS / kWave;
+  __shared__ float2 red[NW];
+  __shared__ float bcast[2];
+  const int tid = threadIdx.x;
+  const int S = p.S;
+  const int64_t r = blockIdx.x / S;
+  const int chunk = (int)(blockIdx.x - r * S);
+  if (r >= p.M) return;
+  const int64_t lo = (int64_t)chunk * p.chunk_vecs;
+  const Chunk<D> cx(p.x + r * p.ldx_bytes, p.N, lo, p.chunk_vecs);
+  const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, lo, p.chunk_vecs);  // same lead (host-checked)
+  u32x4 v[VPT];
+  issue_loads<D, THREADS, VPT, LP>(v, cx);
+  // the gathered element, read by the thread holding its vector before any store of this
+  // chunk (y may be exactly x; other chunks write only their own elements)
+  const int64_t ix = p.idx[r];
+  const bool in_row = ix >= 0 && ix < p.N;
+  const int64_t vt = cx.lead + ix - cx.lo * EPV;  // chunk-local element index
+  const bool owner = in_row && vt >= 0 && vt < (int64_t)cx.nvec * EPV &&
+                     tid == (int)((vt / EPV) % THREADS);
+  float xi = 0.f;
+  if (owner) xi = buf_load_elem<D>(cx.rsrc, (uint32_t)(vt * Elt<D>::kBytes));
+  Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red);
+  st = exchange_row_stats<THREADS>(st, p.partials + r * S, S, chunk, p.flags, bcast);
+  const float c = st.m + logf(st.d);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(cy, k, nll_slot<D>(v[k], c));
+  store_partials<D, THREADS>(cy, cx, [c](float x) { return c - x; });
+  if (owner) p.loss[r] = round_elem<D>(c - xi);
+  else if (!in_row && chunk == 0 && tid == 0) p.loss[r] = __builtin_nanf("");
+}
+
 template <int D, bool NLL>
 __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(SoftmaxFwdParams p) {
   __shared__ float red[2][kStreamThreads / kWave];
@@ -236,6 +274,15 @@ const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
 const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
   if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_NLL, kF32) }
   if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_NLL, kBF16) }
+  return nullptr;
+}
+#define XR_CASE_NLLS(D, T, V)                                                                  \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&nll_split_kernel<D, T, V, kPolicyNT>)             \
+              : reinterpret_cast<const void*>(&nll_split_kernel<D, T, V, kPolicyDefault>);
+const void* nll_split_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_NLLS, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_NLLS, kBF16) }
   return nullptr;
 }
 const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool lp) {

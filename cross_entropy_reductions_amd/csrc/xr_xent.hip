@@ -190,47 +190,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
       d = st.d;
 
       if (S > 1) {
-        // Publish this chunk's pair, then combine the pairs of all chunks of the row in
-        // chunk order (every chunk of the row computes the same (m, d)).
-        if (tid == 0) {
-          uint64_t* slot = p.partials + r * S;
-          __hip_atomic_store(slot + chunk, pack_pair(m, d), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          float ms = kNegInf, ds = 0.f;
-          bool ok = true;
-          // One bounded wait for the whole row; after any timeout in this call no
-          // workgroup waits again (the flag is set), so the kernel always drains.
-          int budget = (__hip_atomic_load(p.ws_flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
-                        kFlagExchangeTimeout) ? 0 : kSpinLimit;
-          for (int q = 0; q < S && ok; ++q) {
-            uint64_t w;
-            while ((w = __hip_atomic_load(slot + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-                   kPartialEmpty) {
-              if (--budget < 0) {
-                ok = false;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
-            }
-            if (!ok) break;
-            const float mc = pair_m(w), dc = pair_d(w);
-            if (mc == kNegInf) continue;
-            const float mx = fmaxf(ms, mc);
-            ds = ((ms == kNegInf) ? 0.f : ds * exp2f((ms - mx) * kLog2e)) +
-                 dc * exp2f((mc - mx) * kLog2e);
-            ms = mx;
-          }
-          if (!ok) {
-            __hip_atomic_fetch_or(p.ws_flags, kFlagExchangeTimeout, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-            ms = __builtin_nanf("");
-          }
-          bcast[0] = ms;
-          bcast[1] = ds;
-        }
-        __syncthreads();
-        m = bcast[0];
-        d = bcast[1];
+        // every chunk of the row combines the same pairs in the same order
+        const Stats row = exchange_row_stats<THREADS>({m, d}, p.partials + r * S, S, chunk,
+                                                       p.ws_flags, bcast);
+        m = row.m;
+        d = row.d;
       }
       // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) - log2|s| is
       // |s| p_j / n (n = 1 unless the reduction is the mean); the sign of s is applied to

@@ -108,12 +108,18 @@ xr_status_t xr_bsr_softmax_bwd(const void* y, int64_t stride_zy, void* dx, int64
  *   out, ld_out  output [M, N] of dtype; may be exactly x (in place)
  *   x, ld_x      input [M, N] of dtype
  *   idx          int64 [M], device;  loss  fp32 [M], device
+ *   workspace    device scratch of at least xr_nll_fwd_workspace_bytes(M, N, dtype) bytes, or
+ *                NULL: with it, long rows are split over several workgroups that exchange
+ *                their (max, sum) pairs through it, as the cross-entropy's split rows do
+ *                (no initialisation needed; scratch between calls); without it every row
+ *                is handled whole
  *   M >= 0 (M == 0 enqueues nothing), N >= 1
- * idx and loss must not overlap the matrices or each other (XR_ERR_ALIAS).
+ * idx, loss and the workspace must not overlap the matrices or each other (XR_ERR_ALIAS).
  */
+size_t xr_nll_fwd_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype);
 xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
                        const int64_t* idx, float* loss, int64_t M, int64_t N, xr_dtype_t dtype,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Layer norm forward (the Triton LayerNorm tutorial page, translated; its code is cut off,
@@ -261,7 +267,7 @@ int32_t xr_version(void);
  * 2 = split row (S > 1 workgroups per row exchanging (max, sum) pairs), 3 = stream
  * (one workgroup per row, several passes over global memory).
  * op: 0 = softmax forward, 1 = softmax backward, 2 = cross-entropy, 3 = negative
- * log-softmax forward.
+ * log-softmax forward (with a workspace).
  * aligned: 0 = the operand rows sit at different addresses modulo 16 bytes (stream path),
  * 1 = they share their address modulo 16 (rows may start anywhere), 2 = moreover every row
  * starts on a 16-byte boundary (the usual contiguous tensors). The cross-entropy has one

@@ -142,18 +142,21 @@ def test_plan_argument_errors(xr):
 
 def test_nll_argument_errors(xr):
     f = xr.lib.xr_nll_fwd
-    Y, X, I, L = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000))
-    assert f(Y, 8, X, 8, I, L, 4, 8, 2, None) == XR_ERR_DTYPE
-    assert f(Y, 8, X, 8, I, L, -1, 8, 0, None) == XR_ERR_SHAPE
-    assert f(Y, 7, X, 8, I, L, 4, 8, 0, None) == XR_ERR_STRIDE
-    assert f(Y, 8, X, 8, None, L, 4, 8, 0, None) == XR_ERR_NULL
-    assert f(Y, 8, X, 8, I, None, 4, 8, 0, None) == XR_ERR_NULL
-    assert f(Y, 8, X, 8, ctypes.c_void_p(0x30004), L, 4, 8, 0, None) == XR_ERR_ALIGN
-    assert f(ctypes.c_void_p(0x10010), 8, ctypes.c_void_p(0x10000), 8, I, L, 4, 8, 0, None) == XR_ERR_ALIAS
+    Y, X, I, L, W = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
+    assert f(Y, 8, X, 8, I, L, 4, 8, 2, None, 0, None) == XR_ERR_DTYPE
+    assert f(Y, 8, X, 8, I, L, -1, 8, 0, None, 0, None) == XR_ERR_SHAPE
+    assert f(Y, 7, X, 8, I, L, 4, 8, 0, None, 0, None) == XR_ERR_STRIDE
+    assert f(Y, 8, X, 8, None, L, 4, 8, 0, None, 0, None) == XR_ERR_NULL
+    assert f(Y, 8, X, 8, I, None, 4, 8, 0, None, 0, None) == XR_ERR_NULL
+    assert f(Y, 8, X, 8, ctypes.c_void_p(0x30004), L, 4, 8, 0, None, 0, None) == XR_ERR_ALIGN
+    assert f(Y, 8, X, 8, I, L, 4, 8, 0, ctypes.c_void_p(0x50004), 4096, None) == XR_ERR_ALIGN
+    assert f(ctypes.c_void_p(0x10010), 8, ctypes.c_void_p(0x10000), 8, I, L, 4, 8, 0, None, 0,
+             None) == XR_ERR_ALIAS
     # the losses may not land inside the output or the input
-    assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x10010), 4, 8, 0, None) == XR_ERR_ALIAS
-    assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x20010), 4, 8, 0, None) == XR_ERR_ALIAS
-    assert f(Y, 8, X, 8, I, L, 0, 8, 0, None) == XR_OK
+    assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x10010), 4, 8, 0, None, 0, None) == XR_ERR_ALIAS
+    assert f(Y, 8, X, 8, I, ctypes.c_void_p(0x20010), 4, 8, 0, None, 0, None) == XR_ERR_ALIAS
+    assert f(Y, 8, X, 8, I, L, 0, 8, 0, W, 4096, None) == XR_OK
+    assert xr.lib.xr_nll_fwd_workspace_bytes(4, 0, 0) == 0
 
 
 def test_layernorm_argument_errors(xr):

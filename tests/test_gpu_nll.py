@@ -145,12 +145,35 @@ def test_nll_all_paths_agree(orc, dtype):
     x = synth.random_rows(12300, M, N, dtype=dtype, scale=3.0)
     idx = synth.random_targets(12301, M, N)
     want, wl = orc.nll_fwd(x, idx)
-    for name, path, grid in (("auto", 0, 0), ("resident", 1, 0), ("persistent", 1, 2),
-                             ("stream", 3, 0)):
+    for name, path, grid, split in (("auto", 0, 0, 0), ("resident", 1, 0, 0),
+                                    ("persistent", 1, 2, 0), ("split2", 2, 0, 2),
+                                    ("split5", 2, 0, 5), ("stream", 3, 0, 0)):
         xr.set_option("path", path)
         xr.set_option("grid", grid)
+        xr.set_option("split", split)
         out, loss, _ = run(x, idx, N)
         check_nll(out, loss, want, wl, f"{dtype} {name}")
+
+
+def test_nll_without_workspace_keeps_rows_whole(orc):
+    """No workspace: long rows run whole (one workgroup each) and give the same results."""
+    import ctypes
+    M, N = 6, 128256
+    x_h = synth.random_rows(12400, M, N, dtype="bf16", scale=2.0)
+    idx = synth.random_targets(12401, M, N)
+    assert xr.plan("nll_fwd", M, N, torch.bfloat16)["split"] > 1
+    x, ix = to_device(x_h), to_device(idx)
+    out = torch.empty_like(x)
+    loss = torch.empty(M, dtype=torch.float32, device="cuda")
+    st = xr.lib.xr_nll_fwd(out.data_ptr(), N, x.data_ptr(), N, ix.data_ptr(), loss.data_ptr(),
+                           M, N, xr.BF16, None, 0,
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    want, wl = orc.nll_fwd(x_h, idx)
+    check_nll(to_host(out), to_host(loss), want, wl, "no workspace")
+    out2, loss2, _ = run(x_h, idx, N)  # split rows
+    check_nll(out2, loss2, want, wl, "split rows")
 
 
 def test_nll_c4_matrix(orc):
