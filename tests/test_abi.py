@@ -203,3 +203,21 @@ def test_bsr_argument_errors(xr):
     assert f(Y, 4096, ctypes.c_void_p(0x100000 + 4096), 4096, 2, L, 20, 4, 4, 32, one, 0,
              None) == XR_ERR_ALIAS
     assert f(Y, 4096, D, 4096, 0, L, 20, 4, 4, 32, one, 0, None) == XR_OK
+
+
+def test_header_is_plain_c_and_links(tmp_path, xr):
+    """include/xr.h compiles as C99 on its own, and a C program linked against libxr.so
+    runs its argument checks (tests/c/abi_check.c)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = os.path.join(ROOT, "tests", "c", "abi_check.c")
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(xr.LIBRARY)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", exe, "-L", libdir, "-lxr", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "ok"
