@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <map>
@@ -22,13 +23,16 @@ constexpr int32_t kVersion = 10100;  // 1.1.0
 constexpr int64_t kMinChunkVecs = 256;
 
 // ----------------------------------------------------------------------------- options
+// Process-wide overrides for tests and sweeps (xr_set_option); atomics, so that setting one
+// while another thread launches work is not a data race (which value that launch sees is
+// unspecified).
 struct Options {
-  int64_t path = 0, split = 0, threads = 0, grid = 0, load_policy = 0;
+  std::atomic<int64_t> path{0}, split{0}, threads{0}, grid{0}, load_policy{0};
 };
 Options g_opt;
 
 // Profiling hook: events recorded around the row kernel of each call (xr_set_profile_events).
-hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+std::atomic<hipEvent_t> g_ev_start{nullptr}, g_ev_stop{nullptr};
 
 // ----------------------------------------------------------------------------- device cache
 struct DeviceInfo {
@@ -289,11 +293,12 @@ xr_status_t launch(const Plan& p, void* params, hipStream_t stream, int threads)
   if (p.grid <= 0) return XR_OK;
   if (p.grid > 0x7FFFFFFF) return XR_ERR_SHAPE;
   const dim3 grid((unsigned)p.grid), block((unsigned)threads);
-  if (g_ev_start && hipEventRecord(g_ev_start, stream) != hipSuccess) return XR_ERR_LAUNCH;
+  const hipEvent_t ev0 = g_ev_start.load(), ev1 = g_ev_stop.load();
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return XR_ERR_LAUNCH;
   hipError_t e = p.coop ? hipLaunchCooperativeKernel(p.kernel, grid, block, args, 0, stream)
                         : hipLaunchKernel(p.kernel, grid, block, args, 0, stream);
   if (e != hipSuccess) return XR_ERR_LAUNCH;
-  if (g_ev_stop && hipEventRecord(g_ev_stop, stream) != hipSuccess) return XR_ERR_LAUNCH;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return XR_ERR_LAUNCH;
   return XR_OK;
 }
 

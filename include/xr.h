@@ -287,15 +287,19 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
                     xr_plan_t* plan /* host */);
 
 /*
- * Process-wide overrides for tests and benchmarks (not for concurrent use with calls in
- * flight). Value 0 restores the automatic choice.
+ * Process-wide overrides for tests and benchmarks. Setting one while another thread
+ * launches work is safe, but which value that launch sees is unspecified. Value 0 restores
+ * the automatic choice.
  *   XR_OPT_PATH     1 resident, 2 split, 3 stream (a forced path the sizes cannot take
- *                   returns XR_ERR_SHAPE from the entry point)
- *   XR_OPT_SPLIT    workgroups per row for the split path (>= 2)
+ *                   returns XR_ERR_SHAPE from the entry point); layer norm: 1 row-resident,
+ *                   3 element-wise
+ *   XR_OPT_SPLIT    workgroups per row for the split path (>= 2): cross-entropy and the
+ *                   negative log-softmax with a workspace
  *   XR_OPT_THREADS  workgroup size of the row-resident kernels (64 .. 1024)
  *   XR_OPT_GRID     0 or -1 = one workgroup per row (or per row chunk), launched normally;
  *                   k >= 1 = a persistent grid of k workgroups per compute unit (launched
- *                   cooperatively for split rows)
+ *                   cooperatively for split cross-entropy rows); layer norm: at most k
+ *                   workgroups per compute unit in its persistent grids
  *   XR_OPT_LOAD_POLICY  row loads: 1 = default cache policy, 2 = non-temporal
  */
 typedef enum xr_option {
@@ -309,7 +313,7 @@ typedef enum xr_option {
 xr_status_t xr_set_option(xr_option_t option, int64_t value);
 
 /*
- * Profiling hook (process-wide, not for concurrent use): while set, every entry point records
+ * Profiling hook (process-wide): while set, every entry point records
  * hipEvent_t `start` on its stream right before launching its row kernel (the kernel that
  * reads and writes the rows; not the small target-scan and mean kernels of the
  * cross-entropy) and `stop` right after it, so hipEventElapsedTime(start, stop) is that
