@@ -142,6 +142,31 @@ def pin_softmax_bwd_rows_sum_to_zero(o):
     assert np.max(np.abs(dx.sum(axis=1))) <= 1e-14, "dx rows must sum to 0 when sum(y) = 1"
 
 
+def pin_softmax_direct_formula_small_inputs(o):
+    """For |x| < 10 the formula without the max shift, exp(x) / sum(exp(x)), is accurate in
+    float64: the oracle's shifted form must agree with it to 1e-14 relative."""
+    x = synth.random_rows(1050, 20, 300, dtype="f32", scale=3.0)
+    x = np.clip(x, -9.5, 9.5).astype(np.float32)
+    e = np.exp(decode(x))
+    direct = e / e.sum(axis=1, keepdims=True)
+    y = o.softmax_fwd(x)
+    assert np.max(np.abs(y - direct) / direct) <= 1e-14
+
+
+def pin_softmax_bwd_jacobian(o):
+    """Brute force on tiny rows: dx = J^T dy with J = diag(y) - y y^T."""
+    for N in (1, 2, 3, 5, 8):
+        y = synth.random_rows(1060 + N, 4, N, dtype="f32", scale=1.0)
+        y = np.abs(y) + np.float32(0.1)
+        y = (y / y.sum(axis=1, keepdims=True)).astype(np.float32)
+        dy = synth.random_rows(1070 + N, 4, N, dtype="f32", scale=1.0)
+        dx = o.softmax_bwd(y, dy)
+        yd, dyd = decode(y), decode(dy)
+        for i in range(4):
+            J = np.diag(yd[i]) - np.outer(yd[i], yd[i])
+            assert np.max(np.abs(dx[i] - J.T @ dyd[i])) <= 1e-15, f"N={N} row {i}"
+
+
 def pin_softmax_bwd_finite_differences(o):
     # phi(x) = sum_j softmax(x)_j dy_j; its gradient is the backward of softmax at y = softmax(x).
     x = _grid_rows(13, 3, 6, 1.0 / 4, -2.0, 2.0)

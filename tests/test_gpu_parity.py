@@ -119,6 +119,16 @@ def test_c2_softmax_fwd_bwd_bf16(orc):
     # dx rows sum to ~0 (sum y ~ 1 up to bf16 rounding of y).
     s = widen(dx_h).sum(axis=1)
     assert np.max(np.abs(s)) < 0.05
+    # The forward -> backward chain against the oracle's own y (float64, held as float32):
+    # it carries the bf16 rounding of y into dx, so it is reported, with a looser bound.
+    y_orc = orc.softmax_fwd(w["x"]).astype(np.float32)
+    dy32 = widen(w["dy"]).astype(np.float32)
+    chain = orc.softmax_bwd(y_orc, dy32)
+    g = widen(dx_h)
+    floor = 2.0 ** -7 * np.max(np.abs(chain), axis=1, keepdims=True)
+    worst = float(np.max(np.abs(g - chain) / np.maximum(np.abs(chain), floor)))
+    print(f"c2 forward -> backward chain vs the oracle's y: worst scaled error {worst:.3e}")
+    assert worst <= 0.1
 
 
 def test_c3_xent_bf16(orc):
