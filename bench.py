@@ -15,7 +15,7 @@ oracle on the same workload on this host's cores.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr]
                     [--reduction mean|sum|none]
-                    [--grad-scale S]
+                    [--grad-scale S] [--rows M]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
 
 The other workloads (c1 softmax fp32 128x1000, c2 softmax forward + backward bf16 4096^2,
@@ -209,7 +209,7 @@ def run_xent(args, name: str) -> dict:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
-    w = synth.WORKLOADS[name]()
+    w = synth.WORKLOADS[name](**({"M": args.rows} if args.rows else {}))
     M, V = w["M"], w["N"]
     t = torch.from_numpy(w["target"]).to(dev)
     x0 = _device_matrix(torch, w["x"], dev)
@@ -246,7 +246,7 @@ def run_xent(args, name: str) -> dict:
                  "threads": p["threads"], "split": p["split"], "grid": p["grid"],
                  "reduction": args.reduction, "grad_scale": args.grad_scale},
                 w["dtype"])
-    if name == "c4" and args.reduction == "mean" and args.grad_scale is None:
+    if name == "c4" and args.reduction == "mean" and args.grad_scale is None and not args.rows:
         out["roofline"]["traffic"] = measured_traffic()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
@@ -405,7 +405,7 @@ def run_softmax(args, name: str) -> dict:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[name]()
+    w = synth.WORKLOADS[name](**({"M": args.rows} if args.rows else {}))
     M, N = w["M"], w["N"]
     x = _device_matrix(torch, w["x"], dev)
     elt = x.element_size()
@@ -469,7 +469,9 @@ def _line(args, name, bmin, M, wall, kernel_ms, kernel, config, dtype, kernel_by
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", **config},
+        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}" +
+                   (f" (rows overridden: M={M}; a scaling check, not the configuration)"
+                    if args.rows else ""), **config},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(M / (wall / steps), 1),
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS,
@@ -521,6 +523,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--workload", default="c4", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--rows", type=int, default=0,
+                    help="c1..c5: run the workload with this many rows instead (scaling checks)")
     ap.add_argument("--reduction", default="mean", choices=["mean", "sum", "none"])
     ap.add_argument("--grad-scale", type=float, default=None,
                     help="upstream gradient folded into the cross-entropy gradient write")
