@@ -18,7 +18,7 @@ import torch
 import oracle
 import oracle_pins
 import synth
-from gpu_util import BF16_FLOOR, BF16_REL, FP32_ABS, to_device, to_host, widen
+from gpu_util import BF16_ABS_FLOOR, BF16_FLOOR, BF16_REL, FP32_ABS, to_device, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -50,12 +50,13 @@ def check_nll(out_gpu: np.ndarray, loss_gpu: np.ndarray, out_want: np.ndarray,
     fin = ~inf
     if out_gpu.dtype == np.uint16:
         rmax = np.max(np.where(fin, np.abs(out_want), 0.0), axis=1, keepdims=True)
-        denom = np.maximum(np.abs(out_want), BF16_FLOOR * rmax)
+        denom = np.maximum(np.abs(out_want), np.maximum(BF16_FLOOR * rmax, BF16_ABS_FLOOR))
         with np.errstate(invalid="ignore", divide="ignore"):
             scaled = np.where(fin & (denom > 0), np.abs(g - out_want) / denom, 0.0)
         worst = float(np.max(scaled)) if scaled.size else 0.0
         assert worst <= BF16_REL, f"{what}: worst scaled error {worst:.3e}"
-        ltol = BF16_REL * np.maximum(np.abs(loss_want), BF16_FLOOR * rmax[:, 0])
+        ltol = BF16_REL * np.maximum(np.abs(loss_want),
+                                     np.maximum(BF16_FLOOR * rmax[:, 0], BF16_ABS_FLOOR))
     else:
         err = np.where(fin, np.abs(g - out_want), 0.0)
         worst = float(np.max(err)) if err.size else 0.0
