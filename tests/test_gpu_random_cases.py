@@ -132,3 +132,53 @@ def test_random_nll(orc, case):
     got = to_host(out)
     from test_gpu_nll import check_nll
     check_nll(got, to_host(loss), want, wl, f"case {case} nll")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_layernorm(orc, case):
+    rng = np.random.Generator(np.random.PCG64(19000 + case))
+    M = int(rng.choice([1, 5, 64, 700]))
+    N = int(rng.choice([8, 16, 1000, 1001, 4096, 12288, 20000]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    ld = N + int(rng.choice([0, 0, 8, 3]))
+    path = int(rng.choice([0, 0, 1, 3]))
+    eps = float(rng.choice([1e-5, 1e-3, 0.5]))
+    print(f"layernorm case {case}: M={M} N={N} ld={ld} {dtype} path={path} eps={eps}", flush=True)
+    x = synth.random_rows(19100 + case, M, N, ld=ld, dtype=dtype, scale=2.0, pad_nan=ld > N)
+    dy = synth.random_rows(19200 + case, M, N, ld=ld, dtype=dtype, scale=1.0, pad_nan=ld > N)
+    wb = synth.random_rows(19300 + case, 2, N, dtype=dtype, scale=1.0)
+    w_h, b_h = np.ascontiguousarray(wb[0]), np.ascontiguousarray(wb[1])
+    force(path, N, dtype)
+    from test_gpu_layernorm import run_case
+    try:
+        run_case(orc, x, w_h, b_h, dy, N, eps, f"layernorm case {case}")
+    except xr.XrError as e:
+        assert path == 1 and e.status == 2, e  # rows these sizes cannot hold in registers
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_element_mul(orc, case):
+    rng = np.random.Generator(np.random.PCG64(20000 + case))
+    M = int(rng.choice([1, 3, 100, 2000]))
+    N = int(rng.choice([1, 5, 8, 1000, 8193, 70000]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    ld = N + int(rng.choice([0, 1, 8]))
+    per_row = bool(rng.integers(2))
+    print(f"element_mul case {case}: M={M} N={N} ld={ld} {dtype} per_row={per_row}", flush=True)
+    x = synth.random_rows(20100 + case, M, N, ld=ld, dtype=dtype, scale=2.0, pad_nan=ld > N)
+    if per_row:
+        s = synth.random_rows(20200 + case, 1, M, dtype="f32", scale=2.0)[0]
+        s[::3] = 1.0
+        s_dev, s_host = to_device(s), s.astype(np.float64)
+    else:
+        s_host = float(rng.choice([0.25, -3.0, 1.0]))
+        s_dev = torch.tensor([s_host], dtype=torch.float32, device="cuda")
+    xd = to_device(x)
+    xr.element_mul(xd[:, :N], s_dev)
+    torch.cuda.synchronize()
+    got = to_host(xd)
+    want = orc.element_mul(x, s_host, n_cols=N)
+    from test_gpu_reductions import check_grad
+    check_grad(got[:, :N], want, float(np.max(np.abs(np.atleast_1d(s_host)))), f"case {case}")
+    if ld > N:
+        assert np.array_equal(got[:, N:].view(np.uint8), x[:, N:].view(np.uint8))
