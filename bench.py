@@ -66,6 +66,10 @@ DESCRIPTIONS = {
     "c4-mul": "element_mul (stored gradient x upstream gradient 0.5, in place), M=16384, "
               "V=128256, bf16",
     "c1": "softmax forward, M=128, N=1000, fp32 logits 3 N(0,1), contiguous",
+    "sm-vocab": "softmax forward + backward over long rows, M=4096, N=128256, bf16 in / fp32 "
+                "accumulation, x and dy N(0,1), split rows through a workspace",
+    "sm-few": "softmax forward + backward with few rows, M=16, N=1048576, fp32, x and dy "
+              "N(0,1), split rows through a workspace",
     "c2": "softmax forward + backward, M=4096, N=4096, bf16 in / fp32 accumulation, "
           "x and dy N(0,1)",
     "c3": "fused cross-entropy loss+grad, M=8192 tokens (B=4, T=2048), V=32000, bf16 logits "
@@ -423,15 +427,18 @@ def run_softmax(args, name: str) -> dict:
     dys = [dy.clone() for _ in range(nsets)] if bwd else None
     ys = [torch.empty_like(x) for _ in range(nsets)]
     dxs = [torch.empty_like(x) for _ in range(nsets)] if bwd else None
+    # one workspace for both directions, allocated before the timed region
+    ws = torch.empty(max(256, xr.softmax_workspace_bytes(M, N, x.dtype)), dtype=torch.uint8,
+                     device=dev)
     ev = HipEvents()
     bwd_events = [(ev.create(), ev.create()) for _ in range(args.warmup + args.steps)]
 
     def launch(i):
         j = i % nsets
-        xr.softmax_fwd(xs[j], ys[j])  # bracketed by the events _timed installs
+        xr.softmax_fwd(xs[j], ys[j], workspace=ws)  # bracketed by the events _timed installs
         if bwd:
             xr.set_profile_events(*bwd_events[i])
-            xr.softmax_bwd(ys[j], dys[j], dxs[j])
+            xr.softmax_bwd(ys[j], dys[j], dxs[j], workspace=ws)
 
     wall, fwd_ms = _timed(ev, args.steps, args.warmup, launch)
     bwd_ms = [ev.elapsed_ms(a, b) for a, b in bwd_events[args.warmup:]] if bwd else []
@@ -440,17 +447,21 @@ def run_softmax(args, name: str) -> dict:
         ev.destroy(b)
     b_fwd = 2 * M * N * elt
     b_bwd = 3 * M * N * elt if bwd else 0
-    p = xr.plan("softmax_fwd", M, N, x.dtype)
-    out = _line(args, name, b_fwd + b_bwd, M, wall, fwd_ms, "softmax_fwd_kernel",
+    p = xr.plan("softmax_fwd_ws", M, N, x.dtype)
+    out = _line(args, name, b_fwd + b_bwd, M, wall, fwd_ms,
+                "softmax_split_kernel" if p["split"] > 1 else "softmax_fwd_kernel",
                 {"M": M, "N": N, "bytes_min": b_fwd + b_bwd, "path": p["path"],
-                 "threads": p["threads"], "grid": p["grid"], "input_sets": nsets},
+                 "threads": p["threads"], "split": p["split"], "grid": p["grid"],
+                 "input_sets": nsets},
                 w["dtype"], kernel_bytes=b_fwd)
     if bwd:
         kavg = statistics.mean(bwd_ms)
         out["roofline_bwd"] = {"bound": "hbm", "achieved": round(b_bwd / kavg / 1e6, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(b_bwd / kavg / 1e6 / PEAK_HBM_GBS, 4),
-                               "kernel": "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5)}
+                               "kernel": "softmax_bwd_split_kernel"
+                               if xr.plan("softmax_bwd_ws", M, N, x.dtype)["split"] > 1
+                               else "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5)}
     return out
 
 
@@ -547,7 +558,7 @@ def main() -> int:
         print("need 1 <= steps and steps + warmup <= 40 (one copy of the logits per step)",
               file=sys.stderr)
         return 2
-    if args.workload in ("c1", "c2"):
+    if args.workload in ("c1", "c2", "sm-vocab", "sm-few"):
         out = run_softmax(args, args.workload)
     elif args.workload == "c4-mul":
         out = run_element_mul(args, args.workload)

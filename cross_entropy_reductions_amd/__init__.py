@@ -37,6 +37,13 @@ lib.xr_softmax_fwd.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p]
 lib.xr_softmax_fwd.restype = ctypes.c_int
 lib.xr_softmax_bwd.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p]
 lib.xr_softmax_bwd.restype = ctypes.c_int
+lib.xr_softmax_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
+lib.xr_softmax_workspace_bytes.restype = _sz
+lib.xr_softmax_fwd_ex.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p, _sz, _p]
+lib.xr_softmax_fwd_ex.restype = ctypes.c_int
+lib.xr_softmax_bwd_ex.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int, _p,
+                                  _sz, _p]
+lib.xr_softmax_bwd_ex.restype = ctypes.c_int
 lib.xr_nll_fwd.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, ctypes.c_int, _p, _sz, _p]
 lib.xr_nll_fwd_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
 lib.xr_nll_fwd_workspace_bytes.restype = _sz
@@ -81,7 +88,8 @@ lib.xr_set_profile_events.argtypes = [_p, _p]
 lib.xr_set_profile_events.restype = ctypes.c_int
 
 # Names exported by include/xr.h (checked against the library by the tests).
-C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_bsr_softmax_bwd", "xr_nll_fwd",
+C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_softmax_workspace_bytes",
+             "xr_softmax_fwd_ex", "xr_softmax_bwd_ex", "xr_bsr_softmax_bwd", "xr_nll_fwd",
              "xr_nll_fwd_workspace_bytes",
              "xr_layernorm_fwd",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
@@ -92,7 +100,8 @@ C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_bsr_softmax_bwd", "xr_nll_f
 F32, BF16 = 0, 1
 OK = 0
 PATHS = {1: "resident", 2: "split", 3: "stream"}
-OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2, "nll_fwd": 3}
+OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2, "nll_fwd": 3, "softmax_fwd_ws": 4,
+       "softmax_bwd_ws": 5}
 OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4, "load_policy": 5}
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
@@ -141,21 +150,46 @@ def _matrix(t: torch.Tensor, name: str):
     return t.data_ptr(), ld, M, N, _DTYPES[t.dtype]
 
 
-def softmax_fwd(x: torch.Tensor, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
-    """Row softmax of x into ``out`` (a new tensor like x, or x itself for in place)."""
+def softmax_workspace_bytes(M: int, N: int, dtype: torch.dtype) -> int:
+    """Workspace bytes the softmax forward and backward need to split rows of this size."""
+    return int(lib.xr_softmax_workspace_bytes(int(M), int(N), _DTYPES[dtype]))
+
+
+def _softmax_ws(workspace, M: int, N: int, dt: int, dev):
+    """(pointer, bytes) of a softmax workspace: a given tensor, a new one when None, or
+    (None, 0) when False (rows handled whole)."""
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        need = int(lib.xr_softmax_workspace_bytes(M, N, dt)) if M > 0 else 0
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or \
+            not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous tensor on the operands' device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def softmax_fwd(x: torch.Tensor, out: torch.Tensor | None = None, *, workspace=None,
+                stream=None) -> torch.Tensor:
+    """Row softmax of x into ``out`` (a new tensor like x, or x itself for in place).
+    ``workspace``: a device tensor of softmax_workspace_bytes() bytes, None to allocate one
+    here, or False to keep every row in one workgroup (no split rows)."""
     px, ldx, M, N, dt = _matrix(x, "x")
     if out is None:
         out = torch.empty_like(x, memory_format=torch.contiguous_format)
     py, ldy, M2, N2, dt2 = _matrix(out, "out")
     if (M2, N2, dt2) != (M, N, dt) or out.device != x.device:
         raise ValueError("out must match x in shape, dtype and device")
-    _check("xr_softmax_fwd", lib.xr_softmax_fwd(py, ldy, px, ldx, M, N, dt, _stream(x, stream)))
+    pw, nw = _softmax_ws(workspace, M, N, dt, x.device)
+    _check("xr_softmax_fwd_ex", lib.xr_softmax_fwd_ex(py, ldy, px, ldx, M, N, dt, pw, nw,
+                                                      _stream(x, stream)))
     return out
 
 
 def softmax_bwd(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = None, *,
-                stream=None) -> torch.Tensor:
-    """dx = y * (dy - sum(y * dy)) per row, into ``out`` (new, or exactly y or dy)."""
+                workspace=None, stream=None) -> torch.Tensor:
+    """dx = y * (dy - sum(y * dy)) per row, into ``out`` (new, or exactly y or dy).
+    ``workspace`` as for softmax_fwd."""
     py, ldy, M, N, dt = _matrix(y, "y")
     pd, ldd, M2, N2, dt2 = _matrix(dy, "dy")
     if (M2, N2, dt2) != (M, N, dt) or dy.device != y.device:
@@ -165,8 +199,9 @@ def softmax_bwd(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = No
     px, ldx, M3, N3, dt3 = _matrix(out, "out")
     if (M3, N3, dt3) != (M, N, dt) or out.device != y.device:
         raise ValueError("out must match y in shape, dtype and device")
-    _check("xr_softmax_bwd",
-           lib.xr_softmax_bwd(px, ldx, py, ldy, pd, ldd, M, N, dt, _stream(y, stream)))
+    pw, nw = _softmax_ws(workspace, M, N, dt, y.device)
+    _check("xr_softmax_bwd_ex",
+           lib.xr_softmax_bwd_ex(px, ldx, py, ldy, pd, ldd, M, N, dt, pw, nw, _stream(y, stream)))
     return out
 
 

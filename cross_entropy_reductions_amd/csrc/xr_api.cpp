@@ -157,6 +157,14 @@ const void* stream_kernel(int op, xr_dtype_t dt) {
   }
 }
 
+const void* split_kernel(int op, xr_dtype_t dt, Shape sh, bool nt) {
+  switch (op) {
+    case kOpSoftmaxFwd: return softmax_fwd_split_kernel_ptr(dt, sh, nt);
+    case kOpSoftmaxBwd: return softmax_bwd_split_kernel_ptr(dt, sh, nt);
+    default: return nll_split_kernel_ptr(dt, sh, nt);
+  }
+}
+
 const void* row_kernel(int op, xr_dtype_t dt, Shape sh, bool nt) {
   switch (op) {
     case kOpSoftmaxFwd: return softmax_fwd_kernel_ptr(dt, sh, nt);
@@ -190,15 +198,16 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     return XR_OK;
   }
 
-  // Workgroups per row (cross-entropy, and the negative log-softmax when it has a workspace
-  // for the exchange; softmax rows stay whole): enough for the row to fit;
+  // Workgroups per row (cross-entropy, and the softmax forward / backward / negative
+  // log-softmax when the call brings a workspace for the exchange; else their rows stay
+  // whole): enough for the row to fit;
   // rows of 32 KB and more in several chunks, so that several workgroups share a compute
   // unit and one's reductions overlap another's memory traffic: ~16 KB chunks (one wave
   // each) up to 64 KB rows, ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s
   // in two chunks, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 in two chunks,
   // 6.0 in eight); and enough chunks to give every compute unit work when the batch is short.
   int64_t S = 1;
-  if (op == kOpXent || (op == kOpNllFwd && can_split)) {
+  if (op == kOpXent || can_split) {
     const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
     const int64_t row_bytes = nvm * 16;
     const int64_t chunk_bytes = row_bytes <= (64 << 10) ? (16 << 10) : (128 << 10);
@@ -238,8 +247,9 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   // faster with the default policy (the cross-entropy over a 128256-wide bf16 vocabulary).
   bool nt_loads = !(S == 1 && nvm * 16 >= (128 << 10));
   if (g_opt.load_policy) nt_loads = g_opt.load_policy == 2;
-  const bool nll_split = op == kOpNllFwd && S > 1;
-  p.kernel = nll_split ? nll_split_kernel_ptr(dt, *sh, nt_loads) : row_kernel(op, dt, *sh, nt_loads);
+  // the split forms of the ops other than the cross-entropy (no persistent form)
+  const bool other_split = op != kOpXent && S > 1;
+  p.kernel = other_split ? split_kernel(op, dt, *sh, nt_loads) : row_kernel(op, dt, *sh, nt_loads);
   if (!p.kernel) return XR_ERR_SHAPE;
   const int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
   if (per_cu <= 0) return XR_ERR_DEVICE;
@@ -252,8 +262,8 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     int64_t g = M;
     if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
     p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
-  } else if (nll_split || (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF)) {
-    if (M * S > 0x7FFFFFFF) {  // (the negative log-softmax has no persistent split form)
+  } else if (other_split || (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF)) {
+    if (M * S > 0x7FFFFFFF) {  // (only the cross-entropy has a persistent split form)
       if (want) return XR_ERR_SHAPE;
       Plan q;
       q.grid = M;
@@ -357,6 +367,24 @@ size_t xent_ws_bytes(const Plan& p, int64_t M) {
   return kWsPartials + (p.path == kPathSplit ? (size_t)M * (size_t)p.S * sizeof(uint64_t) : 0);
 }
 
+// Split rows of the ops other than the cross-entropy: clear the flags and mark every slot of
+// the exchange unpublished (the cross-entropy's target scan with no targets), on `s` before
+// the row kernel. The workspace holds the counts block, then M * S slots.
+xr_status_t prepare_exchange(char* ws, int64_t M, int S, int64_t N, hipStream_t s,
+                             uint64_t** partials, int32_t** flags) {
+  int32_t* ws_counts = reinterpret_cast<int32_t*>(ws + kWsCounts);
+  *partials = reinterpret_cast<uint64_t*>(ws + kWsPartials);
+  *flags = ws_counts + 2;
+  const int64_t* tgt = nullptr;
+  int64_t mm = 0, vv = N, ii = 0, nslots = M * S;
+  void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, partials, &nslots};
+  const int64_t fill_groups = std::min<int64_t>(64, std::max<int64_t>(1, nslots / 1024));
+  if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),
+                      args, 0, s) != hipSuccess)
+    return XR_ERR_LAUNCH;
+  return XR_OK;
+}
+
 }  // namespace
 }  // namespace xr
 
@@ -422,10 +450,13 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
                     xr_plan_t* out) {
   if (!out) return XR_ERR_NULL;
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
-  if (op < 0 || op > 3 || M < 0 || N < 1) return XR_ERR_SHAPE;
+  if (op < 0 || op > 5 || M < 0 || N < 1) return XR_ERR_SHAPE;
+  // ops 4 and 5: the softmax forward / backward with a workspace
+  const bool with_ws = op >= kOpNllFwd;
+  if (op > kOpNllFwd) op -= 4;
   Plan p;
   if (xr_status_t st = make_plan(op, M, N, dtype, op == 2 ? true : aligned != 0, aligned == 2, &p,
-                                 op == kOpNllFwd))
+                                 with_ws))
     return st;
   out->path = p.path;
   out->threads = p.path == kPathStream ? kStreamThreads : p.shape.threads;
@@ -437,8 +468,21 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
   return XR_OK;
 }
 
-xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, int64_t M,
-                           int64_t N, xr_dtype_t dtype, void* stream) {
+size_t xr_softmax_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype) {
+  if (!valid_dtype(dtype) || M < 0 || N < 1) return 0;
+  // the larger of the forward and backward needs, at the worst-case row alignment
+  size_t need = 0;
+  for (int op : {kOpSoftmaxFwd, kOpSoftmaxBwd}) {
+    Plan p;
+    if (make_plan(op, M, N, dtype, true, false, &p, true) == XR_OK)
+      need = std::max(need, xent_ws_bytes(p, M));
+  }
+  return need;
+}
+
+xr_status_t xr_softmax_fwd_ex(void* y, int64_t ld_y, const void* x, int64_t ld_x, int64_t M,
+                              int64_t N, xr_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_x < N || ld_y < N) return XR_ERR_STRIDE;
@@ -447,14 +491,29 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
   const int eb = elt_bytes(dtype);
   if (!aligned_to(x, eb) || !aligned_to(y, eb)) return XR_ERR_ALIGN;
   if (bad_alias(y, ld_y, x, ld_x, M, N, eb)) return XR_ERR_ALIAS;
+  if (workspace && !aligned_to(workspace, 8)) return XR_ERR_ALIGN;
   Plan p;
   const bool on16 = rows_on_16(x, ld_x, M, eb) && rows_on_16(y, ld_y, M, eb);
-  if (xr_status_t st = make_plan(0, M, N, dtype, same_lead(x, ld_x, y, ld_y, eb), on16, &p))
+  if (xr_status_t st = make_plan(kOpSoftmaxFwd, M, N, dtype, same_lead(x, ld_x, y, ld_y, eb), on16,
+                                 &p, workspace != nullptr))
     return st;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N,
-                       nullptr, nullptr, 1, 0, nullptr, nullptr};
-  return launch(p, &prm, static_cast<hipStream_t>(stream),
-                p.path == kPathStream ? kStreamThreads : p.shape.threads);
+                       nullptr, nullptr, p.S, p.chunk_vecs, nullptr, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.path == kPathSplit) {
+    if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    if (spans_overlap(ws, workspace_bytes, y, matrix_span(M, ld_y, N, eb)) ||
+        spans_overlap(ws, workspace_bytes, x, matrix_span(M, ld_x, N, eb)))
+      return XR_ERR_ALIAS;
+    if (xr_status_t st = prepare_exchange(ws, M, p.S, N, s, &prm.partials, &prm.flags)) return st;
+  }
+  return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
+}
+
+xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, int64_t M,
+                           int64_t N, xr_dtype_t dtype, void* stream) {
+  return xr_softmax_fwd_ex(y, ld_y, x, ld_x, M, N, dtype, nullptr, 0, stream);
 }
 
 size_t xr_nll_fwd_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype) {
@@ -496,19 +555,11 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
     if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     if (spans_overlap(ws, workspace_bytes, out, matrix_span(M, ld_out, N, eb)) ||
+        spans_overlap(ws, workspace_bytes, x, matrix_span(M, ld_x, N, eb)) ||
+        spans_overlap(ws, workspace_bytes, idx, (uint64_t)M * 8) ||
         spans_overlap(ws, workspace_bytes, loss, (uint64_t)M * 4))
       return XR_ERR_ALIAS;
-    int32_t* ws_counts = reinterpret_cast<int32_t*>(ws + kWsCounts);
-    prm.partials = reinterpret_cast<uint64_t*>(ws + kWsPartials);
-    prm.flags = ws_counts + 2;
-    // clear the flags and mark every (m, d) slot unpublished (the target scan with no targets)
-    const int64_t* tgt = nullptr;
-    int64_t mm = 0, vv = N, ii = 0, nslots = M * p.S;
-    void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, &prm.partials, &nslots};
-    const int64_t fill_groups = std::min<int64_t>(64, std::max<int64_t>(1, nslots / 1024));
-    if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),
-                        args, 0, s) != hipSuccess)
-      return XR_ERR_LAUNCH;
+    if (xr_status_t st = prepare_exchange(ws, M, p.S, N, s, &prm.partials, &prm.flags)) return st;
   }
   return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
@@ -651,6 +702,13 @@ xr_status_t xr_bsr_softmax_bwd(const void* y, int64_t stride_zy, void* dx, int64
 
 xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y, const void* dy,
                            int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream) {
+  return xr_softmax_bwd_ex(dx, ld_dx, y, ld_y, dy, ld_dy, M, N, dtype, nullptr, 0, stream);
+}
+
+xr_status_t xr_softmax_bwd_ex(void* dx, int64_t ld_dx, const void* y, int64_t ld_y,
+                              const void* dy, int64_t ld_dy, int64_t M, int64_t N,
+                              xr_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_dx < N || ld_y < N || ld_dy < N) return XR_ERR_STRIDE;
@@ -663,12 +721,25 @@ xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y,
   const bool aligned = same_lead(y, ld_y, dy, ld_dy, eb) && same_lead(y, ld_y, dx, ld_dx, eb);
   const bool on16 = rows_on_16(y, ld_y, M, eb) && rows_on_16(dy, ld_dy, M, eb) &&
                     rows_on_16(dx, ld_dx, M, eb);
+  if (workspace && !aligned_to(workspace, 8)) return XR_ERR_ALIGN;
   Plan p;
-  if (xr_status_t st = make_plan(1, M, N, dtype, aligned, on16, &p)) return st;
+  if (xr_status_t st = make_plan(kOpSoftmaxBwd, M, N, dtype, aligned, on16, &p,
+                                 workspace != nullptr))
+    return st;
   SoftmaxBwdParams prm{static_cast<const char*>(y), ld_y * eb, static_cast<const char*>(dy),
-                       ld_dy * eb, static_cast<char*>(dx), ld_dx * eb, M, N};
-  return launch(p, &prm, static_cast<hipStream_t>(stream),
-                p.path == kPathStream ? kStreamThreads : p.shape.threads);
+                       ld_dy * eb, static_cast<char*>(dx), ld_dx * eb, M, N,
+                       p.S, p.chunk_vecs, nullptr, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.path == kPathSplit) {
+    if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    if (spans_overlap(ws, workspace_bytes, dx, matrix_span(M, ld_dx, N, eb)) ||
+        spans_overlap(ws, workspace_bytes, y, matrix_span(M, ld_y, N, eb)) ||
+        spans_overlap(ws, workspace_bytes, dy, matrix_span(M, ld_dy, N, eb)))
+      return XR_ERR_ALIAS;
+    if (xr_status_t st = prepare_exchange(ws, M, p.S, N, s, &prm.partials, &prm.flags)) return st;
+  }
+  return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
 
 size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype) {

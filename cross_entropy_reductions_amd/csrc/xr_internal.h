@@ -138,6 +138,11 @@ struct SoftmaxBwdParams {
   char* dx;
   int64_t lddx_bytes;
   int64_t M, N;
+  // split rows (with a workspace): S workgroups per row exchanging partial dot products
+  int S;
+  int64_t chunk_vecs;
+  uint64_t* partials;
+  int32_t* flags;
 };
 
 // One kernel configuration: workgroup size and 16-byte vectors per thread.
@@ -152,6 +157,8 @@ const void* xent_rows_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* nll_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* softmax_fwd_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
+const void* softmax_bwd_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* xent_stream_kernel_ptr(int dtype);
 const void* softmax_fwd_stream_kernel_ptr(int dtype);

@@ -207,6 +207,54 @@ __device__ __forceinline__ Stats exchange_row_stats(Stats st, uint64_t* slots, i
   return {bcast[0], bcast[1]};
 }
 
+// Split rows of the softmax backward: publish this chunk's partial dot product and add the
+// S partials of the row in chunk order (so every chunk gets bit-identical sums). A published
+// word is the float's bits with 1 in the upper half, never kPartialEmpty. Same bounded wait
+// and timeout flag as exchange_row_stats (the sum is NaN after a timeout).
+template <int THREADS>
+__device__ __forceinline__ float exchange_row_sum(float s, uint64_t* slots, int S, int chunk,
+                                                  int32_t* flags, float* bcast) {
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(slots + chunk, (uint64_t)as_u32(s) | (1ull << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    float t = 0.f;
+    bool ok = true;
+    int budget = (__hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                  kFlagExchangeTimeout) ? 0 : kSpinLimit;
+    for (int q = 0; q < S && ok; ++q) {
+      uint64_t w;
+      while ((w = __hip_atomic_load(slots + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+             kPartialEmpty) {
+        if (--budget < 0) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (!ok) break;
+      t += as_f32((uint32_t)w);
+    }
+    if (!ok) {
+      __hip_atomic_fetch_or(flags, kFlagExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = __builtin_nanf("");
+    }
+    bcast[0] = t;
+  }
+  __syncthreads();
+  return bcast[0];
+}
+
+// One element into a thread's running (m, d): the online-softmax rule, -inf elements adding
+// nothing.
+__device__ __forceinline__ void online_add(Stats& st, float x) {
+  if (x > st.m) {
+    st.d = (st.m == kNegInf ? 0.f : st.d * __builtin_amdgcn_exp2f((st.m - x) * kLog2e)) + 1.f;
+    st.m = x;
+  } else if (x != kNegInf) {
+    st.d += __builtin_amdgcn_exp2f((x - st.m) * kLog2e);
+  }
+}
+
 // exp2(x*log2e - coff) for every element of one slot, in the element type, XOR-ed with
 // `sign` (0, or Elt<D>::kSignWord to negate every result: a negative upstream gradient).
 template <int D>

@@ -81,11 +81,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
-// Negative log-softmax over split rows: workgroup b handles chunk b % S of row b / S (rows
-// too long for one workgroup to keep several per compute unit). The chunks exchange their
-// (m, d) pairs as the cross-entropy's split rows do; the chunk holding idx writes the loss.
-template <int D, int THREADS, int VPT, int LP>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void nll_split_kernel(SoftmaxFwdParams p) {
+// Softmax (NLL = false) or negative log-softmax (NLL = true) over split rows: workgroup b
+// handles chunk b % S of row b / S (long rows, or too few rows to fill the GPU). The chunks
+// exchange their (m, d) pairs as the cross-entropy's split rows do; for NLL the chunk
+// holding idx writes the loss.
+template <int D, int THREADS, int VPT, int LP, bool NLL>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_split_kernel(SoftmaxFwdParams p) {
   constexpr int EPV = Elt<D>::kPerVec;
   constexpr int NW = THREADS / kWave;
   __shared__ float2 red[NW];
@@ -100,9 +101,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, lo, p.chunk_vecs);  // same lead (host-checked)
   u32x4 v[VPT];
   issue_loads<D, THREADS, VPT, LP>(v, cx);
-  // the gathered element, read by the thread holding its vector before any store of this
-  // chunk (y may be exactly x; other chunks write only their own elements)
-  const int64_t ix = p.idx[r];
+  // NLL: the gathered element, read by the thread holding its vector before any store of
+  // this chunk (y may be exactly x; other chunks write only their own elements)
+  const int64_t ix = NLL ? p.idx[r] : -1;
   const bool in_row = ix >= 0 && ix < p.N;
   const int64_t vt = cx.lead + ix - cx.lo * EPV;  // chunk-local element index
   const bool owner = in_row && vt >= 0 && vt < (int64_t)cx.nvec * EPV &&
@@ -111,17 +112,23 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (owner) xi = buf_load_elem<D>(cx.rsrc, (uint32_t)(vt * Elt<D>::kBytes));
   Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red);
   st = exchange_row_stats<THREADS>(st, p.partials + r * S, S, chunk, p.flags, bcast);
-  const float c = st.m + logf(st.d);
+  // softmax: exp2(x*log2e - c), c = m*log2e + log2 d.  NLL: c - x, c = m + log d.
+  const float c = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(cy, k, nll_slot<D>(v[k], c));
-  store_partials<D, THREADS>(cy, cx, [c](float x) { return c - x; });
-  if (owner) p.loss[r] = round_elem<D>(c - xi);
-  else if (!in_row && chunk == 0 && tid == 0) p.loss[r] = __builtin_nanf("");
+  for (int k = 0; k < VPT; ++k)
+    store_slot<D, THREADS>(cy, k, NLL ? nll_slot<D>(v[k], c) : exp_slot<D>(v[k], c));
+  store_partials<D, THREADS>(cy, cx, [c](float x) {
+    return NLL ? c - x : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -c));
+  });
+  if (NLL) {
+    if (owner) p.loss[r] = round_elem<D>(c - xi);
+    else if (!in_row && chunk == 0 && tid == 0) p.loss[r] = __builtin_nanf("");
+  }
 }
 
 template <int D, bool NLL>
 __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(SoftmaxFwdParams p) {
-  __shared__ float red[2][kStreamThreads / kWave];
+  __shared__ float2 red[kStreamThreads / kWave];
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const char* row = p.x + r * p.ldx_bytes;
@@ -135,17 +142,14 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
   const int64_t ix = NLL ? p.idx[r] : -1;
   const bool in_row = ix >= 0 && ix < p.N;
   const float xi = (NLL && tid == 0 && in_row) ? ld(ix) : 0.f;
-  float m = kNegInf;
-  for (int64_t j = tid; j < p.N; j += kStreamThreads) m = fmaxf(m, ld(j));
-  m = block_reduce<kStreamThreads>(m, OpMax(), red[0]);
-  const float mL = m * kLog2e;
-  float d = 0.f;
-  for (int64_t j = tid; j < p.N; j += kStreamThreads)
-    d += __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -mL));
-  d = block_reduce<kStreamThreads>(d, OpAdd(), red[1]);
+  // one pass for (m, d): the online-softmax rule per thread, then the workgroup combine
+  Stats st{kNegInf, 0.f};
+  for (int64_t j = tid; j < p.N; j += kStreamThreads) online_add(st, ld(j));
+  st = block_reduce_stats<kStreamThreads>(st, red);
+  const float m = st.m, d = st.d;
   // In place (y == x) is safe: every element's output depends only on itself and (m, d),
-  // and all reads of the max / sum passes finished before the barrier above.
-  const float coff = NLL ? m + logf(d) : mL + log2f(d);
+  // and all reads of the statistics pass finished before the barrier above.
+  const float coff = NLL ? m + logf(d) : m * kLog2e + log2f(d);
   for (int64_t j = tid; j < p.N; j += kStreamThreads) {
     const float val = NLL ? coff - ld(j) : __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
     if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
@@ -229,6 +233,67 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+// Softmax backward over split rows: workgroup b handles chunk b % S of row b / S; the
+// chunks exchange their partial dot products (summed in chunk order), then each writes its
+// part of dx = y (dy - s). y, dy and dx rows share their alignment (host-checked).
+template <int D, int THREADS, int VPT, int LP>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_bwd_split_kernel(SoftmaxBwdParams p) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int NW = THREADS / kWave;
+  __shared__ float red[NW];
+  __shared__ float bcast[1];
+  const int tid = threadIdx.x;
+  const int S = p.S;
+  const int64_t r = blockIdx.x / S;
+  const int chunk = (int)(blockIdx.x - r * S);
+  if (r >= p.M) return;
+  const int64_t lo = (int64_t)chunk * p.chunk_vecs;
+  const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, lo, p.chunk_vecs);
+  const Chunk<D> cd(p.dy + r * p.lddy_bytes, p.N, lo, p.chunk_vecs);
+  const Chunk<D> cx(p.dx + r * p.lddx_bytes, p.N, lo, p.chunk_vecs);
+  u32x4 vy[VPT], vd[VPT];
+  issue_loads<D, THREADS, VPT, LP>(vy, cy);
+  issue_loads<D, THREADS, VPT, LP>(vd, cd);
+  // out-of-row elements of both operands count as 0: they add nothing to the dot product
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) continue;
+    const u32x4 a = masked_slot<D, THREADS>(vy[k], k, cy, 0u);
+    const u32x4 b = masked_slot<D, THREADS>(vd[k], k, cy, 0u);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s4[e & 3] = __builtin_fmaf(elem<D>(a, e), elem<D>(b, e), s4[e & 3]);
+  }
+  const float part = block_reduce<THREADS>((s4[0] + s4[1]) + (s4[2] + s4[3]), OpAdd(), red);
+  const float dot = exchange_row_sum<THREADS>(part, p.partials + r * S, S, chunk, p.flags, bcast);
+  reg_barrier(vy);
+  reg_barrier(vd);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    OutVec<D> o;
+    u32x4 a = vy[k], b = vd[k];
+    pin(a);
+    pin(b);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+    store_slot<D, THREADS>(cx, k, o.bits());
+  }
+  // partial first / last vectors: re-read y and dy (dx may be exactly y or dy; this chunk
+  // has not written them) and store only the in-row elements
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int vi = q == 0 ? cx.head : cx.tail;
+    if (vi < 0 || tid != vi % THREADS) continue;
+    const uint32_t po = q == 0 ? cx.hoff : cx.toff;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cy.rsrc, (int)po, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cd.rsrc, (int)po, 0, 0);
+    OutVec<D> o;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+    store_partial<D>(cx.rsrc, po, o.bits(), q == 0 ? cx.h0 : cx.t0, q == 0 ? cx.h1 : cx.t1);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream_kernel(SoftmaxBwdParams p) {
   __shared__ float red[kStreamThreads / kWave];
@@ -278,11 +343,29 @@ const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
 }
 #define XR_CASE_NLLS(D, T, V)                                                                  \
   if (s.threads == T && s.vpt == V)                                                              \
-    return lp ? reinterpret_cast<const void*>(&nll_split_kernel<D, T, V, kPolicyNT>)             \
-              : reinterpret_cast<const void*>(&nll_split_kernel<D, T, V, kPolicyDefault>);
+    return lp ? reinterpret_cast<const void*>(&softmax_split_kernel<D, T, V, kPolicyNT, true>)   \
+              : reinterpret_cast<const void*>(&softmax_split_kernel<D, T, V, kPolicyDefault, true>);
+#define XR_CASE_SFWDS(D, T, V)                                                                 \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&softmax_split_kernel<D, T, V, kPolicyNT, false>)  \
+              : reinterpret_cast<const void*>(&softmax_split_kernel<D, T, V, kPolicyDefault, false>);
+#define XR_CASE_SBWDS(D, T, V)                                                                 \
+  if (s.threads == T && s.vpt == V)                                                              \
+    return lp ? reinterpret_cast<const void*>(&softmax_bwd_split_kernel<D, T, V, kPolicyNT>)     \
+              : reinterpret_cast<const void*>(&softmax_bwd_split_kernel<D, T, V, kPolicyDefault>);
 const void* nll_split_kernel_ptr(int dtype, Shape s, bool lp) {
   if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_NLLS, kF32) }
   if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_NLLS, kBF16) }
+  return nullptr;
+}
+const void* softmax_fwd_split_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_SFWDS, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_SFWDS, kBF16) }
+  return nullptr;
+}
+const void* softmax_bwd_split_kernel_ptr(int dtype, Shape s, bool lp) {
+  if (dtype == kF32) { XR_SHAPES_BWD(XR_CASE_SBWDS, kF32) }
+  if (dtype == kBF16) { XR_SHAPES_BWD(XR_CASE_SBWDS, kBF16) }
   return nullptr;
 }
 const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool lp) {

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
 // Stream fallback: one workgroup per row, element-wise, max / sum / write passes over memory.
 template <int D>
 __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams p) {
-  __shared__ float red[2][kStreamThreads / kWave];
+  __shared__ float2 red[kStreamThreads / kWave];
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const int64_t t = p.target[r];
@@ -259,16 +259,13 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams 
   const float sc = p.gscale ? p.gscale[r * p.gstride] : 1.0f;
   const bool neg = __builtin_signbit(sc) != 0;
   const float xt = ld(t);
-  float m = kNegInf;
-  for (int64_t j = tid; j < p.V; j += kStreamThreads) m = fmaxf(m, ld(j));
-  m = block_reduce<kStreamThreads>(m, OpMax(), red[0]);
-  const float mL = m * kLog2e;
-  float d = 0.f;
-  for (int64_t j = tid; j < p.V; j += kStreamThreads)
-    d += __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -mL));
-  d = block_reduce<kStreamThreads>(d, OpAdd(), red[1]);
-  // Every thread has read xt and the row before the barrier inside the reductions.
-  const float coff = mL + log2f(d) + log2f((float)n) - log2f(fabsf(sc));
+  // one pass for (m, d): the online-softmax rule per thread, then the workgroup combine
+  Stats sd{kNegInf, 0.f};
+  for (int64_t j = tid; j < p.V; j += kStreamThreads) online_add(sd, ld(j));
+  sd = block_reduce_stats<kStreamThreads>(sd, red);
+  const float m = sd.m, d = sd.d;
+  // Every thread has read xt and the row before the barrier inside the reduction.
+  const float coff = m * kLog2e + log2f(d) + log2f((float)n) - log2f(fabsf(sc));
   for (int64_t j = tid; j < p.V; j += kStreamThreads) {
     float g;
     if (j == t) {

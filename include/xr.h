@@ -65,6 +65,25 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
                            int64_t N, xr_dtype_t dtype, void* stream);
 
 /*
+ * xr_softmax_fwd / xr_softmax_bwd with a workspace: the same results, but long rows (and
+ * rows too few to give every compute unit work) are split over several workgroups that
+ * exchange their partial statistics through the workspace: the (max, sum) pairs of the
+ * online-softmax combine for the forward (the pairs the cross-entropy's split rows
+ * exchange), the partial dot products sum(y * dy) for the backward, each added in chunk
+ * order, so the results do not depend on timing.
+ *   workspace  device scratch of at least xr_softmax_workspace_bytes(M, N, dtype) bytes
+ *              (covers both directions), 8-byte aligned, or NULL (rows handled whole, as
+ *              without _ex); no initialisation needed; scratch between calls; it must not
+ *              overlap any matrix of the call (XR_ERR_ALIAS)
+ *   workspace_bytes  its size; too small for the plan the call takes: XR_ERR_WORKSPACE
+ * Calls that share a workspace must not run concurrently.
+ */
+size_t xr_softmax_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype);
+xr_status_t xr_softmax_fwd_ex(void* y, int64_t ld_y, const void* x, int64_t ld_x, int64_t M,
+                              int64_t N, xr_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Softmax backward, one row at a time:
  *   dx[i, j] = y[i, j] * (dy[i, j] - s_i),  s_i = sum_k y[i, k] * dy[i, k]
  * The fused softmax backward of the Triton kernel `_backward` on the page "python sum
@@ -75,6 +94,10 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
  */
 xr_status_t xr_softmax_bwd(void* dx, int64_t ld_dx, const void* y, int64_t ld_y, const void* dy,
                            int64_t ld_dy, int64_t M, int64_t N, xr_dtype_t dtype, void* stream);
+xr_status_t xr_softmax_bwd_ex(void* dx, int64_t ld_dx, const void* y, int64_t ld_y,
+                              const void* dy, int64_t ld_dy, int64_t M, int64_t N,
+                              xr_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Block-sparse softmax backward through a look-up table (the Triton kernel `_backward` on
@@ -264,10 +287,12 @@ int32_t xr_version(void);
 /*
  * How a call is carried out (host query, nothing enqueued). path: 1 = row-resident
  * (a row or a row chunk per workgroup, held in registers: one read of the input),
- * 2 = split row (S > 1 workgroups per row exchanging (max, sum) pairs), 3 = stream
- * (one workgroup per row, several passes over global memory).
- * op: 0 = softmax forward, 1 = softmax backward, 2 = cross-entropy, 3 = negative
- * log-softmax forward (with a workspace).
+ * 2 = split row (S > 1 workgroups per row exchanging (max, sum) pairs or partial sums),
+ * 3 = stream (one workgroup per row, two passes over global memory: the row statistics,
+ * then the outputs).
+ * op: 0 = softmax forward, 1 = softmax backward (both without a workspace),
+ * 2 = cross-entropy, 3 = negative log-softmax forward (with a workspace), 4 = softmax
+ * forward and 5 = softmax backward with a workspace (xr_softmax_fwd_ex / _bwd_ex).
  * aligned: 0 = the operand rows sit at different addresses modulo 16 bytes (stream path),
  * 1 = they share their address modulo 16 (rows may start anywhere), 2 = moreover every row
  * starts on a 16-byte boundary (the usual contiguous tensors). The cross-entropy has one
@@ -293,8 +318,8 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
  *   XR_OPT_PATH     1 resident, 2 split, 3 stream (a forced path the sizes cannot take
  *                   returns XR_ERR_SHAPE from the entry point); layer norm: 1 row-resident,
  *                   3 element-wise
- *   XR_OPT_SPLIT    workgroups per row for the split path (>= 2): cross-entropy and the
- *                   negative log-softmax with a workspace
+ *   XR_OPT_SPLIT    workgroups per row for the split path (>= 2): cross-entropy, and the
+ *                   softmax forward / backward and negative log-softmax with a workspace
  *   XR_OPT_THREADS  workgroup size of the row-resident kernels (64 .. 1024)
  *   XR_OPT_GRID     0 or -1 = one workgroup per row (or per row chunk), launched normally;
  *                   k >= 1 = a persistent grid of k workgroups per compute unit (launched

@@ -116,6 +116,26 @@ def softmax_c2(M: int = 4096, N: int = 4096, seed: int = 1002) -> dict:
             "dy": dy}
 
 
+def softmax_long(M: int = 4096, N: int = 128256, dtype: str = "bf16", seed: int = 1008,
+                 name: str = "sm-vocab") -> dict:
+    """Softmax forward + backward over long rows: x and dy = N(0,1) (dy uses seed + 100), in
+    bf16 (bit patterns) or fp32. Defaults: 4096 rows as wide as a 128256-entry vocabulary."""
+    conv = bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a)
+    et = np.uint16 if dtype == "bf16" else np.float32
+    x = np.empty((M, N), dtype=et)
+    dy = np.empty((M, N), dtype=et)
+    _fill_chunks(x, N, seed, lambda rng, rows: conv(_normal(rng, (rows, N), 1.0)))
+    _fill_chunks(dy, N, seed + 100, lambda rng, rows: conv(_normal(rng, (rows, N), 1.0)))
+    return {"name": name, "op": "softmax_fwd_bwd", "dtype": dtype, "M": M, "N": N, "x": x,
+            "dy": dy}
+
+
+def softmax_few(M: int = 16, N: int = 1 << 20, seed: int = 1009) -> dict:
+    """Softmax forward + backward with too few rows to fill the GPU one row per workgroup:
+    16 fp32 rows of 2^20 entries, x and dy = N(0,1)."""
+    return softmax_long(M, N, "f32", seed, "sm-few")
+
+
 def xent_c3(M: int = 8192, V: int = 32000, seed: int = 1003) -> dict:
     """c3: bf16 logits 2 N(0,1), uniform int64 targets, floor(10 % M) rows ignored."""
     x = np.empty((M, V), dtype=np.uint16)
@@ -244,7 +264,8 @@ def bsr_softmax(Z: int = 32, seq: int = 4096, block: int = 64, local: int = 4, s
             "scale": 0.125, "dtype": dtype, **lay}
 
 
-WORKLOADS = {"c1": softmax_c1, "c2": softmax_c2, "c3": xent_c3, "c4": xent_c4, "c5": xent_c5}
+WORKLOADS = {"c1": softmax_c1, "c2": softmax_c2, "c3": xent_c3, "c4": xent_c4, "c5": xent_c5,
+             "sm-vocab": softmax_long, "sm-few": softmax_few}
 
 
 def random_rows(seed: int, M: int, N: int, ld: int | None = None, dtype: str = "f32",

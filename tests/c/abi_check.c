@@ -28,6 +28,10 @@ int main(void) {
   CHECK(xr_softmax_fwd(p, 9, q, 10, 4, 10, XR_F32, NULL) == XR_ERR_STRIDE);
   CHECK(xr_softmax_fwd(p, 10, q, 10, 0, 10, XR_F32, NULL) == XR_OK);
   CHECK(xr_softmax_bwd(p, 8, q, 8, NULL, 8, 2, 8, XR_F32, NULL) == XR_ERR_NULL);
+  CHECK(xr_softmax_fwd_ex(p, 10, q, 10, 4, 10, XR_F32, (void*)0x50004, 4096, NULL) ==
+        XR_ERR_ALIGN);
+  CHECK(xr_softmax_bwd_ex(p, 8, q, 8, NULL, 8, 2, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
+  CHECK(xr_softmax_workspace_bytes(4, 0, XR_F32) == 0);
   CHECK(xr_xent_fwd_bwd(p, 8, t, -1, 8, -100, XR_BF16, f, f, NULL, q, 4096, NULL) == XR_ERR_SHAPE);
   CHECK(xr_xent_fwd_bwd_ex(p, 8, t, 2, 8, -100, XR_BF16, (xr_reduction_t)5, NULL, 0, f, f, NULL,
                            q, 4096, NULL) == XR_ERR_VALUE);

@@ -75,6 +75,27 @@ def test_softmax_bwd_argument_errors(xr):
     assert f(ctypes.c_void_p(0x30008), 8, B, 8, C, 8, 2, 8, 0, None) == XR_ERR_ALIAS
 
 
+def test_softmax_ex_argument_errors(xr):
+    f, g = xr.lib.xr_softmax_fwd_ex, xr.lib.xr_softmax_bwd_ex
+    A, B, C, W = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x50000))
+    # the checks of the calls without a workspace come first, unchanged
+    assert f(A, 10, B, 10, 4, 10, 2, W, 4096, None) == XR_ERR_DTYPE
+    assert f(A, 9, B, 10, 4, 10, 0, W, 4096, None) == XR_ERR_STRIDE
+    assert f(None, 10, B, 10, 4, 10, 0, W, 4096, None) == XR_ERR_NULL
+    assert f(ctypes.c_void_p(0x10010), 10, A, 10, 4, 10, 0, W, 4096, None) == XR_ERR_ALIAS
+    assert g(A, 8, B, 8, C, 7, 2, 8, 0, W, 4096, None) == XR_ERR_STRIDE
+    assert g(ctypes.c_void_p(0x30008), 8, B, 8, C, 8, 2, 8, 0, W, 4096, None) == XR_ERR_ALIAS
+    # a workspace not on an 8-byte boundary
+    assert f(A, 10, B, 10, 4, 10, 0, ctypes.c_void_p(0x50004), 4096, None) == XR_ERR_ALIGN
+    assert g(A, 8, B, 8, C, 8, 2, 8, 1, ctypes.c_void_p(0x50002), 4096, None) == XR_ERR_ALIGN
+    # M == 0: nothing to do, with or without a workspace
+    assert f(A, 10, B, 10, 0, 10, 0, W, 4096, None) == XR_OK
+    assert g(A, 8, B, 8, C, 8, 0, 8, 0, None, 0, None) == XR_OK
+    assert xr.lib.xr_softmax_workspace_bytes(4, 0, 0) == 0
+    assert xr.lib.xr_softmax_workspace_bytes(-1, 8, 0) == 0
+    assert xr.lib.xr_softmax_workspace_bytes(4, 8, 9) == 0
+
+
 def test_xent_argument_errors(xr):
     f = xr.lib.xr_xent_fwd_bwd
     L, T, R, Mn, W = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
@@ -136,7 +157,8 @@ def test_options(xr):
 def test_plan_argument_errors(xr):
     out = xr.XrPlan()
     assert xr.lib.xr_plan(0, 4, 8, 0, 1, None) == XR_ERR_NULL
-    assert xr.lib.xr_plan(4, 4, 8, 0, 1, ctypes.byref(out)) == XR_ERR_SHAPE
+    assert xr.lib.xr_plan(6, 4, 8, 0, 1, ctypes.byref(out)) == XR_ERR_SHAPE
+    assert xr.lib.xr_plan(-1, 4, 8, 0, 1, ctypes.byref(out)) == XR_ERR_SHAPE
     assert xr.lib.xr_plan(0, 4, 8, 5, 1, ctypes.byref(out)) == XR_ERR_DTYPE
 
 

@@ -93,17 +93,20 @@ def test_random_xent(orc, case):
 def test_random_softmax(orc, case):
     rng = np.random.Generator(np.random.PCG64(17000 + case))
     M, N, dtype, ld, path = draw(rng, case)
-    path = 0 if path == 2 else path  # softmax rows are never split
-    print(f"softmax case {case}: M={M} N={N} ld={ld} {dtype} path={path}", flush=True)
+    # rows split over workgroups need a workspace; without one they stay whole
+    use_ws = path == 2 or bool(rng.integers(2))
+    print(f"softmax case {case}: M={M} N={N} ld={ld} {dtype} path={path} workspace={use_ws}",
+          flush=True)
     x = synth.random_rows(17100 + case, M, N, ld=ld, dtype=dtype, scale=3.0, pad_nan=ld > N)
     dy = synth.random_rows(17200 + case, M, N, ld=ld, dtype=dtype, scale=1.0, pad_nan=ld > N)
     force(path, N, dtype)
     xd, dyd = to_device(x), to_device(dy)
     try:
-        y = xr.softmax_fwd(xd[:, :N])
-        dx = xr.softmax_bwd(y, dyd[:, :N])
+        ws = None if use_ws else False
+        y = xr.softmax_fwd(xd[:, :N], workspace=ws)
+        dx = xr.softmax_bwd(y, dyd[:, :N], workspace=ws)
     except xr.XrError as e:
-        assert path == 1 and e.status == 2, e
+        assert path in (1, 2) and e.status == 2, e  # a forced path these sizes cannot take
         return
     torch.cuda.synchronize()
     y_h = to_host(y)

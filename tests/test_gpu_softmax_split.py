@@ -1,0 +1,211 @@
+"""GPU parity of the softmax forward and backward over split rows (xr_softmax_fwd_ex /
+xr_softmax_bwd_ex with a workspace: several workgroups per row exchanging (max, sum) pairs
+or partial dot products) against the float64 oracle, with the suite's tolerances (fp32
+within 1e-5 absolute, bf16 within 2e-2 relative of the row's scale). Covers long rows, rows
+too few to fill the GPU, forced chunk counts (including chunks left empty), in-place calls,
+row pitches, -inf entries, determinism and the workspace's argument checks."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_output, to_device, to_host, widen
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import cross_entropy_reductions_amd as xr
+else:  # collected on a machine without a GPU: every test here is skipped
+    xr = None
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no HIP device")]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    xr.reset_options()
+    yield
+    xr.reset_options()
+
+
+def fwd_bwd(x_h: np.ndarray, dy_h: np.ndarray, N: int, workspace=None):
+    x, dy = to_device(x_h), to_device(dy_h)
+    y = xr.softmax_fwd(x[:, :N], workspace=workspace)
+    dx = xr.softmax_bwd(y, dy[:, :N], workspace=workspace)
+    torch.cuda.synchronize()
+    return to_host(y), to_host(dx)
+
+
+def check(orc, x_h, dy_h, N, y_h, dx_h, what):
+    check_output(y_h, orc.softmax_fwd(x_h, n_cols=N), f"{what} forward")
+    # the backward on the GPU's own y isolates the backward kernel
+    check_output(dx_h, orc.softmax_bwd(y_h, np.ascontiguousarray(dy_h[:, :N])),
+                 f"{what} backward")
+
+
+# (M, N, dtype): long rows (two or more 128 KB chunks), 32-64 KB rows (16 KB chunks), rows
+# too few for the GPU (chunks for every compute unit), ragged sizes.
+SHAPES = [(1, 300001, "bf16"), (3, 70001, "f32"), (5, 128256, "bf16"), (64, 40000, "bf16"),
+          (200, 20000, "f32"), (7, 5000, "f32"), (2, 1 << 20, "f32"), (16, 262147, "bf16"),
+          (300, 8193, "f32")]
+
+
+@pytest.mark.parametrize("M,N,dtype", SHAPES, ids=[f"{m}x{n}-{d}" for m, n, d in SHAPES])
+def test_split_shapes(orc, M, N, dtype):
+    fw = xr.plan("softmax_fwd_ws", M, N, torch.float32 if dtype == "f32" else torch.bfloat16)
+    bw = xr.plan("softmax_bwd_ws", M, N, torch.float32 if dtype == "f32" else torch.bfloat16)
+    print(f"split {M}x{N} {dtype}: forward S={fw['split']}, backward S={bw['split']}", flush=True)
+    assert fw["split"] > 1 and bw["split"] > 1, "these sizes are meant to take the split path"
+    x = synth.random_rows(19000 + N % 97, M, N, dtype=dtype, scale=3.0)
+    dy = synth.random_rows(19001 + N % 97, M, N, dtype=dtype, scale=1.0)
+    y, dx = fwd_bwd(x, dy, N)
+    check(orc, x, dy, N, y, dx, f"{M}x{N} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forced_chunk_counts(orc, dtype):
+    """Chunk counts from 2 to far more chunks than the row has vectors (empty chunks), each
+    against the oracle and bit-identical to the whole-row result where that is exact."""
+    M, N = 37, 3001
+    x = synth.random_rows(19100, M, N, dtype=dtype, scale=3.0)
+    dy = synth.random_rows(19101, M, N, dtype=dtype, scale=1.0)
+    for S in (2, 3, 7, 64, 1000):
+        xr.set_option("split", S)
+        xr.set_option("path", 2)
+        print(f"{dtype} forced S={S}", flush=True)
+        y, dx = fwd_bwd(x, dy, N)
+        check(orc, x, dy, N, y, dx, f"{dtype} S={S}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_in_place_and_pitches(orc, dtype):
+    """y == x for the forward, dx == dy and dx == y for the backward, on rows with a pitch
+    (rows at varying addresses modulo 16, all operands sharing it); padding untouched."""
+    M, N, ld = 9, 90001, 90013
+    x_h = synth.random_rows(19200, M, N, ld=ld, dtype=dtype, scale=3.0, pad_nan=True)
+    dy_h = synth.random_rows(19201, M, N, ld=ld, dtype=dtype, scale=1.0, pad_nan=True)
+    assert xr.plan("softmax_fwd_ws", M, N, torch.float32, aligned=1)["split"] > 1
+    want_y = orc.softmax_fwd(x_h, n_cols=N)
+    x = to_device(x_h)
+    xr.softmax_fwd(x[:, :N], x[:, :N])
+    torch.cuda.synchronize()
+    full = to_host(x)
+    y_h = np.ascontiguousarray(full[:, :N])
+    check_output(y_h, want_y, f"{dtype} in place forward")
+    assert np.array_equal(full[:, N:].view(np.uint8), x_h[:, N:].view(np.uint8)), "padding"
+    want_dx = orc.softmax_bwd(y_h, np.ascontiguousarray(dy_h[:, :N]))
+    # dx written over dy
+    dy = to_device(dy_h)
+    xr.softmax_bwd(x[:, :N], dy[:, :N], dy[:, :N])
+    torch.cuda.synchronize()
+    full = to_host(dy)
+    check_output(np.ascontiguousarray(full[:, :N]), want_dx, f"{dtype} dx over dy")
+    assert np.array_equal(full[:, N:].view(np.uint8), dy_h[:, N:].view(np.uint8)), "padding"
+    # dx written over y
+    dy = to_device(dy_h)
+    xr.softmax_bwd(x[:, :N], dy[:, :N], x[:, :N])
+    torch.cuda.synchronize()
+    check_output(np.ascontiguousarray(to_host(x)[:, :N]), want_dx, f"{dtype} dx over y")
+
+
+def test_split_neg_inf_and_constant_rows(orc):
+    """Rows with -inf runs that leave whole chunks at -inf, a constant row, one finite
+    entry per row: the chunk combine must weigh empty chunks as zero."""
+    M, N = 6, 200000
+    x = synth.random_rows(19300, M, N, dtype="f32", scale=3.0)
+    dy = synth.random_rows(19301, M, N, dtype="f32", scale=1.0)
+    x[0, : N // 2] = -np.inf          # first half of the row (whole chunks) at -inf
+    x[1, N // 3:] = -np.inf           # tail chunks at -inf
+    x[2, :] = 1.25                    # constant: 1 / N everywhere
+    x[3, :] = -np.inf
+    x[3, 12345] = 0.0                 # a single finite entry: probability 1
+    x[4, ::2] = -np.inf
+    y, dx = fwd_bwd(x, dy, N)
+    check(orc, x, dy, N, y, dx, "-inf / constant rows")
+    assert y[3, 12345] == 1.0 and np.count_nonzero(y[3]) == 1
+
+
+def test_split_deterministic(orc):
+    """Chunk-ordered combines: repeated calls give the same bits."""
+    M, N = 4, 500000
+    x = to_device(synth.random_rows(19400, M, N, dtype="bf16", scale=3.0))
+    dy = to_device(synth.random_rows(19401, M, N, dtype="bf16", scale=1.0))
+    outs = []
+    for _ in range(3):
+        y = xr.softmax_fwd(x)
+        outs.append((to_host(y), to_host(xr.softmax_bwd(y, dy))))
+    for y, dx in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(dx, outs[0][1])
+
+
+def test_split_agrees_with_whole_rows(orc):
+    """The same rows whole (no workspace, one workgroup per row) and split: both within the
+    tolerance of the oracle, and within a few roundings of each other."""
+    M, N = 12, 150000
+    x = synth.random_rows(19500, M, N, dtype="f32", scale=3.0)
+    dy = synth.random_rows(19501, M, N, dtype="f32", scale=1.0)
+    y1, dx1 = fwd_bwd(x, dy, N, workspace=False)
+    y2, dx2 = fwd_bwd(x, dy, N)
+    check(orc, x, dy, N, y1, dx1, "whole rows")
+    check(orc, x, dy, N, y2, dx2, "split rows")
+    assert np.max(np.abs(widen(y1) - widen(y2))) <= 1e-6
+
+
+def test_sm_vocab_sampled(orc):
+    """The long-row softmax workload (4096 x 128256 bf16, forward + backward) in the launch
+    configuration the benchmark times (split rows through one shared workspace), on sampled
+    rows; every row's sum checked."""
+    w = synth.softmax_long()
+    M, N = w["M"], w["N"]
+    x, dy = to_device(w["x"]), to_device(w["dy"])
+    ws = torch.empty(xr.softmax_workspace_bytes(M, N, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    y = xr.softmax_fwd(x, workspace=ws)
+    dx = xr.softmax_bwd(y, dy, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 2, 1000, 2047, 4000, M - 1])
+    idx = torch.from_numpy(rows).cuda()
+    y_h, dx_h = to_host(y[idx]), to_host(dx[idx])
+    check(orc, w["x"][rows], w["dy"][rows], N, y_h, dx_h, "4096 x 128256 sampled rows")
+    s = y.float().sum(dim=1).cpu().numpy()
+    assert np.max(np.abs(s - 1.0)) < 2e-2 * 1.0 + 1e-3
+
+
+def test_sm_few_sampled(orc):
+    """The few-row softmax workload (16 x 2^20 fp32, forward + backward), every row."""
+    w = synth.softmax_few()
+    M, N = w["M"], w["N"]
+    y, dx = fwd_bwd(w["x"], w["dy"], N)
+    check(orc, w["x"], w["dy"], N, y, dx, "16 x 2^20 fp32")
+
+
+def test_workspace_errors():
+    M, N = 4, 100000
+    x = torch.randn(M, N, device="cuda")
+    y = torch.empty_like(x)
+    need = xr.softmax_workspace_bytes(M, N, torch.float32)
+    # each direction's own need: a counts block and one slot per row chunk
+    nf = 256 + 8 * M * xr.plan("softmax_fwd_ws", M, N, torch.float32)["split"]
+    nb = 256 + 8 * M * xr.plan("softmax_bwd_ws", M, N, torch.float32)["split"]
+    assert nf > 256 and nb > 256 and need == max(nf, nb)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f, g = xr.lib.xr_softmax_fwd_ex, xr.lib.xr_softmax_bwd_ex
+    # too small
+    assert f(y.data_ptr(), N, x.data_ptr(), N, M, N, xr.F32, ws.data_ptr(), nf - 8, s) == 6
+    assert g(y.data_ptr(), N, y.data_ptr(), N, x.data_ptr(), N, M, N, xr.F32, ws.data_ptr(),
+             nb - 8, s) == 6
+    # the workspace inside an operand
+    assert f(y.data_ptr(), N, x.data_ptr(), N, M, N, xr.F32, x.data_ptr() + 64, need, s) == 5
+    assert g(y.data_ptr(), N, y.data_ptr(), N, x.data_ptr(), N, M, N, xr.F32,
+             y.data_ptr() + 4096, need, s) == 5
+    torch.cuda.synchronize()

@@ -115,3 +115,23 @@ def test_graph_softmax_and_layernorm():
         return [y, dx, yl, dxl, dw, db]
 
     _graph_case(run, [x, dy])
+
+
+def test_graph_softmax_split_rows():
+    """The softmax forward and backward over split rows (a workspace slot fill kernel, then
+    the row kernel, per call) captured and replayed."""
+    M, N = 8, 128256
+    x = to_device(synth.random_rows(15200, M, N, dtype="bf16", scale=2.0))
+    dy = to_device(synth.random_rows(15201, M, N, dtype="bf16", scale=1.0))
+    assert xr.plan("softmax_fwd_ws", M, N, torch.bfloat16)["split"] > 1
+    ws = torch.empty(xr.softmax_workspace_bytes(M, N, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+
+    def run(xx, dd):
+        xr.softmax_fwd(xx, y, workspace=ws)
+        xr.softmax_bwd(y, dd, dx, workspace=ws)
+        return [y, dx]
+
+    _graph_case(run, [x, dy])
