@@ -163,82 +163,95 @@ __device__ __forceinline__ Stats thread_stats(u32x4 (&v)[VPT], const Chunk<D>& c
   return {m, d};
 }
 
+// Wait for slot q of a split row's exchange (lane-private bounded poll): the published word,
+// or kPartialEmpty with ok cleared once the budget runs out.
+__device__ __forceinline__ uint64_t poll_slot(const uint64_t* slot, int& budget, bool& ok) {
+  uint64_t w;
+  while ((w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+         kPartialEmpty) {
+    if (--budget < 0) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return w;
+}
+
 // Split rows: publish this chunk's (m, d) in its slot of the row's S slots (one 64-bit
-// relaxed agent-scope store), then combine the pairs of all S chunks in chunk order, so every
-// chunk of the row gets bit-identical (m, d). Slots hold kPartialEmpty until published. The
-// wait is bounded: after kSpinLimit polls the chunk sets kFlagExchangeTimeout in *flags and
-// returns m = NaN, and once the flag is set no chunk waits again, so the grid always drains.
-// Called by every thread of the workgroup (thread 0 does the exchange; bcast is LDS).
+// relaxed agent-scope store), then combine the pairs of all S chunks. The first wave reads
+// the slots 64 at a time, one per lane (the polls overlap instead of queueing behind one
+// another), and combines them with the fixed butterfly of wave_reduce_stats, blocks in slot
+// order: the order never depends on timing, so every chunk of the row gets bit-identical
+// (m, d). Slots hold kPartialEmpty until published. The wait is bounded: after kSpinLimit
+// polls a lane gives up, the chunk sets kFlagExchangeTimeout in *flags and returns m = NaN,
+// and once the flag is set no chunk waits again, so the grid always drains. Called by every
+// thread of the workgroup (bcast is LDS).
 template <int THREADS>
 __device__ __forceinline__ Stats exchange_row_stats(Stats st, uint64_t* slots, int S, int chunk,
                                                     int32_t* flags, float* bcast) {
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x;
+  if (tid == 0)
     __hip_atomic_store(slots + chunk, pack_pair(st.m, st.d), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    float ms = kNegInf, ds = 0.f;
-    bool ok = true;
+  if (tid < kWave) {
     int budget = (__hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
                   kFlagExchangeTimeout) ? 0 : kSpinLimit;
-    for (int q = 0; q < S && ok; ++q) {
-      uint64_t w;
-      while ((w = __hip_atomic_load(slots + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-             kPartialEmpty) {
-        if (--budget < 0) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    bool ok = true;
+    Stats acc{kNegInf, 0.f};
+    for (int b = 0; b < S; b += kWave) {
+      Stats mine{kNegInf, 0.f};
+      if (b + tid < S && ok) {
+        const uint64_t w = poll_slot(slots + b + tid, budget, ok);
+        if (ok) mine = {pair_m(w), pair_d(w)};
       }
-      if (!ok) break;
-      const float mc = pair_m(w), dc = pair_d(w);
-      if (mc == kNegInf) continue;
-      const float mx = fmaxf(ms, mc);
-      ds = ((ms == kNegInf) ? 0.f : ds * exp2f((ms - mx) * kLog2e)) + dc * exp2f((mc - mx) * kLog2e);
-      ms = mx;
+      acc = combine(acc, wave_reduce_stats(mine));
     }
-    if (!ok) {
-      __hip_atomic_fetch_or(flags, kFlagExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ms = __builtin_nanf("");
+    if (__any(!ok)) {
+      if (tid == 0)
+        __hip_atomic_fetch_or(flags, kFlagExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      acc.m = __builtin_nanf("");
     }
-    bcast[0] = ms;
-    bcast[1] = ds;
+    if (tid == 0) {
+      bcast[0] = acc.m;
+      bcast[1] = acc.d;
+    }
   }
   __syncthreads();
   return {bcast[0], bcast[1]};
 }
 
 // Split rows of the softmax backward: publish this chunk's partial dot product and add the
-// S partials of the row in chunk order (so every chunk gets bit-identical sums). A published
-// word is the float's bits with 1 in the upper half, never kPartialEmpty. Same bounded wait
-// and timeout flag as exchange_row_stats (the sum is NaN after a timeout).
+// S partials of the row, read by the first wave 64 at a time and summed with the fixed
+// butterfly of wave_reduce (bit-identical sums in every chunk). A published word is the
+// float's bits with 1 in the upper half, never kPartialEmpty. Same bounded wait and timeout
+// flag as exchange_row_stats (the sum is NaN after a timeout).
 template <int THREADS>
 __device__ __forceinline__ float exchange_row_sum(float s, uint64_t* slots, int S, int chunk,
                                                   int32_t* flags, float* bcast) {
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x;
+  if (tid == 0)
     __hip_atomic_store(slots + chunk, (uint64_t)as_u32(s) | (1ull << 32), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    float t = 0.f;
-    bool ok = true;
+  if (tid < kWave) {
     int budget = (__hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
                   kFlagExchangeTimeout) ? 0 : kSpinLimit;
-    for (int q = 0; q < S && ok; ++q) {
-      uint64_t w;
-      while ((w = __hip_atomic_load(slots + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-             kPartialEmpty) {
-        if (--budget < 0) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    bool ok = true;
+    float acc = 0.f;
+    for (int b = 0; b < S; b += kWave) {
+      float mine = 0.f;
+      if (b + tid < S && ok) {
+        const uint64_t w = poll_slot(slots + b + tid, budget, ok);
+        if (ok) mine = as_f32((uint32_t)w);
       }
-      if (!ok) break;
-      t += as_f32((uint32_t)w);
+      acc += wave_reduce(mine, OpAdd());
     }
-    if (!ok) {
-      __hip_atomic_fetch_or(flags, kFlagExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      t = __builtin_nanf("");
+    if (__any(!ok)) {
+      if (tid == 0)
+        __hip_atomic_fetch_or(flags, kFlagExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      acc = __builtin_nanf("");
     }
-    bcast[0] = t;
+    if (tid == 0) bcast[0] = acc;
   }
   __syncthreads();
   return bcast[0];
@@ -253,6 +266,54 @@ __device__ __forceinline__ void online_add(Stats& st, float x) {
   } else if (x != kNegInf) {
     st.d += __builtin_amdgcn_exp2f((x - st.m) * kLog2e);
   }
+}
+
+// ----------------------------------------------------------------------------- stream rows
+// The stream kernels walk a row in windows of kStreamWindow vectors (one buffer resource
+// each, so offsets stay 32-bit for rows of any length), kStreamUnroll vectors in flight
+// per thread.
+constexpr int64_t kStreamWindow = int64_t(1) << 26;  // 1 GiB
+constexpr int kStreamUnroll = 4;
+
+// Vector v of chunk c with its out-of-row elements replaced by `fill` (a vector at or past
+// the chunk's end is all fill).
+template <int D>
+__device__ __forceinline__ u32x4 vec_masked(u32x4 x, int v, const Chunk<D>& c, uint32_t fill) {
+  if (v >= c.nvec) return splat(fill);
+  if (v == c.head) x = mask_vec<D>(x, c.h0, c.h1, fill);
+  if (v == c.tail) x = mask_vec<D>(x, c.t0, c.t1, fill);
+  return x;
+}
+
+// One vector folded into a running (m, d): the vector's maximum, one rescale of the running
+// sum, then the vector's terms. -inf elements add nothing; NaN elements make d NaN.
+template <int D>
+__device__ __forceinline__ void online_add_vec(Stats& st, u32x4 x) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  float vm = kNegInf;
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, elem<D>(x, e));
+  const float mn = fmaxf(st.m, vm);
+  const float mnL = mn * kLog2e;
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) {
+    const float xe = elem<D>(x, e);
+    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(xe, kLog2e, -mnL));
+    s += xe == kNegInf ? 0.f : t;
+  }
+  st.d = (st.m == mn ? st.d : st.d * __builtin_amdgcn_exp2f((st.m - mn) * kLog2e)) + s;
+  st.m = mn;
+}
+
+// Store vector v of an output chunk: whole, or only its in-row elements for the partial
+// first / last vector.
+template <int D>
+__device__ __forceinline__ void store_vec(const Chunk<D>& c, int v, const u32x4& bits) {
+  const uint32_t off = (uint32_t)v * 16u;
+  if (v == c.head) store_partial<D>(c.rsrc, off, bits, c.h0, c.h1);
+  else if (v == c.tail) store_partial<D>(c.rsrc, off, bits, c.t0, c.t1);
+  else buf_store(c.rsrc, off, bits);
 }
 
 // exp2(x*log2e - coff) for every element of one slot, in the element type, XOR-ed with

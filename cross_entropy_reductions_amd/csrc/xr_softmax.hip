@@ -126,34 +126,76 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+// Two-pass stream form (rows too long for the row-resident shapes, rows split over no
+// workspace, or operands at different addresses modulo 16): one workgroup per row, a first
+// pass folding every vector into per-thread online (m, d) pairs, the workgroup combine, then
+// a second pass that re-reads the row and writes it. 16-byte vector loads in the input's own
+// alignment; vector stores when the output shares it, element stores otherwise.
 template <int D, bool NLL>
 __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(SoftmaxFwdParams p) {
-  __shared__ float2 red[kStreamThreads / kWave];
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int T = kStreamThreads;
+  constexpr int U = kStreamUnroll;
+  __shared__ float2 red[T / kWave];
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const char* row = p.x + r * p.ldx_bytes;
   char* out = p.y + r * p.ldy_bytes;
   const int tid = threadIdx.x;
-  auto ld = [&](int64_t j) -> float {
-    if (D == kF32) return reinterpret_cast<const float*>(row)[j];
-    return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
-  };
-  // NLL: the gathered element, read before the barriers below (y may be exactly x).
+  const int lead = (int)(((uintptr_t)row & 15u) / Elt<D>::kBytes);
+  const bool same = (((uintptr_t)row ^ (uintptr_t)out) & 15u) == 0;
+  const int64_t nv = (lead + p.N + EPV - 1) / EPV;
+  // NLL: the gathered element, read before the barrier below (y may be exactly x).
   const int64_t ix = NLL ? p.idx[r] : -1;
   const bool in_row = ix >= 0 && ix < p.N;
-  const float xi = (NLL && tid == 0 && in_row) ? ld(ix) : 0.f;
-  // one pass for (m, d): the online-softmax rule per thread, then the workgroup combine
+  float xi = 0.f;
+  if (NLL && tid == 0 && in_row)
+    xi = D == kF32 ? reinterpret_cast<const float*>(row)[ix]
+                   : as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[ix] << 16);
   Stats st{kNegInf, 0.f};
-  for (int64_t j = tid; j < p.N; j += kStreamThreads) online_add(st, ld(j));
-  st = block_reduce_stats<kStreamThreads>(st, red);
-  const float m = st.m, d = st.d;
-  // In place (y == x) is safe: every element's output depends only on itself and (m, d),
-  // and all reads of the statistics pass finished before the barrier above.
-  const float coff = NLL ? m + logf(d) : m * kLog2e + log2f(d);
-  for (int64_t j = tid; j < p.N; j += kStreamThreads) {
-    const float val = NLL ? coff - ld(j) : __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
-    if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
-    else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+    const Chunk<D> cx(row, p.N, lo, kStreamWindow);
+    for (int v0 = tid; v0 < cx.nvec; v0 += U * T) {
+      u32x4 a[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyDefault>(cx.rsrc, (uint32_t)(v0 + q * T) * 16u);
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        online_add_vec<D>(st, vec_masked<D>(a[q], v0 + q * T, cx, Elt<D>::kNegInfWord));
+    }
+  }
+  st = block_reduce_stats<T>(st, red);
+  // In place (y == x) is safe: each vector is re-read and written by the same thread, and
+  // all reads of the statistics pass finished before the barrier above.
+  const float coff = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
+  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+    const Chunk<D> cx(row, p.N, lo, kStreamWindow);
+    const Chunk<D> cy(out, p.N, lo, kStreamWindow);  // the output's geometry when `same`
+    for (int v0 = tid; v0 < cx.nvec; v0 += U * T) {
+      u32x4 a[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyNT>(cx.rsrc, (uint32_t)(v0 + q * T) * 16u);
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int v = v0 + q * T;
+        if (v >= cx.nvec) break;
+        const u32x4 o = NLL ? nll_slot<D>(a[q], coff) : exp_slot<D>(a[q], coff);
+        if (same) {
+          store_vec<D>(cy, v, o);
+        } else {
+          // element stores at the output's own addresses
+          const int e0 = v == cx.head ? cx.h0 : 0;
+          const int e1 = v == cx.head ? cx.h1 : (v == cx.tail ? cx.t1 : EPV);
+          const int64_t j0 = (lo + v) * EPV - lead;  // row index of the vector's element 0
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            if (e < e0 || e >= e1) continue;
+            if (D == kF32) reinterpret_cast<uint32_t*>(out)[j0 + e] = o[e];
+            else reinterpret_cast<uint16_t*>(out)[j0 + e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
   }
   if (NLL && tid == 0) p.loss[r] = in_row ? round_elem<D>(coff - xi) : __builtin_nanf("");
 }
@@ -294,26 +336,83 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+// Two-pass stream form of the backward: the dot product, the workgroup sum, then a second
+// pass that re-reads y and dy and writes dx. 16-byte vectors when y, dy and dx share their
+// address modulo 16; element accesses otherwise.
 template <int D>
 __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream_kernel(SoftmaxBwdParams p) {
-  __shared__ float red[kStreamThreads / kWave];
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int T = kStreamThreads;
+  constexpr int U = kStreamUnroll;
+  __shared__ float red[T / kWave];
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const char* yr = p.y + r * p.ldy_bytes;
   const char* dr = p.dy + r * p.lddy_bytes;
   char* out = p.dx + r * p.lddx_bytes;
   const int tid = threadIdx.x;
-  auto ld = [&](const char* row, int64_t j) -> float {
-    if (D == kF32) return reinterpret_cast<const float*>(row)[j];
-    return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
-  };
-  float s = 0.f;
-  for (int64_t j = tid; j < p.N; j += kStreamThreads) s += ld(yr, j) * ld(dr, j);
-  s = block_reduce<kStreamThreads>(s, OpAdd(), red);
-  for (int64_t j = tid; j < p.N; j += kStreamThreads) {
-    const float val = ld(yr, j) * (ld(dr, j) - s);
-    if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
-    else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+  const bool same = ((((uintptr_t)yr ^ (uintptr_t)dr) | ((uintptr_t)yr ^ (uintptr_t)out)) & 15u) == 0;
+  if (!same) {
+    auto ld = [&](const char* row, int64_t j) -> float {
+      if (D == kF32) return reinterpret_cast<const float*>(row)[j];
+      return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
+    };
+    float s = 0.f;
+    for (int64_t j = tid; j < p.N; j += T) s += ld(yr, j) * ld(dr, j);
+    s = block_reduce<T>(s, OpAdd(), red);
+    for (int64_t j = tid; j < p.N; j += T) {
+      const float val = ld(yr, j) * (ld(dr, j) - s);
+      if (D == kF32) reinterpret_cast<float*>(out)[j] = val;
+      else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+    }
+    return;
+  }
+  const int lead = (int)(((uintptr_t)yr & 15u) / Elt<D>::kBytes);
+  const int64_t nv = (lead + p.N + EPV - 1) / EPV;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+    const Chunk<D> cy(yr, p.N, lo, kStreamWindow);
+    const Chunk<D> cd(dr, p.N, lo, kStreamWindow);
+    for (int v0 = tid; v0 < cy.nvec; v0 += U * T) {
+      u32x4 a[U], b[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        a[q] = buf_load<kPolicyDefault>(cy.rsrc, (uint32_t)(v0 + q * T) * 16u);
+        b[q] = buf_load<kPolicyDefault>(cd.rsrc, (uint32_t)(v0 + q * T) * 16u);
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        // out-of-row elements count as 0 in both operands
+        const u32x4 ya = vec_masked<D>(a[q], v0 + q * T, cy, 0u);
+        const u32x4 da = vec_masked<D>(b[q], v0 + q * T, cy, 0u);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) s4[e & 3] = __builtin_fmaf(elem<D>(ya, e), elem<D>(da, e), s4[e & 3]);
+      }
+    }
+  }
+  const float s = block_reduce<T>((s4[0] + s4[1]) + (s4[2] + s4[3]), OpAdd(), red);
+  // dx may be exactly y or dy: each vector is re-read and written by the same thread.
+  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+    const Chunk<D> cy(yr, p.N, lo, kStreamWindow);
+    const Chunk<D> cd(dr, p.N, lo, kStreamWindow);
+    const Chunk<D> cx(out, p.N, lo, kStreamWindow);
+    for (int v0 = tid; v0 < cy.nvec; v0 += U * T) {
+      u32x4 a[U], b[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        a[q] = buf_load<kPolicyNT>(cy.rsrc, (uint32_t)(v0 + q * T) * 16u);
+        b[q] = buf_load<kPolicyNT>(cd.rsrc, (uint32_t)(v0 + q * T) * 16u);
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int v = v0 + q * T;
+        if (v >= cy.nvec) break;
+        OutVec<D> o;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a[q], e) * (elem<D>(b[q], e) - s);
+        store_vec<D>(cx, v, o.bits());
+      }
+    }
   }
 }
 

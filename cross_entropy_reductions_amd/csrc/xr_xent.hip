@@ -233,48 +233,82 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
-// Stream fallback: one workgroup per row, element-wise, max / sum / write passes over memory.
+// Stream fallback (sizes no row-resident shape takes): one workgroup per row, two passes
+// over memory in 16-byte vectors: per-thread online (m, d) pairs and their workgroup
+// combine, then the gradient written over the logits (each vector re-read and written by
+// the same thread).
 template <int D>
 __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams p) {
-  __shared__ float2 red[kStreamThreads / kWave];
+  constexpr int EPV = Elt<D>::kPerVec;
+  constexpr int T = kStreamThreads;
+  constexpr int U = kStreamUnroll;
+  __shared__ float2 red[T / kWave];
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const int64_t t = p.target[r];
   char* row = p.logits + r * p.ld_bytes;
   const int tid = threadIdx.x;
-  auto ld = [&](int64_t j) -> float {
-    if (D == kF32) return reinterpret_cast<const float*>(row)[j];
-    return as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[j] << 16);
-  };
-  auto st = [&](int64_t j, float val) {
-    if (D == kF32) reinterpret_cast<float*>(row)[j] = val;
-    else reinterpret_cast<uint16_t*>(row)[j] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
-  };
+  const int lead = (int)(((uintptr_t)row & 15u) / Elt<D>::kBytes);
+  const int64_t nv = (lead + p.V + EPV - 1) / EPV;
   if (t == p.ignore_index || t < 0 || t >= p.V) {
-    for (int64_t j = tid; j < p.V; j += kStreamThreads) st(j, 0.f);
+    for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+      const Chunk<D> c(row, p.V, lo, kStreamWindow);
+      for (int v = tid; v < c.nvec; v += T) store_vec<D>(c, v, splat(0u));
+    }
     if (tid == 0) p.row_loss[r] = 0.f;
     return;
   }
-  const int32_t n = p.reduction == kReduceMean ? p.ws_counts[0] : 1;
+  const bool mean = p.reduction == kReduceMean;
+  const int32_t n = mean ? p.ws_counts[0] : 1;
+  const float inv_n = mean ? 1.0f / (float)n : 1.0f;
   const float sc = p.gscale ? p.gscale[r * p.gstride] : 1.0f;
   const bool neg = __builtin_signbit(sc) != 0;
-  const float xt = ld(t);
-  // one pass for (m, d): the online-softmax rule per thread, then the workgroup combine
-  Stats sd{kNegInf, 0.f};
-  for (int64_t j = tid; j < p.V; j += kStreamThreads) online_add(sd, ld(j));
-  sd = block_reduce_stats<kStreamThreads>(sd, red);
-  const float m = sd.m, d = sd.d;
-  // Every thread has read xt and the row before the barrier inside the reduction.
-  const float coff = m * kLog2e + log2f(d) + log2f((float)n) - log2f(fabsf(sc));
-  for (int64_t j = tid; j < p.V; j += kStreamThreads) {
-    float g;
-    if (j == t) {
-      g = (exp2f((xt - m) * kLog2e) / d - 1.0f) / (float)n * sc;
-    } else {
-      g = __builtin_amdgcn_exp2f(__builtin_fmaf(ld(j), kLog2e, -coff));
-      if (neg) g = -g;
+  // the target logit, read by every thread before the barrier below
+  const float xt = D == kF32 ? reinterpret_cast<const float*>(row)[t]
+                             : as_f32((uint32_t)reinterpret_cast<const uint16_t*>(row)[t] << 16);
+  Stats st{kNegInf, 0.f};
+  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+    const Chunk<D> c(row, p.V, lo, kStreamWindow);
+    for (int v0 = tid; v0 < c.nvec; v0 += U * T) {
+      u32x4 a[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyDefault>(c.rsrc, (uint32_t)(v0 + q * T) * 16u);
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        online_add_vec<D>(st, vec_masked<D>(a[q], v0 + q * T, c, Elt<D>::kNegInfWord));
     }
-    st(j, g);
+  }
+  st = block_reduce_stats<T>(st, red);
+  const float m = st.m, d = st.d;
+  // gradient exp2(x*log2e - coff) = s p_j / n for j != target; s (p_t - 1) / n at the target
+  const float coff = m * kLog2e + log2f(d) + log2f((float)n) - log2f(fabsf(sc));
+  const float gt = (exp2f((xt - m) * kLog2e) / d - 1.0f) * inv_n * sc;
+  const int64_t tv = (lead + t) / EPV;  // the target's row vector and element in it
+  const int te = (int)((lead + t) % EPV);
+  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+    const Chunk<D> c(row, p.V, lo, kStreamWindow);
+    for (int v0 = tid; v0 < c.nvec; v0 += U * T) {
+      u32x4 a[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyNT>(c.rsrc, (uint32_t)(v0 + q * T) * 16u);
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int v = v0 + q * T;
+        if (v >= c.nvec) break;
+        OutVec<D> o;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float g = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(a[q], e), kLog2e, -coff));
+          o.v[e] = neg ? -g : g;
+        }
+        if (lo + v == tv) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e)
+            if (e == te) o.v[e] = gt;
+        }
+        store_vec<D>(c, v, o.bits());
+      }
+    }
   }
   if (tid == 0) p.row_loss[r] = m + logf(d) - xt;
 }

@@ -209,3 +209,28 @@ def test_workspace_errors():
     assert g(y.data_ptr(), N, y.data_ptr(), N, x.data_ptr(), N, M, N, xr.F32,
              y.data_ptr() + 4096, need, s) == 5
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stream_long_rows_without_workspace(orc, dtype):
+    """Rows longer than any row-resident shape and no workspace: the two-pass stream
+    kernels (vector loads), with the output sharing the input's alignment (vector stores)
+    and not sharing it (element stores)."""
+    M, N = 3, (1 << 20) + 5
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    assert xr.plan("softmax_fwd", M, N, dt)["path"] == "stream"
+    assert xr.plan("softmax_bwd", M, N, dt)["path"] == "stream"
+    x = synth.random_rows(19600, M, N, dtype=dtype, scale=3.0)
+    dy = synth.random_rows(19601, M, N, dtype=dtype, scale=1.0)
+    y, dx = fwd_bwd(x, dy, N, workspace=False)
+    check(orc, x, dy, N, y, dx, f"stream {dtype}")
+    # an output one element further along each row: other alignment, element stores
+    xd, dyd = to_device(x), to_device(dy)
+    yo = torch.empty((M, N + 1), dtype=dt, device="cuda")[:, 1:]
+    xr.softmax_fwd(xd, yo, workspace=False)
+    dxo = torch.empty((M, N + 1), dtype=dt, device="cuda")[:, 1:]
+    xr.softmax_bwd(yo, dyd, dxo, workspace=False)
+    torch.cuda.synchronize()
+    y2 = to_host(yo)
+    check_output(y2, orc.softmax_fwd(x), f"stream {dtype} other alignment forward")
+    check_output(to_host(dxo), orc.softmax_bwd(y2, dy), f"stream {dtype} other alignment backward")
