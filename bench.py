@@ -115,12 +115,18 @@ def measured_traffic():
     return c.get("traffic_bytes_per_launch")
 
 
+# Timing-only events: no system-scope fence (L2 writeback and invalidate) when they are
+# recorded, so they neither add that work between the kernels they bracket nor time it.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvents:
     """Raw hipEvent_t handles (the library records them on its own launch stream)."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
@@ -128,8 +134,8 @@ class HipEvents:
 
     def create(self) -> int:
         e = ctypes.c_void_p()
-        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         return e.value
 
     def elapsed_ms(self, a: int, b: int) -> float:
