@@ -291,7 +291,7 @@ def run_element_mul(args, name: str) -> dict:
     wall, kernel_ms = _timed(HipEvents(), args.steps, args.warmup, launch)
     bmin = 2 * M * V * 2 + 4
     out = _line(args, name, bmin, M, wall, kernel_ms, "element_mul_kernel",
-                {"M": M, "V": V, "bytes_min": bmin, "threads": 256, "vec_per_thread": 8},
+                {"M": M, "V": V, "bytes_min": bmin, "threads": 1024, "vec_per_thread": 8},
                 "bf16")
     return out
 
