@@ -266,7 +266,11 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
     p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
   } else if (other_split || (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF)) {
-    if (M * S > 0x7FFFFFFF) {  // (only the cross-entropy has a persistent split form)
+    // (only the cross-entropy has a persistent split form). A row's S chunks must be able
+    // to be resident together, or its first chunks could wait for chunks that cannot start
+    // until they finish: more chunks than the GPU holds workgroups of this shape (rows of
+    // tens of MB) take the stream kernels.
+    if (M * S > 0x7FFFFFFF || S > resident) {
       if (want) return XR_ERR_SHAPE;
       Plan q;
       q.grid = M;

@@ -234,3 +234,39 @@ def test_stream_long_rows_without_workspace(orc, dtype):
     y2 = to_host(yo)
     check_output(y2, orc.softmax_fwd(x), f"stream {dtype} other alignment forward")
     check_output(to_host(dxo), orc.softmax_bwd(y2, dy), f"stream {dtype} other alignment backward")
+
+
+def test_plans_for_rows_beyond_the_resident_chunks():
+    """A split row's chunks must be able to be resident together; rows of hundreds of MB,
+    whose chunks could not, take the stream kernels, rows of tens of MB still split."""
+    bf = torch.bfloat16
+    assert xr.plan("softmax_fwd_ws", 1, 1 << 24, bf)["path"] == "split"
+    for op in ("softmax_fwd_ws", "softmax_bwd_ws", "xent", "nll_fwd"):
+        assert xr.plan(op, 1, 1 << 29, bf)["path"] == "stream", op
+
+
+def test_stream_row_across_windows(orc):
+    """One bf16 row of 2^29 + 37 elements (just over 1 GiB): the stream kernels walk it in
+    1 GiB windows, so the second window starts mid-row; every element is checked against
+    the oracle, slice by slice."""
+    M, N = 1, (1 << 29) + 37
+    x = synth.random_rows(19700, M, N, dtype="bf16", scale=3.0)
+    assert xr.plan("softmax_fwd", M, N, torch.bfloat16)["path"] == "stream"
+    xd = to_device(x)
+    y = xr.softmax_fwd(xd, workspace=False)
+    torch.cuda.synchronize()
+    y_h = to_host(y)
+    del xd, y
+    want = orc.softmax_fwd(x)
+    rmax = float(np.max(want))
+    step = 1 << 24
+    worst = 0.0
+    for a in range(0, N, step):
+        g = widen(y_h[:, a:a + step])
+        o = want[:, a:a + step]
+        denom = np.maximum(np.abs(o), max(2.0 ** -7 * rmax, 5e-5 * rmax))
+        worst = max(worst, float(np.max(np.abs(g - o) / denom)))
+    print(f"2^29 + 37 row: worst scaled error {worst:.3e}", flush=True)
+    assert worst <= 2e-2
+    s = float(np.sum(widen(y_h)))
+    assert abs(s - 1.0) < 1e-2, s
