@@ -2,7 +2,7 @@
 
 A thin ctypes binding over ``libxr.so`` (``include/xr.h``): every function here
 checks and marshals its torch tensors into the C ABI call of the same name
-(``softmax_fwd`` -> ``xr_softmax_fwd``, ``softmax_bwd`` -> ``xr_softmax_bwd``,
+(``softmax_fwd`` -> ``xr_softmax_fwd_ex``, ``softmax_bwd`` -> ``xr_softmax_bwd_ex``,
 ``nll_fwd`` -> ``xr_nll_fwd``,
 ``xent_fwd_bwd`` -> ``xr_xent_fwd_bwd_ex``, ``element_mul`` -> ``xr_element_mul``, ...).
 All of the computation runs in the library's HIP kernels; PyTorch only provides device

@@ -176,8 +176,14 @@ const void* ln_dwdb_kernel_ptr(int dtype);
 
 const void* bsr_softmax_bwd_kernel_ptr(int dtype);
 // Block-sparse backward: workgroup size, and listed blocks per row held in registers.
-constexpr int kBsrThreads = 256;
-constexpr int kBsrResident = 12;
+#ifndef XR_BSR_THREADS
+#define XR_BSR_THREADS 256
+#endif
+#ifndef XR_BSR_RESIDENT
+#define XR_BSR_RESIDENT 12
+#endif
+constexpr int kBsrThreads = XR_BSR_THREADS;
+constexpr int kBsrResident = XR_BSR_RESIDENT;
 
 // Workgroup size of the stream, scan and mean kernels.
 constexpr int kStreamThreads = 256;
