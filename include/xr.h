@@ -18,7 +18,9 @@
  *     and the status says which argument is wrong. No C++ exception crosses this ABI.
  *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
  *   - The library keeps no state across calls except a per-device cache of device
- *     properties, and the process-wide overrides of xr_set_option().
+ *     properties, the process-wide overrides of xr_set_option() and the profiling events
+ *     of xr_set_profile_events(). Workspaces are the caller's and hold nothing between
+ *     calls.
  */
 #ifndef XR_H_
 #define XR_H_
@@ -42,7 +44,7 @@ typedef enum xr_status {
   XR_ERR_STRIDE = 3,    /* a row stride is smaller than the number of columns */
   XR_ERR_DTYPE = 4,     /* unknown dtype */
   XR_ERR_ALIAS = 5,     /* an output overlaps an input without being exactly the same matrix */
-  XR_ERR_WORKSPACE = 6, /* workspace NULL or smaller than xr_xent_workspace_bytes() */
+  XR_ERR_WORKSPACE = 6, /* a required workspace is NULL or smaller than its *_bytes() query */
   XR_ERR_ALIGN = 7,     /* a tensor pointer is not aligned to its element size */
   XR_ERR_DEVICE = 8,    /* no usable HIP device, or a device query failed */
   XR_ERR_LAUNCH = 9,    /* a kernel launch failed (the HIP error is reported by HIP) */
