@@ -205,6 +205,35 @@ def softmax_bwd(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = No
     return out
 
 
+class SoftmaxFunction(torch.autograd.Function):
+    """Softmax over the last dimension as a torch.autograd.Function, the way the Triton
+    fused-softmax kernels of the "python sum function examples" page pair a forward with
+    the fused `_backward`: the forward saves y, the backward computes y * (dy - sum(y * dy))
+    per row. Rows are split over workgroups through a workspace when that pays."""
+
+    @staticmethod
+    def forward(ctx, x):
+        x2 = x.reshape(-1, x.shape[-1])
+        if x2.shape[-1] > 1 and x2.stride(-1) != 1:
+            x2 = x2.contiguous()
+        y = softmax_fwd(x2)
+        ctx.save_for_backward(y)
+        return y.reshape(x.shape)
+
+    @staticmethod
+    def backward(ctx, dy):
+        (y,) = ctx.saved_tensors
+        dy2 = dy.reshape(-1, dy.shape[-1])
+        if dy2.shape[-1] > 1 and dy2.stride(-1) != 1:
+            dy2 = dy2.contiguous()
+        return softmax_bwd(y, dy2).reshape(dy.shape)
+
+
+def softmax(x: torch.Tensor) -> torch.Tensor:
+    """Autograd-aware softmax over the last dimension (``SoftmaxFunction``)."""
+    return SoftmaxFunction.apply(x)
+
+
 def bsr_softmax_bwd(y: torch.Tensor, dx: torch.Tensor, lut: torch.Tensor, n_brows: int,
                     n_blocks: int, block: int, scale: float = 1.0, *, stream=None) -> torch.Tensor:
     """Block-sparse softmax backward in place: dx (Z, stride) holds the incoming gradient and

@@ -270,3 +270,25 @@ def test_stream_row_across_windows(orc):
     assert worst <= 2e-2
     s = float(np.sum(widen(y_h)))
     assert abs(s - 1.0) < 1e-2, s
+
+
+@pytest.mark.parametrize("shape,dtype", [((3, 5, 1000), "f32"), ((2, 3, 70001), "bf16"),
+                                         ((4, 300000), "f32")],
+                         ids=["3x5x1000-f32", "2x3x70001-bf16", "4x300000-f32"])
+def test_softmax_autograd(orc, shape, dtype):
+    """xr.softmax as an autograd function: the forward against the oracle, and x.grad for an
+    upstream gradient w against the oracle's backward on the GPU's own y."""
+    N = shape[-1]
+    M = int(np.prod(shape[:-1]))
+    x_h = synth.random_rows(19800 + N % 89, M, N, dtype=dtype, scale=3.0)
+    w_h = synth.random_rows(19801 + N % 89, M, N, dtype=dtype, scale=1.0)
+    x = to_device(x_h).reshape(shape).requires_grad_(True)
+    w = to_device(w_h).reshape(shape)
+    y = xr.softmax(x)
+    (y * w).sum().backward()
+    torch.cuda.synchronize()
+    y_h = to_host(y.detach().reshape(M, N))
+    check_output(y_h, orc.softmax_fwd(x_h), f"autograd {shape} forward")
+    # the upstream gradient is w rounded to the dtype: exactly w_h
+    check_output(to_host(x.grad.reshape(M, N)), orc.softmax_bwd(y_h, w_h),
+                 f"autograd {shape} backward")
