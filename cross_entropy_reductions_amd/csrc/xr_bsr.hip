@@ -14,12 +14,19 @@
 // a wave reads 64 / TPR consecutive rows of a block, i.e. one contiguous span of it. Up to
 // kBsrResident blocks per row stay in registers between the dot product and the write (one
 // read of y and dx, one write); longer rows are read twice. The dot product is a butterfly
-// over the row's TPR lanes (the same bits on every lane, no LDS, no barrier). Table reads
-// and data accesses go through buffer resources sized to the table and to one batch's
-// blocks, so a bad table entry reads zeros and writes nothing instead of faulting.
+// over the row's TPR lanes (the same bits on every lane, no LDS, no barrier). The table is
+// read with scalar loads (it is uniform across the workgroup and read-only for the kernel,
+// which the host checks: it may not overlap dx), every index bounded by the table length;
+// data accesses go through buffer resources sized to one batch's blocks, so a bad block
+// index reads zeros and writes nothing instead of faulting.
 #include "xr_rows.h"
 
 namespace xr {
+
+// The table through the constant address space: uniform loads become scalar loads, which
+// complete apart from the vector loads of the data (a wait for a table entry does not wait
+// for data loads issued before it).
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
 
 template <int D>
 __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))) void bsr_softmax_bwd_kernel(BsrParams p) {
@@ -38,9 +45,10 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int lane = tid % tpr;
   const bool active = tid < R * tpr && i < block;
 
-  const Rsrc lut = make_rsrc(p.lut, (uint32_t)p.lut_len * 4u);
-  const int32_t size = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(lut, (int)(br * 8), 0, 0);
-  const int32_t offset = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(lut, (int)(br * 8 + 4), 0, 0);
+  // words 2 br and 2 br + 1 lie inside the table: the host checks lut_len >= 2 n_brows
+  ConstI32* lut = (ConstI32*)p.lut;
+  const int32_t size = lut[2 * br];
+  const int32_t offset = lut[2 * br + 1];
   // listed blocks, bounded by the entries the table actually holds after `offset`
   const int64_t avail = offset >= 0 && offset <= p.lut_len ? (p.lut_len - offset) / 4 : 0;
   const int n = size > 0 ? (int)(size < avail ? size : avail) : 0;
@@ -49,12 +57,18 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
   const uint32_t in_block = (uint32_t)((i * block + lane * EPV) * Elt<D>::kBytes);
   const uint32_t block_bytes = (uint32_t)(block * block * Elt<D>::kBytes);
 
-  // byte offset of this lane's vector in listed block k (kOffNone: no access)
-  auto vec_off = [&](int k) -> uint32_t {
-    const int32_t bid = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
-        lut, (int)((int64_t)(offset + 4 * k) * 4), 0, 0);
-    if (!active || bid < 0 || bid >= p.n_blocks) return kOffNone;
-    return (uint32_t)bid * block_bytes + in_block;
+  // Byte offsets of this lane's vector in listed blocks k0 .. k0 + NB - 1 (kOffNone: no
+  // access; n >= 1). The table entries are read without branches (indices clamped to the
+  // last listed block, which lies inside the table) so the scalar loads issue together.
+  auto vec_offs = [&](int k0, uint32_t (&vo)[NB]) {
+    int32_t bid[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) bid[q] = lut[offset + 4 * min(k0 + q, n - 1)];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+      vo[q] = (!active || k0 + q >= n || bid[q] < 0 || bid[q] >= p.n_blocks)
+                  ? kOffNone
+                  : (uint32_t)bid[q] * block_bytes + in_block;
   };
 
   auto dot = [&](u32x4 a, u32x4 c, float acc) {
@@ -78,13 +92,14 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
     return s;
   };
 
+  if (n == 0) return;  // nothing listed: nothing to read or write
   if (n <= NB) {
     // every listed block's vector stays in registers: one read of y and dx, one write
     u32x4 vy[NB], vd[NB];
     uint32_t vo[NB];
+    vec_offs(0, vo);
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      vo[q] = q < n ? vec_off(q) : kOffNone;
       vy[q] = buf_load<kPolicyDefault>(ry, vo[q]);
       vd[q] = buf_load<kPolicyDefault>(rd, vo[q]);
     }
@@ -95,16 +110,22 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
     for (int q = 0; q < NB; ++q) buf_store(rd, vo[q], out(vy[q], vd[q], s));
   } else {
-    // longer rows: the dot product over every listed block, then a second read to write
+    // longer rows: the dot product over every listed block, then a second read to write,
+    // NB blocks at a time
     float s = 0.f;
-    for (int k = 0; k < n; ++k) {
-      const uint32_t o = vec_off(k);
-      s = dot(buf_load<kPolicyDefault>(ry, o), buf_load<kPolicyDefault>(rd, o), s);
+    uint32_t vo[NB];
+    for (int k0 = 0; k0 < n; k0 += NB) {
+      vec_offs(k0, vo);
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+        s = dot(buf_load<kPolicyDefault>(ry, vo[q]), buf_load<kPolicyDefault>(rd, vo[q]), s);
     }
     s = row_sum(s);
-    for (int k = 0; k < n; ++k) {
-      const uint32_t o = vec_off(k);
-      buf_store(rd, o, out(buf_load<kPolicyDefault>(ry, o), buf_load<kPolicyDefault>(rd, o), s));
+    for (int k0 = 0; k0 < n; k0 += NB) {
+      vec_offs(k0, vo);
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+        buf_store(rd, vo[q], out(buf_load<kPolicyDefault>(ry, vo[q]), buf_load<kPolicyDefault>(rd, vo[q]), s));
     }
   }
 }
