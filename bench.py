@@ -13,7 +13,7 @@ the library records around that launch on its stream; `cpu_baseline` times the f
 oracle on the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
-                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr]
+                    [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
                     [--reduction mean|sum|none]
                     [--grad-scale S] [--rows M]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
@@ -27,7 +27,10 @@ gradient write; `c4-mul` times the backward's element_mul (the stored gradient t
 upstream gradient of 0.5) over the 16384 x 128256 bf16 matrix; `c4-nll` the negative
 log-softmax forward with a gathered loss over the same matrix, into a separate output;
 `ln` a layer norm forward + backward (both stages) over 16384 x 8192 bf16 rows; `bsr` the
-block-sparse softmax backward over 32 causal 4096 x 4096 maps of 64 x 64 bf16 blocks.
+block-sparse softmax backward over 32 causal 4096 x 4096 maps of 64 x 64 bf16 blocks;
+`sm-vocab` / `sm-few` the softmax forward + backward over split rows (4096 x 128256 bf16,
+16 x 2^20 fp32) through one workspace. The softmax workloads time the oracle's softmax
+(forward, then backward) as their CPU baseline.
 """
 from __future__ import annotations
 
@@ -182,6 +185,47 @@ def cpu_baseline(workload: dict, rows: int, min_seconds: float = 10.0) -> dict:
             "sample": f"first {rows} of {workload['M']} rows of the same workload "
                       f"(V={V} {workload['dtype']}): float64 count, loss, gradient and mean, "
                       f"{passes} whole passes"}
+
+
+def cpu_baseline_softmax(workload: dict, rows: int, min_seconds: float = 10.0) -> dict:
+    """The oracle's softmax forward (and, when the workload has dy, its backward on the
+    forward's output stored in the workload's dtype) on the first `rows` rows, whole passes
+    repeated until `min_seconds` have elapsed; the rate counts the same minimal bytes as
+    the GPU line."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    orc = oracle.get()
+    M, N = workload["M"], workload["N"]
+    rows = min(rows, M)
+    x = workload["x"][:rows]
+    dy = workload["dy"][:rows] if "dy" in workload else None
+    bf16 = workload["dtype"] == "bf16"
+    elt = 2 if bf16 else 4
+    per_pass = rows * N * elt * (2 + (3 if dy is not None else 0))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for r0 in range(0, rows, 256):
+            y = orc.softmax_fwd(x[r0:r0 + 256])
+            if dy is not None:
+                ys = (synth.bf16_bits_from_f32(y.astype(np.float32)) if bf16
+                      else y.astype(np.float32))
+                orc.softmax_bwd(ys, dy[r0:r0 + 256])
+        passes += 1
+        sec = time.perf_counter() - t0
+        if sec >= min_seconds:
+            break
+    return {"value": round(per_pass * passes / sec / 1e9, 3), "unit": "GB/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "rows_per_s": round(rows * passes / sec, 1), "seconds": round(sec, 3),
+            "sample": f"first {rows} of {M} rows of the same workload (N={N} "
+                      f"{workload['dtype']}): float64 softmax forward"
+                      + (", its output stored in the dtype, and the backward"
+                         if dy is not None else "")
+                      + f", {passes} whole passes"}
 
 
 def _device_matrix(torch, a, dev):
@@ -468,6 +512,8 @@ def run_softmax(args, name: str) -> dict:
                                "kernel": "softmax_bwd_split_kernel"
                                if xr.plan("softmax_bwd_ws", M, N, x.dtype)["split"] > 1
                                else "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_softmax(w, args.cpu_rows)
     return out
 
 
