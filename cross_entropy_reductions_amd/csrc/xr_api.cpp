@@ -27,7 +27,7 @@ constexpr int64_t kMinChunkVecs = 256;
 // while another thread launches work is not a data race (which value that launch sees is
 // unspecified).
 struct Options {
-  std::atomic<int64_t> path{0}, split{0}, threads{0}, grid{0}, load_policy{0};
+  std::atomic<int64_t> path{0}, split{0}, threads{0}, grid{0}, load_policy{0}, no_wait{0};
 };
 Options g_opt;
 
@@ -384,7 +384,8 @@ xr_status_t prepare_exchange(char* ws, int64_t M, int S, int64_t N, hipStream_t 
   *flags = ws_counts + 2;
   const int64_t* tgt = nullptr;
   int64_t mm = 0, vv = N, ii = 0, nslots = M * S;
-  void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, partials, &nslots};
+  int32_t init_flags = g_opt.no_wait ? kFlagExchangeTimeout : 0;
+  void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, partials, &nslots, &init_flags};
   const int64_t fill_groups = std::min<int64_t>(64, std::max<int64_t>(1, nslots / 1024));
   if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),
                       args, 0, s) != hipSuccess)
@@ -441,6 +442,10 @@ xr_status_t xr_set_option(xr_option_t option, int64_t value) {
     case XR_OPT_LOAD_POLICY:
       if (value < 0 || value > 2) return XR_ERR_OPTION;
       g_opt.load_policy = value;
+      return XR_OK;
+    case XR_OPT_NO_WAIT:
+      if (value < 0 || value > 1) return XR_ERR_OPTION;
+      g_opt.no_wait = value;
       return XR_OK;
   }
   return XR_ERR_OPTION;
@@ -794,7 +799,9 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
   {
     const int64_t* tgt = target;
     int64_t mm = M, vv = V, ii = ignore_index;
-    void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, &partials, const_cast<int64_t*>(&nslots)};
+    int32_t init_flags = g_opt.no_wait ? kFlagExchangeTimeout : 0;
+    void* args[] = {&tgt, &mm, &vv, &ii, &ws_counts, &partials, const_cast<int64_t*>(&nslots),
+                    &init_flags};
     // one workgroup counts; the slot fill is spread over up to 64 (8 KB of slots each)
     const int64_t fill_groups = std::min<int64_t>(64, std::max<int64_t>(1, nslots / 1024));
     if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),

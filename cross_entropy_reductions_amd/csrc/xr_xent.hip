@@ -44,14 +44,16 @@ namespace xr {
 
 // ============================================================================ cross-entropy
 // Target scan: n = #{t != ignore_index}, bad = #{t != ignore_index, t outside [0, V)},
-// counted by workgroup 0 (16-byte loads, two targets each, all issued before the sums);
-// every workgroup marks its share of the split-row (m, d) slots as unpublished.
+// counted by workgroup 0 (16-byte loads, two targets each, all issued before the sums),
+// which also sets the error flags to `init_flags` (0; a test sets the exchange-timeout flag
+// so that split rows do not wait); every workgroup marks its share of the split-row (m, d)
+// slots as unpublished.
 __global__ __launch_bounds__(kScanThreads) void xent_scan_kernel(const int64_t* __restrict__ target,
                                                                  int64_t M, int64_t V,
                                                                  int64_t ignore_index,
                                                                  int32_t* __restrict__ ws_counts,
                                                                  uint64_t* __restrict__ partials,
-                                                                 int64_t nslots) {
+                                                                 int64_t nslots, int32_t init_flags) {
   __shared__ int red[2][kScanThreads / kWave];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kScanThreads) void xent_scan_kernel(const int64_t* 
     if (tid == 0) {
       ws_counts[0] = n;
       ws_counts[1] = bad;
-      ws_counts[2] = 0;
+      ws_counts[2] = init_flags;
       ws_counts[3] = 0;
     }
   }

@@ -328,13 +328,19 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
  *                   cooperatively for split cross-entropy rows); layer norm: at most k
  *                   workgroups per compute unit in its persistent grids
  *   XR_OPT_LOAD_POLICY  row loads: 1 = default cache policy, 2 = non-temporal
+ *   XR_OPT_NO_WAIT  1 = split-row exchanges start as if a wait had already timed out: a chunk
+ *                   reads each partner's slot once and, if it is not yet published, gives
+ *                   up (its row's outputs and loss become NaN; the cross-entropy reports
+ *                   the timeout flag in counts[2], set from the start). For testing the
+ *                   bounded-wait path; never faster.
  */
 typedef enum xr_option {
   XR_OPT_PATH = 1,
   XR_OPT_SPLIT = 2,
   XR_OPT_THREADS = 3,
   XR_OPT_GRID = 4,
-  XR_OPT_LOAD_POLICY = 5
+  XR_OPT_LOAD_POLICY = 5,
+  XR_OPT_NO_WAIT = 6
 } xr_option_t;
 
 xr_status_t xr_set_option(xr_option_t option, int64_t value);

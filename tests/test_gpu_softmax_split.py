@@ -292,3 +292,48 @@ def test_softmax_autograd(orc, shape, dtype):
     # the upstream gradient is w rounded to the dtype: exactly w_h
     check_output(to_host(x.grad.reshape(M, N)), orc.softmax_bwd(y_h, w_h),
                  f"autograd {shape} backward")
+
+
+def _rows_correct_or_nan(got: np.ndarray, want: np.ndarray, what: str) -> int:
+    """Every row either passes the suite's check or holds NaN; returns the NaN rows."""
+    g = widen(got)
+    bad = 0
+    for i in range(g.shape[0]):
+        if np.isnan(g[i]).any():
+            bad += 1
+            continue
+        check_output(got[i:i + 1], want[i:i + 1], f"{what} row {i}")
+    return bad
+
+
+def test_exchange_that_does_not_wait(orc):
+    """The bounded wait of the split-row exchange, forced from the host (XR_OPT_NO_WAIT: a
+    chunk reads each partner's slot once and gives up if it is not yet published): every
+    call returns, the cross-entropy reports the timeout flag, every row is either correct
+    or NaN; the same workspace then gives exact results again once the option is off."""
+    M, V = 64, 128256
+    x_h = synth.random_rows(19900, M, V, dtype="bf16", scale=2.0)
+    t_h = synth.random_targets(19901, M, V)
+    assert xr.plan("xent", M, V, torch.bfloat16)["split"] > 1
+    ws = torch.empty(max(xr.xent_workspace_bytes(M, V, torch.bfloat16),
+                         xr.softmax_workspace_bytes(M, V, torch.bfloat16)),
+                     dtype=torch.uint8, device="cuda")
+    g_want, l_want, _, _ = orc.xent(x_h, t_h, V)
+    sm_want = orc.softmax_fwd(x_h)
+    for no_wait in (1, 0):
+        xr.set_option("no_wait", no_wait)
+        xd = to_device(x_h)
+        _, rows, counts = xr.xent_fwd_bwd(xd, to_device(t_h), workspace=ws)
+        y = xr.softmax_fwd(to_device(x_h), workspace=ws)
+        torch.cuda.synchronize()
+        c = to_host(counts).tolist()
+        assert c[2] == no_wait, c
+        nan_g = _rows_correct_or_nan(to_host(xd), g_want, f"no_wait={no_wait} gradient")
+        nan_y = _rows_correct_or_nan(to_host(y), sm_want, f"no_wait={no_wait} softmax")
+        loss = to_host(rows).astype(np.float64)
+        ok = np.isnan(loss) | (np.abs(loss - l_want) <= 1e-4 * np.abs(l_want) + 1e-5)
+        assert ok.all()
+        print(f"no_wait={no_wait}: {nan_g} NaN gradient rows, {nan_y} NaN softmax rows, "
+              f"{int(np.isnan(loss).sum())} NaN losses", flush=True)
+        if not no_wait:
+            assert nan_g == 0 and nan_y == 0 and not np.isnan(loss).any()
