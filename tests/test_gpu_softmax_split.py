@@ -337,3 +337,20 @@ def test_exchange_that_does_not_wait(orc):
               f"{int(np.isnan(loss).sum())} NaN losses", flush=True)
         if not no_wait:
             assert nan_g == 0 and nan_y == 0 and not np.isnan(loss).any()
+
+
+def test_empty_batches():
+    """Zero rows: every call succeeds, enqueues nothing and returns empty results."""
+    for dt in (torch.float32, torch.bfloat16):
+        x = torch.empty((0, 1000), dtype=dt, device="cuda")
+        y = xr.softmax_fwd(x)
+        dx = xr.softmax_bwd(y, torch.empty_like(x))
+        assert y.shape == (0, 1000) and dx.shape == (0, 1000)
+        out, loss = xr.nll_fwd(x, torch.empty(0, dtype=torch.int64, device="cuda"))
+        assert out.shape == (0, 1000) and loss.numel() == 0
+        w = torch.ones(1000, dtype=dt, device="cuda")
+        b = torch.zeros(1000, dtype=dt, device="cuda")
+        yl, mean, rstd = xr.layernorm_fwd(x, w, b)
+        assert yl.shape == (0, 1000) and mean.numel() == 0
+        xr.element_mul(x, 2.0)
+    torch.cuda.synchronize()
