@@ -124,10 +124,11 @@ bool same_lead(const void* a, int64_t lda, const void* b, int64_t ldb, int eb) {
 }
 
 // Smallest shape of the menu holding `vecs` vectors per workgroup (optionally a forced size).
-const Shape* pick_shape(const Shape* menu, int count, int64_t vecs) {
+const Shape* pick_shape(const Shape* menu, int count, int64_t vecs, int max_vpt = 0) {
   for (int i = 0; i < count; ++i) {
     const Shape& s = menu[i];
     if (g_opt.threads && s.threads != g_opt.threads) continue;
+    if (max_vpt && s.vpt > max_vpt) continue;
     if ((int64_t)s.threads * s.vpt >= vecs) return &s;
   }
   return nullptr;
@@ -202,9 +203,9 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   // log-softmax when the call brings a workspace for the exchange; else their rows stay
   // whole): enough for the row to fit;
   // rows of 32 KB and more in several chunks, so that several workgroups share a compute
-  // unit and one's reductions overlap another's memory traffic: ~16 KB chunks (one wave
-  // each) up to 64 KB rows, ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s
-  // in two chunks, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 in two chunks,
+  // unit and one's reductions overlap another's memory traffic: ~16 KB chunks up to 64 KB
+  // rows, ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s in two chunks of
+  // 64 x 16 vectors, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 in two chunks,
   // 6.0 in eight); and enough chunks to give every compute unit work when the batch is short.
   int64_t S = 1;
   if (op == kOpXent || can_split) {
@@ -236,7 +237,13 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   }
 
   const int64_t chunk = (nvm + S - 1) / S;
-  const Shape* sh = pick_shape(menu, nmenu, chunk);
+  // Cross-entropy chunks take a shape of at most 8 vectors per thread when one holds the
+  // chunk (more threads, fewer loads in flight per thread): measured on 8192 x 32000 bf16,
+  // four 16 KB chunks per row at 5.62 TB/s on 64 threads x 16 vectors, 5.80-5.84 on
+  // 128 x 8 (and two 32 KB chunks on 256 x 8 alike); the 128 KB chunks of longer rows keep
+  // 512 x 16, which measured the same as 512 x 8 / 256 x 8 with more chunks.
+  const Shape* sh = op == kOpXent ? pick_shape(menu, nmenu, chunk, 8) : nullptr;
+  if (!sh) sh = pick_shape(menu, nmenu, chunk);
   if (!sh) {
     if (want) return XR_ERR_SHAPE;
     p.kernel = stream_kernel(op, dt);

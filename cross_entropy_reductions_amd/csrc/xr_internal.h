@@ -199,7 +199,7 @@ constexpr int kMulThreads = XR_MUL_THREADS;
 constexpr int kMulVpt = XR_MUL_VPT;
 
 // Shapes available to the row-resident kernels, smallest capacity first.
-constexpr int kNumFwdShapes = 7;
+constexpr int kNumFwdShapes = 10;
 extern const Shape kFwdShapes[kNumFwdShapes];  // xent and softmax forward
 constexpr int kNumBwdShapes = 6;
 extern const Shape kBwdShapes[kNumBwdShapes];  // softmax backward (two row operands)

@@ -342,7 +342,8 @@ __device__ __forceinline__ u32x4 mul_slot(u32x4 v, float s) {
 
 // Instantiation lists of the row kernels (the shapes of kFwdShapes / kBwdShapes).
 #define XR_SHAPES_FWD(X, D)                                                                     \
-  X(D, 64, 4) X(D, 64, 8) X(D, 64, 16) X(D, 128, 16) X(D, 256, 16) X(D, 512, 16) X(D, 1024, 16)
+  X(D, 64, 4) X(D, 64, 8) X(D, 64, 16) X(D, 128, 8) X(D, 128, 16) X(D, 256, 8) X(D, 256, 16)  \
+  X(D, 512, 8) X(D, 512, 16) X(D, 1024, 16)
 #define XR_SHAPES_BWD(X, D) \
   X(D, 64, 4) X(D, 64, 8) X(D, 128, 8) X(D, 256, 8) X(D, 512, 8) X(D, 1024, 8)
 

@@ -7,8 +7,11 @@
 
 namespace xr {
 
-const Shape kFwdShapes[kNumFwdShapes] = {{64, 4},   {64, 8},   {64, 16},  {128, 16},
-                                         {256, 16}, {512, 16}, {1024, 16}};
+// In order of capacity (threads x vectors); of two shapes of equal capacity the one with
+// fewer threads comes first, so the default pick of a whole row is the narrower workgroup.
+const Shape kFwdShapes[kNumFwdShapes] = {{64, 4},   {64, 8},   {64, 16},  {128, 8},
+                                         {128, 16}, {256, 8},  {256, 16}, {512, 8},
+                                         {512, 16}, {1024, 16}};
 const Shape kBwdShapes[kNumBwdShapes] = {{64, 4},  {64, 8},   {128, 8},
                                          {256, 8}, {512, 8}, {1024, 8}};
 
