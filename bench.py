@@ -30,7 +30,9 @@ log-softmax forward with a gathered loss over the same matrix, into a separate o
 block-sparse softmax backward over 32 causal 4096 x 4096 maps of 64 x 64 bf16 blocks;
 `sm-vocab` / `sm-few` the softmax forward + backward over split rows (4096 x 128256 bf16,
 16 x 2^20 fp32) through one workspace. The softmax workloads time the oracle's softmax
-(forward, then backward) as their CPU baseline.
+(forward, then backward) as their CPU baseline; c4-mul, c4-nll, ln and bsr the oracle's
+element_mul, negative log-softmax, layer norm (forward, then backward) and block-sparse
+backward on a leading sample of the same inputs.
 """
 from __future__ import annotations
 
@@ -228,6 +230,115 @@ def cpu_baseline_softmax(workload: dict, rows: int, min_seconds: float = 10.0) -
                       + f", {passes} whole passes"}
 
 
+def _cpu_passes(one_pass, min_seconds: float):
+    """Run `one_pass` until `min_seconds` have elapsed (at least once); (passes, seconds)."""
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        passes += 1
+        sec = time.perf_counter() - t0
+        if sec >= min_seconds:
+            return passes, sec
+
+
+def _cpu_line(bytes_per_pass: int, rows: int, passes: int, sec: float, cores: int,
+              sample: str) -> dict:
+    return {"value": round(bytes_per_pass * passes / sec / 1e9, 3), "unit": "GB/s",
+            "cores": cores, "kind": "oracle", "rows_per_s": round(rows * passes / sec, 1),
+            "seconds": round(sec, 3), "sample": f"{sample}, {passes} whole passes"}
+
+
+def cpu_baseline_element_mul(workload: dict, rows: int, scale: float,
+                             min_seconds: float = 10.0) -> dict:
+    """The oracle's element_mul (x times the row's upstream gradient) on the first `rows` rows
+    of the matrix, 256 rows at a time; the rate counts the GPU line's minimal bytes."""
+    import oracle
+
+    orc = oracle.get()
+    M, V = workload["M"], workload["N"]
+    rows = min(rows, M)
+    x = workload["x"][:rows]
+
+    def one_pass():
+        for r0 in range(0, rows, 256):
+            orc.element_mul(x[r0:r0 + 256], scale)
+
+    passes, sec = _cpu_passes(one_pass, min_seconds)
+    return _cpu_line(2 * rows * V * 2, rows, passes, sec, orc.num_threads(),
+                     f"first {rows} of {M} rows of the same matrix (V={V} bf16): float64 "
+                     f"element_mul by {scale}")
+
+
+def cpu_baseline_nll(workload: dict, idx, rows: int, min_seconds: float = 10.0) -> dict:
+    """The oracle's negative log-softmax with the gathered loss on the first `rows` rows."""
+    import oracle
+
+    orc = oracle.get()
+    M, N = workload["M"], workload["N"]
+    rows = min(rows, M)
+    x = workload["x"][:rows]
+
+    def one_pass():
+        for r0 in range(0, rows, 256):
+            orc.nll_fwd(x[r0:r0 + 256], idx[r0:r0 + 256])
+
+    passes, sec = _cpu_passes(one_pass, min_seconds)
+    return _cpu_line(2 * rows * N * 2 + 12 * rows, rows, passes, sec, orc.num_threads(),
+                     f"first {rows} of {M} rows of the same matrix (N={N} bf16): float64 "
+                     "-log softmax and the gathered loss")
+
+
+def cpu_baseline_layernorm(workload: dict, rows: int, min_seconds: float = 10.0) -> dict:
+    """The oracle's layer norm forward, then its backward, on the first `rows` rows, 1024 rows
+    at a time (dw, db summed per piece); the rate counts the GPU line's minimal bytes."""
+    import oracle
+
+    orc = oracle.get()
+    M, N = workload["M"], workload["N"]
+    rows = min(rows, M)
+    x, dy, w, b, eps = workload["x"][:rows], workload["dy"][:rows], workload["w"], workload["b"], \
+        workload["eps"]
+    elt = 2 if workload["dtype"] == "bf16" else 4
+
+    def one_pass():
+        for r0 in range(0, rows, 1024):
+            orc.layernorm_fwd(x[r0:r0 + 1024], w, b, eps)
+            orc.layernorm_bwd(dy[r0:r0 + 1024], x[r0:r0 + 1024], w, eps)
+
+    passes, sec = _cpu_passes(one_pass, min_seconds)
+    per_pass = (2 * rows * N * elt + 2 * N * elt + 8 * rows) + \
+        (3 * rows * N * elt + N * elt + 8 * rows + 2 * N * elt)
+    return _cpu_line(per_pass, rows, passes, sec, orc.num_threads(),
+                     f"first {rows} of {M} rows of the same workload (N={N} "
+                     f"{workload['dtype']}): float64 layer norm forward, then backward")
+
+
+def cpu_baseline_bsr(workload: dict, maps: int, min_seconds: float = 10.0) -> dict:
+    """The oracle's block-sparse softmax backward on the first `maps` attention maps, one map at
+    a time; the rate counts the GPU line's minimal bytes for those maps."""
+    import oracle
+
+    orc = oracle.get()
+    Z = workload["Z"]
+    maps = max(1, min(maps, Z))
+    y, dy, lut = workload["y"], workload["dy"], workload["lut"]
+    elt = 2 if workload["dtype"] == "bf16" else 4
+
+    def one_pass():
+        for z in range(maps):
+            orc.bsr_softmax_bwd(y[z:z + 1], dy[z:z + 1], lut, workload["n_brows"],
+                                workload["block"], workload["scale"])
+
+    passes, sec = _cpu_passes(one_pass, min_seconds)
+    listed = int(workload["layout"].sum()) * maps * workload["block"] ** 2
+    rows = maps * workload["n_brows"] * workload["block"]
+    return _cpu_line(3 * listed * elt + lut.size * 4, rows, passes, sec, orc.num_threads(),
+                     f"first {maps} of {Z} maps of the same workload ({workload['seq']}^2 in "
+                     f"{workload['block']}-blocks, {workload['dtype']}): float64 block-sparse "
+                     "softmax backward")
+
+
 def _device_matrix(torch, a, dev):
     import numpy as np
     if a.dtype == np.uint16:
@@ -337,11 +448,14 @@ def run_element_mul(args, name: str) -> dict:
     out = _line(args, name, bmin, M, wall, kernel_ms, "element_mul_kernel",
                 {"M": M, "V": V, "bytes_min": bmin, "threads": 1024, "vec_per_thread": 8},
                 "bf16")
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_element_mul(w, args.cpu_rows, 0.5)
     return out
 
 
 def run_nll(args, name: str) -> dict:
     """-log softmax of the c4 logits into a separate output, plus the gathered losses."""
+    import numpy as np
     import torch
 
     import cross_entropy_reductions_amd as xr
@@ -364,10 +478,13 @@ def run_nll(args, name: str) -> dict:
     wall, kernel_ms = _timed(HipEvents(), args.steps, args.warmup, launch)
     bmin = 2 * M * N * 2 + 12 * M
     p = xr.plan("nll_fwd", M, N, x.dtype)
-    return _line(args, name, bmin, M, wall, kernel_ms, "softmax_fwd_kernel (negative log)",
-                 {"M": M, "N": N, "bytes_min": bmin, "path": p["path"], "threads": p["threads"],
-                  "vec_per_thread": p["vec_per_thread"], "split": p["split"], "grid": p["grid"]},
-                 "bf16")
+    res = _line(args, name, bmin, M, wall, kernel_ms, "softmax_fwd_kernel (negative log)",
+                {"M": M, "N": N, "bytes_min": bmin, "path": p["path"], "threads": p["threads"],
+                 "vec_per_thread": p["vec_per_thread"], "split": p["split"], "grid": p["grid"]},
+                "bf16")
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_nll(w, np.clip(w["target"], 0, None), args.cpu_rows)
+    return res
 
 
 def run_layernorm(args, name: str) -> dict:
@@ -422,6 +539,8 @@ def run_layernorm(args, name: str) -> dict:
                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": round(b_bwd / kavg / 1e6 / PEAK_HBM_GBS, 4),
                            "kernel": "ln_bwd_kernel (stage 1)", "kernel_ms_avg": round(kavg, 5)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_layernorm(wl, args.cpu_rows)
     return out
 
 
@@ -452,9 +571,12 @@ def run_bsr(args, name: str) -> dict:
     listed = int(w["layout"].sum()) * w["Z"] * w["block"] ** 2
     bmin = 3 * listed * elt + lut.numel() * 4
     rows = w["Z"] * w["n_brows"] * w["block"]
-    return _line(args, name, bmin, rows, wall, kernel_ms, "bsr_softmax_bwd_kernel",
-                 {"Z": w["Z"], "seq": w["seq"], "block": w["block"], "n_blocks": w["n_blocks"],
-                  "bytes_min": bmin, "input_sets": nsets}, "bf16")
+    out = _line(args, name, bmin, rows, wall, kernel_ms, "bsr_softmax_bwd_kernel",
+                {"Z": w["Z"], "seq": w["seq"], "block": w["block"], "n_blocks": w["n_blocks"],
+                 "bytes_min": bmin, "input_sets": nsets}, "bf16")
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_bsr(w, max(1, args.cpu_rows * w["Z"] // 16384))
+    return out
 
 
 def run_softmax(args, name: str) -> dict:
