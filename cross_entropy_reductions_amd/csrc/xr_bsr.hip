@@ -13,7 +13,7 @@
 // per 16-byte vector) consecutive lanes per row, one vector of each listed block per lane:
 // a wave reads 64 / TPR consecutive rows of a block, i.e. one contiguous span of it. Up to
 // kBsrResident blocks per row stay in registers between the dot product and the write (one
-// read of y and dx, one write); longer rows are read twice. The dot product is a butterfly
+// non-temporal read of y and dx, one write); longer rows are read twice. The dot product is a butterfly
 // over the row's TPR lanes (the same bits on every lane, no LDS, no barrier). The table is
 // read with scalar loads (it is uniform across the workgroup and read-only for the kernel,
 // which the host checks: it may not overlap dx), every index bounded by the table length;
@@ -94,14 +94,16 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
 
   if (n == 0) return;  // nothing listed: nothing to read or write
   if (n <= NB) {
-    // every listed block's vector stays in registers: one read of y and dx, one write
+    // every listed block's vector stays in registers: one read of y and dx, one write. The
+    // loads are non-temporal (nothing reads these lines again; measured 4.96-4.98 TB/s with
+    // the default policy, 5.61-5.62 non-temporal, on 32 causal 4096 x 4096 maps of 64-blocks)
     u32x4 vy[NB], vd[NB];
     uint32_t vo[NB];
     vec_offs(0, vo);
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      vy[q] = buf_load<kPolicyDefault>(ry, vo[q]);
-      vd[q] = buf_load<kPolicyDefault>(rd, vo[q]);
+      vy[q] = buf_load<kPolicyNT>(ry, vo[q]);
+      vd[q] = buf_load<kPolicyNT>(rd, vo[q]);
     }
     float s = 0.f;
 #pragma unroll
@@ -110,8 +112,8 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
     for (int q = 0; q < NB; ++q) buf_store(rd, vo[q], out(vy[q], vd[q], s));
   } else {
-    // longer rows: the dot product over every listed block, then a second read to write,
-    // NB blocks at a time
+    // longer rows: the dot product over every listed block (default policy: the lines are
+    // read again), then a second, non-temporal read to write, NB blocks at a time
     float s = 0.f;
     uint32_t vo[NB];
     for (int k0 = 0; k0 < n; k0 += NB) {
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kBsrThreads) __attribute__((amdgpu_waves_per_eu(4))
       vec_offs(k0, vo);
 #pragma unroll
       for (int q = 0; q < NB; ++q)
-        buf_store(rd, vo[q], out(buf_load<kPolicyDefault>(ry, vo[q]), buf_load<kPolicyDefault>(rd, vo[q]), s));
+        buf_store(rd, vo[q], out(buf_load<kPolicyNT>(ry, vo[q]), buf_load<kPolicyNT>(rd, vo[q]), s));
     }
   }
 }
