@@ -296,6 +296,26 @@ def test_xent_workgroup_sizes(orc, threads):
     compare_xent(orc, x, t, V, g, rows, mean, counts, f"threads {threads}")
 
 
+@pytest.mark.parametrize("V,dtype,split,want", [
+    (32000, "bf16", 0, (128, 8, 4)),    # 64 KB rows: four 16 KB chunks on 128 x 8
+    (32000, "bf16", 2, (256, 8, 2)),    # the same rows forced into two 32 KB chunks
+    (16000, "f32", 0, (128, 8, 4)),     # 64 KB fp32 rows
+    (64000, "bf16", 0, (512, 8, 2)),    # 128 KB rows: two 64 KB chunks on 512 x 8
+    (128256, "bf16", 0, (512, 16, 2)),  # 256 KB rows: 128 KB chunks, no 8-vector shape holds
+])
+def test_xent_chunk_shapes(orc, V, dtype, split, want):
+    """Cross-entropy chunks take the smallest shape of at most 8 vectors per thread that
+    holds them, else the smallest shape that does; each plan matches the oracle."""
+    M = 300
+    xr.set_option("split", split)
+    p = xr.plan("xent", M, V, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    assert (p["threads"], p["vec_per_thread"], p["split"]) == want, p
+    x = synth.random_rows(9650 + V % 97, M, V, dtype=dtype, scale=2.0)
+    t = synth.random_targets(9651 + V % 97, M, V, ignore_frac=0.1)
+    g, rows, mean, counts = run_xent(x, t, V)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"V {V} {dtype} split {split}")
+
+
 @pytest.mark.parametrize("grid", [1, 2, -1])
 def test_xent_grid_shapes(orc, grid):
     """Persistent grids (rows g, g + G, ... with the next row's loads issued while the
