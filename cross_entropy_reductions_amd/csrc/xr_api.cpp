@@ -141,6 +141,7 @@ struct Plan {
   int64_t grid = 0;
   bool coop = false;
   int64_t chunk_vecs = 0;
+  int group_rows = 1;  // cross-entropy split rows: adjacent rows written back together
   const void* kernel = nullptr;
 };
 
@@ -291,6 +292,16 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     // are resident or about to be; the wait is bounded in any case.
     p.path = kPathSplit;
     p.grid = M * S;
+    // Cross-entropy chunks of 64 KiB and more are written back in groups of 8 adjacent rows:
+    // a chunk holds its gradient stores until the chunks of the rows around it have
+    // published their (m, d) (same-box A/B, 16384 x 128256 bf16 in 128 KB chunks: 6.10-6.14
+    // TB/s ungrouped, 6.22-6.23 grouped; 2048 x 256000 fp32: 6.40-6.44 to 6.51-6.52; groups
+    // of 16 measured no better than 8; with 16 KB chunks (8192 x 32000 bf16) groups were
+    // 1-2 % slower). A group's chunks have consecutive workgroup ids, so in a normal launch
+    // a chunk waits only for chunks resident or next in line; the group must fit the GPU
+    // many times over.
+    if (op == kOpXent && chunk * 16 >= (64 << 10) && (int64_t)kXentGroupRows * S * 4 <= resident)
+      p.group_rows = kXentGroupRows;
   } else {
     p.path = kPathSplit;
     if (!di.coop) return XR_ERR_DEVICE;
@@ -819,7 +830,7 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
     XentParams prm{static_cast<char*>(logits), ld * eb, target, M, V, ignore_index, row_loss,
                    ws_counts, ws_counts + 2, partials, p.chunk_vecs, p.S,
                    (int)(p.path == kPathSplit ? p.grid / p.S : p.grid), (int)reduction,
-                   grad_scale, grad_scale_stride};
+                   grad_scale, grad_scale_stride, p.group_rows};
     if (xr_status_t st = launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads))
       return st;
   }

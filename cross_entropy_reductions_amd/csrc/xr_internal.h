@@ -36,6 +36,7 @@ struct XentParams {
   int reduction;          // Reduction: the mean divides the gradient by n
   const float* gscale;    // upstream gradient, row i at gscale[i * gstride]; nullptr = 1
   int64_t gstride;
+  int group_rows;         // split rows written back in groups of kXentGroupRows rows (or 1: none)
 };
 
 // Rows x[i, 0:V) scaled in place by scale[i * sstride]; chunk_vecs 16-byte vectors per
@@ -182,6 +183,7 @@ const void* bsr_softmax_bwd_kernel_ptr(int dtype);
 #ifndef XR_BSR_RESIDENT
 #define XR_BSR_RESIDENT 12
 #endif
+constexpr int kXentGroupRows = 8;  // cross-entropy write groups (rows, a power of two; see the plan)
 constexpr int kBsrThreads = XR_BSR_THREADS;
 constexpr int kBsrResident = XR_BSR_RESIDENT;
 

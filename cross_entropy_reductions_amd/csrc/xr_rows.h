@@ -221,6 +221,48 @@ __device__ __forceinline__ Stats exchange_row_stats(Stats st, uint64_t* slots, i
   return {bcast[0], bcast[1]};
 }
 
+// Write grouping of split rows: row r's chunks, once they have their (m, d), wait until the
+// chunks of the other rows of its group of G adjacent rows (rows g0 .. g0 + G - 1, g0 a
+// multiple of G, cut at M) whose gradient is not zero (target neither
+// ignore_index nor outside [0, V)) have published their slots. Nothing is combined: the wait
+// only holds a chunk's gradient stores until its neighbours' chunks are ready to store
+// theirs too, so that adjacent rows are written back together. The first wave polls up to
+// 64 slots at a time, one per lane, after loading the slot's row target. The timeout flag is
+// read only for a slot found unpublished: the wait is bounded like the exchange's, ends at
+// once when the flag is set and, as it decides nothing, simply ends when its budget runs
+// out. Called by every thread of the workgroup.
+template <int G>
+__device__ __forceinline__ void wait_row_group(const uint64_t* partials, const int64_t* target,
+                                               int64_t ignore_index, int64_t V, int64_t r,
+                                               int64_t M, int S, const int32_t* flags) {
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    const int64_t g0 = r - r % G;                         // G is a power of two
+    const int rows = (int)(M - g0 < G ? M - g0 : G);
+    const int n = rows * S;                               // slots of the group
+    int budget = kSpinLimit;
+    for (int b = 0; b < n; b += kWave) {
+      const int q = b + tid;
+      if (q >= n) continue;
+      const int64_t rr = g0 + q / S;
+      if (rr == r) continue;
+      const int64_t t = target[rr];
+      if (t == ignore_index || t < 0 || t >= V) continue;  // a row that publishes nothing
+      const uint64_t* slot = partials + g0 * S + q;
+      if (__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kPartialEmpty)
+        continue;
+      // not yet published: the timeout flag decides whether to wait at all
+      if (__hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+          kFlagExchangeTimeout)
+        break;
+      bool ok = true;
+      (void)poll_slot(slot, budget, ok);
+      if (!ok) break;
+    }
+  }
+  __syncthreads();
+}
+
 // Split rows of the softmax backward: publish this chunk's partial dot product and add the
 // S partials of the row, read by the first wave 64 at a time and summed with the fixed
 // butterfly of wave_reduce (bit-identical sums in every chunk). A published word is the

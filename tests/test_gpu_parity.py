@@ -316,6 +316,26 @@ def test_xent_chunk_shapes(orc, V, dtype, split, want):
     compare_xent(orc, x, t, V, g, rows, mean, counts, f"V {V} {dtype} split {split}")
 
 
+@pytest.mark.parametrize("M,V,dtype,ld", [
+    (261, 66000, "bf16", None),   # two 64.5 KiB chunks per row; a last group of 5 rows
+    (259, 40000, "f32", 40064),   # two 80 KB chunks per padded row; a last group of 3
+    (264, 128256, "bf16", None),  # two 128 KB chunks per row; 33 whole groups
+])
+def test_xent_write_groups(orc, M, V, dtype, ld):
+    """Split rows with chunks of 64 KB and more are written back in groups of adjacent rows
+    (a chunk holds its stores until its neighbours' chunks have published): ignored rows and
+    out-of-range targets inside a group, and a last group cut short by M, give the oracle's
+    results and leave no error flag."""
+    x = synth.random_rows(9800 + M, M, V, ld=ld, dtype=dtype, scale=2.0)
+    t = synth.random_targets(9801 + M, M, V, ignore_frac=0.25)
+    t[min(3, M - 1)] = V + 5
+    t[min(6, M - 1)] = -7
+    p = xr.plan("xent", M, V, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    assert p["path"] == "split" and p["chunk_vecs"] * 16 >= 64 << 10, p
+    g, rows, mean, counts = run_xent(x, t, V)
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"groups M {M} V {V} {dtype}")
+
+
 @pytest.mark.parametrize("grid", [1, 2, -1])
 def test_xent_grid_shapes(orc, grid):
     """Persistent grids (rows g, g + G, ... with the next row's loads issued while the
