@@ -292,16 +292,19 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     // are resident or about to be; the wait is bounded in any case.
     p.path = kPathSplit;
     p.grid = M * S;
-    // Cross-entropy chunks of 64 KiB and more are written back in groups of 8 adjacent rows:
-    // a chunk holds its gradient stores until the chunks of the rows around it have
-    // published their (m, d) (same-box A/B, 16384 x 128256 bf16 in 128 KB chunks: 6.10-6.14
-    // TB/s ungrouped, 6.22-6.23 grouped; 2048 x 256000 fp32: 6.40-6.44 to 6.51-6.52; groups
-    // of 16 measured no better than 8; with 16 KB chunks (8192 x 32000 bf16) groups were
-    // 1-2 % slower). A group's chunks have consecutive workgroup ids, so in a normal launch
-    // a chunk waits only for chunks resident or next in line; the group must fit the GPU
-    // many times over.
-    if (op == kOpXent && chunk * 16 >= (64 << 10) && (int64_t)kXentGroupRows * S * 4 <= resident)
-      p.group_rows = kXentGroupRows;
+    // Forward chunks (cross-entropy, softmax, negative log-softmax) of 64 KiB and more are
+    // written back in groups of 8 adjacent rows: a chunk holds its stores until the chunks
+    // of the rows around it have published their (m, d) (same-box A/B, cross-entropy over
+    // 16384 x 128256 bf16 in 128 KB chunks: 6.10-6.14 TB/s ungrouped, 6.22-6.23 grouped;
+    // 2048 x 256000 fp32: 6.40-6.44 to 6.51-6.52; negative log-softmax 16384 x 128256 bf16:
+    // 6.23 to 6.43-6.45; softmax 4096 x 128256 bf16: 5.78-5.80 to 5.86-5.87; groups of 16
+    // measured no better than 8; with 16 KB chunks (8192 x 32000 bf16) groups were 1-2 %
+    // slower, with 32 KB chunks no different). A group's chunks have consecutive workgroup
+    // ids, so in a normal launch a chunk waits only for chunks resident or next in line;
+    // the group must fit the GPU many times over.
+    if (op != kOpSoftmaxBwd && chunk * 16 >= (64 << 10) &&
+        (int64_t)kWriteGroupRows * S * 4 <= resident)
+      p.group_rows = kWriteGroupRows;
   } else {
     p.path = kPathSplit;
     if (!di.coop) return XR_ERR_DEVICE;
@@ -528,7 +531,7 @@ xr_status_t xr_softmax_fwd_ex(void* y, int64_t ld_y, const void* x, int64_t ld_x
                                  &p, workspace != nullptr))
     return st;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N,
-                       nullptr, nullptr, p.S, p.chunk_vecs, nullptr, nullptr};
+                       nullptr, nullptr, p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.path == kPathSplit) {
     if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
@@ -579,7 +582,7 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
                                  &p, workspace != nullptr))
     return st;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(out), ld_out * eb,
-                       M, N, idx, loss, p.S, p.chunk_vecs, nullptr, nullptr};
+                       M, N, idx, loss, p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.path == kPathSplit) {
     if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;

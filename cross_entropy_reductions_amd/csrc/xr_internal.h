@@ -36,7 +36,7 @@ struct XentParams {
   int reduction;          // Reduction: the mean divides the gradient by n
   const float* gscale;    // upstream gradient, row i at gscale[i * gstride]; nullptr = 1
   int64_t gstride;
-  int group_rows;         // split rows written back in groups of kXentGroupRows rows (or 1: none)
+  int group_rows;         // split rows written back in groups of kWriteGroupRows rows (or 1: none)
 };
 
 // Rows x[i, 0:V) scaled in place by scale[i * sstride]; chunk_vecs 16-byte vectors per
@@ -65,6 +65,7 @@ struct SoftmaxFwdParams {
   int64_t chunk_vecs;
   uint64_t* partials;
   int32_t* flags;
+  int group_rows;  // split rows written back in groups of kWriteGroupRows rows (or 1: none)
 };
 
 // Layer norm forward: y = (x - mean) rstd w + b per row; mean and rstd saved.
@@ -183,7 +184,7 @@ const void* bsr_softmax_bwd_kernel_ptr(int dtype);
 #ifndef XR_BSR_RESIDENT
 #define XR_BSR_RESIDENT 12
 #endif
-constexpr int kXentGroupRows = 8;  // cross-entropy write groups (rows, a power of two; see the plan)
+constexpr int kWriteGroupRows = 8;  // split-row write groups (rows, a power of two; see the plan)
 constexpr int kBsrThreads = XR_BSR_THREADS;
 constexpr int kBsrResident = XR_BSR_RESIDENT;
 

@@ -223,14 +223,15 @@ __device__ __forceinline__ Stats exchange_row_stats(Stats st, uint64_t* slots, i
 
 // Write grouping of split rows: row r's chunks, once they have their (m, d), wait until the
 // chunks of the other rows of its group of G adjacent rows (rows g0 .. g0 + G - 1, g0 a
-// multiple of G, cut at M) whose gradient is not zero (target neither
-// ignore_index nor outside [0, V)) have published their slots. Nothing is combined: the wait
-// only holds a chunk's gradient stores until its neighbours' chunks are ready to store
-// theirs too, so that adjacent rows are written back together. The first wave polls up to
-// 64 slots at a time, one per lane, after loading the slot's row target. The timeout flag is
-// read only for a slot found unpublished: the wait is bounded like the exchange's, ends at
-// once when the flag is set and, as it decides nothing, simply ends when its budget runs
-// out. Called by every thread of the workgroup.
+// multiple of G, cut at M) have published their slots; for the cross-entropy (target given)
+// only rows whose gradient is not zero (target neither ignore_index nor outside [0, V))
+// publish, and only those are waited for. Nothing is combined: the wait only holds a
+// chunk's stores until its neighbours' chunks are ready to store theirs too, so that
+// adjacent rows are written back together. The first wave polls up to 64 slots at a time,
+// one per lane (after loading the slot's row target, if any). The timeout flag is read only
+// for a slot found unpublished: the wait is bounded like the exchange's, ends at once when
+// the flag is set and, as it decides nothing, simply ends when its budget runs out. Called
+// by every thread of the workgroup.
 template <int G>
 __device__ __forceinline__ void wait_row_group(const uint64_t* partials, const int64_t* target,
                                                int64_t ignore_index, int64_t V, int64_t r,
@@ -246,8 +247,10 @@ __device__ __forceinline__ void wait_row_group(const uint64_t* partials, const i
       if (q >= n) continue;
       const int64_t rr = g0 + q / S;
       if (rr == r) continue;
-      const int64_t t = target[rr];
-      if (t == ignore_index || t < 0 || t >= V) continue;  // a row that publishes nothing
+      if (target) {  // cross-entropy: rows with a zero gradient publish nothing
+        const int64_t t = target[rr];
+        if (t == ignore_index || t < 0 || t >= V) continue;
+      }
       const uint64_t* slot = partials + g0 * S + q;
       if (__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kPartialEmpty)
         continue;

@@ -115,6 +115,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (owner) xi = buf_load_elem<D>(cx.rsrc, (uint32_t)(vt * Elt<D>::kBytes));
   Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red);
   st = exchange_row_stats<THREADS>(st, p.partials + r * S, S, chunk, p.flags, bcast);
+  if (p.group_rows > 1)
+    wait_row_group<kWriteGroupRows>(p.partials, nullptr, 0, 0, r, p.M, S, p.flags);
   // softmax: exp2(x*log2e - c), c = m*log2e + log2 d.  NLL: c - x, c = m + log d.
   const float c = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
 #pragma unroll

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
         m = row.m;
         d = row.d;
         if (p.group_rows > 1)
-          wait_row_group<kXentGroupRows>(p.partials, p.target, p.ignore_index, p.V, r, p.M, S,
+          wait_row_group<kWriteGroupRows>(p.partials, p.target, p.ignore_index, p.V, r, p.M, S,
                                          p.ws_flags);
       }
       // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) - log2|s| is
