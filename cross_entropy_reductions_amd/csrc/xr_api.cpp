@@ -292,18 +292,18 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     // are resident or about to be; the wait is bounded in any case.
     p.path = kPathSplit;
     p.grid = M * S;
-    // Forward chunks (cross-entropy, softmax, negative log-softmax) of 64 KiB and more are
-    // written back in groups of 8 adjacent rows: a chunk holds its stores until the chunks
-    // of the rows around it have published their (m, d) (same-box A/B, cross-entropy over
-    // 16384 x 128256 bf16 in 128 KB chunks: 6.10-6.14 TB/s ungrouped, 6.22-6.23 grouped;
-    // 2048 x 256000 fp32: 6.40-6.44 to 6.51-6.52; negative log-softmax 16384 x 128256 bf16:
-    // 6.23 to 6.43-6.45; softmax 4096 x 128256 bf16: 5.78-5.80 to 5.86-5.87; groups of 16
-    // measured no better than 8; with 16 KB chunks (8192 x 32000 bf16) groups were 1-2 %
-    // slower, with 32 KB chunks no different). A group's chunks have consecutive workgroup
-    // ids, so in a normal launch a chunk waits only for chunks resident or next in line;
-    // the group must fit the GPU many times over.
-    if (op != kOpSoftmaxBwd && chunk * 16 >= (64 << 10) &&
-        (int64_t)kWriteGroupRows * S * 4 <= resident)
+    // Split rows with chunks of 32 KiB and more, at most 8 per row, are written back in
+    // groups of 8 adjacent rows: a chunk holds its stores until the chunks of the rows
+    // around it have published (same-box A/B: cross-entropy over 16384 x 128256 bf16 in
+    // 128 KB chunks 6.10-6.14 TB/s ungrouped, 6.22-6.23 grouped; 2048 x 256000 fp32, 8
+    // chunks per row, 6.40-6.44 to 6.51-6.52; negative log-softmax 16384 x 128256 bf16
+    // 6.11-6.18 to 6.39; softmax 4096 x 128256 bf16 forward 5.75-5.78 to 5.84-5.87, backward
+    // in 62.6 KiB chunks 6.22 to 6.40; groups of 16 no better than 8; 8192 x 32000 bf16 in
+    // 32 KB chunks no different, in 16 KB chunks 1-2 % slower; 16 rows of 2^20 fp32 in 32
+    // or 64 chunks per row 2-7 % slower, a group then being hundreds of slots). A group's
+    // chunks have consecutive workgroup ids, so in a normal launch a chunk waits only for
+    // chunks resident or next in line; the group must fit the GPU many times over.
+    if (chunk * 16 >= (32 << 10) && S <= 8 && (int64_t)kWriteGroupRows * S * 4 <= resident)
       p.group_rows = kWriteGroupRows;
   } else {
     p.path = kPathSplit;
@@ -761,7 +761,7 @@ xr_status_t xr_softmax_bwd_ex(void* dx, int64_t ld_dx, const void* y, int64_t ld
     return st;
   SoftmaxBwdParams prm{static_cast<const char*>(y), ld_y * eb, static_cast<const char*>(dy),
                        ld_dy * eb, static_cast<char*>(dx), ld_dx * eb, M, N,
-                       p.S, p.chunk_vecs, nullptr, nullptr};
+                       p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.path == kPathSplit) {
     if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;

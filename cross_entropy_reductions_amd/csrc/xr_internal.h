@@ -145,6 +145,7 @@ struct SoftmaxBwdParams {
   int64_t chunk_vecs;
   uint64_t* partials;
   int32_t* flags;
+  int group_rows;  // split rows written back in groups of kWriteGroupRows rows (or 1: none)
 };
 
 // One kernel configuration: workgroup size and 16-byte vectors per thread.

@@ -313,6 +313,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
   const float part = block_reduce<THREADS>((s4[0] + s4[1]) + (s4[2] + s4[3]), OpAdd(), red);
   const float dot = exchange_row_sum<THREADS>(part, p.partials + r * S, S, chunk, p.flags, bcast);
+  if (p.group_rows > 1)
+    wait_row_group<kWriteGroupRows>(p.partials, nullptr, 0, 0, r, p.M, S, p.flags);
   reg_barrier(vy);
   reg_barrier(vd);
 #pragma unroll

@@ -53,10 +53,12 @@ def check(orc, x_h, dy_h, N, y_h, dx_h, what):
 
 
 # (M, N, dtype): long rows (two or more 128 KB chunks), 32-64 KB rows (16 KB chunks), rows
-# too few for the GPU (chunks for every compute unit), ragged sizes.
+# too few for the GPU (chunks for every compute unit), ragged sizes, and batches whose rows
+# are written back in groups of 8 (chunks of 32 KiB and more, at most 8 per row; the last
+# group cut short by M).
 SHAPES = [(1, 300001, "bf16"), (3, 70001, "f32"), (5, 128256, "bf16"), (64, 40000, "bf16"),
           (200, 20000, "f32"), (7, 5000, "f32"), (2, 1 << 20, "f32"), (16, 262147, "bf16"),
-          (300, 8193, "f32")]
+          (300, 8193, "f32"), (261, 66000, "bf16"), (259, 40000, "f32")]
 
 
 @pytest.mark.parametrize("M,N,dtype", SHAPES, ids=[f"{m}x{n}-{d}" for m, n, d in SHAPES])
