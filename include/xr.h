@@ -72,7 +72,9 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
  * exchange their partial statistics through the workspace: the (max, sum) pairs of the
  * online-softmax combine for the forward (the pairs the cross-entropy's split rows
  * exchange), the partial dot products sum(y * dy) for the backward, each added in chunk
- * order, so the results do not depend on timing.
+ * order, so the results do not depend on timing. Rows of a few large chunks are also
+ * written back in groups of adjacent rows (a chunk holds its stores until its neighbours'
+ * chunks have published: a bounded wait that never changes a result).
  *   workspace  device scratch of at least xr_softmax_workspace_bytes(M, N, dtype) bytes
  *              (covers both directions), 8-byte aligned, or NULL (rows handled whole, as
  *              without _ex); no initialisation needed; scratch between calls; it must not
@@ -331,8 +333,9 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
  *   XR_OPT_NO_WAIT  1 = split-row exchanges start as if a wait had already timed out: a chunk
  *                   reads each partner's slot once and, if it is not yet published, gives
  *                   up (its row's outputs and loss become NaN; the cross-entropy reports
- *                   the timeout flag in counts[2], set from the start). For testing the
- *                   bounded-wait path; never faster.
+ *                   the timeout flag in counts[2], set from the start); the waits that
+ *                   group adjacent rows' stores end at once. For testing the bounded-wait
+ *                   path; never faster.
  */
 typedef enum xr_option {
   XR_OPT_PATH = 1,
