@@ -34,7 +34,9 @@
 //     is -inf being the identity. A row's chunks have consecutive workgroup ids, so in a
 //     normal launch a chunk waits only for chunks already started or next in line (a
 //     persistent grid is launched cooperatively); the wait is bounded and reports a flag
-//     if it expires.
+//     if it expires. Rows of a few large chunks are written back in groups of 8 adjacent
+//     rows: after its own row's exchange a chunk also waits (bounded, deciding nothing)
+//     for the other rows of its group to publish, so that their stores go out together.
 //   * Stream kernels (one workgroup per row, element-wise, several passes over global
 //     memory) handle anything the row-resident kernels do not: rows whose operands are
 //     not equally aligned, rows too long for the split grid.
