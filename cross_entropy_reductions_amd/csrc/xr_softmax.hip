@@ -59,7 +59,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     const Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red[buf]);
     buf ^= 1;
     // softmax: exp2(x*log2e - coff), coff = m*log2e + log2 d.  NLL: c - x, c = m + log d.
-    const float coff = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
+    const float coff = NLL ? st.m + logf(st.d) : exp_offset(scaled_max(st.m), log2f(st.d));
     auto out_slot = [coff](u32x4 x) { return NLL ? nll_slot<D>(x, coff) : exp_slot<D>(x, coff); };
     if (rn < p.M) {
       const Chunk<D> cn(p.x + rn * p.ldx_bytes, p.N, 0, cv);
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (p.group_rows > 1)
     wait_row_group<kWriteGroupRows>(p.partials, nullptr, 0, 0, r, p.M, S, p.flags);
   // softmax: exp2(x*log2e - c), c = m*log2e + log2 d.  NLL: c - x, c = m + log d.
-  const float c = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
+  const float c = NLL ? st.m + logf(st.d) : exp_offset(scaled_max(st.m), log2f(st.d));
 #pragma unroll
   for (int k = 0; k < VPT; ++k)
     store_slot<D, THREADS>(cy, k, NLL ? nll_slot<D>(v[k], c) : exp_slot<D>(v[k], c));
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
   st = block_reduce_stats<T>(st, red);
   // In place (y == x) is safe: each vector is re-read and written by the same thread, and
   // all reads of the statistics pass finished before the barrier above.
-  const float coff = NLL ? st.m + logf(st.d) : st.m * kLog2e + log2f(st.d);
+  const float coff = NLL ? st.m + logf(st.d) : exp_offset(scaled_max(st.m), log2f(st.d));
   for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
     const Chunk<D> cx(row, p.N, lo, kStreamWindow);
     const Chunk<D> cy(out, p.N, lo, kStreamWindow);  // the output's geometry when `same`

@@ -206,7 +206,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
       // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) - log2|s| is
       // |s| p_j / n (n = 1 unless the reduction is the mean); the sign of s is applied to
       // the result bits.
-      coff = m * kLog2e + log2f(d) + log2n - log2f(fabsf(sc));
+      coff = exp_offset(scaled_max(m), log2f(d) + log2n - log2f(fabsf(sc)));
       neg = __builtin_signbit(sc) != 0;
     }
 
@@ -229,8 +229,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
       return ignored ? 0.f : (neg ? -g : g);
     });
     if (owner) {
-      // Target column: s (p_t - 1)/n, stored after this thread's vector store.
-      const float pt = exp2f((xt - m) * kLog2e) / d;
+      // Target column: s (p_t - 1)/n, stored after this thread's vector store. p_t's
+      // numerator is formed as the sum pass forms the terms of d, so that p_t near 1 keeps
+      // its accuracy (p_t - 1 cancels).
+      const float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -scaled_max(m))) / d;
       store_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes), (pt - 1.0f) * inv_n * sc);
       p.row_loss[r] = m + logf(d) - xt;
     }
@@ -288,8 +290,9 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams 
   st = block_reduce_stats<T>(st, red);
   const float m = st.m, d = st.d;
   // gradient exp2(x*log2e - coff) = s p_j / n for j != target; s (p_t - 1) / n at the target
-  const float coff = m * kLog2e + log2f(d) + log2f((float)n) - log2f(fabsf(sc));
-  const float gt = (exp2f((xt - m) * kLog2e) / d - 1.0f) * inv_n * sc;
+  const float mL = scaled_max(m);
+  const float coff = exp_offset(mL, log2f(d) + log2f((float)n) - log2f(fabsf(sc)));
+  const float gt = (__builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -mL)) / d - 1.0f) * inv_n * sc;
   const int64_t tv = (lead + t) / EPV;  // the target's row vector and element in it
   const int te = (int)((lead + t) % EPV);
   for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {

@@ -2,10 +2,14 @@
 the float64 oracle.
 
 Outputs: fp32 within 1e-5 absolute, bf16 within the suite's 2e-2 relative bound (floored
-at 2^-7 of the row's largest value). The loss is the stored output element, so it carries
-the output's rounding: fp32 losses within 1e-5, bf16 losses within the bf16 bound of their
-row. +inf outputs (from -inf logits) and NaN losses (indices outside the row) must match
-exactly.
+at 2^-7 of the row's largest value) plus the absolute error the fp32 arithmetic can leave
+before the bf16 rounding: the output (m + log d) - x_j is one fp32 subtraction of values up
+to |m| + log d, after one fp32 addition and a log accurate to a few ulps, so each row gets
+2^-21 (max_j |x_j| + log d + 1), a few ulps of its largest magnitude (this matters where
+the result is near 0: the row's maximum when d is near 1, e.g. a one-column row, where the
+exact result is 0). The loss is the stored output element, so it carries the output's
+rounding: fp32 losses within 1e-5, bf16 losses within the bf16 bound of their row. +inf
+outputs (from -inf logits) and NaN losses (indices outside the row) must match exactly.
 """
 from __future__ import annotations
 
@@ -18,7 +22,7 @@ import torch
 import oracle
 import oracle_pins
 import synth
-from gpu_util import BF16_ABS_FLOOR, BF16_FLOOR, BF16_REL, FP32_ABS, to_device, to_host, widen
+from gpu_util import BF16_FLOOR, BF16_REL, FP32_ABS, to_device, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -42,21 +46,25 @@ def _reset_options():
 
 
 def check_nll(out_gpu: np.ndarray, loss_gpu: np.ndarray, out_want: np.ndarray,
-              loss_want: np.ndarray, what: str) -> None:
+              loss_want: np.ndarray, what: str, x: np.ndarray) -> None:
+    """x: the input rows (host bytes; their first out_want.shape[1] columns are the rows)."""
     g = widen(out_gpu)
     assert g.shape == out_want.shape, what
     inf = np.isinf(out_want)
     assert np.array_equal(np.isinf(g), inf) and np.all(g[inf] == out_want[inf]), f"{what}: +inf"
     fin = ~inf
     if out_gpu.dtype == np.uint16:
+        xin = widen(np.ascontiguousarray(x[:, :out_want.shape[1]]))
+        xmax = np.max(np.where(np.isfinite(xin), np.abs(xin), 0.0), axis=1, keepdims=True)
+        logd = np.min(np.where(fin, out_want, np.inf), axis=1, keepdims=True)
+        allow = 2.0 ** -21 * (xmax + np.abs(logd) + 1.0)
         rmax = np.max(np.where(fin, np.abs(out_want), 0.0), axis=1, keepdims=True)
-        denom = np.maximum(np.abs(out_want), np.maximum(BF16_FLOOR * rmax, BF16_ABS_FLOOR))
-        with np.errstate(invalid="ignore", divide="ignore"):
-            scaled = np.where(fin & (denom > 0), np.abs(g - out_want) / denom, 0.0)
+        bound = BF16_REL * np.maximum(np.abs(out_want), BF16_FLOOR * rmax) + allow
+        with np.errstate(invalid="ignore"):
+            scaled = np.where(fin, np.abs(g - out_want) / bound, 0.0)
         worst = float(np.max(scaled)) if scaled.size else 0.0
-        assert worst <= BF16_REL, f"{what}: worst scaled error {worst:.3e}"
-        ltol = BF16_REL * np.maximum(np.abs(loss_want),
-                                     np.maximum(BF16_FLOOR * rmax[:, 0], BF16_ABS_FLOOR))
+        assert worst <= 1.0, f"{what}: worst error over its bound {worst:.3e}"
+        ltol = BF16_REL * np.maximum(np.abs(loss_want), BF16_FLOOR * rmax[:, 0]) + allow[:, 0]
     else:
         err = np.where(fin, np.abs(g - out_want), 0.0)
         worst = float(np.max(err)) if err.size else 0.0
@@ -94,7 +102,7 @@ def test_worked_example(orc):
         out, loss, _ = run(x, np.array(case["idx"], dtype=np.int64), x.shape[1])
         want = np.array([[oracle_pins.closed_form(v) for v in r] for r in case["out"]])
         wl = np.array([oracle_pins.closed_form(v) for v in case["loss"]])
-        check_nll(out, loss, want, wl, case["name"])
+        check_nll(out, loss, want, wl, case["name"], x)
 
 
 SHAPES = [(1, 1, "f32"), (3, 2, "bf16"), (19, 257, "f32"), (128, 1000, "f32"),
@@ -111,7 +119,7 @@ def test_nll_shapes(orc, M, N, dtype):
         idx[2] = -1
     out, loss, _ = run(x, idx, N)
     want, wl = orc.nll_fwd(x, idx)
-    check_nll(out, loss, want, wl, f"nll {M}x{N} {dtype}")
+    check_nll(out, loss, want, wl, f"nll {M}x{N} {dtype}", x)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -121,11 +129,11 @@ def test_nll_in_place_strides_and_unaligned(orc, dtype):
     idx = synth.random_targets(12101, M, N)
     want, wl = orc.nll_fwd(x, idx, n_cols=N)
     out, loss, full = run(x, idx, N, in_place=True)
-    check_nll(out, loss, want, wl, f"{dtype} in place")
+    check_nll(out, loss, want, wl, f"{dtype} in place", x)
     assert np.array_equal(full[:, N:].view(np.uint8), x[:, N:].view(np.uint8)), "padding changed"
     # a separate output with another row stride (rows at other addresses mod 16: stream path)
     out, loss, _ = run(x, idx, N, out_ld=N + 3)
-    check_nll(out, loss, want, wl, f"{dtype} out-of-place, other stride")
+    check_nll(out, loss, want, wl, f"{dtype} out-of-place, other stride", x)
 
 
 def test_nll_neg_inf_entries(orc):
@@ -136,7 +144,7 @@ def test_nll_neg_inf_entries(orc):
     idx[0] = 3  # a -inf entry: loss +inf
     out, loss, _ = run(x, idx, N)
     want, wl = orc.nll_fwd(x, idx)
-    check_nll(out, loss, want, wl, "-inf entries")
+    check_nll(out, loss, want, wl, "-inf entries", x)
     assert np.isinf(loss[0]) and loss[0] > 0
 
 
@@ -153,7 +161,7 @@ def test_nll_all_paths_agree(orc, dtype):
         xr.set_option("grid", grid)
         xr.set_option("split", split)
         out, loss, _ = run(x, idx, N)
-        check_nll(out, loss, want, wl, f"{dtype} {name}")
+        check_nll(out, loss, want, wl, f"{dtype} {name}", x)
 
 
 def test_nll_without_workspace_keeps_rows_whole(orc):
@@ -172,9 +180,9 @@ def test_nll_without_workspace_keeps_rows_whole(orc):
     assert st == 0
     torch.cuda.synchronize()
     want, wl = orc.nll_fwd(x_h, idx)
-    check_nll(to_host(out), to_host(loss), want, wl, "no workspace")
+    check_nll(to_host(out), to_host(loss), want, wl, "no workspace", x_h)
     out2, loss2, _ = run(x_h, idx, N)  # split rows
-    check_nll(out2, loss2, want, wl, "split rows")
+    check_nll(out2, loss2, want, wl, "split rows", x_h)
 
 
 def test_nll_c4_matrix(orc):
@@ -189,7 +197,7 @@ def test_nll_c4_matrix(orc):
     rows = np.array([0, 1, 2, 777, 8191, 12000, M - 1])
     got = to_host(out[torch.from_numpy(rows).cuda()])
     want, wl = orc.nll_fwd(x_h[rows], idx[rows])
-    check_nll(got, to_host(loss)[rows], want, wl, "16384 x 128256 sampled rows")
+    check_nll(got, to_host(loss)[rows], want, wl, "16384 x 128256 sampled rows", x_h[rows])
     # every loss: -log p of the gathered element, against the float64 loss of each row
     loss_h = to_host(loss).astype(np.float64)
     _, l_all = orc.xent_rows(x_h, idx, N, 1, ignore_index=-(1 << 62), want_grad=False)

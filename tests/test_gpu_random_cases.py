@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import check_losses, check_output, to_device, to_host
+from gpu_util import check_losses, check_output, check_probs, check_xent_grad, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +74,8 @@ def test_random_xent(orc, case):
     g, l_rows, red, (n, bad) = orc.xent(x, t, V, reduction=reduction, scale=scale)
     assert to_host(counts).tolist()[:2] == [n, bad] and int(to_host(counts)[2]) == 0
     got = to_host(xd)
-    if scale is None or got.dtype == np.uint16:
-        check_output(got[:, :V], g, f"case {case} gradient")
-    else:
-        from gpu_util import check_fp32
-        check_fp32(got[:, :V], g, f"case {case} gradient", tol=1e-5 * max(1.0, abs(scale)))
+    check_xent_grad(got[:, :V], g, t, V, n if reduction == "mean" else 1, f"case {case} gradient",
+                    scale=scale)
     if ld > V:
         assert np.array_equal(got[:, V:].view(np.uint8), x[:, V:].view(np.uint8))
     want_red = 0.0 if red is None else red
@@ -110,7 +107,7 @@ def test_random_softmax(orc, case):
         return
     torch.cuda.synchronize()
     y_h = to_host(y)
-    check_output(y_h, orc.softmax_fwd(x, n_cols=N), f"case {case} softmax")
+    check_probs(y_h, orc.softmax_fwd(x, n_cols=N), f"case {case} softmax")
     dy_c = np.ascontiguousarray(dy[:, :N])
     check_output(to_host(dx), orc.softmax_bwd(y_h, dy_c), f"case {case} softmax backward")
 
@@ -134,7 +131,7 @@ def test_random_nll(orc, case):
     want, wl = orc.nll_fwd(x, idx, n_cols=N)
     got = to_host(out)
     from test_gpu_nll import check_nll
-    check_nll(got, to_host(loss), want, wl, f"case {case} nll")
+    check_nll(got, to_host(loss), want, wl, f"case {case} nll", x)
 
 
 @pytest.mark.parametrize("case", range(12))
@@ -181,7 +178,7 @@ def test_random_element_mul(orc, case):
     torch.cuda.synchronize()
     got = to_host(xd)
     want = orc.element_mul(x, s_host, n_cols=N)
-    from test_gpu_reductions import check_grad
-    check_grad(got[:, :N], want, float(np.max(np.abs(np.atleast_1d(s_host)))), f"case {case}")
+    from test_gpu_reductions import check_products
+    check_products(got[:, :N], want, float(np.max(np.abs(np.atleast_1d(s_host)))), f"case {case}")
     if ld > N:
         assert np.array_equal(got[:, N:].view(np.uint8), x[:, N:].view(np.uint8))

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import check_output, to_device, to_host, widen
+from gpu_util import check_output, check_probs, to_device, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def fwd_bwd(x_h: np.ndarray, dy_h: np.ndarray, N: int, workspace=None):
 
 
 def check(orc, x_h, dy_h, N, y_h, dx_h, what):
-    check_output(y_h, orc.softmax_fwd(x_h, n_cols=N), f"{what} forward")
+    check_probs(y_h, orc.softmax_fwd(x_h, n_cols=N), f"{what} forward")
     # the backward on the GPU's own y isolates the backward kernel
     check_output(dx_h, orc.softmax_bwd(y_h, np.ascontiguousarray(dy_h[:, :N])),
                  f"{what} backward")
@@ -102,7 +102,7 @@ def test_split_in_place_and_pitches(orc, dtype):
     torch.cuda.synchronize()
     full = to_host(x)
     y_h = np.ascontiguousarray(full[:, :N])
-    check_output(y_h, want_y, f"{dtype} in place forward")
+    check_probs(y_h, want_y, f"{dtype} in place forward")
     assert np.array_equal(full[:, N:].view(np.uint8), x_h[:, N:].view(np.uint8)), "padding"
     want_dx = orc.softmax_bwd(y_h, np.ascontiguousarray(dy_h[:, :N]))
     # dx written over dy
@@ -234,7 +234,7 @@ def test_stream_long_rows_without_workspace(orc, dtype):
     xr.softmax_bwd(yo, dyd, dxo, workspace=False)
     torch.cuda.synchronize()
     y2 = to_host(yo)
-    check_output(y2, orc.softmax_fwd(x), f"stream {dtype} other alignment forward")
+    check_probs(y2, orc.softmax_fwd(x), f"stream {dtype} other alignment forward")
     check_output(to_host(dxo), orc.softmax_bwd(y2, dy), f"stream {dtype} other alignment backward")
 
 
@@ -290,7 +290,7 @@ def test_softmax_autograd(orc, shape, dtype):
     (y * w).sum().backward()
     torch.cuda.synchronize()
     y_h = to_host(y.detach().reshape(M, N))
-    check_output(y_h, orc.softmax_fwd(x_h), f"autograd {shape} forward")
+    check_probs(y_h, orc.softmax_fwd(x_h), f"autograd {shape} forward")
     # the upstream gradient is w rounded to the dtype: exactly w_h
     check_output(to_host(x.grad.reshape(M, N)), orc.softmax_bwd(y_h, w_h),
                  f"autograd {shape} backward")
