@@ -9,13 +9,19 @@ logits (made before the timed region).
 Prints one JSON line on stdout. Throughput is B_min / t, where B_min is the method's
 minimal traffic: every non-ignored row read once, every row written once, the targets read
 and the row losses written. `roofline` reports the row kernel alone, timed with HIP events
-the library records around that launch on its stream; `cpu_baseline` times the float64
-oracle on the same workload on this host's cores.
+the library records around that launch on its stream (and, under `profiled`, the same
+kernel's average from the committed rocprofv3 trace of this command, while that trace
+matches the kernel sources); `cpu_baseline` times the float64 oracle on the same workload
+on this host's cores. After the headline, the default run times the other configurations
+of the 75 %-of-peak target in the same process -- the softmax forward and backward over
+4096 x 4096 bf16, the cross-entropy over 8192 x 32000 bf16 and over 2048 x 256000 fp32 --
+and reports each kernel's figures under `other_configs` (`value`, `config` and
+`ms_per_step` stay the headline's).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
                     [--reduction mean|sum|none]
-                    [--grad-scale S] [--rows M]
+                    [--grad-scale S] [--rows M] [--no-extras]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
 
 The other workloads (c1 softmax fp32 128x1000, c2 softmax forward + backward bf16 4096^2,
@@ -53,6 +59,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 COUNTERS = os.path.join(ROOT, "profiles", "xent_c4_hbm_counters.json")
+TRACE = os.path.join(ROOT, "profiles", "xent_c4_kernel_trace.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "cross_entropy_reductions_amd", "csrc", f)
                   for f in ("xr_xent.hip", "xr_softmax.hip", "xr_rows.h", "xr_device.h",
                             "xr_internal.h", "xr_api.cpp")]
@@ -118,6 +125,20 @@ def measured_traffic():
     if c.get("kernel_source_hash") != kernel_source_hash():
         return None
     return c.get("traffic_bytes_per_launch")
+
+
+def profiled_kernel():
+    """The row kernel's average duration from the committed rocprofv3 kernel trace of this
+    command (a JSON beside its summary), or None if it is absent or was taken on other
+    kernel sources."""
+    try:
+        with open(TRACE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c
 
 
 # Timing-only events: no system-scope fence (L2 writeback and invalidate) when they are
@@ -419,6 +440,13 @@ def run_xent(args, name: str) -> dict:
                 w["dtype"])
     if name == "c4" and args.reduction == "mean" and args.grad_scale is None and not args.rows:
         out["roofline"]["traffic"] = measured_traffic()
+        prof = profiled_kernel()
+        if prof is not None:
+            ms = prof["kernel_ms_avg"]
+            out["roofline"]["profiled"] = {
+                "kernel_ms_avg": ms, "achieved": round(bmin / ms / 1e6, 1),
+                "frac": round(bmin / ms / 1e6 / PEAK_HBM_GBS, 4), "calls": prof["calls"],
+                "source": "profiles/xent_c4_kernel_trace.md"}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
     return out
@@ -633,7 +661,8 @@ def run_softmax(args, name: str) -> dict:
                                "frac": round(b_bwd / kavg / 1e6 / PEAK_HBM_GBS, 4),
                                "kernel": "softmax_bwd_split_kernel"
                                if xr.plan("softmax_bwd_ws", M, N, x.dtype)["split"] > 1
-                               else "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5)}
+                               else "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5),
+                               "kernel_ms_min": round(min(bwd_ms), 5), "bytes": b_bwd}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_softmax(w, args.cpu_rows)
     return out
@@ -670,6 +699,40 @@ def _line(args, name, bmin, M, wall, kernel_ms, kernel, config, dtype, kernel_by
                      "kernel": kernel, "kernel_ms_avg": round(kavg, 5),
                      "kernel_ms_min": round(min(kernel_ms), 5)},
     }
+
+
+EXTRAS = ("c2", "c3", "c5")
+
+
+def run_extras(args) -> dict:
+    """The other configurations the 75 % target covers, timed the same way in the same
+    process after the headline: per kernel, its minimal bytes, average and fastest launch
+    (HIP events), achieved GB/s and fraction of 8 TB/s, and the whole step."""
+    import copy
+
+    import torch
+
+    out = {}
+    for name in EXTRAS:
+        torch.cuda.empty_cache()
+        a = copy.copy(args)
+        a.no_cpu, a.rows, a.reduction, a.grad_scale = True, 0, "mean", None
+        line = run_softmax(a, name) if name == "c2" else run_xent(a, name)
+        kernels = [("softmax_fwd" if name == "c2" else "xent", line["roofline"])]
+        if "roofline_bwd" in line:
+            kernels.append(("softmax_bwd", line["roofline_bwd"]))
+        bmin = line["config"]["bytes_min"]
+        out[name] = {
+            "workload": line["config"]["workload"], "bytes_min": bmin,
+            "ms_per_step": line["ms_per_step"], "step_GBps": line["value"],
+            "kernels": {
+                k: {"kernel": r["kernel"], "kernel_ms_avg": r["kernel_ms_avg"],
+                    "kernel_ms_min": r.get("kernel_ms_min"), "achieved_GBps": r["achieved"],
+                    "frac": r["frac"]} for k, r in kernels}}
+        print(f"[bench] {name}: " + ", ".join(
+            f"{k} {v['achieved_GBps']} GB/s ({100 * v['frac']:.1f} %)"
+            for k, v in out[name]["kernels"].items()), file=sys.stderr, flush=True)
+    return out
 
 
 def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
@@ -722,6 +785,8 @@ def main() -> int:
     ap.add_argument("--grad-scale", type=float, default=None,
                     help="upstream gradient folded into the cross-entropy gradient write")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run: skip timing the other configurations after c4")
     args = ap.parse_args()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
@@ -746,6 +811,9 @@ def main() -> int:
         out = run_bsr(args, args.workload)
     else:
         out = run_xent(args, args.workload)
+        if args.workload == "c4" and not (args.no_extras or args.rows or args.grad_scale is not None
+                                          or args.reduction != "mean"):
+            out["other_configs"] = run_extras(args)
     print(json.dumps(out), flush=True)
     return 0
 

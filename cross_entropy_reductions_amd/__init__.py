@@ -69,6 +69,8 @@ lib.xr_xent_fwd_bwd_ex.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int,
 lib.xr_xent_fwd_bwd_ex.restype = ctypes.c_int
 lib.xr_element_mul.argtypes = [_p, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p]
 lib.xr_element_mul.restype = ctypes.c_int
+lib.xr_workspace_status.argtypes = [_p, _sz, _p, _p]
+lib.xr_workspace_status.restype = ctypes.c_int
 lib.xr_status_string.argtypes = [ctypes.c_int]
 lib.xr_status_string.restype = ctypes.c_char_p
 lib.xr_version.argtypes = []
@@ -77,11 +79,15 @@ lib.xr_version.restype = _i32
 
 class XrPlan(ctypes.Structure):
     _fields_ = [("path", _i32), ("threads", _i32), ("vec_per_thread", _i32), ("split", _i32),
-                ("grid", _i32), ("cooperative", _i32), ("chunk_vecs", _i64)]
+                ("grid", _i32), ("cooperative", _i32), ("chunk_vecs", _i64),
+                ("group_rows", _i32), ("reserved", _i32), ("grid_total", _i64)]
 
 
 lib.xr_plan.argtypes = [_i32, _i64, _i64, ctypes.c_int, _i32, ctypes.POINTER(XrPlan)]
 lib.xr_plan.restype = ctypes.c_int
+lib.xr_plan_model.argtypes = [_i32, _i64, _i64, ctypes.c_int, _i32, _i32, _i32,
+                              ctypes.POINTER(XrPlan)]
+lib.xr_plan_model.restype = ctypes.c_int
 lib.xr_set_option.argtypes = [ctypes.c_int, _i64]
 lib.xr_set_option.restype = ctypes.c_int
 lib.xr_set_profile_events.argtypes = [_p, _p]
@@ -94,8 +100,9 @@ C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_softmax_workspace_bytes",
              "xr_layernorm_fwd",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
-             "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_status_string", "xr_version",
-             "xr_plan", "xr_set_option", "xr_set_profile_events")
+             "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_workspace_status",
+             "xr_status_string", "xr_version", "xr_plan", "xr_plan_model", "xr_set_option",
+             "xr_set_profile_events")
 
 F32, BF16 = 0, 1
 OK = 0
@@ -425,7 +432,8 @@ def xent_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int =
     device tensor of one value or one value per row). Returns ``(loss, row_loss, counts)``:
     the reduced loss as a 1-element fp32 tensor (the row losses themselves for "none"),
     the fp32 row losses and int32 ``[n_non_ignore, n_bad_target, error_flags]``, all on the
-    device (nothing is synchronised).
+    device (nothing is synchronised). ``row_loss=False`` (mean and sum only) keeps the row
+    losses in the workspace instead; row_loss is then returned as None.
     """
     pl, ld, M, V, dt = _matrix(logits, "logits")
     dev = logits.device
@@ -435,13 +443,17 @@ def xent_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int =
         raise TypeError("target must be an int64 tensor on the logits' device")
     if target.dim() != 1 or target.shape[0] != M or (M > 1 and target.stride(0) != 1):
         raise ValueError("target must be a contiguous 1-D tensor of one entry per row")
+    if row_loss is False and reduction == "none":
+        raise ValueError('the row losses are the result of reduction="none"')
     if row_loss is None:
         row_loss = torch.empty(M, dtype=torch.float32, device=dev)
     if mean_loss is None and reduction != "none":
         mean_loss = torch.empty(1, dtype=torch.float32, device=dev)
     if counts is None:
         counts = torch.empty(3, dtype=torch.int32, device=dev)
-    outs = [(row_loss, "row_loss", torch.float32, M), (counts, "counts", torch.int32, 3)]
+    outs = [(counts, "counts", torch.int32, 3)]
+    if row_loss is not False:
+        outs.append((row_loss, "row_loss", torch.float32, M))
     if reduction != "none":
         outs.append((mean_loss, "mean_loss", torch.float32, 1))
     for t, name, dtp, n in outs:
@@ -454,11 +466,29 @@ def xent_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int =
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("xr_xent_fwd_bwd_ex",
            lib.xr_xent_fwd_bwd_ex(pl, ld, target.data_ptr(), M, V, int(ignore_index), dt,
-                                  REDUCTIONS[reduction], ps, sstride, row_loss.data_ptr(),
+                                  REDUCTIONS[reduction], ps, sstride,
+                                  None if row_loss is False else row_loss.data_ptr(),
                                   None if reduction == "none" else mean_loss.data_ptr(),
                                   counts.data_ptr(), workspace.data_ptr(), ws_bytes,
                                   _stream(logits, stream)))
+    if row_loss is False:
+        row_loss = None
     return (row_loss if reduction == "none" else mean_loss), row_loss, counts
+
+
+def workspace_status(workspace: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """The status word the last call left in ``workspace`` (0, or bit 0 when a split row's
+    exchange timed out), copied on the device into a new 1-element int32 tensor (nothing is
+    synchronised)."""
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or \
+            not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous device tensor")
+    out = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    _check("xr_workspace_status",
+           lib.xr_workspace_status(workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), out.data_ptr(),
+                                   _stream(workspace, stream)))
+    return out
 
 
 def element_mul(x: torch.Tensor, grad_output, *, stream=None) -> torch.Tensor:
@@ -477,17 +507,20 @@ class CrossEntropyFunction(torch.autograd.Function):
     stored in the logits' own memory (the logits are overwritten); the backward multiplies
     that stored gradient by the upstream gradient (``element_mul``; skipped on the device
     for rows whose upstream value is exactly 1.0). As on the Liger-Kernel page, the logits
-    tensor passed in must not be needed afterwards by anything else."""
+    tensor passed in must not be needed afterwards by anything else. The forward returns
+    the loss and the call's int32 counts ``[n_non_ignore, n_bad_target, error_flags]`` (on
+    the device, not differentiable)."""
 
     @staticmethod
     def forward(ctx, logits, target, ignore_index=-100, reduction="mean"):
-        loss, _, _ = xent_fwd_bwd(logits, target, ignore_index, reduction=reduction)
+        loss, _, counts = xent_fwd_bwd(logits, target, ignore_index, reduction=reduction)
         ctx.reduction = reduction
         ctx.save_for_backward(logits.detach())
-        return loss.reshape(()) if reduction != "none" else loss
+        ctx.mark_non_differentiable(counts)
+        return (loss.reshape(()) if reduction != "none" else loss), counts
 
     @staticmethod
-    def backward(ctx, grad_output):
+    def backward(ctx, grad_output, _grad_counts=None):
         (grad,) = ctx.saved_tensors
         g = grad_output
         if g.dtype != torch.float32:
@@ -499,9 +532,13 @@ class CrossEntropyFunction(torch.autograd.Function):
 
 
 def cross_entropy(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
-                  reduction: str = "mean") -> torch.Tensor:
-    """Autograd-aware fused cross-entropy (``CrossEntropyFunction``); logits are consumed."""
-    return CrossEntropyFunction.apply(logits, target, ignore_index, reduction)
+                  reduction: str = "mean", return_counts: bool = False):
+    """Autograd-aware fused cross-entropy (``CrossEntropyFunction``); logits are consumed.
+    With ``return_counts``, also the int32 device tensor ``[n_non_ignore, n_bad_target,
+    error_flags]`` (bit 0 of error_flags: a split row's exchange timed out), read without a
+    host synchronisation."""
+    loss, counts = CrossEntropyFunction.apply(logits, target, ignore_index, reduction)
+    return (loss, counts) if return_counts else loss
 
 
 def plan(op: str, M: int, N: int, dtype: torch.dtype, aligned: int = 2) -> dict:
@@ -512,9 +549,25 @@ def plan(op: str, M: int, N: int, dtype: torch.dtype, aligned: int = 2) -> dict:
     out = XrPlan()
     _check("xr_plan", lib.xr_plan(OPS[op], int(M), int(N), _DTYPES[dtype], int(aligned),
                                   ctypes.byref(out)))
+    return _plan_dict(out)
+
+
+def _plan_dict(out: XrPlan) -> dict:
     return {"path": PATHS.get(out.path, str(out.path)), "threads": out.threads,
             "vec_per_thread": out.vec_per_thread, "split": out.split, "grid": out.grid,
-            "cooperative": bool(out.cooperative), "chunk_vecs": out.chunk_vecs}
+            "cooperative": bool(out.cooperative), "chunk_vecs": out.chunk_vecs,
+            "group_rows": out.group_rows, "grid_total": out.grid_total}
+
+
+def plan_model(op: str, M: int, N: int, dtype: torch.dtype, compute_units: int,
+               blocks_per_cu: int, aligned: int = 2) -> dict:
+    """plan() for a modelled device (no GPU needed): compute_units compute units holding
+    blocks_per_cu workgroups of the planned shape each (see xr_plan_model in include/xr.h)."""
+    out = XrPlan()
+    _check("xr_plan_model", lib.xr_plan_model(OPS[op], int(M), int(N), _DTYPES[dtype],
+                                              int(aligned), int(compute_units),
+                                              int(blocks_per_cu), ctypes.byref(out)))
+    return _plan_dict(out)
 
 
 def set_option(name: str, value: int) -> None:

@@ -19,8 +19,9 @@
 namespace xr {
 namespace {
 
-constexpr int32_t kVersion = 10100;  // 1.1.0
+constexpr int32_t kVersion = 10200;  // 1.2.0
 constexpr int64_t kMinChunkVecs = 256;
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups in one launch
 
 // ----------------------------------------------------------------------------- options
 // Process-wide overrides for tests and sweeps (xr_set_option); atomics, so that setting one
@@ -38,6 +39,8 @@ std::atomic<hipEvent_t> g_ev_start{nullptr}, g_ev_stop{nullptr};
 struct DeviceInfo {
   int cus = 0;
   int coop = 0;
+  int model_per_cu = 0;  // > 0: a modelled device (xr_plan_model), holding this many
+                         // workgroups of any shape per compute unit (no occupancy query)
 };
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_dev;
@@ -180,10 +183,11 @@ const void* row_kernel(int op, xr_dtype_t dt, Shape sh, bool nt) {
 // operand row has the same address modulo 16; `on16`: moreover every row starts on a
 // 16-byte boundary (then a row touches exactly ceil(N / elements-per-vector) vectors).
 xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned, bool on16,
-                      Plan* plan, bool can_split = false) {
+                      Plan* plan, bool can_split = false, const DeviceInfo* model = nullptr) {
   int dev = 0;
   DeviceInfo di;
-  if (xr_status_t st = device_info(&dev, &di)) return st;
+  if (model) di = *model;
+  else if (xr_status_t st = device_info(&dev, &di)) return st;
   const bool bwd = op == kOpSoftmaxBwd;
   const Shape* menu = bwd ? kBwdShapes : kFwdShapes;
   const int nmenu = bwd ? kNumBwdShapes : kNumFwdShapes;
@@ -262,7 +266,7 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   const bool other_split = op != kOpXent && S > 1;
   p.kernel = other_split ? split_kernel(op, dt, *sh, nt_loads) : row_kernel(op, dt, *sh, nt_loads);
   if (!p.kernel) return XR_ERR_SHAPE;
-  const int per_cu = blocks_per_cu(dev, p.kernel, sh->threads);
+  const int per_cu = di.model_per_cu > 0 ? di.model_per_cu : blocks_per_cu(dev, p.kernel, sh->threads);
   if (per_cu <= 0) return XR_ERR_DEVICE;
   const int64_t resident = (int64_t)di.cus * per_cu;
   if (S == 1) {
@@ -395,6 +399,31 @@ size_t xent_ws_bytes(const Plan& p, int64_t M) {
   return kWsPartials + (p.path == kPathSplit ? (size_t)M * (size_t)p.S * sizeof(uint64_t) : 0);
 }
 
+size_t align16(size_t b) { return (b + 15) & ~size_t(15); }
+
+// Byte offset of the row losses kept in a cross-entropy workspace when the caller passes no
+// row_loss: after the counts block and the plan's split slots, on a 16-byte boundary.
+size_t xent_rowloss_offset(const Plan& p, int64_t M) { return align16(xent_ws_bytes(p, M)); }
+
+// Every launch of a call fits the grid limit (checked before the call enqueues anything).
+bool grid_fits(const Plan& p) { return p.grid <= kMaxGrid; }
+
+// A byte span of a call's operands, for the overlap checks.
+struct Span {
+  const void* p;
+  uint64_t bytes;
+  bool written;
+};
+// Does any written span overlap another span of the list?
+bool any_overlap(const Span* s, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if ((s[i].written || s[j].written) && s[i].p && s[j].p &&
+          spans_overlap(s[i].p, s[i].bytes, s[j].p, s[j].bytes))
+        return true;
+  return false;
+}
+
 // Split rows of the ops other than the cross-entropy: clear the flags and mark every slot of
 // the exchange unpublished (the cross-entropy's target scan with no targets), on `s` before
 // the row kernel. The workspace holds the counts block, then M * S slots.
@@ -411,6 +440,23 @@ xr_status_t prepare_exchange(char* ws, int64_t M, int S, int64_t N, hipStream_t 
   if (hipLaunchKernel(xent_scan_kernel_ptr(), dim3((unsigned)fill_groups), dim3(kScanThreads),
                       args, 0, s) != hipSuccess)
     return XR_ERR_LAUNCH;
+  return XR_OK;
+}
+
+// The workspace of a softmax / negative log-softmax call: checked against the plan's size
+// and against the call's matrices (`spans`, none of which it may overlap), then, for split
+// rows, the exchange is prepared on `s`; otherwise the row kernel only writes 0 to the
+// status word. Nothing is enqueued on an error.
+xr_status_t use_workspace(const Plan& p, int64_t M, int64_t N, void* workspace,
+                          size_t workspace_bytes, const Span* spans, int nspans, hipStream_t s,
+                          uint64_t** partials, int32_t** flags) {
+  if (!workspace) return XR_OK;
+  if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
+  for (int i = 0; i < nspans; ++i)
+    if (spans_overlap(workspace, workspace_bytes, spans[i].p, spans[i].bytes)) return XR_ERR_ALIAS;
+  char* ws = static_cast<char*>(workspace);
+  if (p.path == kPathSplit) return prepare_exchange(ws, M, p.S, N, s, partials, flags);
+  *flags = reinterpret_cast<int32_t*>(ws + kWsCounts) + 2;
   return XR_OK;
 }
 
@@ -479,8 +525,8 @@ xr_status_t xr_set_profile_events(void* start, void* stop) {
   return XR_OK;
 }
 
-xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
-                    xr_plan_t* out) {
+static xr_status_t plan_query(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
+                              xr_plan_t* out, const DeviceInfo* model) {
   if (!out) return XR_ERR_NULL;
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
   if (op < 0 || op > 5 || M < 0 || N < 1) return XR_ERR_SHAPE;
@@ -489,27 +535,45 @@ xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t 
   if (op > kOpNllFwd) op -= 4;
   Plan p;
   if (xr_status_t st = make_plan(op, M, N, dtype, op == 2 ? true : aligned != 0, aligned == 2, &p,
-                                 with_ws))
+                                 with_ws, model))
     return st;
   out->path = p.path;
   out->threads = p.path == kPathStream ? kStreamThreads : p.shape.threads;
   out->vec_per_thread = p.path == kPathStream ? 0 : p.shape.vpt;
   out->split = p.S;
-  out->grid = (int32_t)std::min<int64_t>(p.grid, 0x7FFFFFFF);
+  out->grid = (int32_t)std::min<int64_t>(p.grid, kMaxGrid);
   out->cooperative = p.coop ? 1 : 0;
   out->chunk_vecs = p.chunk_vecs;
+  out->group_rows = p.path == kPathSplit ? p.group_rows : 1;
+  out->grid_total = p.grid;
   return XR_OK;
+}
+
+xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
+                    xr_plan_t* out) {
+  return plan_query(op, M, N, dtype, aligned, out, nullptr);
+}
+
+xr_status_t xr_plan_model(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
+                          int32_t compute_units, int32_t blocks_per_cu, xr_plan_t* out) {
+  if (compute_units < 1 || blocks_per_cu < 1) return XR_ERR_VALUE;
+  DeviceInfo model;
+  model.cus = compute_units;
+  model.coop = 1;
+  model.model_per_cu = blocks_per_cu;
+  return plan_query(op, M, N, dtype, aligned, out, &model);
 }
 
 size_t xr_softmax_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype) {
   if (!valid_dtype(dtype) || M < 0 || N < 1) return 0;
-  // the larger of the forward and backward needs, at the worst-case row alignment
+  // the larger of the forward and backward needs, over the row alignments a call can have
   size_t need = 0;
-  for (int op : {kOpSoftmaxFwd, kOpSoftmaxBwd}) {
-    Plan p;
-    if (make_plan(op, M, N, dtype, true, false, &p, true) == XR_OK)
-      need = std::max(need, xent_ws_bytes(p, M));
-  }
+  for (int op : {kOpSoftmaxFwd, kOpSoftmaxBwd})
+    for (bool on16 : {false, true}) {
+      Plan p;
+      if (make_plan(op, M, N, dtype, true, on16, &p, true) == XR_OK)
+        need = std::max(need, xent_ws_bytes(p, M));
+    }
   return need;
 }
 
@@ -530,17 +594,14 @@ xr_status_t xr_softmax_fwd_ex(void* y, int64_t ld_y, const void* x, int64_t ld_x
   if (xr_status_t st = make_plan(kOpSoftmaxFwd, M, N, dtype, same_lead(x, ld_x, y, ld_y, eb), on16,
                                  &p, workspace != nullptr))
     return st;
+  if (!grid_fits(p)) return XR_ERR_SHAPE;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N,
                        nullptr, nullptr, p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.path == kPathSplit) {
-    if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
-    if (spans_overlap(ws, workspace_bytes, y, matrix_span(M, ld_y, N, eb)) ||
-        spans_overlap(ws, workspace_bytes, x, matrix_span(M, ld_x, N, eb)))
-      return XR_ERR_ALIAS;
-    if (xr_status_t st = prepare_exchange(ws, M, p.S, N, s, &prm.partials, &prm.flags)) return st;
-  }
+  const Span mats[] = {{y, matrix_span(M, ld_y, N, eb), true}, {x, matrix_span(M, ld_x, N, eb), false}};
+  if (xr_status_t st = use_workspace(p, M, N, workspace, workspace_bytes, mats, 2, s, &prm.partials,
+                                     &prm.flags))
+    return st;
   return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
 
@@ -551,9 +612,13 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
 
 size_t xr_nll_fwd_workspace_bytes(int64_t M, int64_t N, xr_dtype_t dtype) {
   if (!valid_dtype(dtype) || M < 0 || N < 1) return 0;
-  Plan p;
-  if (make_plan(kOpNllFwd, M, N, dtype, true, false, &p, true) != XR_OK) return 0;
-  return xent_ws_bytes(p, M);
+  size_t need = 0;
+  for (bool on16 : {false, true}) {
+    Plan p;
+    if (make_plan(kOpNllFwd, M, N, dtype, true, on16, &p, true) == XR_OK)
+      need = std::max(need, xent_ws_bytes(p, M));
+  }
+  return need;
 }
 
 xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
@@ -581,19 +646,17 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
   if (xr_status_t st = make_plan(kOpNllFwd, M, N, dtype, same_lead(x, ld_x, out, ld_out, eb), on16,
                                  &p, workspace != nullptr))
     return st;
+  if (!grid_fits(p)) return XR_ERR_SHAPE;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(out), ld_out * eb,
                        M, N, idx, loss, p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.path == kPathSplit) {
-    if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
-    if (spans_overlap(ws, workspace_bytes, out, matrix_span(M, ld_out, N, eb)) ||
-        spans_overlap(ws, workspace_bytes, x, matrix_span(M, ld_x, N, eb)) ||
-        spans_overlap(ws, workspace_bytes, idx, (uint64_t)M * 8) ||
-        spans_overlap(ws, workspace_bytes, loss, (uint64_t)M * 4))
-      return XR_ERR_ALIAS;
-    if (xr_status_t st = prepare_exchange(ws, M, p.S, N, s, &prm.partials, &prm.flags)) return st;
-  }
+  const Span mats[] = {{out, matrix_span(M, ld_out, N, eb), true},
+                       {x, matrix_span(M, ld_x, N, eb), false},
+                       {idx, (uint64_t)M * 8, false},
+                       {loss, (uint64_t)M * 4, true}};
+  if (xr_status_t st = use_workspace(p, M, N, workspace, workspace_bytes, mats, 4, s, &prm.partials,
+                                     &prm.flags))
+    return st;
   return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
 
@@ -674,6 +737,8 @@ xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld
   float* part_dw = static_cast<float*>(workspace);
   float* part_db = part_dw + std::max<int64_t>(G, 1) * ps;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t blocks = (N + kLnReduceCols - 1) / kLnReduceCols;
+  if (blocks > kMaxGrid || G > kMaxGrid) return XR_ERR_SHAPE;
   if (G > 0) {
     LnBwdParams prm{static_cast<const char*>(dy), ld_dy * eb, static_cast<const char*>(x), ld_x * eb,
                     static_cast<char*>(dx), ld_dx * eb, static_cast<const char*>(w), mean, rstd,
@@ -685,8 +750,6 @@ xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld
   }
   LnReduceParams rp{part_dw, part_db, ps, (int)G, static_cast<char*>(dw), static_cast<char*>(db), N};
   void* args[] = {&rp};
-  const int64_t blocks = (N + kLnReduceCols - 1) / kLnReduceCols;
-  if (blocks > 0x7FFFFFFF) return XR_ERR_SHAPE;
   if (hipLaunchKernel(ln_dwdb_kernel_ptr(dtype), dim3((unsigned)blocks), dim3(kLnReduceThreads),
                       args, 0, s) != hipSuccess)
     return XR_ERR_LAUNCH;
@@ -759,28 +822,33 @@ xr_status_t xr_softmax_bwd_ex(void* dx, int64_t ld_dx, const void* y, int64_t ld
   if (xr_status_t st = make_plan(kOpSoftmaxBwd, M, N, dtype, aligned, on16, &p,
                                  workspace != nullptr))
     return st;
+  if (!grid_fits(p)) return XR_ERR_SHAPE;
   SoftmaxBwdParams prm{static_cast<const char*>(y), ld_y * eb, static_cast<const char*>(dy),
                        ld_dy * eb, static_cast<char*>(dx), ld_dx * eb, M, N,
                        p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.path == kPathSplit) {
-    if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
-    if (spans_overlap(ws, workspace_bytes, dx, matrix_span(M, ld_dx, N, eb)) ||
-        spans_overlap(ws, workspace_bytes, y, matrix_span(M, ld_y, N, eb)) ||
-        spans_overlap(ws, workspace_bytes, dy, matrix_span(M, ld_dy, N, eb)))
-      return XR_ERR_ALIAS;
-    if (xr_status_t st = prepare_exchange(ws, M, p.S, N, s, &prm.partials, &prm.flags)) return st;
-  }
+  const Span mats[] = {{dx, matrix_span(M, ld_dx, N, eb), true},
+                       {y, matrix_span(M, ld_y, N, eb), false},
+                       {dy, matrix_span(M, ld_dy, N, eb), false}};
+  if (xr_status_t st = use_workspace(p, M, N, workspace, workspace_bytes, mats, 3, s, &prm.partials,
+                                     &prm.flags))
+    return st;
   return launch(p, &prm, s, p.path == kPathStream ? kStreamThreads : p.shape.threads);
 }
 
 size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype) {
   if (!valid_dtype(dtype) || M < 0 || V < 1) return 0;
-  // Worst-case row alignment: a call's plan never uses more split slots than this one.
-  Plan p;
-  if (make_plan(2, M, V, dtype, true, false, &p) != XR_OK) return 0;
-  return xent_ws_bytes(p, M);
+  // Enough for the plan of either row alignment, with room for the row losses (used when
+  // the caller passes no row_loss).
+  size_t need = 0;
+  bool any = false;
+  for (bool on16 : {false, true}) {
+    Plan p;
+    if (make_plan(kOpXent, M, V, dtype, true, on16, &p) != XR_OK) continue;
+    any = true;
+    need = std::max(need, xent_rowloss_offset(p, M) + (size_t)M * sizeof(float));
+  }
+  return any ? need : 0;
 }
 
 xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, int64_t M,
@@ -799,22 +867,40 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
   if (reduction != XR_REDUCTION_NONE && !loss) return XR_ERR_NULL;
   if (reduction == XR_REDUCTION_NONE) loss = nullptr;
   if (!workspace) return XR_ERR_NULL;
-  if (M > 0 && (!logits || !target || !row_loss)) return XR_ERR_NULL;
+  // the row losses are the result of the none reduction; the others may keep them in the
+  // workspace
+  if (M > 0 && (!logits || !target || (reduction == XR_REDUCTION_NONE && !row_loss)))
+    return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if ((logits && !aligned_to(logits, eb)) || (target && !aligned_to(target, 8)) ||
       (row_loss && !aligned_to(row_loss, 4)) || (loss && !aligned_to(loss, 4)) ||
       (counts && !aligned_to(counts, 4)) || (grad_scale && !aligned_to(grad_scale, 4)) ||
       !aligned_to(workspace, 8))
     return XR_ERR_ALIGN;
+  // The written spans (logits, row losses, loss, counts, workspace) overlap nothing else
+  // of the call.
+  const Span spans[] = {
+      {logits, matrix_span(M, ld, V, eb), true},
+      {row_loss, row_loss ? (uint64_t)M * 4 : 0, true},
+      {loss, 4, true},
+      {counts, 12, true},
+      {workspace, workspace_bytes, true},
+      {target, (uint64_t)M * 8, false},
+      {grad_scale, grad_scale && M > 0 ? (uint64_t)((M - 1) * grad_scale_stride + 1) * 4 : 0, false}};
+  if (any_overlap(spans, 7)) return XR_ERR_ALIAS;
   Plan p;
   const bool on16 = logits == nullptr || rows_on_16(logits, ld, M, eb);
-  if (xr_status_t st = make_plan(2, M, V, dtype, true, on16, &p)) return st;
-  if (workspace_bytes < xent_ws_bytes(p, M)) return XR_ERR_WORKSPACE;
+  if (xr_status_t st = make_plan(kOpXent, M, V, dtype, true, on16, &p)) return st;
+  if (!grid_fits(p)) return XR_ERR_SHAPE;
+  const size_t rl_off = xent_rowloss_offset(p, M);
+  const size_t need = row_loss ? xent_ws_bytes(p, M) : rl_off + (size_t)M * sizeof(float);
+  if (workspace_bytes < need) return XR_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int32_t* ws_counts = reinterpret_cast<int32_t*>(ws + kWsCounts);
   uint64_t* partials = reinterpret_cast<uint64_t*>(ws + kWsPartials);
+  if (!row_loss) row_loss = reinterpret_cast<float*>(ws + rl_off);
   const int64_t nslots = p.path == kPathSplit ? M * p.S : 0;
 
   {
@@ -894,6 +980,20 @@ xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t
   p.kernel = kern;
   p.grid = grid;
   return launch(p, &prm, static_cast<hipStream_t>(stream), kMulThreads);
+}
+
+xr_status_t xr_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                                void* stream) {
+  if (!workspace || !status) return XR_ERR_NULL;
+  if (!aligned_to(workspace, 8) || !aligned_to(status, 4)) return XR_ERR_ALIGN;
+  if (workspace_bytes < kWsPartials) return XR_ERR_WORKSPACE;
+  const int32_t* word = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
+                                                         kWsCounts) + 2;
+  if (spans_overlap(word, 4, status, 4)) return XR_ERR_ALIAS;
+  if (hipMemcpyAsync(status, word, sizeof(int32_t), hipMemcpyDeviceToDevice,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return XR_ERR_LAUNCH;
+  return XR_OK;
 }
 
 }  // extern "C"

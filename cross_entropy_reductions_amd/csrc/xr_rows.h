@@ -30,6 +30,13 @@ __device__ __forceinline__ float exp_offset(float mL, float small) {
 
 __device__ __forceinline__ u32x4 splat(uint32_t w) { return (u32x4){w, w, w, w}; }
 
+// A call given a workspace leaves the workspace's status word defined: rows that are not
+// split exchange nothing and cannot time out, so the grid's first thread writes 0 (split
+// rows have theirs written by the kernel that prepares the exchange).
+__device__ __forceinline__ void clear_status(int32_t* flags) {
+  if (flags != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *flags = 0;
+}
+
 __device__ __forceinline__ uint64_t pack_pair(float m, float d) {
   return (uint64_t)as_u32(m) | ((uint64_t)as_u32(d) << 32);
 }

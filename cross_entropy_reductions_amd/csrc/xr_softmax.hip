@@ -37,6 +37,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   int buf = 0;
   const int64_t G = gridDim.x;
   const int64_t cv = p.N + Elt<D>::kPerVec;  // more vectors than any row has: whole rows
+  clear_status(p.flags);
 
   u32x4 v[VPT];
   int64_t r = blockIdx.x;
@@ -142,6 +143,7 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
   constexpr int T = kStreamThreads;
   constexpr int U = kStreamUnroll;
   __shared__ float2 red[T / kWave];
+  clear_status(p.flags);
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const char* row = p.x + r * p.ldx_bytes;
@@ -213,6 +215,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ float red[2][NW];
   const int64_t G = gridDim.x;
   const int64_t cv = p.N + EPV;
+  clear_status(p.flags);
 
   u32x4 vy[VPT], vd[VPT];
   int64_t r = blockIdx.x;
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream_kernel(Soft
   constexpr int T = kStreamThreads;
   constexpr int U = kStreamUnroll;
   __shared__ float red[T / kWave];
+  clear_status(p.flags);
   const int64_t r = blockIdx.x;
   if (r >= p.M) return;
   const char* yr = p.y + r * p.ldy_bytes;

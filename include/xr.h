@@ -14,8 +14,9 @@
  *   - stream is a hipStream_t (NULL = the legacy default stream). Every entry point only
  *     enqueues work on it: nothing is synchronised, nothing is allocated or freed, and no
  *     device memory is read or written by the host.
- *   - Arguments are validated before anything is enqueued; on an error nothing is enqueued
- *     and the status says which argument is wrong. No C++ exception crosses this ABI.
+ *   - Arguments, and the launch limits of the sizes given, are validated before anything is
+ *     enqueued; on an error nothing is enqueued and the status says what is wrong. No C++
+ *     exception crosses this ABI.
  *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
  *   - The library keeps no state across calls except a per-device cache of device
  *     properties, the process-wide overrides of xr_set_option() and the profiling events
@@ -75,6 +76,9 @@ xr_status_t xr_softmax_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x, i
  * order, so the results do not depend on timing. Rows of a few large chunks are also
  * written back in groups of adjacent rows (a chunk holds its stores until its neighbours'
  * chunks have published: a bounded wait that never changes a result).
+ * A chunk's wait for its row's partners is bounded too: should it expire, the row's
+ * outputs are NaN and the workspace's status word gets bit 0 (xr_workspace_status()).
+ * Every call given a workspace leaves that word defined (0 when nothing timed out).
  *   workspace  device scratch of at least xr_softmax_workspace_bytes(M, N, dtype) bytes
  *              (covers both directions), 8-byte aligned, or NULL (rows handled whole, as
  *              without _ex); no initialisation needed; scratch between calls; it must not
@@ -138,8 +142,9 @@ xr_status_t xr_bsr_softmax_bwd(const void* y, int64_t stride_zy, void* dx, int64
  *   workspace    device scratch of at least xr_nll_fwd_workspace_bytes(M, N, dtype) bytes, or
  *                NULL: with it, long rows are split over several workgroups that exchange
  *                their (max, sum) pairs through it, as the cross-entropy's split rows do
- *                (no initialisation needed; scratch between calls); without it every row
- *                is handled whole
+ *                (no initialisation needed; scratch between calls; its status word is
+ *                reported by xr_workspace_status() as for xr_softmax_fwd_ex); without it
+ *                every row is handled whole
  *   M >= 0 (M == 0 enqueues nothing), N >= 1
  * idx, loss and the workspace must not overlap the matrices or each other (XR_ERR_ALIAS).
  */
@@ -197,8 +202,9 @@ xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld
 
 /*
  * Bytes of device workspace xr_xent_fwd_bwd() needs for these sizes on the current device
- * (host query; 0 if the sizes are invalid). The caller owns the workspace; its contents
- * need no initialisation and are scratch between calls.
+ * (host query; 0 if the sizes are invalid), with room for the row losses of a call that
+ * passes no row_loss. The caller owns the workspace; its contents need no initialisation
+ * and are scratch between calls.
  */
 size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype);
 
@@ -213,7 +219,7 @@ size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype);
  *                  are never touched
  *   target         int64 [M], device; ignore_index is compared first, so an ignore_index
  *                  inside [0, V) still ignores its rows
- *   row_loss       fp32 [M], device, required
+ *   row_loss       fp32 [M], device, or NULL (the row losses are then kept in the workspace)
  *   mean_loss      fp32 [1], device, required
  *   counts         int32 [3], device, or NULL: counts[0] = n, counts[1] = targets that are
  *                  neither ignore_index nor inside [0, V) (their rows get zero gradient and
@@ -223,7 +229,8 @@ size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype);
  *   M >= 0 (M == 0 still writes mean_loss = NaN and counts = {0, 0, 0}), V >= 1
  * Rows whose only finite logits are missing (all -inf), or a target logit of -inf, give
  * NaN / +inf; NaN and +inf logits are outside the contract.
- * logits must not overlap target, row_loss, mean_loss, counts or the workspace.
+ * No written buffer (logits, row_loss, mean_loss, counts, the workspace) may overlap another
+ * buffer of the call (XR_ERR_ALIAS); target and grad_scale are only read.
  */
 xr_status_t xr_xent_fwd_bwd(void* logits, int64_t ld, const int64_t* target, int64_t M,
                             int64_t V, int64_t ignore_index, xr_dtype_t dtype, float* row_loss,
@@ -254,7 +261,9 @@ typedef enum {
  *   loss               fp32 [1], device: the mean (XR_REDUCTION_MEAN, NaN when n == 0) or
  *                      the sum (XR_REDUCTION_SUM, 0 when M == 0); required for those two,
  *                      ignored and may be NULL for XR_REDUCTION_NONE
- *   row_loss           fp32 [M], device, required: the unscaled row losses (0 for ignored rows)
+ *   row_loss           fp32 [M], device: the unscaled row losses (0 for ignored rows);
+ *                      required for XR_REDUCTION_NONE (they are its result), may be NULL
+ *                      for the other two (then kept in the workspace)
  * Everything else is as in xr_xent_fwd_bwd(), which equals this call with
  * XR_REDUCTION_MEAN and grad_scale NULL.
  */
@@ -282,6 +291,17 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
 xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t dtype,
                            const float* grad_output, int64_t grad_output_stride, void* stream);
 
+/*
+ * Status word of a workspace, written by the last call that used it (xr_softmax_fwd_ex,
+ * xr_softmax_bwd_ex, xr_nll_fwd, xr_xent_fwd_bwd / _ex): 0, or bit 0 when a split row's
+ * exchange timed out (its row then holds NaN). Enqueues on `stream` a 4-byte device copy of
+ * the word into *status, a DEVICE int32 (no synchronisation): read it after that stream's
+ * work is done. The cross-entropy reports the same word in counts[2].
+ *   workspace, workspace_bytes  the workspace as passed to that call (>= 256 bytes)
+ */
+xr_status_t xr_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                                void* stream);
+
 /* Static, human-readable text for a status code (host). */
 const char* xr_status_string(xr_status_t status);
 
@@ -307,13 +327,26 @@ typedef struct xr_plan {
   int32_t threads;         /* workgroup size */
   int32_t vec_per_thread;  /* 16-byte vectors held per thread and operand */
   int32_t split;           /* workgroups per row (S) */
-  int32_t grid;            /* workgroups launched */
+  int32_t grid;            /* workgroups launched (capped at INT32_MAX; see grid_total) */
   int32_t cooperative;     /* 1 if launched as a cooperative grid */
   int64_t chunk_vecs;      /* 16-byte vectors per workgroup chunk of a row */
+  int32_t group_rows;      /* split rows: adjacent rows whose chunks store together (1: none) */
+  int32_t reserved;
+  int64_t grid_total;      /* workgroups the plan asks for (above INT32_MAX the call fails) */
 } xr_plan_t;
 
 xr_status_t xr_plan(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
                     xr_plan_t* plan /* host */);
+
+/*
+ * xr_plan() for a modelled device instead of the current one (host only, no device needed):
+ * compute_units compute units, each holding blocks_per_cu workgroups of the planned shape
+ * at once (the occupancy a real device reports per kernel), cooperative launch available.
+ * For planning and for checking the launch plans' residency conditions without a GPU.
+ * compute_units or blocks_per_cu below 1 returns XR_ERR_VALUE.
+ */
+xr_status_t xr_plan_model(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, int32_t aligned,
+                          int32_t compute_units, int32_t blocks_per_cu, xr_plan_t* plan /* host */);
 
 /*
  * Process-wide overrides for tests and benchmarks. Setting one while another thread

@@ -40,7 +40,7 @@ def test_status_strings_and_version(xr):
     for code in range(1, 12):
         assert xr.status_string(code) != "unknown status"
     assert xr.status_string(99) == "unknown status"
-    assert xr.version() == 10100
+    assert xr.version() == 10200
 
 
 XR_OK, XR_ERR_NULL, XR_ERR_SHAPE, XR_ERR_STRIDE, XR_ERR_DTYPE, XR_ERR_ALIAS = 0, 1, 2, 3, 4, 5
@@ -125,6 +125,54 @@ def test_xent_ex_argument_errors(xr):
     assert f(L, 8, T, 2, 8, -100, 0, 2, None, 0, None, None, None, W, 4096, None) == XR_ERR_NULL
     assert f(L, 8, T, 2, 8, -100, 0, 2, ctypes.c_void_p(0x60002), 1, R, None, None, W, 4096,
              None) == XR_ERR_ALIGN
+
+
+def test_xent_overlap_errors(xr):
+    """No written buffer of the cross-entropy (logits, row losses, loss, counts, workspace)
+    may overlap another buffer of the call; the check runs before anything is enqueued."""
+    f = xr.lib.xr_xent_fwd_bwd_ex
+    L, T, R, Mn, C, W, S = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000,
+                                                          0x500000, 0x600000, 0x700000))
+    M, V = 4, 1000  # logits span 0x100000 + 4 * 1000 * 2 bytes (bf16)
+    inside = ctypes.c_void_p(0x100000 + 4000)
+    ok_args = dict(L=L, T=T, R=R, Mn=Mn, C=C, W=W, S=S)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return f(a["L"], V, a["T"], M, V, -100, 1, 0, a["S"], 1, a["R"], a["Mn"], a["C"], a["W"],
+                 4096, None)
+    for name in ("T", "R", "Mn", "C", "W", "S"):  # each one moved inside the logits
+        assert call(**{name: inside}) == XR_ERR_ALIAS, name
+    # the workspace over the row losses, the counts over the mean, the loss over the targets
+    assert call(W=ctypes.c_void_p(0x300000 - 64)) == XR_ERR_ALIAS
+    assert call(C=ctypes.c_void_p(0x400000 + 0)) == XR_ERR_ALIAS
+    assert call(Mn=ctypes.c_void_p(0x200000 + 8)) == XR_ERR_ALIAS
+    # read-only buffers may overlap each other (targets and upstream gradient)
+    assert call(S=ctypes.c_void_p(0x200000)) not in (XR_ERR_ALIAS,)
+    # exactly adjacent spans do not overlap
+    assert call(R=ctypes.c_void_p(0x100000 + 8000)) != XR_ERR_ALIAS
+
+
+def test_xent_row_loss_may_be_null(xr):
+    """row_loss may be NULL for the mean and sum (kept in the workspace), not for none (the
+    row losses are its result)."""
+    f = xr.lib.xr_xent_fwd_bwd_ex
+    L, T, Mn, W = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x400000, 0x600000))
+    assert f(L, 8, T, 2, 8, -100, 0, 2, None, 0, None, None, None, W, 4096, None) == XR_ERR_NULL
+    for red in (0, 1):  # past the argument checks (a device is needed beyond them)
+        assert f(L, 8, T, 2, 8, -100, 0, red, None, 0, None, Mn, None, W, 4096, None) not in \
+            (XR_ERR_NULL, XR_ERR_ALIAS, XR_ERR_ALIGN)
+
+
+def test_workspace_status_argument_errors(xr):
+    f = xr.lib.xr_workspace_status
+    W, S = ctypes.c_void_p(0x600000), ctypes.c_void_p(0x700000)
+    assert f(None, 4096, S, None) == XR_ERR_NULL
+    assert f(W, 4096, None, None) == XR_ERR_NULL
+    assert f(ctypes.c_void_p(0x600004), 4096, S, None) == XR_ERR_ALIGN
+    assert f(W, 4096, ctypes.c_void_p(0x700002), None) == XR_ERR_ALIGN
+    assert f(W, 64, S, None) == 6  # XR_ERR_WORKSPACE: smaller than the counts block
+    assert f(W, 4096, ctypes.c_void_p(0x600008), None) == XR_ERR_ALIAS
 
 
 def test_element_mul_argument_errors(xr):

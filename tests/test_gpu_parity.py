@@ -352,6 +352,31 @@ def test_xent_grid_shapes(orc, grid):
     compare_xent(orc, x, t, V, g, rows, mean, counts, f"split grid {grid}")
 
 
+@pytest.mark.parametrize("M,V,dtype,path", [(600, 32000, "bf16", 0), (40, 50000, "f32", 3),
+                                             (300, 5000, "bf16", 1), (9, 128256, "bf16", 0)])
+def test_xent_row_loss_in_workspace(orc, M, V, dtype, path):
+    """row_loss = NULL: the row losses are kept in the workspace (whose size query allows for
+    them); the gradient, the mean and the sum match the oracle and, bit for bit, a call that
+    is given row_loss."""
+    x = synth.random_rows(9900 + M, M, V, dtype=dtype, scale=2.0)
+    t = synth.random_targets(9901 + M, M, V, ignore_frac=0.1)
+    xr.set_option("path", path)
+    for reduction in ("mean", "sum"):
+        a, b = to_device(x), to_device(x)
+        la, ra, ca = xr.xent_fwd_bwd(a, to_device(t), reduction=reduction)
+        lb, rb, cb = xr.xent_fwd_bwd(b, to_device(t), reduction=reduction, row_loss=False)
+        torch.cuda.synchronize()
+        assert rb is None
+        assert torch.equal(a.view(torch.int16 if dtype == "bf16" else torch.int32),
+                           b.view(torch.int16 if dtype == "bf16" else torch.int32))
+        assert torch.equal(la, lb) and torch.equal(ca, cb)
+        g, rows, red, (n, _) = orc.xent(x, t, V, reduction=reduction)
+        check_xent_grad(to_host(b), g, t, V, n if reduction == "mean" else 1,
+                        f"{M}x{V} {reduction} without row_loss")
+        check_losses(to_host(ra), float(lb.item()), rows, red, f"{M}x{V} {reduction}",
+                     mean_abs=1e-5 * (M if reduction == "sum" else 1))
+
+
 def test_xent_deterministic():
     w = synth.xent_c3(M=600)
     outs = [run_xent(w["x"], w["target"], w["N"]) for _ in range(3)]

@@ -250,6 +250,13 @@ def test_autograd_mean_sum_none(orc, dtype):
     check_losses(to_host(loss.detach()), 0.0, loss_rows, 0.0, f"{dtype} autograd none losses")
 
     x = to_device(x_h).requires_grad_(True)
+    loss, counts = xr.cross_entropy(x, t, return_counts=True)  # counts without a host sync
+    assert not counts.requires_grad and counts.dtype == torch.int32
+    n, bad = orc.xent_count(t_h, V)
+    assert to_host(counts).tolist() == [n, bad, 0]
+    loss.backward()
+
+    x = to_device(x_h).requires_grad_(True)
     xr.cross_entropy(x, t, reduction="none").sum().backward()  # stride-0 upstream of ones
     g, _, _, _ = orc.xent(x_h, t_h, V, reduction="none")
     check_xent_grad(to_host(x.grad), g, t_h, V, 1, f"{dtype} autograd none summed")

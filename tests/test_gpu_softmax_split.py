@@ -341,6 +341,49 @@ def test_exchange_that_does_not_wait(orc):
             assert nan_g == 0 and nan_y == 0 and not np.isnan(loss).any()
 
 
+def test_workspace_status_reports_the_timeout(orc):
+    """xr_workspace_status: the softmax forward / backward and the negative log-softmax report
+    a timed-out exchange (forced from the host) in the workspace's status word, and a later
+    call on the same workspace leaves it defined again: 0 after split rows that completed,
+    0 after rows that were not split at all."""
+    M, N = 16, 262147
+    x_h = synth.random_rows(19950, M, N, dtype="bf16", scale=2.0)
+    dy_h = synth.random_rows(19951, M, N, dtype="bf16", scale=1.0)
+    idx = synth.random_targets(19952, M, N)
+    assert xr.plan("softmax_fwd_ws", M, N, torch.bfloat16)["split"] > 1
+    assert xr.plan("softmax_bwd_ws", M, N, torch.bfloat16)["split"] > 1
+    assert xr.plan("nll_fwd", M, N, torch.bfloat16)["split"] > 1
+    ws = torch.empty(max(xr.softmax_workspace_bytes(M, N, torch.bfloat16),
+                         int(xr.lib.xr_nll_fwd_workspace_bytes(M, N, xr.BF16))),
+                     dtype=torch.uint8, device="cuda")
+    x, dy = to_device(x_h), to_device(dy_h)
+    small = to_device(synth.random_rows(19953, 4, 100, dtype="bf16", scale=2.0))
+    assert xr.plan("softmax_fwd_ws", 4, 100, torch.bfloat16)["split"] == 1
+
+    def status():
+        return int(xr.workspace_status(ws).item())
+
+    for no_wait in (1, 0):
+        xr.set_option("no_wait", no_wait)
+        y = xr.softmax_fwd(x, workspace=ws)
+        assert status() == no_wait, f"softmax forward, no_wait={no_wait}"
+        xr.softmax_bwd(y, dy, workspace=ws)
+        assert status() == no_wait, f"softmax backward, no_wait={no_wait}"
+        xr.nll_fwd(x, to_device(idx), workspace=ws)
+        assert status() == no_wait, f"negative log-softmax, no_wait={no_wait}"
+        if no_wait:
+            xr.set_option("no_wait", 0)
+            xr.softmax_fwd(small, workspace=ws)  # rows held whole: the word is cleared
+            assert status() == 0, "a call without split rows leaves 0"
+            xr.set_option("no_wait", 1)
+            xr.softmax_fwd(x, workspace=ws)
+            assert status() == 1
+            xr.softmax_bwd(xr.softmax_fwd(small, workspace=False), small, workspace=ws)
+            assert status() == 0, "the backward without split rows leaves 0"
+    y = xr.softmax_fwd(x, workspace=ws)
+    check_probs(to_host(y), orc.softmax_fwd(x_h), "after the forced timeouts")
+
+
 def test_empty_batches():
     """Zero rows: every call succeeds, enqueues nothing and returns empty results."""
     for dt in (torch.float32, torch.bfloat16):
