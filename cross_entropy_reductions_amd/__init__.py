@@ -69,6 +69,9 @@ lib.xr_xent_fwd_bwd_ex.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int,
 lib.xr_xent_fwd_bwd_ex.restype = ctypes.c_int
 lib.xr_element_mul.argtypes = [_p, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p]
 lib.xr_element_mul.restype = ctypes.c_int
+lib.xr_xent_fwd_bwd_noalloc.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int,
+                                        ctypes.c_int, _p, _i64, _p, _p, _p, _p]
+lib.xr_xent_fwd_bwd_noalloc.restype = ctypes.c_int
 lib.xr_workspace_status.argtypes = [_p, _sz, _p, _p]
 lib.xr_workspace_status.restype = ctypes.c_int
 lib.xr_status_string.argtypes = [ctypes.c_int]
@@ -100,7 +103,8 @@ C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_softmax_workspace_bytes",
              "xr_layernorm_fwd",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
-             "xr_xent_fwd_bwd_ex", "xr_element_mul", "xr_workspace_status",
+             "xr_xent_fwd_bwd_ex", "xr_xent_fwd_bwd_noalloc", "xr_element_mul",
+             "xr_workspace_status",
              "xr_status_string", "xr_version", "xr_plan", "xr_plan_model", "xr_set_option",
              "xr_set_profile_events")
 

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libxr.so")
-SOURCES = ["xr_xent.hip", "xr_softmax.hip", "xr_layernorm.hip", "xr_bsr.hip", "xr_api.cpp"]
+SOURCES = ["xr_xent.hip", "xr_softmax.hip", "xr_layernorm.hip", "xr_bsr.hip", "xr_noalloc.hip",
+           "xr_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -481,6 +481,7 @@ const char* xr_status_string(xr_status_t s) {
     case XR_ERR_LAUNCH: return "kernel launch failed";
     case XR_ERR_OPTION: return "unknown option or value";
     case XR_ERR_VALUE: return "invalid argument value";
+    case XR_ERR_TOO_LARGE: return "sizes need more scratch than the no-allocation entry point holds";
   }
   return "unknown status";
 }

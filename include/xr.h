@@ -50,7 +50,8 @@ typedef enum xr_status {
   XR_ERR_DEVICE = 8,    /* no usable HIP device, or a device query failed */
   XR_ERR_LAUNCH = 9,    /* a kernel launch failed (the HIP error is reported by HIP) */
   XR_ERR_OPTION = 10,   /* unknown option or value in xr_set_option() */
-  XR_ERR_VALUE = 11     /* an argument has an invalid value (reduction, negative stride) */
+  XR_ERR_VALUE = 11,    /* an argument has an invalid value (reduction, negative stride) */
+  XR_ERR_TOO_LARGE = 12 /* the sizes need more scratch than xr_xent_fwd_bwd_noalloc() has */
 } xr_status_t;
 
 /*
@@ -273,6 +274,26 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
                                int64_t grad_scale_stride, float* row_loss, float* loss,
                                int32_t* counts, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * xr_xent_fwd_bwd_ex() for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument; the
+ * call's scratch (the counts, the split rows' exchange slots and, when row_loss is NULL, the
+ * row losses) lives in a static device array of the library, XR_NOALLOC_SCRATCH_BYTES on
+ * each device it runs on, held until the process ends. Sizes whose scratch would not fit
+ * return XR_ERR_TOO_LARGE with nothing enqueued (xr_xent_workspace_bytes() tells the need;
+ * for instance 16384 x 128256 bf16 needs 256 + 16384 x 2 x 8 bytes, plus 4 per row without
+ * row_loss). Nothing is allocated, freed or synchronised; the kernels initialise what must
+ * start at zero. Every call on a device shares that device's array and leaves its contents
+ * behind: calls that overlap in time on one device (several streams, several threads) race
+ * and must not be made. Arguments and results are otherwise those of xr_xent_fwd_bwd_ex().
+ */
+#define XR_NOALLOC_SCRATCH_BYTES (4u << 20)
+xr_status_t xr_xent_fwd_bwd_noalloc(void* logits, int64_t ld, const int64_t* target, int64_t M,
+                                    int64_t V, int64_t ignore_index, xr_dtype_t dtype,
+                                    xr_reduction_t reduction, const float* grad_scale,
+                                    int64_t grad_scale_stride, float* row_loss, float* loss,
+                                    int32_t* counts, void* stream);
 
 /*
  * The backward's scaling of a stored cross-entropy gradient by the upstream gradient, in

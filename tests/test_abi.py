@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(xr):
 
 def test_status_strings_and_version(xr):
     assert xr.status_string(0) == "ok"
-    for code in range(1, 12):
+    for code in range(1, 13):
         assert xr.status_string(code) != "unknown status"
     assert xr.status_string(99) == "unknown status"
     assert xr.version() == 10200
