@@ -23,6 +23,7 @@ and reports each kernel's figures under `other_configs` (`value`, `config` and
                     [--reduction mean|sum|none]
                     [--grad-scale S] [--rows M] [--no-extras]
     python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
+    python bench.py --summarize-trace KERNEL_TRACE.csv [--steps K] (rocprofv3 --kernel-trace)
 
 The other workloads (c1 softmax fp32 128x1000, c2 softmax forward + backward bf16 4096^2,
 c3 cross-entropy bf16 8192x32000, c5 cross-entropy fp32 2048x256000 padded) print the same
@@ -392,6 +393,49 @@ def _timed(ev, steps, warmup, launch):
     return wall, ms
 
 
+# Launch shapes of the row kernels (threads, 16-byte vectors per thread): one row operand,
+# and two (the softmax backward).
+FWD_SHAPES = [(64, 4), (64, 8), (64, 16), (128, 8), (128, 16), (256, 8), (256, 16), (512, 8),
+              (512, 16), (1024, 16)]
+BWD_SHAPES = [(64, 4), (64, 8), (128, 8), (256, 8), (512, 8), (1024, 8)]
+
+
+def probe_shapes(nv: int, two_inputs: bool):
+    """(threads, vpt, split): the row-kernel shapes that hold a row of nv 16-byte vectors in
+    1-32 chunks of at least 64 vectors, each chunk filling more than half of the shape."""
+    out = []
+    for S in (1, 2, 4, 8, 16, 32):
+        chunk = -(-nv // S)
+        if chunk < 64:
+            break
+        for t, v in (BWD_SHAPES if two_inputs else FWD_SHAPES):
+            if chunk <= t * v < 2 * chunk:
+                out.append((t, v, S))
+    return out
+
+
+def ceiling(args, kernel_ms: float, nbytes: int, shape, shapes, launch_probe) -> dict:
+    """The memory-ceiling probe (xr_probe_rows: the row kernels' loads and stores, none of
+    their arithmetic) over the same rows and buffers: timed in the kernel's own launch shape
+    and in every shape of `shapes`, the same way as the kernel (HIP events around each
+    launch). Returns the probe's figures and the kernel's time as a fraction of them."""
+    res = {}
+    best = None
+    for sh in dict.fromkeys([tuple(shape)] + [tuple(x) for x in shapes]):
+        _, ms = _timed(HipEvents(), args.steps, args.warmup, lambda i, sh=sh: launch_probe(i, *sh))
+        avg = statistics.mean(ms)
+        if sh == tuple(shape):
+            res["same_shape"] = {"shape": list(sh), "ms_avg": round(avg, 5),
+                                 "GBps": round(nbytes / avg / 1e6, 1)}
+        if best is None or avg < best[1]:
+            best = (sh, avg)
+    res["best"] = {"shape": list(best[0]), "ms_avg": round(best[1], 5),
+                   "GBps": round(nbytes / best[1] / 1e6, 1)}
+    res["kernel_frac_of_same_shape"] = round(res["same_shape"]["ms_avg"] / kernel_ms, 4)
+    res["kernel_frac_of_best"] = round(best[1] / kernel_ms, 4)
+    return res
+
+
 def run_xent(args, name: str) -> dict:
     import torch
 
@@ -447,6 +491,18 @@ def run_xent(args, name: str) -> dict:
                 "kernel_ms_avg": ms, "achieved": round(bmin / ms / 1e6, 1),
                 "frac": round(bmin / ms / 1e6 / PEAK_HBM_GBS, 4), "calls": prof["calls"],
                 "source": "profiles/xent_c4_kernel_trace.md"}
+    if getattr(args, "ceiling", False) and args.grad_scale is None and args.reduction == "mean":
+        import cross_entropy_reductions_amd as xr_
+
+        nv = V * elt // 16
+
+        def probe(i, t_, v_, s_):
+            x = copies[i][:, :V]
+            xr_.probe_rows(x, x, threads=t_, vpt=v_, split=s_, target=t)
+
+        out["roofline"]["ceiling"] = ceiling(
+            args, out["roofline"]["kernel_ms_avg"], bmin,
+            (p["threads"], p["vec_per_thread"], p["split"]), probe_shapes(nv, False), probe)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
     return out
@@ -663,6 +719,24 @@ def run_softmax(args, name: str) -> dict:
                                if xr.plan("softmax_bwd_ws", M, N, x.dtype)["split"] > 1
                                else "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5),
                                "kernel_ms_min": round(min(bwd_ms), 5), "bytes": b_bwd}
+    if getattr(args, "ceiling", False) and name == "c2":
+        nv = N * elt // 16
+
+        def probe_fwd(i, t_, v_, s_):
+            j = i % nsets
+            xr.probe_rows(ys[j], xs[j], threads=t_, vpt=v_, split=s_)
+
+        def probe_bwd(i, t_, v_, s_):
+            j = i % nsets
+            xr.probe_rows(dxs[j], ys[j], dys[j], threads=t_, vpt=v_, split=s_)
+
+        out["roofline"]["ceiling"] = ceiling(
+            args, out["roofline"]["kernel_ms_avg"], b_fwd,
+            (p["threads"], p["vec_per_thread"], p["split"]), probe_shapes(nv, False), probe_fwd)
+        pb = xr.plan("softmax_bwd_ws", M, N, x.dtype)
+        out["roofline_bwd"]["ceiling"] = ceiling(
+            args, out["roofline_bwd"]["kernel_ms_avg"], b_bwd,
+            (pb["threads"], pb["vec_per_thread"], pb["split"]), probe_shapes(nv, True), probe_bwd)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_softmax(w, args.cpu_rows)
     return out
@@ -717,6 +791,7 @@ def run_extras(args) -> dict:
         torch.cuda.empty_cache()
         a = copy.copy(args)
         a.no_cpu, a.rows, a.reduction, a.grad_scale = True, 0, "mean", None
+        a.ceiling = not args.no_ceiling
         line = run_softmax(a, name) if name == "c2" else run_xent(a, name)
         kernels = [("softmax_fwd" if name == "c2" else "xent", line["roofline"])]
         if "roofline_bwd" in line:
@@ -728,7 +803,8 @@ def run_extras(args) -> dict:
             "kernels": {
                 k: {"kernel": r["kernel"], "kernel_ms_avg": r["kernel_ms_avg"],
                     "kernel_ms_min": r.get("kernel_ms_min"), "achieved_GBps": r["achieved"],
-                    "frac": r["frac"]} for k, r in kernels}}
+                    "frac": r["frac"], **({"ceiling": r["ceiling"]} if "ceiling" in r else {})}
+                for k, r in kernels}}
         print(f"[bench] {name}: " + ", ".join(
             f"{k} {v['achieved_GBps']} GB/s ({100 * v['frac']:.1f} %)"
             for k, v in out[name]["kernels"].items()), file=sys.stderr, flush=True)
@@ -771,6 +847,26 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
             "dispatches": {"row_kernel": len(f[ROW_KERNEL]), "copy": len(copy_f)}}
 
 
+def summarize_trace(trace_csv: str, steps: int) -> dict:
+    """The headline row kernel's average duration from a rocprofv3 --kernel-trace CSV of the
+    default command: its launches over the 16384 x 128256 rows (grid of 32768 workgroups of
+    512 work-items, told apart from the same kernel's launches on the other workloads), the
+    last `steps` of them in launch order being the timed steps."""
+    launches = []
+    with open(trace_csv) as f:
+        for row in csv.DictReader(f):
+            if ROW_KERNEL in row["Kernel_Name"] and "<1, 512, 16, 2>" in row["Kernel_Name"] \
+                    and int(row["Grid_Size_X"]) == 32768 * 512:
+                launches.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    launches.sort()
+    ns = [e - s for s, e in launches[-steps:]]
+    return {"kernel": ROW_KERNEL, "kernel_source_hash": kernel_source_hash(),
+            "kernel_ms_avg": round(statistics.mean(ns) / 1e6, 5),
+            "kernel_ms_min": round(min(ns) / 1e6, 5), "calls": len(ns),
+            "launches_traced": len(launches),
+            "bytes_min": xent_bmin(C4_M, C4_V, C4_KEEP, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -785,11 +881,18 @@ def main() -> int:
     ap.add_argument("--grad-scale", type=float, default=None,
                     help="upstream gradient folded into the cross-entropy gradient write")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="the headline kernel's average from a rocprofv3 kernel trace")
     ap.add_argument("--no-extras", action="store_true",
                     help="default run: skip timing the other configurations after c4")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the memory-ceiling probes timed beside each kernel")
     args = ap.parse_args()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return 0
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace, args.steps), indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
@@ -800,6 +903,7 @@ def main() -> int:
               file=sys.stderr)
         return 2
     if args.workload in ("c1", "c2", "sm-vocab", "sm-few"):
+        args.ceiling = args.workload == "c2" and not (args.no_ceiling or args.rows)
         out = run_softmax(args, args.workload)
     elif args.workload == "c4-mul":
         out = run_element_mul(args, args.workload)
@@ -810,6 +914,7 @@ def main() -> int:
     elif args.workload == "bsr":
         out = run_bsr(args, args.workload)
     else:
+        args.ceiling = args.workload in ("c3", "c4", "c5") and not (args.no_ceiling or args.rows)
         out = run_xent(args, args.workload)
         if args.workload == "c4" and not (args.no_extras or args.rows or args.grad_scale is not None
                                           or args.reduction != "mean"):

@@ -72,6 +72,9 @@ lib.xr_element_mul.restype = ctypes.c_int
 lib.xr_xent_fwd_bwd_noalloc.argtypes = [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int,
                                         ctypes.c_int, _p, _i64, _p, _p, _p, _p]
 lib.xr_xent_fwd_bwd_noalloc.restype = ctypes.c_int
+lib.xr_probe_rows.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, ctypes.c_int, _i32, _i32, _i32,
+                              _p, _i64, _p]
+lib.xr_probe_rows.restype = ctypes.c_int
 lib.xr_workspace_status.argtypes = [_p, _sz, _p, _p]
 lib.xr_workspace_status.restype = ctypes.c_int
 lib.xr_status_string.argtypes = [ctypes.c_int]
@@ -104,7 +107,7 @@ C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_softmax_workspace_bytes",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
              "xr_xent_fwd_bwd_ex", "xr_xent_fwd_bwd_noalloc", "xr_element_mul",
-             "xr_workspace_status",
+             "xr_workspace_status", "xr_probe_rows",
              "xr_status_string", "xr_version", "xr_plan", "xr_plan_model", "xr_set_option",
              "xr_set_profile_events")
 
@@ -478,6 +481,27 @@ def xent_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int =
     if row_loss is False:
         row_loss = None
     return (row_loss if reduction == "none" else mean_loss), row_loss, counts
+
+
+def probe_rows(out: torch.Tensor, in0: torch.Tensor, in1: torch.Tensor | None = None, *,
+               threads: int, vpt: int, split: int, target: torch.Tensor | None = None,
+               ignore_index: int = -100, stream=None) -> torch.Tensor:
+    """The memory-ceiling probe (xr_probe_rows): the row kernels' loads and stores over these
+    rows in the given launch shape, with none of their arithmetic. Returns out."""
+    po, ldo, M, N, dt = _matrix(out, "out")
+    p0, ld0, M0, N0, dt0 = _matrix(in0, "in0")
+    if (M0, N0, dt0) != (M, N, dt):
+        raise ValueError("in0 must match out in shape and dtype")
+    p1 = None
+    if in1 is not None:
+        p1, ld1, M1, N1, dt1 = _matrix(in1, "in1")
+        if (M1, N1, dt1, ld1) != (M, N, dt, ld0):
+            raise ValueError("in1 must match in0 in shape, dtype and row stride")
+    pt = None if target is None else target.data_ptr()
+    _check("xr_probe_rows", lib.xr_probe_rows(po, ldo, p0, p1, ld0, M, N, dt, int(threads),
+                                              int(vpt), int(split), pt, int(ignore_index),
+                                              _stream(out, stream)))
+    return out
 
 
 def workspace_status(workspace: torch.Tensor, *, stream=None) -> torch.Tensor:

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libxr.so")
 SOURCES = ["xr_xent.hip", "xr_softmax.hip", "xr_layernorm.hip", "xr_bsr.hip", "xr_noalloc.hip",
-           "xr_api.cpp"]
+           "xr_probe.hip", "xr_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -983,6 +983,36 @@ xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t
   return launch(p, &prm, static_cast<hipStream_t>(stream), kMulThreads);
 }
 
+xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void* in1,
+                          int64_t ld_in, int64_t M, int64_t N, xr_dtype_t dtype, int32_t threads,
+                          int32_t vpt, int32_t split, const int64_t* target,
+                          int64_t ignore_index, void* stream) {
+  if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
+  if (M < 0 || N < 1 || split < 1) return XR_ERR_SHAPE;
+  if (ld_in < N || ld_out < N) return XR_ERR_STRIDE;
+  if (M == 0) return XR_OK;
+  if (!out || !in0) return XR_ERR_NULL;
+  const int eb = elt_bytes(dtype);
+  // whole 16-byte vectors only: every row on a 16-byte boundary, N a whole number of vectors
+  if (!rows_on_16(out, ld_out, M, eb) || !rows_on_16(in0, ld_in, M, eb) ||
+      (in1 && !rows_on_16(in1, ld_in, M, eb)) || (N * eb) % 16 != 0 ||
+      (target && !aligned_to(target, 8)))
+    return XR_ERR_ALIGN;
+  const Shape sh{threads, vpt};
+  const void* kernel = probe_rows_kernel_ptr(dtype, sh, in1 ? 2 : 1);
+  if (!kernel) return XR_ERR_SHAPE;
+  const int64_t nv = N * eb / 16;
+  const int64_t chunk = (nv + split - 1) / split;
+  if (chunk > (int64_t)threads * vpt) return XR_ERR_SHAPE;
+  Plan p;
+  p.kernel = kernel;
+  p.grid = M * split;
+  if (!grid_fits(p)) return XR_ERR_SHAPE;
+  ProbeParams prm{static_cast<const char*>(in0), static_cast<const char*>(in1), ld_in * eb,
+                  static_cast<char*>(out), ld_out * eb, M, N, target, ignore_index, split, chunk};
+  return launch(p, &prm, static_cast<hipStream_t>(stream), threads);
+}
+
 xr_status_t xr_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* status,
                                 void* stream) {
   if (!workspace || !status) return XR_ERR_NULL;

@@ -129,6 +129,21 @@ struct BsrParams {
   float scale;
 };
 
+// Memory-ceiling probe (xr_probe_rows): workgroup b moves chunk b % S of row b / S from in0
+// (and in1) to out with the row kernels' access pattern and none of their arithmetic.
+struct ProbeParams {
+  const char* in0;
+  const char* in1;  // nullptr: one input
+  int64_t ldin_bytes;
+  char* out;
+  int64_t ldout_bytes;
+  int64_t M, N;
+  const int64_t* target;  // rows whose target is ignore_index are not read (zeros written)
+  int64_t ignore_index;
+  int S;
+  int64_t chunk_vecs;
+};
+
 // Operations of the row kernels (also the `op` argument of xr_plan).
 enum Op : int { kOpSoftmaxFwd = 0, kOpSoftmaxBwd = 1, kOpXent = 2, kOpNllFwd = 3 };
 
@@ -178,6 +193,7 @@ const void* ln_bwd_stream_kernel_ptr(int dtype);
 const void* ln_dwdb_kernel_ptr(int dtype);
 
 const void* bsr_softmax_bwd_kernel_ptr(int dtype);
+const void* probe_rows_kernel_ptr(int dtype, Shape s, int inputs);
 // Block-sparse backward: workgroup size, and listed blocks per row held in registers.
 #ifndef XR_BSR_THREADS
 #define XR_BSR_THREADS 256

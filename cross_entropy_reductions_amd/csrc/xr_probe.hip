@@ -1,0 +1,48 @@
+// xr_probe.hip -- the memory-ceiling probe of the measurement: the row kernels' launch (the
+// same workgroup shapes, chunks per row, buffer loads and non-temporal stores, every load of
+// a chunk landed and a workgroup barrier before its first store), with none of their
+// arithmetic, statistics exchange or row groups. Timed beside a row kernel on the same rows,
+// it shows what that launch shape can move at that size.
+#include "xr_rows.h"
+
+namespace xr {
+
+template <int D, int THREADS, int VPT, int NIN>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void probe_rows_kernel(ProbeParams p) {
+  const int S = p.S;
+  const int64_t r = blockIdx.x / S;
+  const int64_t lo = (int64_t)(blockIdx.x % S) * p.chunk_vecs;
+  const bool read = !(p.target != nullptr && p.target[r] == p.ignore_index);
+  u32x4 a[VPT], b[VPT];
+  if (read) {
+    issue_loads<D, THREADS, VPT, kPolicyNT>(a, Chunk<D>(p.in0 + r * p.ldin_bytes, p.N, lo, p.chunk_vecs));
+    if (NIN == 2)
+      issue_loads<D, THREADS, VPT, kPolicyNT>(b, Chunk<D>(p.in1 + r * p.ldin_bytes, p.N, lo, p.chunk_vecs));
+    reg_barrier(a);  // every load of the chunk has landed
+    if (NIN == 2) reg_barrier(b);
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) a[k] = b[k] = splat(0u);
+  }
+  __syncthreads();
+  const Chunk<D> co(p.out + r * p.ldout_bytes, p.N, lo, p.chunk_vecs);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(co, k, NIN == 2 ? (a[k] ^ b[k]) : a[k]);
+}
+
+#define XR_CASE_PROBE1(D, T, V) \
+  if (s.threads == T && s.vpt == V) return reinterpret_cast<const void*>(&probe_rows_kernel<D, T, V, 1>);
+#define XR_CASE_PROBE2(D, T, V) \
+  if (s.threads == T && s.vpt == V) return reinterpret_cast<const void*>(&probe_rows_kernel<D, T, V, 2>);
+const void* probe_rows_kernel_ptr(int dtype, Shape s, int inputs) {
+  if (inputs == 1) {
+    if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_PROBE1, kF32) }
+    if (dtype == kBF16) { XR_SHAPES_FWD(XR_CASE_PROBE1, kBF16) }
+  } else if (inputs == 2) {
+    if (dtype == kF32) { XR_SHAPES_BWD(XR_CASE_PROBE2, kF32) }
+    if (dtype == kBF16) { XR_SHAPES_BWD(XR_CASE_PROBE2, kBF16) }
+  }
+  return nullptr;
+}
+
+}  // namespace xr

@@ -323,6 +323,27 @@ xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t
 xr_status_t xr_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* status,
                                 void* stream);
 
+/*
+ * Memory-ceiling probe, for measurement (what a row kernel's launch can move at a given
+ * size): the row kernels' loads and stores with none of their arithmetic. Each of `split`
+ * workgroups per row, of `threads` threads holding `vpt` 16-byte vectors each per input,
+ * loads its chunk of the row from in0 (and from in1 when in1 is not NULL) with non-temporal
+ * loads, waits for every load and a workgroup barrier, then stores the chunk (in0 ^ in1 with
+ * two inputs) to out with non-temporal stores. Rows whose target equals ignore_index (target
+ * may be NULL) are not read and are written with zeros, as the cross-entropy does with
+ * ignored rows. out may be exactly in0 (in place).
+ *   M rows of N elements of dtype; in0 / in1 with row stride ld_in, out with ld_out; every
+ *   row on a 16-byte boundary and N * element size a multiple of 16, else XR_ERR_ALIGN
+ *   threads x vpt: a shape of the row kernels (one input: 64x4, 64x8, 64x16, 128x8, 128x16,
+ *   256x8, 256x16, 512x8, 512x16, 1024x16; two inputs: 64x4, 64x8, 128x8, 256x8, 512x8,
+ *   1024x8) holding a chunk of ceil(vectors per row / split) vectors, else XR_ERR_SHAPE
+ * Enqueued like the other calls (the profiling events of xr_set_profile_events() bracket it).
+ */
+xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void* in1,
+                          int64_t ld_in, int64_t M, int64_t N, xr_dtype_t dtype, int32_t threads,
+                          int32_t vpt, int32_t split, const int64_t* target, int64_t ignore_index,
+                          void* stream);
+
 /* Static, human-readable text for a status code (host). */
 const char* xr_status_string(xr_status_t status);
 

@@ -175,6 +175,22 @@ def test_workspace_status_argument_errors(xr):
     assert f(W, 4096, ctypes.c_void_p(0x600008), None) == XR_ERR_ALIAS
 
 
+def test_probe_argument_errors(xr):
+    f = xr.lib.xr_probe_rows
+    O, A, B = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000))
+    # (out, ld_out, in0, in1, ld_in, M, N, dtype, threads, vpt, split, target, ignore, stream)
+    assert f(O, 64, A, None, 64, 4, 64, 3, 64, 4, 1, None, -100, None) == XR_ERR_DTYPE
+    assert f(O, 64, A, None, 64, 4, 64, 0, 64, 4, 0, None, -100, None) == XR_ERR_SHAPE
+    assert f(O, 63, A, None, 64, 4, 64, 0, 64, 4, 1, None, -100, None) == XR_ERR_STRIDE
+    assert f(None, 64, A, None, 64, 4, 64, 0, 64, 4, 1, None, -100, None) == XR_ERR_NULL
+    assert f(O, 64, A, None, 64, 4, 62, 0, 64, 4, 1, None, -100, None) == XR_ERR_ALIGN
+    assert f(ctypes.c_void_p(0x100004), 64, A, None, 64, 4, 64, 0, 64, 4, 1, None, -100,
+             None) == XR_ERR_ALIGN
+    assert f(O, 64, A, None, 64, 4, 64, 0, 96, 4, 1, None, -100, None) == XR_ERR_SHAPE
+    assert f(O, 64, A, B, 64, 4, 64, 0, 64, 16, 1, None, -100, None) == XR_ERR_SHAPE
+    assert f(O, 64, A, None, 64, 0, 64, 0, 64, 4, 1, None, -100, None) == XR_OK
+
+
 def test_element_mul_argument_errors(xr):
     f = xr.lib.xr_element_mul
     X, G = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x90000)

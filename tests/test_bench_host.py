@@ -86,3 +86,40 @@ def test_cpu_baselines_on_small_inputs():
         assert c["kind"] == "oracle" and c["unit"] == "GB/s"
         assert c["value"] > 0 and c["cores"] >= 1 and c["seconds"] > 0
         assert "whole passes" in c["sample"]
+
+
+def test_trace_summary_takes_the_headline_launches(tmp_path):
+    """The headline kernel's average comes from its own launches only (the same kernel on
+    other workloads has other template arguments or grids), the last `steps` in launch
+    order."""
+    path = tmp_path / "trace.csv"
+    head = "void xr::xent_rows_kernel<1, 512, 16, 2>(xr::XentParams)"
+    rows = [(head, 32768 * 512, 1000 + 10 * k, 1000 + 10 * k + d)
+            for k, d in enumerate([9, 9, 9, 1, 2, 3])]
+    rows += [("void xr::xent_rows_kernel<1, 128, 8, 2>(xr::XentParams)", 32768 * 128, 5000, 5100),
+             (head, 512 * 512, 6000, 9000), ("__amd_rocclr_copyBuffer", 1024, 7000, 7500)]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Start_Timestamp",
+                                          "End_Timestamp"])
+        w.writeheader()
+        for name, grid, s, e in reversed(rows):
+            w.writerow({"Kernel_Name": name, "Grid_Size_X": grid, "Start_Timestamp": s,
+                        "End_Timestamp": e})
+    out = bench.summarize_trace(str(path), 3)
+    assert out["calls"] == 3 and out["launches_traced"] == 6
+    assert out["kernel_ms_avg"] == round(2 / 1e6, 5) and out["kernel_ms_min"] == round(1 / 1e6, 5)
+    assert out["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_probe_shapes_hold_the_row():
+    """The ceiling probe's launch shapes: each holds a chunk of the row, filled more than half,
+    in 1-32 chunks of at least 64 vectors; two-input shapes come from the backward's menu."""
+    for nv, two in ((512, False), (512, True), (4000, False), (16032, False), (64000, False)):
+        shapes = bench.probe_shapes(nv, two)
+        assert shapes
+        for t, v, s in shapes:
+            chunk = -(-nv // s)
+            assert chunk <= t * v < 2 * chunk and chunk >= 64
+            assert (t, v) in (bench.BWD_SHAPES if two else bench.FWD_SHAPES)
+    assert (128, 8, 4) in bench.probe_shapes(4000, False)  # the 8192 x 32000 plan
+    assert (512, 16, 2) in bench.probe_shapes(16032, False)  # the 16384 x 128256 plan
