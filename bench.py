@@ -22,7 +22,8 @@ and reports each kernel's figures under `other_configs` (`value`, `config` and
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
                     [--reduction mean|sum|none]
                     [--grad-scale S] [--rows M] [--no-extras]
-    python bench.py --summarize-counters FETCH.csv WRITE.csv   (rocprofv3 --pmc output)
+    python bench.py --summarize-counters FETCH.csv WRITE.csv [--workload c4|c3|c5|c2]
+                                                               (rocprofv3 --pmc output)
     python bench.py --summarize-trace KERNEL_TRACE.csv [--steps K] (rocprofv3 --kernel-trace)
 
 The other workloads (c1 softmax fp32 128x1000, c2 softmax forward + backward bf16 4096^2,
@@ -811,20 +812,32 @@ def run_extras(args) -> dict:
     return out
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the row kernel on the default workload,
-    each scaled by what the same counter reads for the runtime's device copy of the 4.2 GB
-    logit matrix (the per-step copies bench.py makes before its timed region: one known read
-    and one known write of the whole matrix)."""
-    matrix = C4_M * C4_V * 2
+# Counter summaries: per workload, the matrix the benchmark copies before its timed region
+# (bytes of one copy), and the kernels to summarise with their minimal bytes per launch.
+COUNTER_WORKLOADS = {
+    "c4": (C4_M * C4_V * 2, [(ROW_KERNEL, xent_bmin(C4_M, C4_V, C4_KEEP, 2))]),
+    "c3": (8192 * 32000 * 2, [(ROW_KERNEL, xent_bmin(8192, 32000, 7373, 2))]),
+    "c5": (2048 * 256064 * 4, [(ROW_KERNEL, xent_bmin(2048, 256000, 2048, 4))]),
+    "c2": (4096 * 4096 * 2, [("softmax_fwd_kernel", 2 * 4096 * 4096 * 2),
+                             ("softmax_bwd_kernel", 3 * 4096 * 4096 * 2)]),
+}
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str = "c4") -> dict:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a workload's row kernel(s) from a run of
+    `bench.py --workload <workload>`, each scaled by what the same counter reads for the
+    runtime's device copies of the workload's input matrix (the copies bench.py makes before
+    its timed region: one known read and one known write of the whole matrix). For c4 the
+    result is what bench.py reports as roofline.traffic."""
+    matrix, kernels = COUNTER_WORKLOADS[workload]
 
     def per_kernel(path):
         vals = {}
         with open(path) as f:
             for row in csv.DictReader(f):
                 name = row.get("Kernel_Name", "")
-                key = (ROW_KERNEL if ROW_KERNEL in name else
-                       COPY_KERNEL if COPY_KERNEL in name else None)
+                key = COPY_KERNEL if COPY_KERNEL in name else next(
+                    (k for k, _ in kernels if k in name), None)
                 if key is not None:
                     vals.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
         return vals
@@ -836,15 +849,17 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     copy_w = [v for v in w[COPY_KERNEL] if v > 0.25 * matrix]
     scale_f = matrix / statistics.median(copy_f)
     scale_w = matrix / statistics.median(copy_w)
-    fetch = statistics.median(f[ROW_KERNEL]) * scale_f
-    write = statistics.median(w[ROW_KERNEL]) * scale_w
-    bmin = xent_bmin(C4_M, C4_V, C4_KEEP, 2)
-    return {"kernel": ROW_KERNEL, "kernel_source_hash": kernel_source_hash(),
-            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
-            "traffic_bytes_per_launch": round(fetch + write), "bytes_min": bmin,
-            "traffic_over_bytes_min": round((fetch + write) / bmin, 4),
-            "copy_scale_fetch": round(scale_f, 4), "copy_scale_write": round(scale_w, 4),
-            "dispatches": {"row_kernel": len(f[ROW_KERNEL]), "copy": len(copy_f)}}
+    out = {}
+    for name, bmin in kernels:
+        fetch = statistics.median(f[name]) * scale_f
+        write = statistics.median(w[name]) * scale_w
+        out[name] = {"kernel": name, "kernel_source_hash": kernel_source_hash(),
+                     "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+                     "traffic_bytes_per_launch": round(fetch + write), "bytes_min": bmin,
+                     "traffic_over_bytes_min": round((fetch + write) / bmin, 4),
+                     "copy_scale_fetch": round(scale_f, 4), "copy_scale_write": round(scale_w, 4),
+                     "dispatches": {"row_kernel": len(f[name]), "copy": len(copy_f)}}
+    return out[ROW_KERNEL] if workload == "c4" else {"workload": workload, "kernels": out}
 
 
 def summarize_trace(trace_csv: str, steps: int) -> dict:
@@ -889,7 +904,8 @@ def main() -> int:
                     help="skip the memory-ceiling probes timed beside each kernel")
     args = ap.parse_args()
     if args.summarize_counters:
-        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        print(json.dumps(summarize_counters(*args.summarize_counters, workload=args.workload),
+                         indent=1))
         return 0
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace, args.steps), indent=1))
