@@ -862,16 +862,29 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str = "c4") -> 
     return out[ROW_KERNEL] if workload == "c4" else {"workload": workload, "kernels": out}
 
 
+def headline_launch():
+    """(workgroup size, work-items) of the headline row kernel's launch, from the library's
+    plan for the 16384 x 128256 bf16 rows on a modelled 256-CU device (the plan of rows this
+    many does not depend on the occupancy)."""
+    import torch
+
+    import cross_entropy_reductions_amd as xr
+
+    p = xr.plan_model("xent", C4_M, C4_V, torch.bfloat16, 256, 2)
+    return p["threads"], p["grid_total"] * p["threads"]
+
+
 def summarize_trace(trace_csv: str, steps: int) -> dict:
     """The headline row kernel's average duration from a rocprofv3 --kernel-trace CSV of the
-    default command: its launches over the 16384 x 128256 rows (grid of 32768 workgroups of
-    512 work-items, told apart from the same kernel's launches on the other workloads), the
-    last `steps` of them in launch order being the timed steps."""
+    default command: its bf16 launches in the headline's launch shape (told apart from the
+    same kernel's launches on the other workloads by workgroup and grid size), the last
+    `steps` of them in launch order being the timed steps."""
+    threads, items = headline_launch()
     launches = []
     with open(trace_csv) as f:
         for row in csv.DictReader(f):
-            if ROW_KERNEL in row["Kernel_Name"] and "<1, 512, 16, 2>" in row["Kernel_Name"] \
-                    and int(row["Grid_Size_X"]) == 32768 * 512:
+            if f"{ROW_KERNEL}<1, {threads}," in row["Kernel_Name"] \
+                    and int(row["Workgroup_Size_X"]) == threads and int(row["Grid_Size_X"]) == items:
                 launches.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
     launches.sort()
     ns = [e - s for s, e in launches[-steps:]]

@@ -209,16 +209,24 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   // whole): enough for the row to fit;
   // rows of 32 KB and more in several chunks, so that several workgroups share a compute
   // unit and one's reductions overlap another's memory traffic: ~16 KB chunks up to 64 KB
-  // rows, ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s in two chunks of
-  // 64 x 16 vectors, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole, 6.2 in two chunks,
-  // 6.0 in eight); and enough chunks to give every compute unit work when the batch is short.
+  // rows, ~64 KB chunks up to 512 KB rows (at most 8 chunks, so that their rows are still
+  // written back in groups), ~128 KB chunks above (measured: 8192 x 32000 bf16 at 5.5 TB/s
+  // in two chunks of 64 x 16 vectors, 5.65 in four; 16384 x 128256 bf16 at 5.6 TB/s whole,
+  // 6.2 in two 128 KB chunks; then, with write groups, 6.15 in two, 6.24 in four 64 KB
+  // chunks on 256 x 16, 6.20 in eight; 2048 x 256000 fp32 6.52 in eight 128 KB chunks, 6.28
+  // in sixteen 64 KB ones); and enough chunks to give every compute unit work when the
+  // batch is short.
   int64_t S = 1;
   if (op == kOpXent || can_split) {
     const int64_t s_cap = (nvm + cap_max - 1) / cap_max;
     const int64_t row_bytes = nvm * 16;
-    // (the softmax backward holds two operands per thread: half the chunk above 64 KB;
-    // measured on 4096 x 128256 bf16: 5.85 TB/s in two chunks, 6.29 in four)
-    const int64_t big_chunk = op == kOpSoftmaxBwd ? (64 << 10) : (128 << 10);
+    // (the softmax backward holds two operands per thread: 64 KB chunks at every length;
+    // measured on 4096 x 128256 bf16: 5.85 TB/s in two chunks, 6.29 in four. The softmax
+    // forward over those rows: 5.70 in two 128 KB chunks, 5.91 in four 64 KB ones. The
+    // negative log-softmax, writing a separate output, keeps 128 KB chunks: over the
+    // 16384 x 128256 bf16 logits 0.3 % slower in 64 KB ones.)
+    const bool chunks64 = op == kOpSoftmaxBwd || (op != kOpNllFwd && row_bytes <= (512 << 10));
+    const int64_t big_chunk = chunks64 ? (64 << 10) : (128 << 10);
     const int64_t chunk_bytes = row_bytes <= (64 << 10) ? (16 << 10) : big_chunk;
     const int64_t s_bw = row_bytes >= (32 << 10)
                              ? std::max<int64_t>(2, (row_bytes + chunk_bytes - 1) / chunk_bytes)
@@ -242,12 +250,14 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
   }
 
   const int64_t chunk = (nvm + S - 1) / S;
-  // Cross-entropy chunks take a shape of at most 8 vectors per thread when one holds the
-  // chunk (more threads, fewer loads in flight per thread): measured on 8192 x 32000 bf16,
-  // four 16 KB chunks per row at 5.62 TB/s on 64 threads x 16 vectors, 5.80-5.84 on
-  // 128 x 8 (and two 32 KB chunks on 256 x 8 alike); the 128 KB chunks of longer rows keep
-  // 512 x 16, which measured the same as 512 x 8 / 256 x 8 with more chunks.
-  const Shape* sh = op == kOpXent ? pick_shape(menu, nmenu, chunk, 8) : nullptr;
+  // Cross-entropy chunks of up to 32 KB take a shape of at most 8 vectors per thread when
+  // one holds the chunk (more threads, fewer loads in flight per thread): measured on
+  // 8192 x 32000 bf16, four 16 KB chunks per row at 5.62 TB/s on 64 threads x 16 vectors,
+  // 5.80-5.84 on 128 x 8 (and two 32 KB chunks on 256 x 8 alike). Larger chunks take the
+  // smallest shape that holds them: 16384 x 128256 bf16 in four 64 KB chunks at 6.24 TB/s
+  // on 256 x 16, 6.13-6.17 on 512 x 8; the 128 KB chunks of longer rows 512 x 16.
+  const Shape* sh = (op == kOpXent && chunk * 16 <= (32 << 10)) ? pick_shape(menu, nmenu, chunk, 8)
+                                                                 : nullptr;
   if (!sh) sh = pick_shape(menu, nmenu, chunk);
   if (!sh) {
     if (want) return XR_ERR_SHAPE;

@@ -93,18 +93,22 @@ def test_trace_summary_takes_the_headline_launches(tmp_path):
     other workloads has other template arguments or grids), the last `steps` in launch
     order."""
     path = tmp_path / "trace.csv"
-    head = "void xr::xent_rows_kernel<1, 512, 16, 2>(xr::XentParams)"
-    rows = [(head, 32768 * 512, 1000 + 10 * k, 1000 + 10 * k + d)
+    threads, items = bench.headline_launch()
+    head = f"void xr::xent_rows_kernel<1, {threads}, 16, 2>(xr::XentParams)"
+    rows = [(head, items, threads, 1000 + 10 * k, 1000 + 10 * k + d)
             for k, d in enumerate([9, 9, 9, 1, 2, 3])]
-    rows += [("void xr::xent_rows_kernel<1, 128, 8, 2>(xr::XentParams)", 32768 * 128, 5000, 5100),
-             (head, 512 * 512, 6000, 9000), ("__amd_rocclr_copyBuffer", 1024, 7000, 7500)]
+    rows += [("void xr::xent_rows_kernel<1, 128, 8, 2>(xr::XentParams)", 32768 * 128, 128, 5000,
+              5100),
+             (head, 512 * threads, threads, 6000, 9000),
+             ("void xr::xent_rows_kernel<0, 512, 16, 2>(xr::XentParams)", items, 512, 6500, 6600),
+             ("__amd_rocclr_copyBuffer", 1024, 512, 7000, 7500)]
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Start_Timestamp",
-                                          "End_Timestamp"])
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X",
+                                          "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
-        for name, grid, s, e in reversed(rows):
-            w.writerow({"Kernel_Name": name, "Grid_Size_X": grid, "Start_Timestamp": s,
-                        "End_Timestamp": e})
+        for name, grid, wg, s, e in reversed(rows):
+            w.writerow({"Kernel_Name": name, "Grid_Size_X": grid, "Workgroup_Size_X": wg,
+                        "Start_Timestamp": s, "End_Timestamp": e})
     out = bench.summarize_trace(str(path), 3)
     assert out["calls"] == 3 and out["launches_traced"] == 6
     assert out["kernel_ms_avg"] == round(2 / 1e6, 5) and out["kernel_ms_min"] == round(1 / 1e6, 5)

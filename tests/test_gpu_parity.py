@@ -294,12 +294,15 @@ def test_xent_workgroup_sizes(orc, threads):
     (32000, "bf16", 0, (128, 8, 4)),    # 64 KB rows: four 16 KB chunks on 128 x 8
     (32000, "bf16", 2, (256, 8, 2)),    # the same rows forced into two 32 KB chunks
     (16000, "f32", 0, (128, 8, 4)),     # 64 KB fp32 rows
-    (64000, "bf16", 0, (512, 8, 2)),    # 128 KB rows: two 64 KB chunks on 512 x 8
-    (128256, "bf16", 0, (512, 16, 2)),  # 256 KB rows: 128 KB chunks, no 8-vector shape holds
+    (64000, "bf16", 0, (256, 16, 2)),   # 128 KB rows: two 64 KB chunks on 256 x 16
+    (128256, "bf16", 0, (256, 16, 4)),  # 256 KB rows: four ~64 KB chunks on 256 x 16
+    (128256, "bf16", 2, (512, 16, 2)),  # the same rows forced into two 128 KB chunks
+    (256000, "f32", 0, (512, 16, 8)),   # 1 MB rows: eight 128 KB chunks (64 KB would be 16)
 ])
 def test_xent_chunk_shapes(orc, V, dtype, split, want):
-    """Cross-entropy chunks take the smallest shape of at most 8 vectors per thread that
-    holds them, else the smallest shape that does; each plan matches the oracle."""
+    """Cross-entropy chunks of up to 32 KB take the smallest shape of at most 8 vectors per
+    thread that holds them; larger chunks (64 KB up to 512 KB rows, 128 KB above) the
+    smallest shape that holds them; each plan matches the oracle."""
     M = 300
     xr.set_option("split", split)
     p = xr.plan("xent", M, V, torch.bfloat16 if dtype == "bf16" else torch.float32)
@@ -311,21 +314,22 @@ def test_xent_chunk_shapes(orc, V, dtype, split, want):
 
 
 @pytest.mark.parametrize("M,V,dtype,ld", [
-    (261, 66000, "bf16", None),   # two 64.5 KiB chunks per row; a last group of 5 rows
-    (259, 40000, "f32", 40064),   # two 80 KB chunks per padded row; a last group of 3
-    (264, 128256, "bf16", None),  # two 128 KB chunks per row; 33 whole groups
+    (261, 66000, "bf16", None),   # three 43 KiB chunks per row; a last group of 5 rows
+    (259, 40000, "f32", 40064),   # three 53 KB chunks per padded row; a last group of 3
+    (264, 128256, "bf16", None),  # four 64 KB chunks per row; 33 whole groups
+    (40, 256000, "f32", 256064),  # eight 128 KB chunks per row; 5 whole groups
 ])
 def test_xent_write_groups(orc, M, V, dtype, ld):
-    """Split rows with chunks of 64 KB and more are written back in groups of adjacent rows
-    (a chunk holds its stores until its neighbours' chunks have published): ignored rows and
-    out-of-range targets inside a group, and a last group cut short by M, give the oracle's
-    results and leave no error flag."""
+    """Split rows with chunks of 32 KiB and more (at most 8 per row) are written back in
+    groups of adjacent rows (a chunk holds its stores until its neighbours' chunks have
+    published): ignored rows and out-of-range targets inside a group, and a last group cut
+    short by M, give the oracle's results and leave no error flag."""
     x = synth.random_rows(9800 + M, M, V, ld=ld, dtype=dtype, scale=2.0)
     t = synth.random_targets(9801 + M, M, V, ignore_frac=0.25)
     t[min(3, M - 1)] = V + 5
     t[min(6, M - 1)] = -7
     p = xr.plan("xent", M, V, torch.bfloat16 if dtype == "bf16" else torch.float32)
-    assert p["path"] == "split" and p["chunk_vecs"] * 16 >= 64 << 10, p
+    assert p["path"] == "split" and p["chunk_vecs"] * 16 >= 32 << 10 and p["group_rows"] == 8, p
     g, rows, mean, counts = run_xent(x, t, V)
     compare_xent(orc, x, t, V, g, rows, mean, counts, f"groups M {M} V {V} {dtype}")
     # the wait decides nothing: a second call gives bit-identical results

@@ -52,7 +52,7 @@ def check(orc, x_h, dy_h, N, y_h, dx_h, what):
                  f"{what} backward")
 
 
-# (M, N, dtype): long rows (two or more 128 KB chunks), 32-64 KB rows (16 KB chunks), rows
+# (M, N, dtype): long rows (64 KB chunks up to 512 KB rows, 128 KB above), 32-64 KB rows (16 KB chunks), rows
 # too few for the GPU (chunks for every compute unit), ragged sizes, and batches whose rows
 # are written back in groups of 8 (chunks of 32 KiB and more, at most 8 per row; the last
 # group cut short by M).
