@@ -116,7 +116,8 @@ OK = 0
 PATHS = {1: "resident", 2: "split", 3: "stream"}
 OPS = {"softmax_fwd": 0, "softmax_bwd": 1, "xent": 2, "nll_fwd": 3, "softmax_fwd_ws": 4,
        "softmax_bwd_ws": 5}
-OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4, "load_policy": 5, "no_wait": 6}
+OPTIONS = {"path": 1, "split": 2, "threads": 3, "grid": 4, "load_policy": 5, "no_wait": 6,
+           "groups": 7}
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}

@@ -28,7 +28,7 @@ constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups in one launch
 // while another thread launches work is not a data race (which value that launch sees is
 // unspecified).
 struct Options {
-  std::atomic<int64_t> path{0}, split{0}, threads{0}, grid{0}, load_policy{0}, no_wait{0};
+  std::atomic<int64_t> path{0}, split{0}, threads{0}, grid{0}, load_policy{0}, no_wait{0}, groups{0};
 };
 Options g_opt;
 
@@ -317,7 +317,8 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     // or 64 chunks per row 2-7 % slower, a group then being hundreds of slots). A group's
     // chunks have consecutive workgroup ids, so in a normal launch a chunk waits only for
     // chunks resident or next in line; the group must fit the GPU many times over.
-    if (chunk * 16 >= (32 << 10) && S <= 8 && (int64_t)kWriteGroupRows * S * 4 <= resident)
+    const bool group_ok = S <= 8 && (int64_t)kWriteGroupRows * S * 4 <= resident;
+    if (group_ok && (g_opt.groups == 2 || (g_opt.groups == 0 && chunk * 16 >= (32 << 10))))
       p.group_rows = kWriteGroupRows;
   } else {
     p.path = kPathSplit;
@@ -524,6 +525,10 @@ xr_status_t xr_set_option(xr_option_t option, int64_t value) {
     case XR_OPT_NO_WAIT:
       if (value < 0 || value > 1) return XR_ERR_OPTION;
       g_opt.no_wait = value;
+      return XR_OK;
+    case XR_OPT_GROUPS:
+      if (value < 0 || value > 2) return XR_ERR_OPTION;
+      g_opt.groups = value;
       return XR_OK;
   }
   return XR_ERR_OPTION;

@@ -411,6 +411,9 @@ xr_status_t xr_plan_model(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype, in
  *                   the timeout flag in counts[2], set from the start); the waits that
  *                   group adjacent rows' stores end at once. For testing the bounded-wait
  *                   path; never faster.
+ *   XR_OPT_GROUPS   write groups of split rows: 1 = never, 2 = whenever the plan's
+ *                   residency condition allows them (chunks of any size); 0 = the automatic
+ *                   choice (chunks of 32 KiB and more)
  */
 typedef enum xr_option {
   XR_OPT_PATH = 1,
@@ -418,7 +421,8 @@ typedef enum xr_option {
   XR_OPT_THREADS = 3,
   XR_OPT_GRID = 4,
   XR_OPT_LOAD_POLICY = 5,
-  XR_OPT_NO_WAIT = 6
+  XR_OPT_NO_WAIT = 6,
+  XR_OPT_GROUPS = 7
 } xr_option_t;
 
 xr_status_t xr_set_option(xr_option_t option, int64_t value);

@@ -213,7 +213,8 @@ def test_options(xr):
     assert o(1, 4) == XR_ERR_OPTION and o(2, 1) == XR_ERR_OPTION and o(3, 96) == XR_ERR_OPTION
     assert o(4, -2) == XR_ERR_OPTION and o(99, 0) == XR_ERR_OPTION
     assert o(5, 3) == XR_ERR_OPTION and o(6, 2) == XR_ERR_OPTION and o(6, -1) == XR_ERR_OPTION
-    for opt, val in ((1, 3), (2, 4), (3, 256), (4, -1), (5, 2), (6, 1)):
+    assert o(7, 3) == XR_ERR_OPTION and o(7, -1) == XR_ERR_OPTION
+    for opt, val in ((1, 3), (2, 4), (3, 256), (4, -1), (5, 2), (6, 1), (7, 2), (7, 1)):
         assert o(opt, val) == XR_OK
     xr.reset_options()
 

@@ -338,6 +338,25 @@ def test_xent_write_groups(orc, M, V, dtype, ld):
     assert np.array_equal(rows.view(np.uint8), rows2.view(np.uint8)) and mean == mean2
 
 
+@pytest.mark.parametrize("M,V,dtype", [(300, 32000, "bf16"), (72, 128256, "bf16"),
+                                       (33, 70001, "f32")])
+def test_xent_write_groups_decide_nothing(orc, M, V, dtype):
+    """Write groups forced off, automatic and forced on (XR_OPT_GROUPS 1, 0, 2) give
+    bit-identical gradients and losses that match the oracle."""
+    x = synth.random_rows(9850 + M, M, V, dtype=dtype, scale=2.0)
+    t = synth.random_targets(9851 + M, M, V, ignore_frac=0.2)
+    outs = []
+    for groups in (1, 0, 2):
+        xr.set_option("groups", groups)
+        outs.append(run_xent(x, t, V))
+    xr.set_option("groups", 0)
+    g, rows, mean, counts = outs[1]
+    compare_xent(orc, x, t, V, g, rows, mean, counts, f"groups {M}x{V} {dtype}")
+    for g2, rows2, mean2, _ in outs[::2]:
+        assert np.array_equal(g.view(np.uint8), g2.view(np.uint8)), "gradient differs"
+        assert np.array_equal(rows.view(np.uint8), rows2.view(np.uint8)) and mean == mean2
+
+
 @pytest.mark.parametrize("grid", [1, 2, -1])
 def test_xent_grid_shapes(orc, grid):
     """Persistent grids (rows g, g + G, ... with the next row's loads issued while the
