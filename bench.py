@@ -788,6 +788,10 @@ def run_extras(args) -> dict:
     import torch
 
     out = {}
+    prof = profiled_kernel()
+    profiled = {w: {k: {key: v[key] for key in ("kernel_ms_avg", "achieved_GBps", "frac", "calls")}
+                    for k, v in ks.items()}
+                for w, ks in (prof or {}).get("other_configs", {}).items()}
     for name in EXTRAS:
         torch.cuda.empty_cache()
         a = copy.copy(args)
@@ -804,7 +808,9 @@ def run_extras(args) -> dict:
             "kernels": {
                 k: {"kernel": r["kernel"], "kernel_ms_avg": r["kernel_ms_avg"],
                     "kernel_ms_min": r.get("kernel_ms_min"), "achieved_GBps": r["achieved"],
-                    "frac": r["frac"], **({"ceiling": r["ceiling"]} if "ceiling" in r else {})}
+                    "frac": r["frac"], **({"ceiling": r["ceiling"]} if "ceiling" in r else {}),
+                    **({"profiled": profiled[name][k]}
+                       if name in profiled and k in profiled[name] else {})}
                 for k, r in kernels}}
         print(f"[bench] {name}: " + ", ".join(
             f"{k} {v['achieved_GBps']} GB/s ({100 * v['frac']:.1f} %)"
@@ -862,37 +868,61 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str = "c4") -> 
     return out[ROW_KERNEL] if workload == "c4" else {"workload": workload, "kernels": out}
 
 
-def headline_launch():
-    """(workgroup size, work-items) of the headline row kernel's launch, from the library's
-    plan for the 16384 x 128256 bf16 rows on a modelled 256-CU device (the plan of rows this
-    many does not depend on the occupancy)."""
+def traced_launches():
+    """Every traced kernel of the default run: (name in the summary, kernel name prefix and
+    dtype template argument, workgroup size, work-items, minimal bytes), from the library's
+    plans on a modelled 256-CU device (plans of rows this many do not depend on occupancy)."""
     import torch
 
     import cross_entropy_reductions_amd as xr
 
-    p = xr.plan_model("xent", C4_M, C4_V, torch.bfloat16, 256, 2)
-    return p["threads"], p["grid_total"] * p["threads"]
+    def xent(M, V, keep, dt, elt):
+        p = xr.plan_model("xent", M, V, dt, 256, 2)
+        return (f"{ROW_KERNEL}<{1 if dt == torch.bfloat16 else 0}, {p['threads']},", p["threads"],
+                p["grid_total"] * p["threads"], xent_bmin(M, V, keep, elt))
+
+    def soft(op, kernel, nbytes):
+        p = xr.plan_model(op, 4096, 4096, torch.bfloat16, 256, 2)
+        return (f"{kernel}<1, {p['threads']},", p["threads"], p["grid_total"] * p["threads"],
+                nbytes)
+
+    return {"c4": {"xent": xent(C4_M, C4_V, C4_KEEP, torch.bfloat16, 2)},
+            "c3": {"xent": xent(8192, 32000, 7373, torch.bfloat16, 2)},
+            "c5": {"xent": xent(2048, 256000, 2048, torch.float32, 4)},
+            "c2": {"softmax_fwd": soft("softmax_fwd_ws", "softmax_fwd_kernel", 2 * 4096 * 4096 * 2),
+                   "softmax_bwd": soft("softmax_bwd_ws", "softmax_bwd_kernel", 3 * 4096 * 4096 * 2)}}
 
 
 def summarize_trace(trace_csv: str, steps: int) -> dict:
-    """The headline row kernel's average duration from a rocprofv3 --kernel-trace CSV of the
-    default command: its bf16 launches in the headline's launch shape (told apart from the
-    same kernel's launches on the other workloads by workgroup and grid size), the last
-    `steps` of them in launch order being the timed steps."""
-    threads, items = headline_launch()
-    launches = []
+    """Each benchmarked kernel's average duration from a rocprofv3 --kernel-trace CSV of the
+    default command: its launches in its plan's launch shape (told apart from the same
+    kernel's launches on the other workloads by dtype, workgroup and grid size), the last
+    `steps` of them in launch order being the timed steps. The headline's figures sit at the
+    top level, the others under other_configs, all with the kernel-source hash."""
+    want = traced_launches()
+    launches = {(w, k): [] for w, ks in want.items() for k in ks}
     with open(trace_csv) as f:
         for row in csv.DictReader(f):
-            if f"{ROW_KERNEL}<1, {threads}," in row["Kernel_Name"] \
-                    and int(row["Workgroup_Size_X"]) == threads and int(row["Grid_Size_X"]) == items:
-                launches.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
-    launches.sort()
-    ns = [e - s for s, e in launches[-steps:]]
-    return {"kernel": ROW_KERNEL, "kernel_source_hash": kernel_source_hash(),
-            "kernel_ms_avg": round(statistics.mean(ns) / 1e6, 5),
-            "kernel_ms_min": round(min(ns) / 1e6, 5), "calls": len(ns),
-            "launches_traced": len(launches),
-            "bytes_min": xent_bmin(C4_M, C4_V, C4_KEEP, 2)}
+            for (w, k), lst in launches.items():
+                prefix, threads, items, _ = want[w][k]
+                if prefix in row["Kernel_Name"] and int(row["Workgroup_Size_X"]) == threads \
+                        and int(row["Grid_Size_X"]) == items:
+                    lst.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+
+    def fig(w, k):
+        ns = [e - s for s, e in sorted(launches[(w, k)])[-steps:]]
+        ms = statistics.mean(ns) / 1e6
+        b = want[w][k][3]
+        return {"kernel_ms_avg": round(ms, 5), "kernel_ms_min": round(min(ns) / 1e6, 5),
+                "calls": len(ns), "launches_traced": len(launches[(w, k)]), "bytes_min": b,
+                "achieved_GBps": round(b / ms / 1e6, 1),
+                "frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+    out = {"kernel": ROW_KERNEL, "kernel_source_hash": kernel_source_hash(), **fig("c4", "xent")}
+    out["other_configs"] = {w: {k: fig(w, k) for k in ks if launches[(w, k)]}
+                            for w, ks in want.items() if w != "c4"}
+    return out
+
 
 
 def main() -> int:

@@ -282,8 +282,8 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
  * row losses) lives in a static device array of the library, XR_NOALLOC_SCRATCH_BYTES on
  * each device it runs on, held until the process ends. Sizes whose scratch would not fit
  * return XR_ERR_TOO_LARGE with nothing enqueued (xr_xent_workspace_bytes() tells the need;
- * for instance 16384 x 128256 bf16 needs 256 + 16384 x 2 x 8 bytes, plus 4 per row without
- * row_loss). Nothing is allocated, freed or synchronised; the kernels initialise what must
+ * for instance 16384 x 128256 bf16, four chunks per row, needs 256 + 16384 x 4 x 8 bytes,
+ * plus 4 per row without row_loss). Nothing is allocated, freed or synchronised; the kernels initialise what must
  * start at zero. Every call on a device shares that device's array and leaves its contents
  * behind: calls that overlap in time on one device (several streams, several threads) race
  * and must not be made. Arguments and results are otherwise those of xr_xent_fwd_bwd_ex().

@@ -93,7 +93,7 @@ def test_trace_summary_takes_the_headline_launches(tmp_path):
     other workloads has other template arguments or grids), the last `steps` in launch
     order."""
     path = tmp_path / "trace.csv"
-    threads, items = bench.headline_launch()
+    _, threads, items, _ = bench.traced_launches()["c4"]["xent"]
     head = f"void xr::xent_rows_kernel<1, {threads}, 16, 2>(xr::XentParams)"
     rows = [(head, items, threads, 1000 + 10 * k, 1000 + 10 * k + d)
             for k, d in enumerate([9, 9, 9, 1, 2, 3])]
@@ -111,6 +111,10 @@ def test_trace_summary_takes_the_headline_launches(tmp_path):
                         "Start_Timestamp": s, "End_Timestamp": e})
     out = bench.summarize_trace(str(path), 3)
     assert out["calls"] == 3 and out["launches_traced"] == 6
+    # the 8192 x 32000 workload's one launch is told apart by its shape; c2 and c5 are absent
+    assert out["other_configs"]["c3"]["xent"]["calls"] == 1
+    assert out["other_configs"]["c3"]["xent"]["kernel_ms_avg"] == round(100 / 1e6, 5)
+    assert out["other_configs"]["c2"] == {} and out["other_configs"]["c5"] == {}
     assert out["kernel_ms_avg"] == round(2 / 1e6, 5) and out["kernel_ms_min"] == round(1 / 1e6, 5)
     assert out["kernel_source_hash"] == bench.kernel_source_hash()
 
