@@ -100,3 +100,52 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
     assert counts.tolist() == [M, 0, 0]
     # one column: loss 0 and gradient 0 in exact arithmetic (fp32 leaves the loss a residue)
     assert abs(float(loss.item())) < 1e-6 and bool((x == 0).all())
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for: two calls of different sizes captured into one HIP graph
+    (kernels only: nothing to allocate, no memset), replayed three times on fresh copies of
+    the inputs with eager work between the replays; every replay equals the eager results
+    bit for bit."""
+    cases = [(256, 32000, 31300), (8, 128256, 31310)]
+    xs, ts, eager = [], [], []
+    for M, V, seed in cases:
+        x_h = synth.random_rows(seed, M, V, dtype="bf16", scale=2.0)
+        t_h = synth.random_targets(seed + 1, M, V, ignore_frac=0.1)
+        xs.append(to_device(x_h))
+        ts.append(to_device(t_h))
+        a = xs[-1].clone()
+        st, loss, rows, counts = noalloc(a, ts[-1])
+        assert st == 0, xr.status_string(st)
+        eager.append([a, loss, rows, counts])
+    torch.cuda.synchronize()
+    static_x = [x.clone() for x in xs]
+    outs = [(torch.empty(1, dtype=torch.float32, device="cuda"),
+             torch.empty(M, dtype=torch.float32, device="cuda"),
+             torch.empty(3, dtype=torch.int32, device="cuda")) for M, _, _ in cases]
+    stream = ctypes.c_void_p
+
+    def run():
+        for (M, V, _), x, t, (loss, rows, counts) in zip(cases, static_x, ts, outs):
+            st = xr.lib.xr_xent_fwd_bwd_noalloc(
+                x.data_ptr(), V, t.data_ptr(), M, V, -100, xr.BF16, xr.REDUCTIONS["mean"], None,
+                0, rows.data_ptr(), loss.data_ptr(), counts.data_ptr(),
+                stream(torch.cuda.current_stream().cuda_stream))
+            assert st == 0, xr.status_string(st)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for k in range(3):
+        for dst, src in zip(static_x, xs):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (x, (loss, rows, counts)) in enumerate(zip(static_x, outs)):
+            want = eager[i]
+            assert torch.equal(bits(x), bits(want[0])), f"replay {k} case {i}: gradient"
+            assert torch.equal(bits(loss), bits(want[1])), f"replay {k} case {i}: loss"
+            assert torch.equal(bits(rows), bits(want[2])), f"replay {k} case {i}: row losses"
+            assert torch.equal(counts, want[3]), f"replay {k} case {i}: counts"
+        _ = (static_x[0].float() * 2).sum().item()  # the program's own work between replays
