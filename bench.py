@@ -22,7 +22,7 @@ and reports each kernel's figures under `other_configs` (`value`, `config` and
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
                     [--reduction mean|sum|none]
                     [--grad-scale S] [--rows M] [--no-extras]
-    python bench.py --summarize-counters FETCH.csv WRITE.csv [--workload c4|c3|c5|c2]
+    python bench.py --summarize-counters FETCH.csv WRITE.csv [--workload <name>]
                                                                (rocprofv3 --pmc output)
     python bench.py --summarize-trace KERNEL_TRACE.csv [--steps K] (rocprofv3 --kernel-trace)
 
@@ -550,7 +550,8 @@ def run_nll(args, name: str) -> dict:
     torch.cuda.set_device(dev)
     w = synth.xent_c4()
     M, N = w["M"], w["N"]
-    x = _device_matrix(torch, w["x"], dev)
+    # one device copy of known size before the timed region (it calibrates HBM counters)
+    x = _device_matrix(torch, w["x"], dev).clone()
     idx = torch.from_numpy(w["target"]).clamp(min=0).to(dev)
     out = torch.empty_like(x)
     loss = torch.empty(M, dtype=torch.float32, device=dev)
@@ -820,13 +821,39 @@ def run_extras(args) -> dict:
 
 # Counter summaries: per workload, the matrix the benchmark copies before its timed region
 # (bytes of one copy), and the kernels to summarise with their minimal bytes per launch.
+LN_M, LN_N = 16384, 8192
+VOCAB_M, VOCAB_N = 4096, 128256
+FEW_M, FEW_N = 16, 1 << 20
 COUNTER_WORKLOADS = {
     "c4": (C4_M * C4_V * 2, [(ROW_KERNEL, xent_bmin(C4_M, C4_V, C4_KEEP, 2))]),
     "c3": (8192 * 32000 * 2, [(ROW_KERNEL, xent_bmin(8192, 32000, 7373, 2))]),
     "c5": (2048 * 256064 * 4, [(ROW_KERNEL, xent_bmin(2048, 256000, 2048, 4))]),
     "c2": (4096 * 4096 * 2, [("softmax_fwd_kernel", 2 * 4096 * 4096 * 2),
                              ("softmax_bwd_kernel", 3 * 4096 * 4096 * 2)]),
+    "c4-mul": (C4_M * C4_V * 2, [("element_mul_kernel", 2 * C4_M * C4_V * 2 + 4)]),
+    "c4-nll": (C4_M * C4_V * 2, [("softmax_split_kernel", 2 * C4_M * C4_V * 2 + 12 * C4_M)]),
+    # layer norm: the backward's stage 1 also writes one row of fp32 column sums per workgroup
+    # (not counted here: they are the price of a deterministic dw / db)
+    "ln": (LN_M * LN_N * 2, [("ln_fwd_kernel", 2 * LN_M * LN_N * 2 + 2 * LN_N * 2 + 8 * LN_M),
+                             ("ln_bwd_kernel", 3 * LN_M * LN_N * 2 + LN_N * 2 + 8 * LN_M)]),
+    "sm-vocab": (VOCAB_M * VOCAB_N * 2,
+                 [("softmax_split_kernel", 2 * VOCAB_M * VOCAB_N * 2),
+                  ("softmax_bwd_split_kernel", 3 * VOCAB_M * VOCAB_N * 2)]),
+    "sm-few": (FEW_M * FEW_N * 4, [("softmax_split_kernel", 2 * FEW_M * FEW_N * 4),
+                                   ("softmax_bwd_split_kernel", 3 * FEW_M * FEW_N * 4)]),
 }
+
+
+def counter_workload(name: str):
+    """(bytes of the copied matrix, [(kernel, minimal bytes per launch)]) of a workload."""
+    if name != "bsr":
+        return COUNTER_WORKLOADS[name]
+    import synth
+    w = synth.bsr_softmax(Z=1)  # the layout only: Z, seq and block are the workload's
+    Z, seq, block = 32, w["seq"], w["block"]
+    listed = int(w["layout"].sum()) * Z * block * block
+    stored = Z * w["n_blocks"] * block * block * 2
+    return stored, [("bsr_softmax_bwd_kernel", 3 * listed * 2 + w["lut"].size * 4)]
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, workload: str = "c4") -> dict:
@@ -835,7 +862,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str = "c4") -> 
     runtime's device copies of the workload's input matrix (the copies bench.py makes before
     its timed region: one known read and one known write of the whole matrix). For c4 the
     result is what bench.py reports as roofline.traffic."""
-    matrix, kernels = COUNTER_WORKLOADS[workload]
+    matrix, kernels = counter_workload(workload)
 
     def per_kernel(path):
         vals = {}

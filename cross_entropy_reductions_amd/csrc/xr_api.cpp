@@ -287,6 +287,9 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     int64_t g = M;
     if (g_opt.grid > 0) g = (int64_t)di.cus * std::min<int64_t>(g_opt.grid, per_cu);
     p.grid = std::max<int64_t>(1, std::min<int64_t>(M, g));
+    // the backward's loop-free form when every row has a workgroup of its own
+    if (bwd && p.grid >= M) p.kernel = softmax_bwd_kernel_ptr(dt, *sh, nt_loads, true);
+    if (!p.kernel) return XR_ERR_SHAPE;
   } else if (other_split || (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF)) {
     // (only the cross-entropy has a persistent split form). A row's S chunks must be able
     // to be resident together, or its first chunks could wait for chunks that cannot start

@@ -177,7 +177,8 @@ const void* nll_fwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* nll_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_fwd_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
 const void* softmax_bwd_split_kernel_ptr(int dtype, Shape s, bool nt_loads);
-const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads);
+// one_row: the form for a grid of at least M workgroups (one row each, no loop).
+const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool nt_loads, bool one_row = false);
 const void* xent_stream_kernel_ptr(int dtype);
 const void* softmax_fwd_stream_kernel_ptr(int dtype);
 const void* nll_fwd_stream_kernel_ptr(int dtype);

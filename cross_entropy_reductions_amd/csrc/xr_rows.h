@@ -54,6 +54,21 @@ __device__ __forceinline__ void issue_loads(u32x4 (&v)[VPT], const Chunk<D>& c) 
   for (int k = 0; k < VPT; ++k) v[k] = buf_load<LP>(c.slot(k * THREADS), off);
 }
 
+// The loads of two chunks of the same layout, issued in pairs (a[0], b[0], a[1], b[1], ...):
+// loads complete in issue order, so work on slot k can start once slot k of both has arrived
+// (the scheduler would otherwise regroup them by resource).
+template <int D, int THREADS, int VPT, int LP>
+__device__ __forceinline__ void issue_loads2(u32x4 (&a)[VPT], const Chunk<D>& ca, u32x4 (&b)[VPT],
+                                             const Chunk<D>& cb) {
+  const uint32_t off = threadIdx.x * 16u;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    a[k] = buf_load<LP>(ca.slot(k * THREADS), off);
+    b[k] = buf_load<LP>(cb.slot(k * THREADS), off);
+    __builtin_amdgcn_sched_barrier(0);  // keep the pairs in this order
+  }
+}
+
 // How slot k relates to a chunk of nvec vectors (workgroup-uniform): every lane inside,
 // some lanes inside (the last slot), or none.
 enum SlotKind { kSlotFull, kSlotPart, kSlotNone };

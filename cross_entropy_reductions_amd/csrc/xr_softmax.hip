@@ -208,7 +208,72 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
 }
 
 // ============================================================================ softmax backward
-template <int D, int THREADS, int VPT, int LP>
+// One row of the backward: vy / vd hold row r's y and dy (their loads issued in pairs);
+// dx = y (dy - sum(y dy)). With PREFETCH, the loads of row rn (if rn < M) are issued as the
+// slots of row r are stored.
+template <int D, int THREADS, int VPT, int LP, bool PREFETCH>
+__device__ __forceinline__ void softmax_bwd_row(const SoftmaxBwdParams& p, int64_t r, int64_t rn,
+                                                u32x4 (&vy)[VPT], u32x4 (&vd)[VPT], float* red) {
+  constexpr int EPV = Elt<D>::kPerVec;
+  const int64_t cv = p.N + EPV;
+  // y, dy and dx rows share their alignment (host-checked), hence their vector layout.
+  const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);
+  const Chunk<D> cx(p.dx + r * p.lddx_bytes, p.N, 0, cv);
+  // Out-of-row elements of both operands count as 0: they add nothing to the dot product.
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) continue;
+    const u32x4 a = masked_slot<D, THREADS>(vy[k], k, cy, 0u);
+    const u32x4 b = masked_slot<D, THREADS>(vd[k], k, cy, 0u);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e)
+      s[e & 3] = __builtin_fmaf(elem<D>(a, e), elem<D>(b, e), s[e & 3]);
+  }
+  const float dot = block_reduce<THREADS>((s[0] + s[1]) + (s[2] + s[3]), OpAdd(), red);
+  reg_barrier(vy);
+  reg_barrier(vd);
+  const bool pf = PREFETCH && rn < p.M;
+  const Chunk<D> cyn(p.y + (pf ? rn : r) * p.ldy_bytes, p.N, 0, cv);
+  const Chunk<D> cdn(p.dy + (pf ? rn : r) * p.lddy_bytes, p.N, 0, cv);
+  const uint32_t off = threadIdx.x * 16u;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    OutVec<D> o;
+    u32x4 a = vy[k], b = vd[k];
+    pin(a);  // fp32 too: unpinned, the fp32 shapes with 8 vectors per thread spill
+    pin(b);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+    store_slot<D, THREADS>(cx, k, o.bits());
+    if (pf) {
+      vy[k] = buf_load<LP>(cyn.slot(k * THREADS), off);
+      vd[k] = buf_load<LP>(cdn.slot(k * THREADS), off);
+    }
+  }
+  // Partial first / last vectors: re-read y and dy (this workgroup has not written them;
+  // dx may be exactly y or dy) and store only the in-row elements.
+  const Chunk<D> cd(p.dy + r * p.lddy_bytes, p.N, 0, cv);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int vi = q == 0 ? cx.head : cx.tail;
+    if (vi < 0 || (int)threadIdx.x != vi % THREADS) continue;
+    const uint32_t po = q == 0 ? cx.hoff : cx.toff;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cy.rsrc, (int)po, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cd.rsrc, (int)po, 0, 0);
+    OutVec<D> o;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+    store_partial<D>(cx.rsrc, po, o.bits(), q == 0 ? cx.h0 : cx.t0, q == 0 ? cx.h1 : cx.t1);
+  }
+}
+
+// Workgroup b handles rows b, b + G, ... (G = the grid). ONE_ROW: the grid covers the rows
+// (G >= M, the plans' default; the host checks it), and the row is handled without the
+// loop: the compiler's waits for the loads then follow the pairs as they arrive, where the
+// loop's prefetch of the next row would merge them with that row's loads (and the two forms
+// in one kernel would raise its register count until it spilled).
+template <int D, int THREADS, int VPT, int LP, bool ONE_ROW>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void softmax_bwd_kernel(SoftmaxBwdParams p) {
   constexpr int EPV = Elt<D>::kPerVec;
   constexpr int NW = THREADS / kWave;
@@ -219,67 +284,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
 
   u32x4 vy[VPT], vd[VPT];
   int64_t r = blockIdx.x;
-  int buf = 0;
-  if (r < p.M) {
-    issue_loads<D, THREADS, VPT, LP>(vy, Chunk<D>(p.y + r * p.ldy_bytes, p.N, 0, cv));
-    issue_loads<D, THREADS, VPT, LP>(vd, Chunk<D>(p.dy + r * p.lddy_bytes, p.N, 0, cv));
-  }
-  while (r < p.M) {
-    const int64_t rn = r + G;
-    // y, dy and dx rows share their alignment (host-checked), hence their vector layout.
-    const Chunk<D> cy(p.y + r * p.ldy_bytes, p.N, 0, cv);
-    const Chunk<D> cx(p.dx + r * p.lddx_bytes, p.N, 0, cv);
-    // Out-of-row elements of both operands count as 0: they add nothing to the dot product.
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) continue;
-      const u32x4 a = masked_slot<D, THREADS>(vy[k], k, cy, 0u);
-      const u32x4 b = masked_slot<D, THREADS>(vd[k], k, cy, 0u);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e)
-        s[e & 3] = __builtin_fmaf(elem<D>(a, e), elem<D>(b, e), s[e & 3]);
+  if (r >= p.M) return;
+  issue_loads2<D, THREADS, VPT, LP>(vy, Chunk<D>(p.y + r * p.ldy_bytes, p.N, 0, cv), vd,
+                                    Chunk<D>(p.dy + r * p.lddy_bytes, p.N, 0, cv));
+  if constexpr (ONE_ROW) {
+    softmax_bwd_row<D, THREADS, VPT, LP, false>(p, r, p.M, vy, vd, red[0]);
+  } else {
+    int buf = 0;
+    while (r < p.M) {
+      const int64_t rn = r + G;
+      softmax_bwd_row<D, THREADS, VPT, LP, true>(p, r, rn, vy, vd, red[buf]);
+      buf ^= 1;
+      r = rn;
     }
-    const float dot = block_reduce<THREADS>((s[0] + s[1]) + (s[2] + s[3]), OpAdd(), red[buf]);
-    buf ^= 1;
-    reg_barrier(vy);
-    reg_barrier(vd);
-    const bool pf = rn < p.M;
-    const Chunk<D> cyn(p.y + (pf ? rn : r) * p.ldy_bytes, p.N, 0, cv);
-    const Chunk<D> cdn(p.dy + (pf ? rn : r) * p.lddy_bytes, p.N, 0, cv);
-    const uint32_t off = threadIdx.x * 16u;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      OutVec<D> o;
-      u32x4 a = vy[k], b = vd[k];
-      pin(a);  // fp32 too: unpinned, the fp32 shapes with 8 vectors per thread spill
-      pin(b);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
-      store_slot<D, THREADS>(cx, k, o.bits());
-      if (pf) {
-        vy[k] = buf_load<LP>(cyn.slot(k * THREADS), off);
-        vd[k] = buf_load<LP>(cdn.slot(k * THREADS), off);
-      }
-    }
-    // Partial first / last vectors: re-read y and dy (this workgroup has not written them;
-    // dx may be exactly y or dy) and store only the in-row elements.
-    {
-      const Chunk<D> cd(p.dy + r * p.lddy_bytes, p.N, 0, cv);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int vi = q == 0 ? cx.head : cx.tail;
-        if (vi < 0 || (int)threadIdx.x != vi % THREADS) continue;
-        const uint32_t po = q == 0 ? cx.hoff : cx.toff;
-        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cy.rsrc, (int)po, 0, 0);
-        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cd.rsrc, (int)po, 0, 0);
-        OutVec<D> o;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
-        store_partial<D>(cx.rsrc, po, o.bits(), q == 0 ? cx.h0 : cx.t0, q == 0 ? cx.h1 : cx.t1);
-      }
-    }
-    r = rn;
   }
 }
 
@@ -437,9 +454,13 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream_kernel(Soft
     return lp ? reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyNT, true>)     \
               : reinterpret_cast<const void*>(&softmax_fwd_kernel<D, T, V, kPolicyDefault, true>);
 #define XR_CASE_SBWD(D, T, V)                                                                  \
-  if (s.threads == T && s.vpt == V)                                                              \
-    return lp ? reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyNT>)           \
-              : reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyDefault>);
+  if (s.threads == T && s.vpt == V) {                                                            \
+    if (one_row)                                                                                 \
+      return lp ? reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyNT, true>)   \
+                : reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyDefault, true>); \
+    return lp ? reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyNT, false>)    \
+              : reinterpret_cast<const void*>(&softmax_bwd_kernel<D, T, V, kPolicyDefault, false>); \
+  }
 
 const void* softmax_fwd_kernel_ptr(int dtype, Shape s, bool lp) {
   if (dtype == kF32) { XR_SHAPES_FWD(XR_CASE_SFWD, kF32) }
@@ -478,7 +499,7 @@ const void* softmax_bwd_split_kernel_ptr(int dtype, Shape s, bool lp) {
   if (dtype == kBF16) { XR_SHAPES_BWD(XR_CASE_SBWDS, kBF16) }
   return nullptr;
 }
-const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool lp) {
+const void* softmax_bwd_kernel_ptr(int dtype, Shape s, bool lp, bool one_row) {
   if (dtype == kF32) { XR_SHAPES_BWD(XR_CASE_SBWD, kF32) }
   if (dtype == kBF16) { XR_SHAPES_BWD(XR_CASE_SBWD, kBF16) }
   return nullptr;

@@ -72,6 +72,29 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
     assert out["kernel_source_hash"] == bench.kernel_source_hash()
 
 
+def test_counter_summary_of_every_workload(tmp_path):
+    """Every workload's kernels are told apart by name (the forward's split kernel is not the
+    backward's), and traffic equal to the minimal bytes reads as 1.0."""
+    copy = "__amd_rocclr_copyBuffer"
+    names = {"softmax_split_kernel": "void xr::softmax_split_kernel<1, 512, 16, 8, false>(xr::SoftmaxFwdParams)",
+             "softmax_bwd_split_kernel": "void xr::softmax_bwd_split_kernel<1, 512, 16, 8>(xr::SoftmaxBwdParams)"}
+    for wl in ["c2", "c3", "c5", "c4-mul", "c4-nll", "ln", "bsr", "sm-vocab", "sm-few"]:
+        matrix, kernels = bench.counter_workload(wl)
+        fetch_rows, write_rows = [(copy, matrix / 2048.0)] * 2, [(copy, matrix / 1024.0)] * 2
+        for k, bmin in kernels:
+            name = names.get(k, f"void xr::{k}<1, 256, 8>(xr::Params)")
+            fetch_rows += [(name, bmin / 2 / 2048.0)] * 3   # half of it read, at half scale
+            write_rows += [(name, bmin / 2 / 1024.0)] * 3
+        f, w = tmp_path / f"{wl}_f.csv", tmp_path / f"{wl}_w.csv"
+        _write_counters(f, fetch_rows)
+        _write_counters(w, write_rows)
+        out = bench.summarize_counters(str(f), str(w), workload=wl)
+        got = {k: v["traffic_over_bytes_min"] for k, v in out["kernels"].items()}
+        assert got == {k: 1.0 for k, _ in kernels}, (wl, got)
+    # the block-sparse workload: 32 maps of 453 stored 64 x 64 bf16 blocks
+    assert bench.counter_workload("bsr")[0] == 32 * 453 * 64 * 64 * 2
+
+
 def test_cpu_baselines_on_small_inputs():
     """The oracle baselines run on a small sample and report the contract's fields."""
     x = synth.random_rows(31, 40, 1024, dtype="bf16", scale=1.0)

@@ -464,6 +464,34 @@ def test_softmax_bwd_aliases(orc):
     check_fp32(to_host(yd), want, "dx == y")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_softmax_bwd_grid_forms(orc, dtype):
+    """The backward's two forms: one workgroup per row (the loop-free form the plans pick) and
+    persistent grids of 1 and 2 workgroups per compute unit (rows r, r + G, ... with the next
+    row's loads issued while the current one is written). Same bits from all three, matching
+    the oracle; the rows' pitch puts partial vectors at both ends of most rows."""
+    M, N, ld = 700, 3001, 3013
+    y_h = synth.random_rows(12300, M, N, ld=ld, dtype=dtype, scale=0.01)
+    dy_h = synth.random_rows(12301, M, N, ld=ld, dtype=dtype, scale=1.0)
+    want = orc.softmax_bwd(np.ascontiguousarray(y_h[:, :N]), np.ascontiguousarray(dy_h[:, :N]))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    outs = []
+    for grid in (0, 1, 2):
+        xr.set_option("grid", grid)
+        p = xr.plan("softmax_bwd", M, N, tdt, aligned=1)
+        assert p["path"] == "resident" and (p["grid"] == M) == (grid == 0), p
+        y, dy = to_device(y_h), to_device(dy_h)
+        dx = torch.full((M, ld), float("nan"), dtype=tdt, device="cuda")
+        xr.softmax_bwd(y[:, :N], dy[:, :N], dx[:, :N])
+        got = to_host(dx)
+        check_output(np.ascontiguousarray(got[:, :N]), want, f"{dtype} grid {grid}")
+        assert np.all(np.isnan(widen(got[:, N:]))), "padding written"
+        outs.append(got[:, :N].copy())
+    xr.reset_options()
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8)), "forms differ"
+
+
 def test_softmax_neg_inf(orc):
     x = synth.random_rows(12200, 5, 3000, dtype="f32", scale=3.0)
     x[0, :2999] = -np.inf
