@@ -16,7 +16,11 @@ on this host's cores. After the headline, the default run times the other config
 of the 75 %-of-peak target in the same process -- the softmax forward and backward over
 4096 x 4096 bf16, the cross-entropy over 8192 x 32000 bf16 and over 2048 x 256000 fp32 --
 and reports each kernel's figures under `other_configs` (`value`, `config` and
-`ms_per_step` stay the headline's).
+`ms_per_step` stay the headline's). Beside each of these kernels, `ceiling` times the
+no-arithmetic probe of the row kernels' launch shapes over the same rows (xr_probe_rows);
+beside the headline, `ceiling.copy` also times a plain copy of its logit matrix, one read
+and one write of every byte (xr_probe_copy: the runtime's device-to-device copy and a
+grid-stride copy kernel over a range of grids), the achievable rate of that traffic.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
@@ -504,9 +508,44 @@ def run_xent(args, name: str) -> dict:
         out["roofline"]["ceiling"] = ceiling(
             args, out["roofline"]["kernel_ms_avg"], bmin,
             (p["threads"], p["vec_per_thread"], p["split"]), probe_shapes(nv, False), probe)
+        if name == "c4" and not args.rows:
+            out["roofline"]["ceiling"]["copy"] = copy_ceiling(
+                args, copies, out["roofline"]["kernel_ms_avg"], bmin)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
     return out
+
+
+# Launches of the plain copy of the ceiling: (workgroups, threads); 0 workgroups is the
+# runtime's device-to-device copy.
+COPY_LAUNCHES = [(0, 0)] + [(g, 256) for g in (4096, 16384, 65536, 131072, 262144, 524288,
+                                                1048576)] + \
+    [(g, 512) for g in (131072, 262144, 524288)]
+
+
+def copy_ceiling(args, mats, kernel_ms: float, bmin: int) -> dict:
+    """One read and one write of every byte of a matrix, nothing else (xr_probe_copy): the
+    runtime's device-to-device copy and a grid-stride copy kernel over a range of grids,
+    timed like the row kernel (HIP events around each launch, from one matrix of `mats` into
+    the next). Returns each rate and the row kernel's rate over the fastest copy's."""
+    import cross_entropy_reductions_amd as xr
+
+    nbytes = 2 * mats[0].numel() * mats[0].element_size()  # read + written
+    n = len(mats)
+    res = {"bytes_moved": nbytes, "launches": {}}
+    best = None
+    for g, t_ in COPY_LAUNCHES:
+        _, ms = _timed(HipEvents(), args.steps, args.warmup,
+                       lambda i, g=g, t_=t_: xr.probe_copy(mats[(i + 1) % n], mats[i % n],
+                                                           workgroups=g, threads=t_ or 256))
+        avg = statistics.mean(ms)
+        key = "memcpy" if g == 0 else f"{g}x{t_}"
+        res["launches"][key] = {"ms_avg": round(avg, 5), "GBps": round(nbytes / avg / 1e6, 1)}
+        if best is None or avg < best[1]:
+            best = (key, avg)
+    res["best"] = {"launch": best[0], "GBps": round(nbytes / best[1] / 1e6, 1)}
+    res["kernel_rate_over_copy"] = round((bmin / kernel_ms) / (nbytes / best[1]), 4)
+    return res
 
 
 def run_element_mul(args, name: str) -> dict:

@@ -75,6 +75,8 @@ lib.xr_xent_fwd_bwd_noalloc.restype = ctypes.c_int
 lib.xr_probe_rows.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, ctypes.c_int, _i32, _i32, _i32,
                               _p, _i64, _p]
 lib.xr_probe_rows.restype = ctypes.c_int
+lib.xr_probe_copy.argtypes = [_p, _p, _i64, _i32, _i32, _p]
+lib.xr_probe_copy.restype = ctypes.c_int
 lib.xr_workspace_status.argtypes = [_p, _sz, _p, _p]
 lib.xr_workspace_status.restype = ctypes.c_int
 lib.xr_status_string.argtypes = [ctypes.c_int]
@@ -107,7 +109,7 @@ C_SYMBOLS = ("xr_softmax_fwd", "xr_softmax_bwd", "xr_softmax_workspace_bytes",
              "xr_layernorm_bwd_workspace_bytes", "xr_layernorm_bwd", "xr_xent_workspace_bytes",
              "xr_xent_fwd_bwd",
              "xr_xent_fwd_bwd_ex", "xr_xent_fwd_bwd_noalloc", "xr_element_mul",
-             "xr_workspace_status", "xr_probe_rows",
+             "xr_workspace_status", "xr_probe_rows", "xr_probe_copy",
              "xr_status_string", "xr_version", "xr_plan", "xr_plan_model", "xr_set_option",
              "xr_set_profile_events")
 
@@ -502,6 +504,22 @@ def probe_rows(out: torch.Tensor, in0: torch.Tensor, in1: torch.Tensor | None = 
     _check("xr_probe_rows", lib.xr_probe_rows(po, ldo, p0, p1, ld0, M, N, dt, int(threads),
                                               int(vpt), int(split), pt, int(ignore_index),
                                               _stream(out, stream)))
+    return out
+
+
+def probe_copy(out: torch.Tensor, src: torch.Tensor, *, workgroups: int, threads: int = 256,
+               stream=None) -> torch.Tensor:
+    """The copy ceiling (xr_probe_copy): src's bytes copied into out by a grid-stride copy
+    kernel of ``workgroups`` workgroups of ``threads`` threads, or by the runtime's
+    device-to-device copy when ``workgroups`` is 0. Returns out."""
+    for t, name in ((out, "out"), (src, "src")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if out.numel() * out.element_size() != nbytes:
+        raise ValueError("out and src must hold the same number of bytes")
+    _check("xr_probe_copy", lib.xr_probe_copy(out.data_ptr(), src.data_ptr(), nbytes,
+                                              int(workgroups), int(threads), _stream(out, stream)))
     return out
 
 

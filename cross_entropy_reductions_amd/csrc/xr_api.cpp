@@ -19,7 +19,7 @@
 namespace xr {
 namespace {
 
-constexpr int32_t kVersion = 10200;  // 1.2.0
+constexpr int32_t kVersion = 10300;  // 1.3.0
 constexpr int64_t kMinChunkVecs = 256;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups in one launch
 
@@ -1029,6 +1029,30 @@ xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void
   ProbeParams prm{static_cast<const char*>(in0), static_cast<const char*>(in1), ld_in * eb,
                   static_cast<char*>(out), ld_out * eb, M, N, target, ignore_index, split, chunk};
   return launch(p, &prm, static_cast<hipStream_t>(stream), threads);
+}
+
+xr_status_t xr_probe_copy(void* out, const void* in, int64_t bytes, int32_t workgroups,
+                          int32_t threads, void* stream) {
+  if (bytes < 0 || workgroups < 0) return XR_ERR_SHAPE;
+  if (bytes == 0) return XR_OK;
+  if (!out || !in) return XR_ERR_NULL;
+  if (!aligned_to(out, 16) || !aligned_to(in, 16) || bytes % 16 != 0) return XR_ERR_ALIGN;
+  if (spans_overlap(out, bytes, in, bytes)) return XR_ERR_ALIAS;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (workgroups == 0) {  // the runtime's copy, bracketed by the profiling events like a kernel
+    const hipEvent_t ev0 = g_ev_start.load(), ev1 = g_ev_stop.load();
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return XR_ERR_LAUNCH;
+    if (hipMemcpyAsync(out, in, (size_t)bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return XR_ERR_LAUNCH;
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return XR_ERR_LAUNCH;
+    return XR_OK;
+  }
+  Plan p;
+  p.kernel = probe_copy_kernel_ptr(threads);
+  if (!p.kernel) return XR_ERR_SHAPE;
+  p.grid = workgroups;
+  CopyParams prm{static_cast<const char*>(in), static_cast<char*>(out), bytes / 16};
+  return launch(p, &prm, s, threads);
 }
 
 xr_status_t xr_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* status,

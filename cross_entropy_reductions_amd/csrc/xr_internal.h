@@ -144,6 +144,13 @@ struct ProbeParams {
   int64_t chunk_vecs;
 };
 
+// The ceiling's plain copy (xr_probe_copy): nvec 16-byte vectors from in to out.
+struct CopyParams {
+  const char* in;
+  char* out;
+  int64_t nvec;
+};
+
 // Operations of the row kernels (also the `op` argument of xr_plan).
 enum Op : int { kOpSoftmaxFwd = 0, kOpSoftmaxBwd = 1, kOpXent = 2, kOpNllFwd = 3 };
 
@@ -195,6 +202,9 @@ const void* ln_dwdb_kernel_ptr(int dtype);
 
 const void* bsr_softmax_bwd_kernel_ptr(int dtype);
 const void* probe_rows_kernel_ptr(int dtype, Shape s, int inputs);
+// The ceiling's plain copy (xr_probe_copy): 256, 512 or 1024 threads per workgroup.
+const void* probe_copy_kernel_ptr(int threads);
+constexpr int kCopyUnroll = 4;  // 16-byte vectors in flight per thread of the plain copy
 // Block-sparse backward: workgroup size, and listed blocks per row held in registers.
 #ifndef XR_BSR_THREADS
 #define XR_BSR_THREADS 256

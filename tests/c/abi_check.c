@@ -22,7 +22,7 @@ int main(void) {
   void* q = (void*)0x20000;
   float* f = (float*)0x30000;
   int64_t* t = (int64_t*)0x40000;
-  CHECK(xr_version() >= 10200);
+  CHECK(xr_version() >= 10300);
   CHECK(strcmp(xr_status_string(XR_OK), "ok") == 0);
   CHECK(xr_softmax_fwd(p, 10, q, 10, 4, 10, (xr_dtype_t)7, NULL) == XR_ERR_DTYPE);
   CHECK(xr_softmax_fwd(p, 9, q, 10, 4, 10, XR_F32, NULL) == XR_ERR_STRIDE);
@@ -44,6 +44,8 @@ int main(void) {
                            NULL, q, 4096, NULL) == XR_ERR_NULL);
   CHECK(xr_workspace_status(q, 4096, NULL, NULL) == XR_ERR_NULL);
   CHECK(xr_workspace_status(q, 64, (int32_t*)f, NULL) == XR_ERR_WORKSPACE);
+  CHECK(xr_probe_copy(q, (char*)q + 16, 4096, 8, 256, NULL) == XR_ERR_ALIAS);
+  CHECK(xr_probe_copy(q, p, 4096, 8, 100, NULL) == XR_ERR_SHAPE);
   CHECK(xr_element_mul(p, 8, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_nll_fwd(p, 8, q, 8, NULL, f, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_layernorm_fwd(p, 8, q, 8, q, q, f, f, 4, 8, -1.0f, XR_F32, NULL) == XR_ERR_VALUE);

@@ -1,5 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every entry point include/xr.h declares,
-and rejects bad arguments before touching a device (no kernel is launched here)."""
+and rejects bad arguments before touching a device. No call here can enqueue anything, with
+or without a GPU: the pointers are made-up addresses, so every call either fails a check or
+has nothing to do (M == 0)."""
 import ctypes
 import os
 import re
@@ -40,11 +42,11 @@ def test_status_strings_and_version(xr):
     for code in range(1, 13):
         assert xr.status_string(code) != "unknown status"
     assert xr.status_string(99) == "unknown status"
-    assert xr.version() == 10200
+    assert xr.version() == 10300
 
 
 XR_OK, XR_ERR_NULL, XR_ERR_SHAPE, XR_ERR_STRIDE, XR_ERR_DTYPE, XR_ERR_ALIAS = 0, 1, 2, 3, 4, 5
-XR_ERR_ALIGN, XR_ERR_OPTION, XR_ERR_VALUE = 7, 10, 11
+XR_ERR_WORKSPACE, XR_ERR_ALIGN, XR_ERR_DEVICE, XR_ERR_OPTION, XR_ERR_VALUE = 6, 7, 8, 10, 11
 
 
 def test_softmax_argument_errors(xr):
@@ -137,20 +139,23 @@ def test_xent_overlap_errors(xr):
     inside = ctypes.c_void_p(0x100000 + 4000)
     ok_args = dict(L=L, T=T, R=R, Mn=Mn, C=C, W=W, S=S)
 
-    def call(**kw):
+    def call(wsb=4096, **kw):
         a = {**ok_args, **kw}
         return f(a["L"], V, a["T"], M, V, -100, 1, 0, a["S"], 1, a["R"], a["Mn"], a["C"], a["W"],
-                 4096, None)
+                 wsb, None)
     for name in ("T", "R", "Mn", "C", "W", "S"):  # each one moved inside the logits
         assert call(**{name: inside}) == XR_ERR_ALIAS, name
     # the workspace over the row losses, the counts over the mean, the loss over the targets
     assert call(W=ctypes.c_void_p(0x300000 - 64)) == XR_ERR_ALIAS
     assert call(C=ctypes.c_void_p(0x400000 + 0)) == XR_ERR_ALIAS
     assert call(Mn=ctypes.c_void_p(0x200000 + 8)) == XR_ERR_ALIAS
-    # read-only buffers may overlap each other (targets and upstream gradient)
-    assert call(S=ctypes.c_void_p(0x200000)) not in (XR_ERR_ALIAS,)
-    # exactly adjacent spans do not overlap
-    assert call(R=ctypes.c_void_p(0x100000 + 8000)) != XR_ERR_ALIAS
+    # Calls that pass the overlap checks stop at the next ones, before anything is enqueued:
+    # without a device at the device query, with one at the 8-byte workspace (these
+    # addresses are not device memory: a launch on them would fault a GPU).
+    # Read-only buffers may overlap each other (targets and upstream gradient) ...
+    assert call(wsb=8, S=ctypes.c_void_p(0x200000)) in (XR_ERR_DEVICE, XR_ERR_WORKSPACE)
+    # ... and exactly adjacent spans do not overlap.
+    assert call(wsb=8, R=ctypes.c_void_p(0x100000 + 8000)) in (XR_ERR_DEVICE, XR_ERR_WORKSPACE)
 
 
 def test_xent_row_loss_may_be_null(xr):
@@ -159,9 +164,9 @@ def test_xent_row_loss_may_be_null(xr):
     f = xr.lib.xr_xent_fwd_bwd_ex
     L, T, Mn, W = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x400000, 0x600000))
     assert f(L, 8, T, 2, 8, -100, 0, 2, None, 0, None, None, None, W, 4096, None) == XR_ERR_NULL
-    for red in (0, 1):  # past the argument checks (a device is needed beyond them)
-        assert f(L, 8, T, 2, 8, -100, 0, red, None, 0, None, Mn, None, W, 4096, None) not in \
-            (XR_ERR_NULL, XR_ERR_ALIAS, XR_ERR_ALIGN)
+    for red in (0, 1):  # past the argument checks, stopped before anything is enqueued (above)
+        assert f(L, 8, T, 2, 8, -100, 0, red, None, 0, None, Mn, None, W, 8, None) in \
+            (XR_ERR_DEVICE, XR_ERR_WORKSPACE)
 
 
 def test_workspace_status_argument_errors(xr):
@@ -189,6 +194,22 @@ def test_probe_argument_errors(xr):
     assert f(O, 64, A, None, 64, 4, 64, 0, 96, 4, 1, None, -100, None) == XR_ERR_SHAPE
     assert f(O, 64, A, B, 64, 4, 64, 0, 64, 16, 1, None, -100, None) == XR_ERR_SHAPE
     assert f(O, 64, A, None, 64, 0, 64, 0, 64, 4, 1, None, -100, None) == XR_OK
+
+
+def test_probe_copy_argument_errors(xr):
+    f = xr.lib.xr_probe_copy
+    O, A = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    # (out, in, bytes, workgroups, threads, stream)
+    assert f(O, A, -16, 64, 256, None) == XR_ERR_SHAPE
+    assert f(O, A, 4096, -1, 256, None) == XR_ERR_SHAPE
+    assert f(O, A, 0, 64, 256, None) == XR_OK            # nothing to copy: nothing enqueued
+    assert f(None, A, 4096, 64, 256, None) == XR_ERR_NULL
+    assert f(O, None, 4096, 0, 256, None) == XR_ERR_NULL
+    assert f(ctypes.c_void_p(0x100008), A, 4096, 64, 256, None) == XR_ERR_ALIGN
+    assert f(O, A, 4100, 64, 256, None) == XR_ERR_ALIGN
+    assert f(O, ctypes.c_void_p(0x100800), 4096, 64, 256, None) == XR_ERR_ALIAS
+    assert f(O, ctypes.c_void_p(0x100800), 4096, 0, 256, None) == XR_ERR_ALIAS
+    assert f(O, A, 4096, 64, 128, None) == XR_ERR_SHAPE   # not a copy-kernel workgroup size
 
 
 def test_element_mul_argument_errors(xr):

@@ -1,6 +1,8 @@
-"""The memory-ceiling probe (xr_probe_rows) moves exactly the bytes it claims: every row
+"""The memory-ceiling probes move exactly the bytes they claim. xr_probe_rows: every row
 copied (or the XOR of two inputs), rows whose target is ignore_index written with zeros and
-not read, padding untouched, in every launch shape the benchmark times it in."""
+not read, padding untouched, in every launch shape the benchmark times it in. xr_probe_copy:
+every byte copied and nothing written past the end, by the copy kernel and the runtime's
+copy."""
 from __future__ import annotations
 
 import numpy as np
@@ -58,3 +60,19 @@ def test_probe_two_inputs(shape):
                   split=shape[2])
     torch.cuda.synchronize()
     assert np.array_equal(to_host(out), a_h ^ b_h)
+
+
+@pytest.mark.parametrize("nbytes,workgroups,threads", [
+    (16 * 1000003, 7, 256),        # a ragged tail: fewer vectors than a whole unrolled pass
+    (16 * (1 << 20), 1024, 512),   # whole unrolled passes
+    (16 * 4099, 4096, 1024),       # more threads than vectors
+    (16 * 123457, 0, 0),           # the runtime's device-to-device copy
+])
+def test_probe_copy_moves_exactly_its_bytes(nbytes, workgroups, threads):
+    """xr_probe_copy: every byte of the source copied, nothing past the end written."""
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.full((nbytes // 4 + 64,), -7, dtype=torch.int32, device="cuda")
+    xr.probe_copy(dst[:nbytes // 4], src, workgroups=workgroups, threads=threads or 256)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes // 4], src), "copy"
+    assert bool((dst[nbytes // 4:] == -7).all()), "past the end"
