@@ -18,9 +18,10 @@ of the 75 %-of-peak target in the same process -- the softmax forward and backwa
 and reports each kernel's figures under `other_configs` (`value`, `config` and
 `ms_per_step` stay the headline's). Beside each of these kernels, `ceiling` times the
 no-arithmetic probe of the row kernels' launch shapes over the same rows (xr_probe_rows);
-beside the headline, `ceiling.copy` also times a plain copy of its logit matrix, one read
-and one write of every byte (xr_probe_copy: the runtime's device-to-device copy and a
-grid-stride copy kernel over a range of grids), the achievable rate of that traffic.
+and `ceiling.copy` a plain stream of the same traffic, nothing else (xr_probe_copy: one read
+and one write of every byte of the matrix, or two reads per write for the softmax backward,
+through the runtime's device-to-device copy and a grid-stride copy kernel over a range of
+grids), the achievable rate of that traffic at that size in any launch shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
@@ -508,36 +509,40 @@ def run_xent(args, name: str) -> dict:
         out["roofline"]["ceiling"] = ceiling(
             args, out["roofline"]["kernel_ms_avg"], bmin,
             (p["threads"], p["vec_per_thread"], p["split"]), probe_shapes(nv, False), probe)
-        if name == "c4" and not args.rows:
+        if not args.rows:
+            n_c = len(copies)
             out["roofline"]["ceiling"]["copy"] = copy_ceiling(
-                args, copies, out["roofline"]["kernel_ms_avg"], bmin)
+                args, out["roofline"]["kernel_ms_avg"], bmin,
+                2 * copies[0].numel() * copies[0].element_size(),
+                lambda i, g, t_: xr_.probe_copy(copies[(i + 1) % n_c], copies[i % n_c],
+                                                workgroups=g, threads=t_))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
     return out
 
 
-# Launches of the plain copy of the ceiling: (workgroups, threads); 0 workgroups is the
-# runtime's device-to-device copy.
-COPY_LAUNCHES = [(0, 0)] + [(g, 256) for g in (4096, 16384, 65536, 131072, 262144, 524288,
-                                                1048576)] + \
-    [(g, 512) for g in (131072, 262144, 524288)]
+# Launches of the plain copy of the ceiling: (threads, 16-byte vectors per thread), the grid
+# following from the size; (0, 0) is the runtime's device-to-device copy (one input only).
+COPY_LAUNCHES = [(0, 0)] + [(256, v) for v in (1, 2, 4, 8, 32, 128)] + [(512, v) for v in (1, 2)]
 
 
-def copy_ceiling(args, mats, kernel_ms: float, bmin: int) -> dict:
-    """One read and one write of every byte of a matrix, nothing else (xr_probe_copy): the
-    runtime's device-to-device copy and a grid-stride copy kernel over a range of grids,
-    timed like the row kernel (HIP events around each launch, from one matrix of `mats` into
-    the next). Returns each rate and the row kernel's rate over the fastest copy's."""
-    import cross_entropy_reductions_amd as xr
-
-    nbytes = 2 * mats[0].numel() * mats[0].element_size()  # read + written
-    n = len(mats)
-    res = {"bytes_moved": nbytes, "launches": {}}
+def copy_ceiling(args, kernel_ms: float, bmin: int, nbytes: int, launch_copy,
+                 two_inputs: bool = False) -> dict:
+    """The plain copy of a kernel's traffic, nothing else (xr_probe_copy): one read and one
+    write of every byte (or two reads per write with two inputs) through the runtime's
+    device-to-device copy and a grid-stride copy kernel over a range of grids, timed like the
+    row kernel (HIP events around each launch; launch_copy(i, workgroups, threads) rotates
+    through the benchmark's buffers). nbytes: bytes read plus written by one launch. Returns
+    each launch's rate and the row kernel's rate over the fastest copy's."""
+    nvec = nbytes // (3 if two_inputs else 2) // 16
+    res = {"bytes_moved": nbytes, "inputs": 2 if two_inputs else 1, "launches": {}}
     best = None
-    for g, t_ in COPY_LAUNCHES:
+    for t_, v in COPY_LAUNCHES:
+        if t_ == 0 and two_inputs:
+            continue
+        g = 0 if t_ == 0 else max(1, min(-(-nvec // (t_ * v)), 2 ** 31 - 1))
         _, ms = _timed(HipEvents(), args.steps, args.warmup,
-                       lambda i, g=g, t_=t_: xr.probe_copy(mats[(i + 1) % n], mats[i % n],
-                                                           workgroups=g, threads=t_ or 256))
+                       lambda i, g=g, t_=t_: launch_copy(i, g, t_ or 256))
         avg = statistics.mean(ms)
         key = "memcpy" if g == 0 else f"{g}x{t_}"
         res["launches"][key] = {"ms_avg": round(avg, 5), "GBps": round(nbytes / avg / 1e6, 1)}
@@ -778,6 +783,15 @@ def run_softmax(args, name: str) -> dict:
         out["roofline_bwd"]["ceiling"] = ceiling(
             args, out["roofline_bwd"]["kernel_ms_avg"], b_bwd,
             (pb["threads"], pb["vec_per_thread"], pb["split"]), probe_shapes(nv, True), probe_bwd)
+        if not args.rows:
+            out["roofline"]["ceiling"]["copy"] = copy_ceiling(
+                args, out["roofline"]["kernel_ms_avg"], b_fwd, b_fwd,
+                lambda i, g, t_: xr.probe_copy(ys[i % nsets], xs[i % nsets], workgroups=g,
+                                               threads=t_))
+            out["roofline_bwd"]["ceiling"]["copy"] = copy_ceiling(
+                args, out["roofline_bwd"]["kernel_ms_avg"], b_bwd, b_bwd,
+                lambda i, g, t_: xr.probe_copy(dxs[i % nsets], ys[i % nsets], dys[i % nsets],
+                                               workgroups=g, threads=t_), two_inputs=True)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_softmax(w, args.cpu_rows)
     return out

@@ -75,7 +75,7 @@ lib.xr_xent_fwd_bwd_noalloc.restype = ctypes.c_int
 lib.xr_probe_rows.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, ctypes.c_int, _i32, _i32, _i32,
                               _p, _i64, _p]
 lib.xr_probe_rows.restype = ctypes.c_int
-lib.xr_probe_copy.argtypes = [_p, _p, _i64, _i32, _i32, _p]
+lib.xr_probe_copy.argtypes = [_p, _p, _p, _i64, _i32, _i32, _p]
 lib.xr_probe_copy.restype = ctypes.c_int
 lib.xr_workspace_status.argtypes = [_p, _sz, _p, _p]
 lib.xr_workspace_status.restype = ctypes.c_int
@@ -507,19 +507,24 @@ def probe_rows(out: torch.Tensor, in0: torch.Tensor, in1: torch.Tensor | None = 
     return out
 
 
-def probe_copy(out: torch.Tensor, src: torch.Tensor, *, workgroups: int, threads: int = 256,
-               stream=None) -> torch.Tensor:
-    """The copy ceiling (xr_probe_copy): src's bytes copied into out by a grid-stride copy
-    kernel of ``workgroups`` workgroups of ``threads`` threads, or by the runtime's
-    device-to-device copy when ``workgroups`` is 0. Returns out."""
-    for t, name in ((out, "out"), (src, "src")):
+def probe_copy(out: torch.Tensor, src: torch.Tensor, src1: torch.Tensor | None = None, *,
+               workgroups: int, threads: int = 256, stream=None) -> torch.Tensor:
+    """The copy ceiling (xr_probe_copy): src's bytes (src ^ src1's with a second input) into
+    out, by a grid-stride kernel of ``workgroups`` workgroups of ``threads`` threads, or by
+    the runtime's device-to-device copy when ``workgroups`` is 0. Returns out."""
+    for t, name in ((out, "out"), (src, "src"), (src1, "src1")):
+        if t is None:
+            continue
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous device tensor")
     nbytes = src.numel() * src.element_size()
-    if out.numel() * out.element_size() != nbytes:
-        raise ValueError("out and src must hold the same number of bytes")
-    _check("xr_probe_copy", lib.xr_probe_copy(out.data_ptr(), src.data_ptr(), nbytes,
-                                              int(workgroups), int(threads), _stream(out, stream)))
+    for t in (out, src1):
+        if t is not None and t.numel() * t.element_size() != nbytes:
+            raise ValueError("out, src and src1 must hold the same number of bytes")
+    _check("xr_probe_copy", lib.xr_probe_copy(out.data_ptr(), src.data_ptr(),
+                                              None if src1 is None else src1.data_ptr(), nbytes,
+                                              int(workgroups), int(threads),
+                                              _stream(out, stream)))
     return out
 
 

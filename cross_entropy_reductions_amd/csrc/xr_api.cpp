@@ -1031,15 +1031,19 @@ xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void
   return launch(p, &prm, static_cast<hipStream_t>(stream), threads);
 }
 
-xr_status_t xr_probe_copy(void* out, const void* in, int64_t bytes, int32_t workgroups,
-                          int32_t threads, void* stream) {
+xr_status_t xr_probe_copy(void* out, const void* in, const void* in1, int64_t bytes,
+                          int32_t workgroups, int32_t threads, void* stream) {
   if (bytes < 0 || workgroups < 0) return XR_ERR_SHAPE;
   if (bytes == 0) return XR_OK;
   if (!out || !in) return XR_ERR_NULL;
-  if (!aligned_to(out, 16) || !aligned_to(in, 16) || bytes % 16 != 0) return XR_ERR_ALIGN;
-  if (spans_overlap(out, bytes, in, bytes)) return XR_ERR_ALIAS;
+  if (!aligned_to(out, 16) || !aligned_to(in, 16) || (in1 && !aligned_to(in1, 16)) ||
+      bytes % 16 != 0)
+    return XR_ERR_ALIGN;
+  if (spans_overlap(out, bytes, in, bytes) || (in1 && spans_overlap(out, bytes, in1, bytes)))
+    return XR_ERR_ALIAS;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (workgroups == 0) {  // the runtime's copy, bracketed by the profiling events like a kernel
+    if (in1) return XR_ERR_VALUE;
     const hipEvent_t ev0 = g_ev_start.load(), ev1 = g_ev_stop.load();
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return XR_ERR_LAUNCH;
     if (hipMemcpyAsync(out, in, (size_t)bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -1048,10 +1052,11 @@ xr_status_t xr_probe_copy(void* out, const void* in, int64_t bytes, int32_t work
     return XR_OK;
   }
   Plan p;
-  p.kernel = probe_copy_kernel_ptr(threads);
+  p.kernel = probe_copy_kernel_ptr(threads, in1 ? 2 : 1);
   if (!p.kernel) return XR_ERR_SHAPE;
   p.grid = workgroups;
-  CopyParams prm{static_cast<const char*>(in), static_cast<char*>(out), bytes / 16};
+  CopyParams prm{static_cast<const char*>(in), static_cast<const char*>(in1),
+                 static_cast<char*>(out), bytes / 16};
   return launch(p, &prm, s, threads);
 }
 

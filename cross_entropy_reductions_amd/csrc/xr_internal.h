@@ -144,9 +144,11 @@ struct ProbeParams {
   int64_t chunk_vecs;
 };
 
-// The ceiling's plain copy (xr_probe_copy): nvec 16-byte vectors from in to out.
+// The ceiling's plain copy (xr_probe_copy): nvec 16-byte vectors from in to out, or
+// in ^ in1 when in1 is not null.
 struct CopyParams {
   const char* in;
+  const char* in1;
   char* out;
   int64_t nvec;
 };
@@ -202,8 +204,9 @@ const void* ln_dwdb_kernel_ptr(int dtype);
 
 const void* bsr_softmax_bwd_kernel_ptr(int dtype);
 const void* probe_rows_kernel_ptr(int dtype, Shape s, int inputs);
-// The ceiling's plain copy (xr_probe_copy): 256, 512 or 1024 threads per workgroup.
-const void* probe_copy_kernel_ptr(int threads);
+// The ceiling's plain copy (xr_probe_copy): 256, 512 or 1024 threads per workgroup, one or
+// two inputs.
+const void* probe_copy_kernel_ptr(int threads, int inputs);
 constexpr int kCopyUnroll = 4;  // 16-byte vectors in flight per thread of the plain copy
 // Block-sparse backward: workgroup size, and listed blocks per row held in registers.
 #ifndef XR_BSR_THREADS

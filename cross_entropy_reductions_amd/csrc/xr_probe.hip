@@ -30,33 +30,51 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(co, k, NIN == 2 ? (a[k] ^ b[k]) : a[k]);
 }
 
-// The plain copy of the ceiling: a grid-stride loop over 16-byte vectors, kCopyUnroll loads in
-// flight per thread before their stores, non-temporal both ways. nvec vectors of 16 bytes.
-template <int THREADS>
+// The plain copy of the ceiling: a grid-stride loop over 16-byte vectors, kCopyUnroll vectors
+// in flight per thread before their stores, non-temporal both ways; with two inputs the
+// stored vector is in ^ in1 (two reads per write, as the softmax backward). nvec vectors.
+template <int THREADS, int NIN>
 __global__ __launch_bounds__(THREADS) void probe_copy_kernel(CopyParams p) {
   constexpr int U = kCopyUnroll;
   const u32x4* __restrict__ in = reinterpret_cast<const u32x4*>(p.in);
+  const u32x4* __restrict__ in1 = reinterpret_cast<const u32x4*>(p.in1);
   u32x4* __restrict__ out = reinterpret_cast<u32x4*>(p.out);
   const int64_t nvec = p.nvec;
   const int64_t stride = (int64_t)gridDim.x * THREADS;
   int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
   for (; i + (U - 1) * stride < nvec; i += U * stride) {
-    u32x4 v[U];
+    u32x4 v[U], w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(in + i + u * stride);
+    for (int u = 0; u < U; ++u) {
+      v[u] = __builtin_nontemporal_load(in + i + u * stride);
+      if (NIN == 2) w[u] = __builtin_nontemporal_load(in1 + i + u * stride);
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], out + i + u * stride);
+    for (int u = 0; u < U; ++u)
+      __builtin_nontemporal_store(NIN == 2 ? (v[u] ^ w[u]) : v[u], out + i + u * stride);
   }
-  for (; i < nvec; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(in + i), out + i);
+  for (; i < nvec; i += stride) {
+    u32x4 v = __builtin_nontemporal_load(in + i);
+    if (NIN == 2) v ^= __builtin_nontemporal_load(in1 + i);
+    __builtin_nontemporal_store(v, out + i);
+  }
 }
 
-const void* probe_copy_kernel_ptr(int threads) {
-  switch (threads) {
-    case 256: return reinterpret_cast<const void*>(&probe_copy_kernel<256>);
-    case 512: return reinterpret_cast<const void*>(&probe_copy_kernel<512>);
-    case 1024: return reinterpret_cast<const void*>(&probe_copy_kernel<1024>);
-    default: return nullptr;
+const void* probe_copy_kernel_ptr(int threads, int inputs) {
+  if (inputs == 1) {
+    switch (threads) {
+      case 256: return reinterpret_cast<const void*>(&probe_copy_kernel<256, 1>);
+      case 512: return reinterpret_cast<const void*>(&probe_copy_kernel<512, 1>);
+      case 1024: return reinterpret_cast<const void*>(&probe_copy_kernel<1024, 1>);
+    }
+  } else if (inputs == 2) {
+    switch (threads) {
+      case 256: return reinterpret_cast<const void*>(&probe_copy_kernel<256, 2>);
+      case 512: return reinterpret_cast<const void*>(&probe_copy_kernel<512, 2>);
+      case 1024: return reinterpret_cast<const void*>(&probe_copy_kernel<1024, 2>);
+    }
   }
+  return nullptr;
 }
 
 #define XR_CASE_PROBE1(D, T, V) \

@@ -345,17 +345,19 @@ xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void
                           void* stream);
 
 /*
- * Copy ceiling, for measurement: what a plain copy of `bytes` bytes moves (the achievable
- * rate of one read and one write per byte, against which a row kernel's rate is read).
- * workgroups > 0: a grid-stride copy kernel of that many workgroups of `threads` threads
- * (256, 512 or 1024, else XR_ERR_SHAPE), 16-byte non-temporal loads and stores, four vectors
- * in flight per thread; workgroups == 0: the runtime's device-to-device copy
- * (hipMemcpyAsync). Either is bracketed by the events of xr_set_profile_events().
- *   in, out: device memory on 16-byte boundaries, bytes a multiple of 16 (else XR_ERR_ALIGN);
- *   the two spans must not overlap (XR_ERR_ALIAS); bytes == 0 enqueues nothing
+ * Copy ceiling, for measurement: what a plain stream of `bytes` bytes moves (the achievable
+ * rate of that traffic, against which a row kernel's rate is read). With in1 NULL, one read
+ * and one write per byte (out = in); with in1, two reads per write (out = in ^ in1, the
+ * softmax backward's mix). workgroups > 0: a grid-stride kernel of that many workgroups of
+ * `threads` threads (256, 512 or 1024, else XR_ERR_SHAPE), 16-byte non-temporal loads and
+ * stores, four vectors in flight per thread; workgroups == 0: the runtime's device-to-device
+ * copy (hipMemcpyAsync; in1 must be NULL, else XR_ERR_VALUE). Either is bracketed by the
+ * events of xr_set_profile_events().
+ *   in, in1, out: device memory on 16-byte boundaries, bytes a multiple of 16 (else
+ *   XR_ERR_ALIGN); out must not overlap an input (XR_ERR_ALIAS); bytes == 0 enqueues nothing
  */
-xr_status_t xr_probe_copy(void* out, const void* in, int64_t bytes, int32_t workgroups,
-                          int32_t threads, void* stream);
+xr_status_t xr_probe_copy(void* out, const void* in, const void* in1, int64_t bytes,
+                          int32_t workgroups, int32_t threads, void* stream);
 
 /* Static, human-readable text for a status code (host). */
 const char* xr_status_string(xr_status_t status);

@@ -44,8 +44,9 @@ int main(void) {
                            NULL, q, 4096, NULL) == XR_ERR_NULL);
   CHECK(xr_workspace_status(q, 4096, NULL, NULL) == XR_ERR_NULL);
   CHECK(xr_workspace_status(q, 64, (int32_t*)f, NULL) == XR_ERR_WORKSPACE);
-  CHECK(xr_probe_copy(q, (char*)q + 16, 4096, 8, 256, NULL) == XR_ERR_ALIAS);
-  CHECK(xr_probe_copy(q, p, 4096, 8, 100, NULL) == XR_ERR_SHAPE);
+  CHECK(xr_probe_copy(q, (char*)q + 16, NULL, 4096, 8, 256, NULL) == XR_ERR_ALIAS);
+  CHECK(xr_probe_copy(q, p, NULL, 4096, 8, 100, NULL) == XR_ERR_SHAPE);
+  CHECK(xr_probe_copy(q, p, p, 4096, 0, 256, NULL) == XR_ERR_VALUE);
   CHECK(xr_element_mul(p, 8, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_nll_fwd(p, 8, q, 8, NULL, f, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_layernorm_fwd(p, 8, q, 8, q, q, f, f, 4, 8, -1.0f, XR_F32, NULL) == XR_ERR_VALUE);

@@ -198,18 +198,21 @@ def test_probe_argument_errors(xr):
 
 def test_probe_copy_argument_errors(xr):
     f = xr.lib.xr_probe_copy
-    O, A = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
-    # (out, in, bytes, workgroups, threads, stream)
-    assert f(O, A, -16, 64, 256, None) == XR_ERR_SHAPE
-    assert f(O, A, 4096, -1, 256, None) == XR_ERR_SHAPE
-    assert f(O, A, 0, 64, 256, None) == XR_OK            # nothing to copy: nothing enqueued
-    assert f(None, A, 4096, 64, 256, None) == XR_ERR_NULL
-    assert f(O, None, 4096, 0, 256, None) == XR_ERR_NULL
-    assert f(ctypes.c_void_p(0x100008), A, 4096, 64, 256, None) == XR_ERR_ALIGN
-    assert f(O, A, 4100, 64, 256, None) == XR_ERR_ALIGN
-    assert f(O, ctypes.c_void_p(0x100800), 4096, 64, 256, None) == XR_ERR_ALIAS
-    assert f(O, ctypes.c_void_p(0x100800), 4096, 0, 256, None) == XR_ERR_ALIAS
-    assert f(O, A, 4096, 64, 128, None) == XR_ERR_SHAPE   # not a copy-kernel workgroup size
+    O, A, B = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000))
+    # (out, in, in1, bytes, workgroups, threads, stream)
+    assert f(O, A, None, -16, 64, 256, None) == XR_ERR_SHAPE
+    assert f(O, A, None, 4096, -1, 256, None) == XR_ERR_SHAPE
+    assert f(O, A, B, 0, 64, 256, None) == XR_OK           # nothing to copy: nothing enqueued
+    assert f(None, A, None, 4096, 64, 256, None) == XR_ERR_NULL
+    assert f(O, None, B, 4096, 0, 256, None) == XR_ERR_NULL
+    assert f(ctypes.c_void_p(0x100008), A, None, 4096, 64, 256, None) == XR_ERR_ALIGN
+    assert f(O, A, ctypes.c_void_p(0x300004), 4096, 64, 256, None) == XR_ERR_ALIGN
+    assert f(O, A, None, 4100, 64, 256, None) == XR_ERR_ALIGN
+    assert f(O, ctypes.c_void_p(0x100800), None, 4096, 64, 256, None) == XR_ERR_ALIAS
+    assert f(O, A, ctypes.c_void_p(0x100800), 4096, 64, 256, None) == XR_ERR_ALIAS
+    assert f(O, ctypes.c_void_p(0x100800), None, 4096, 0, 256, None) == XR_ERR_ALIAS
+    assert f(O, A, B, 4096, 0, 256, None) == XR_ERR_VALUE   # the runtime's copy has one input
+    assert f(O, A, B, 4096, 64, 128, None) == XR_ERR_SHAPE  # not a copy-kernel workgroup size
 
 
 def test_element_mul_argument_errors(xr):

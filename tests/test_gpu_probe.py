@@ -1,8 +1,8 @@
 """The memory-ceiling probes move exactly the bytes they claim. xr_probe_rows: every row
 copied (or the XOR of two inputs), rows whose target is ignore_index written with zeros and
 not read, padding untouched, in every launch shape the benchmark times it in. xr_probe_copy:
-every byte copied and nothing written past the end, by the copy kernel and the runtime's
-copy."""
+every byte copied (or the XOR of two inputs) and nothing written past the end, by the copy
+kernel and the runtime's copy."""
 from __future__ import annotations
 
 import numpy as np
@@ -76,3 +76,10 @@ def test_probe_copy_moves_exactly_its_bytes(nbytes, workgroups, threads):
     torch.cuda.synchronize()
     assert torch.equal(dst[:nbytes // 4], src), "copy"
     assert bool((dst[nbytes // 4:] == -7).all()), "past the end"
+    if workgroups:  # two inputs: their XOR
+        src1 = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32,
+                             device="cuda")
+        xr.probe_copy(dst[:nbytes // 4], src, src1, workgroups=workgroups, threads=threads)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes // 4], src ^ src1), "xor of two inputs"
+        assert bool((dst[nbytes // 4:] == -7).all()), "past the end"
