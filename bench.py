@@ -210,7 +210,7 @@ def cpu_baseline(workload: dict, rows: int, min_seconds: float = 10.0) -> dict:
             break
     elt = 2 if workload["dtype"] == "bf16" else 4
     b = xent_bmin(rows, V, int((t != -100).sum()), elt) * passes
-    return {"value": round(b / sec / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
+    return {"value": float(f"{b / sec / 1e9:.4g}"), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle", "rows_per_s": round(rows * passes / sec, 1), "seconds": round(sec, 3),
             "sample": f"first {rows} of {workload['M']} rows of the same workload "
                       f"(V={V} {workload['dtype']}): float64 count, loss, gradient and mean, "
@@ -248,7 +248,7 @@ def cpu_baseline_softmax(workload: dict, rows: int, min_seconds: float = 10.0) -
         sec = time.perf_counter() - t0
         if sec >= min_seconds:
             break
-    return {"value": round(per_pass * passes / sec / 1e9, 3), "unit": "GB/s",
+    return {"value": float(f"{per_pass * passes / sec / 1e9:.4g}"), "unit": "GB/s",
             "cores": orc.num_threads(), "kind": "oracle",
             "rows_per_s": round(rows * passes / sec, 1), "seconds": round(sec, 3),
             "sample": f"first {rows} of {M} rows of the same workload (N={N} "
@@ -272,7 +272,7 @@ def _cpu_passes(one_pass, min_seconds: float):
 
 def _cpu_line(bytes_per_pass: int, rows: int, passes: int, sec: float, cores: int,
               sample: str) -> dict:
-    return {"value": round(bytes_per_pass * passes / sec / 1e9, 3), "unit": "GB/s",
+    return {"value": float(f"{bytes_per_pass * passes / sec / 1e9:.4g}"), "unit": "GB/s",
             "cores": cores, "kind": "oracle", "rows_per_s": round(rows * passes / sec, 1),
             "seconds": round(sec, 3), "sample": f"{sample}, {passes} whole passes"}
 
