@@ -32,7 +32,8 @@ from hypothesis import strategies as st
 import oracle
 import synth
 
-SETTINGS = settings(max_examples=40, deadline=None,
+# derandomized: every run draws the same cases (other seeds were explored while writing these)
+SETTINGS = settings(max_examples=40, deadline=None, derandomize=True,
                     suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 
 
