@@ -209,8 +209,13 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
 
 // ============================================================================ softmax backward
 // One row of the backward: vy / vd hold row r's y and dy (their loads issued in pairs);
-// dx = y (dy - sum(y dy)). With PREFETCH, the loads of row rn (if rn < M) are issued as the
-// slots of row r are stored.
+// dx = y (dy - s), s = sum(y dy), formed as fma(-y, s, y dy) with the product y dy rounded
+// once. Without PREFETCH (one row per workgroup) the products are kept in registers from the
+// pass that sums them, so the pass that writes dx, which must wait for the last pair and
+// the reduction, has one widening and one fma per element; with PREFETCH (the persistent
+// loop, whose registers also carry the next row) they are formed again there, to the same
+// bits. With PREFETCH, the loads of row rn (if rn < M) are issued as the slots of row r are
+// stored.
 template <int D, int THREADS, int VPT, int LP, bool PREFETCH>
 __device__ __forceinline__ void softmax_bwd_row(const SoftmaxBwdParams& p, int64_t r, int64_t rn,
                                                 u32x4 (&vy)[VPT], u32x4 (&vd)[VPT], float* red) {
@@ -221,18 +226,27 @@ __device__ __forceinline__ void softmax_bwd_row(const SoftmaxBwdParams& p, int64
   const Chunk<D> cx(p.dx + r * p.lddx_bytes, p.N, 0, cv);
   // Out-of-row elements of both operands count as 0: they add nothing to the dot product.
   float s[4] = {0.f, 0.f, 0.f, 0.f};
+  float prod[PREFETCH ? 1 : VPT][EPV];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) continue;
+    if (slot_kind<THREADS>(k, cy.nvec) == kSlotNone) {
+      if constexpr (!PREFETCH) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) prod[k][e] = 0.f;
+      }
+      continue;
+    }
     const u32x4 a = masked_slot<D, THREADS>(vy[k], k, cy, 0u);
     const u32x4 b = masked_slot<D, THREADS>(vd[k], k, cy, 0u);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e)
+    for (int e = 0; e < EPV; ++e) {
       s[e & 3] = __builtin_fmaf(elem<D>(a, e), elem<D>(b, e), s[e & 3]);
+      if constexpr (!PREFETCH) prod[k][e] = elem<D>(a, e) * elem<D>(b, e);
+    }
   }
   const float dot = block_reduce<THREADS>((s[0] + s[1]) + (s[2] + s[3]), OpAdd(), red);
   reg_barrier(vy);
-  reg_barrier(vd);
+  if constexpr (PREFETCH) reg_barrier(vd);  // (without it dy is dead once its products are formed)
   const bool pf = PREFETCH && rn < p.M;
   const Chunk<D> cyn(p.y + (pf ? rn : r) * p.ldy_bytes, p.N, 0, cv);
   const Chunk<D> cdn(p.dy + (pf ? rn : r) * p.lddy_bytes, p.N, 0, cv);
@@ -240,11 +254,20 @@ __device__ __forceinline__ void softmax_bwd_row(const SoftmaxBwdParams& p, int64
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     OutVec<D> o;
-    u32x4 a = vy[k], b = vd[k];
+    u32x4 a = vy[k];
     pin(a);  // fp32 too: unpinned, the fp32 shapes with 8 vectors per thread spill
-    pin(b);
+    if constexpr (PREFETCH) {
+      u32x4 b = vd[k];
+      pin(b);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+      for (int e = 0; e < EPV; ++e)
+        o.v[e] = __builtin_fmaf(-elem<D>(a, e), dot, elem<D>(a, e) * elem<D>(b, e));
+    } else {
+      // lanes past the row hold masked products: their stores are dropped, and the
+      // partial first / last vectors are written below
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) o.v[e] = __builtin_fmaf(-elem<D>(a, e), dot, prod[k][e]);
+    }
     store_slot<D, THREADS>(cx, k, o.bits());
     if (pf) {
       vy[k] = buf_load<LP>(cyn.slot(k * THREADS), off);
@@ -263,7 +286,8 @@ __device__ __forceinline__ void softmax_bwd_row(const SoftmaxBwdParams& p, int64
     const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cd.rsrc, (int)po, 0, 0);
     OutVec<D> o;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) o.v[e] = elem<D>(a, e) * (elem<D>(b, e) - dot);
+    for (int e = 0; e < EPV; ++e)
+      o.v[e] = __builtin_fmaf(-elem<D>(a, e), dot, elem<D>(a, e) * elem<D>(b, e));
     store_partial<D>(cx.rsrc, po, o.bits(), q == 0 ? cx.h0 : cx.t0, q == 0 ? cx.h1 : cx.t1);
   }
 }
