@@ -577,6 +577,12 @@ def run_element_mul(args, name: str) -> dict:
     out = _line(args, name, bmin, M, wall, kernel_ms, "element_mul_kernel",
                 {"M": M, "V": V, "bytes_min": bmin, "threads": 1024, "vec_per_thread": 8},
                 "bf16")
+    if getattr(args, "ceiling", False):
+        n_c = len(copies)
+        out["roofline"]["ceiling"] = {"copy": copy_ceiling(
+            args, out["roofline"]["kernel_ms_avg"], bmin, 2 * M * V * 2,
+            lambda i, g, t_: xr.probe_copy(copies[(i + 1) % n_c], copies[i % n_c], workgroups=g,
+                                           threads=t_))}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_element_mul(w, args.cpu_rows, 0.5)
     return out
@@ -612,6 +618,10 @@ def run_nll(args, name: str) -> dict:
                 {"M": M, "N": N, "bytes_min": bmin, "path": p["path"], "threads": p["threads"],
                  "vec_per_thread": p["vec_per_thread"], "split": p["split"], "grid": p["grid"]},
                 "bf16")
+    if getattr(args, "ceiling", False):
+        res["roofline"]["ceiling"] = {"copy": copy_ceiling(
+            args, res["roofline"]["kernel_ms_avg"], bmin, 2 * M * N * 2,
+            lambda i, g, t_: xr.probe_copy(out, x, workgroups=g, threads=t_))}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_nll(w, np.clip(w["target"], 0, None), args.cpu_rows)
     return res
@@ -669,6 +679,16 @@ def run_layernorm(args, name: str) -> dict:
                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": round(b_bwd / kavg / 1e6 / PEAK_HBM_GBS, 4),
                            "kernel": "ln_bwd_kernel (stage 1)", "kernel_ms_avg": round(kavg, 5)}
+    if getattr(args, "ceiling", False):
+        mat = M * N * elt
+        out["roofline"]["ceiling"] = {"copy": copy_ceiling(
+            args, out["roofline"]["kernel_ms_avg"], b_fwd, 2 * mat,
+            lambda i, g, t_: xr.probe_copy(ys[i % nsets], xs[i % nsets], workgroups=g,
+                                           threads=t_))}
+        out["roofline_bwd"]["ceiling"] = {"copy": copy_ceiling(
+            args, kavg, b_bwd, 3 * mat,
+            lambda i, g, t_: xr.probe_copy(dxs[i % nsets], xs[i % nsets], dys[i % nsets],
+                                           workgroups=g, threads=t_), two_inputs=True)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_layernorm(wl, args.cpu_rows)
     return out
@@ -704,6 +724,12 @@ def run_bsr(args, name: str) -> dict:
     out = _line(args, name, bmin, rows, wall, kernel_ms, "bsr_softmax_bwd_kernel",
                 {"Z": w["Z"], "seq": w["seq"], "block": w["block"], "n_blocks": w["n_blocks"],
                  "bytes_min": bmin, "input_sets": nsets}, "bf16")
+    if getattr(args, "ceiling", False):
+        # y and dy read, the result written to another buffer of the same size
+        out["roofline"]["ceiling"] = {"copy": copy_ceiling(
+            args, out["roofline"]["kernel_ms_avg"], bmin, 3 * y.numel() * elt,
+            lambda i, g, t_: xr.probe_copy(ds[(i + 1) % nsets], ys[i % nsets], ds[i % nsets],
+                                           workgroups=g, threads=t_), two_inputs=True)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_bsr(w, max(1, args.cpu_rows * w["Z"] // 16384))
     return out
@@ -765,6 +791,16 @@ def run_softmax(args, name: str) -> dict:
                                if xr.plan("softmax_bwd_ws", M, N, x.dtype)["split"] > 1
                                else "softmax_bwd_kernel", "kernel_ms_avg": round(kavg, 5),
                                "kernel_ms_min": round(min(bwd_ms), 5), "bytes": b_bwd}
+    if getattr(args, "ceiling", False) and name != "c2":
+        out["roofline"]["ceiling"] = {"copy": copy_ceiling(
+            args, out["roofline"]["kernel_ms_avg"], b_fwd, b_fwd,
+            lambda i, g, t_: xr.probe_copy(ys[i % nsets], xs[i % nsets], workgroups=g,
+                                           threads=t_))}
+        if bwd:
+            out["roofline_bwd"]["ceiling"] = {"copy": copy_ceiling(
+                args, out["roofline_bwd"]["kernel_ms_avg"], b_bwd, b_bwd,
+                lambda i, g, t_: xr.probe_copy(dxs[i % nsets], ys[i % nsets], dys[i % nsets],
+                                               workgroups=g, threads=t_), two_inputs=True)}
     if getattr(args, "ceiling", False) and name == "c2":
         nv = N * elt // 16
 
@@ -1041,8 +1077,8 @@ def main() -> int:
         print("need 1 <= steps and steps + warmup <= 40 (one copy of the logits per step)",
               file=sys.stderr)
         return 2
+    args.ceiling = args.workload != "c1" and not (args.no_ceiling or args.rows)
     if args.workload in ("c1", "c2", "sm-vocab", "sm-few"):
-        args.ceiling = args.workload == "c2" and not (args.no_ceiling or args.rows)
         out = run_softmax(args, args.workload)
     elif args.workload == "c4-mul":
         out = run_element_mul(args, args.workload)
@@ -1053,7 +1089,6 @@ def main() -> int:
     elif args.workload == "bsr":
         out = run_bsr(args, args.workload)
     else:
-        args.ceiling = args.workload in ("c3", "c4", "c5") and not (args.no_ceiling or args.rows)
         out = run_xent(args, args.workload)
         if args.workload == "c4" and not (args.no_extras or args.rows or args.grad_scale is not None
                                           or args.reduction != "mean"):
