@@ -113,6 +113,39 @@ def test_random_softmax(orc, case):
 
 
 @pytest.mark.parametrize("case", range(CASES))
+def test_random_softmax_bwd_resident(orc, case):
+    """The backward on y, dy and dx sharing one row pitch (so the row-resident kernels take
+    them, partial first / last vectors included): the one-row form and the persistent form,
+    against the oracle, and the two forms to the same bits."""
+    rng = np.random.Generator(np.random.PCG64(17500 + case))
+    M = int(rng.choice([1, 3, 64, 300, 700]))
+    N = int(rng.choice([1, 7, 9, 100, 1000, 3001, 4096, 8191]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    ld = N + int(rng.choice([0, 1, 3, 8, 13]))
+    print(f"softmax bwd case {case}: M={M} N={N} ld={ld} {dtype}", flush=True)
+    x = synth.random_rows(17600 + case, M, N, dtype="f32", scale=3.0)
+    y_rows = orc.softmax_fwd(x)
+    y_h = synth.random_rows(17700 + case, M, N, ld=ld, dtype=dtype, scale=0.0, pad_nan=ld > N)
+    y_h[:, :N] = synth.bf16_bits_from_f32(y_rows.astype(np.float32)) if dtype == "bf16" \
+        else y_rows.astype(np.float32)
+    dy_h = synth.random_rows(17800 + case, M, N, ld=ld, dtype=dtype, scale=1.0, pad_nan=ld > N)
+    want = orc.softmax_bwd(np.ascontiguousarray(y_h[:, :N]), np.ascontiguousarray(dy_h[:, :N]))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    outs = []
+    for grid in (0, 1):
+        xr.set_option("grid", grid)
+        p = xr.plan("softmax_bwd", M, N, tdt, aligned=1)
+        y, dy = to_device(y_h), to_device(dy_h)
+        dx = torch.full((M, ld), float("nan"), dtype=tdt, device="cuda")
+        xr.softmax_bwd(y[:, :N], dy[:, :N], dx[:, :N])
+        torch.cuda.synchronize()
+        got = to_host(dx)
+        check_output(np.ascontiguousarray(got[:, :N]), want, f"case {case} grid {grid} {p['path']}")
+        outs.append(got[:, :N].copy())
+    assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8)), "forms differ"
+
+
+@pytest.mark.parametrize("case", range(CASES))
 def test_random_nll(orc, case):
     rng = np.random.Generator(np.random.PCG64(18000 + case))
     M, N, dtype, ld, path = draw(rng, case)
