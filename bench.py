@@ -21,7 +21,9 @@ no-arithmetic probe of the row kernels' launch shapes over the same rows (xr_pro
 and `ceiling.copy` a plain stream of the same traffic, nothing else (xr_probe_copy: one read
 and one write of every byte of the matrix, or two reads per write for the softmax backward,
 through the runtime's device-to-device copy and a grid-stride copy kernel over a range of
-grids), the achievable rate of that traffic at that size in any launch shape.
+grids), the achievable rate of that traffic at that size in any launch shape; for the
+kernels that overwrite their input (the cross-entropy, element_mul), `ceiling.copy.in_place`
+times the copy kernel in place as well, every vector written back where it was read.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-rows R]
                     [--workload c4|c3|c5|c2|c1|c4-mul|c4-nll|ln|bsr|sm-vocab|sm-few]
@@ -515,7 +517,9 @@ def run_xent(args, name: str) -> dict:
                 args, out["roofline"]["kernel_ms_avg"], bmin,
                 2 * copies[0].numel() * copies[0].element_size(),
                 lambda i, g, t_: xr_.probe_copy(copies[(i + 1) % n_c], copies[i % n_c],
-                                                workgroups=g, threads=t_))
+                                                workgroups=g, threads=t_),
+                launch_in_place=lambda i, g, t_: xr_.probe_copy(copies[i], copies[i],
+                                                                workgroups=g, threads=t_))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, M))
     return out
@@ -527,29 +531,38 @@ COPY_LAUNCHES = [(0, 0)] + [(256, v) for v in (1, 2, 4, 8, 32, 128)] + [(512, v)
 
 
 def copy_ceiling(args, kernel_ms: float, bmin: int, nbytes: int, launch_copy,
-                 two_inputs: bool = False) -> dict:
+                 two_inputs: bool = False, launch_in_place=None) -> dict:
     """The plain copy of a kernel's traffic, nothing else (xr_probe_copy): one read and one
     write of every byte (or two reads per write with two inputs) through the runtime's
     device-to-device copy and a grid-stride copy kernel over a range of grids, timed like the
     row kernel (HIP events around each launch; launch_copy(i, workgroups, threads) rotates
     through the benchmark's buffers). nbytes: bytes read plus written by one launch. Returns
-    each launch's rate and the row kernel's rate over the fastest copy's."""
+    each launch's rate and the row kernel's rate over the fastest copy's. For a kernel that
+    overwrites its input, launch_in_place(i, workgroups, threads) times the copy kernel in
+    place as well (every vector written back where it was read), reported under "in_place"."""
     nvec = nbytes // (3 if two_inputs else 2) // 16
-    res = {"bytes_moved": nbytes, "inputs": 2 if two_inputs else 1, "launches": {}}
-    best = None
-    for t_, v in COPY_LAUNCHES:
-        if t_ == 0 and two_inputs:
-            continue
-        g = 0 if t_ == 0 else max(1, min(-(-nvec // (t_ * v)), 2 ** 31 - 1))
-        _, ms = _timed(HipEvents(), args.steps, args.warmup,
-                       lambda i, g=g, t_=t_: launch_copy(i, g, t_ or 256))
-        avg = statistics.mean(ms)
-        key = "memcpy" if g == 0 else f"{g}x{t_}"
-        res["launches"][key] = {"ms_avg": round(avg, 5), "GBps": round(nbytes / avg / 1e6, 1)}
-        if best is None or avg < best[1]:
-            best = (key, avg)
-    res["best"] = {"launch": best[0], "GBps": round(nbytes / best[1] / 1e6, 1)}
-    res["kernel_rate_over_copy"] = round((bmin / kernel_ms) / (nbytes / best[1]), 4)
+
+    def sweep(launch, with_memcpy):
+        launches, best = {}, None
+        for t_, v in COPY_LAUNCHES:
+            if t_ == 0 and not with_memcpy:
+                continue
+            g = 0 if t_ == 0 else max(1, min(-(-nvec // (t_ * v)), 2 ** 31 - 1))
+            _, ms = _timed(HipEvents(), args.steps, args.warmup,
+                           lambda i, g=g, t_=t_: launch(i, g, t_ or 256))
+            avg = statistics.mean(ms)
+            key = "memcpy" if g == 0 else f"{g}x{t_}"
+            launches[key] = {"ms_avg": round(avg, 5), "GBps": round(nbytes / avg / 1e6, 1)}
+            if best is None or avg < best[1]:
+                best = (key, avg)
+        return {"launches": launches,
+                "best": {"launch": best[0], "GBps": round(nbytes / best[1] / 1e6, 1)},
+                "kernel_rate_over_copy": round((bmin / kernel_ms) / (nbytes / best[1]), 4)}
+
+    res = {"bytes_moved": nbytes, "inputs": 2 if two_inputs else 1}
+    res.update(sweep(launch_copy, not two_inputs))
+    if launch_in_place is not None:
+        res["in_place"] = sweep(launch_in_place, False)
     return res
 
 
@@ -582,7 +595,9 @@ def run_element_mul(args, name: str) -> dict:
         out["roofline"]["ceiling"] = {"copy": copy_ceiling(
             args, out["roofline"]["kernel_ms_avg"], bmin, 2 * M * V * 2,
             lambda i, g, t_: xr.probe_copy(copies[(i + 1) % n_c], copies[i % n_c], workgroups=g,
-                                           threads=t_))}
+                                           threads=t_),
+            launch_in_place=lambda i, g, t_: xr.probe_copy(copies[i], copies[i], workgroups=g,
+                                                           threads=t_))}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_element_mul(w, args.cpu_rows, 0.5)
     return out

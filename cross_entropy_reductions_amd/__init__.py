@@ -511,7 +511,9 @@ def probe_copy(out: torch.Tensor, src: torch.Tensor, src1: torch.Tensor | None =
                workgroups: int, threads: int = 256, stream=None) -> torch.Tensor:
     """The copy ceiling (xr_probe_copy): src's bytes (src ^ src1's with a second input) into
     out, by a grid-stride kernel of ``workgroups`` workgroups of ``threads`` threads, or by
-    the runtime's device-to-device copy when ``workgroups`` is 0. Returns out."""
+    the runtime's device-to-device copy when ``workgroups`` is 0. ``src`` being ``out`` (the
+    same memory) is the kernel's stream in place, every vector read and written back. Returns
+    out."""
     for t, name in ((out, "out"), (src, "src"), (src1, "src1")):
         if t is None:
             continue

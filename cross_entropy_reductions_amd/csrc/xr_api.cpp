@@ -1039,8 +1039,12 @@ xr_status_t xr_probe_copy(void* out, const void* in, const void* in1, int64_t by
   if (!aligned_to(out, 16) || !aligned_to(in, 16) || (in1 && !aligned_to(in1, 16)) ||
       bytes % 16 != 0)
     return XR_ERR_ALIGN;
-  if (spans_overlap(out, bytes, in, bytes) || (in1 && spans_overlap(out, bytes, in1, bytes)))
+  // in place: out == in exactly, one input, the copy kernel
+  const bool in_place = out == in;
+  if ((!in_place && spans_overlap(out, bytes, in, bytes)) ||
+      (in1 && spans_overlap(out, bytes, in1, bytes)) || (in_place && workgroups == 0))
     return XR_ERR_ALIAS;
+  if (in_place && in1) return XR_ERR_VALUE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (workgroups == 0) {  // the runtime's copy, bracketed by the profiling events like a kernel
     if (in1) return XR_ERR_VALUE;
@@ -1052,7 +1056,7 @@ xr_status_t xr_probe_copy(void* out, const void* in, const void* in1, int64_t by
     return XR_OK;
   }
   Plan p;
-  p.kernel = probe_copy_kernel_ptr(threads, in1 ? 2 : 1);
+  p.kernel = probe_copy_kernel_ptr(threads, in_place ? 0 : in1 ? 2 : 1);
   if (!p.kernel) return XR_ERR_SHAPE;
   p.grid = workgroups;
   CopyParams prm{static_cast<const char*>(in), static_cast<const char*>(in1),

@@ -205,7 +205,7 @@ const void* ln_dwdb_kernel_ptr(int dtype);
 const void* bsr_softmax_bwd_kernel_ptr(int dtype);
 const void* probe_rows_kernel_ptr(int dtype, Shape s, int inputs);
 // The ceiling's plain copy (xr_probe_copy): 256, 512 or 1024 threads per workgroup, one or
-// two inputs.
+// two inputs, or none (in place: the output read and written back).
 const void* probe_copy_kernel_ptr(int threads, int inputs);
 constexpr int kCopyUnroll = 4;  // 16-byte vectors in flight per thread of the plain copy
 // Block-sparse backward: workgroup size, and listed blocks per row held in registers.

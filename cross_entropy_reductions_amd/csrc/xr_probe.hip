@@ -60,8 +60,42 @@ __global__ __launch_bounds__(THREADS) void probe_copy_kernel(CopyParams p) {
   }
 }
 
+// The same stream in place: every vector read and written back to where it was, by the thread
+// that read it (the traffic of a kernel that overwrites its input). A store of the value just
+// loaded from the same address is a no-op to the compiler, which would drop the loop; the
+// empty asm statement (no instruction) makes each vector opaque to it.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void probe_inplace_kernel(CopyParams p) {
+  constexpr int U = kCopyUnroll;
+  u32x4* io = reinterpret_cast<u32x4*>(p.out);
+  const int64_t nvec = p.nvec;
+  const int64_t stride = (int64_t)gridDim.x * THREADS;
+  int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+  for (; i + (U - 1) * stride < nvec; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(io + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      asm volatile("" : "+v"(v[u]));
+      __builtin_nontemporal_store(v[u], io + i + u * stride);
+    }
+  }
+  for (; i < nvec; i += stride) {
+    u32x4 v = __builtin_nontemporal_load(io + i);
+    asm volatile("" : "+v"(v));
+    __builtin_nontemporal_store(v, io + i);
+  }
+}
+
 const void* probe_copy_kernel_ptr(int threads, int inputs) {
-  if (inputs == 1) {
+  if (inputs == 0) {
+    switch (threads) {
+      case 256: return reinterpret_cast<const void*>(&probe_inplace_kernel<256>);
+      case 512: return reinterpret_cast<const void*>(&probe_inplace_kernel<512>);
+      case 1024: return reinterpret_cast<const void*>(&probe_inplace_kernel<1024>);
+    }
+  } else if (inputs == 1) {
     switch (threads) {
       case 256: return reinterpret_cast<const void*>(&probe_copy_kernel<256, 1>);
       case 512: return reinterpret_cast<const void*>(&probe_copy_kernel<512, 1>);

@@ -352,9 +352,13 @@ xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void
  * `threads` threads (256, 512 or 1024, else XR_ERR_SHAPE), 16-byte non-temporal loads and
  * stores, four vectors in flight per thread; workgroups == 0: the runtime's device-to-device
  * copy (hipMemcpyAsync; in1 must be NULL, else XR_ERR_VALUE). Either is bracketed by the
- * events of xr_set_profile_events().
+ * events of xr_set_profile_events(). out == in (exactly) with in1 NULL and workgroups > 0 is
+ * the same kernel stream in place, every vector read and written back (the traffic of a
+ * kernel that overwrites its input, as the cross-entropy's gradient does).
  *   in, in1, out: device memory on 16-byte boundaries, bytes a multiple of 16 (else
- *   XR_ERR_ALIGN); out must not overlap an input (XR_ERR_ALIAS); bytes == 0 enqueues nothing
+ *   XR_ERR_ALIGN); out must not overlap an input other than as that exact in-place call
+ *   (XR_ERR_ALIAS; in place with workgroups == 0 too); in place with in1: XR_ERR_VALUE;
+ *   bytes == 0 enqueues nothing
  */
 xr_status_t xr_probe_copy(void* out, const void* in, const void* in1, int64_t bytes,
                           int32_t workgroups, int32_t threads, void* stream);

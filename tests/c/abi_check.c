@@ -47,6 +47,8 @@ int main(void) {
   CHECK(xr_probe_copy(q, (char*)q + 16, NULL, 4096, 8, 256, NULL) == XR_ERR_ALIAS);
   CHECK(xr_probe_copy(q, p, NULL, 4096, 8, 100, NULL) == XR_ERR_SHAPE);
   CHECK(xr_probe_copy(q, p, p, 4096, 0, 256, NULL) == XR_ERR_VALUE);
+  CHECK(xr_probe_copy(q, q, NULL, 4096, 0, 256, NULL) == XR_ERR_ALIAS);
+  CHECK(xr_probe_copy(q, q, p, 4096, 8, 256, NULL) == XR_ERR_VALUE);
   CHECK(xr_element_mul(p, 8, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_nll_fwd(p, 8, q, 8, NULL, f, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_layernorm_fwd(p, 8, q, 8, q, q, f, f, 4, 8, -1.0f, XR_F32, NULL) == XR_ERR_VALUE);

@@ -213,6 +213,11 @@ def test_probe_copy_argument_errors(xr):
     assert f(O, ctypes.c_void_p(0x100800), None, 4096, 0, 256, None) == XR_ERR_ALIAS
     assert f(O, A, B, 4096, 0, 256, None) == XR_ERR_VALUE   # the runtime's copy has one input
     assert f(O, A, B, 4096, 64, 128, None) == XR_ERR_SHAPE  # not a copy-kernel workgroup size
+    # in place (out == in exactly): the copy kernel only, with one input
+    assert f(O, O, None, 4096, 0, 256, None) == XR_ERR_ALIAS
+    assert f(O, O, B, 4096, 64, 256, None) == XR_ERR_VALUE
+    assert f(O, O, ctypes.c_void_p(0x100800), 4096, 64, 256, None) == XR_ERR_ALIAS
+    assert f(O, O, None, 4096, 64, 128, None) == XR_ERR_SHAPE
 
 
 def test_element_mul_argument_errors(xr):

@@ -69,7 +69,8 @@ def test_probe_two_inputs(shape):
     (16 * 123457, 0, 0),           # the runtime's device-to-device copy
 ])
 def test_probe_copy_moves_exactly_its_bytes(nbytes, workgroups, threads):
-    """xr_probe_copy: every byte of the source copied, nothing past the end written."""
+    """xr_probe_copy: every byte of the source copied (or, in place, written back unchanged),
+    nothing past the end written."""
     src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
     dst = torch.full((nbytes // 4 + 64,), -7, dtype=torch.int32, device="cuda")
     xr.probe_copy(dst[:nbytes // 4], src, workgroups=workgroups, threads=threads or 256)
@@ -82,4 +83,10 @@ def test_probe_copy_moves_exactly_its_bytes(nbytes, workgroups, threads):
         xr.probe_copy(dst[:nbytes // 4], src, src1, workgroups=workgroups, threads=threads)
         torch.cuda.synchronize()
         assert torch.equal(dst[:nbytes // 4], src ^ src1), "xor of two inputs"
+        assert bool((dst[nbytes // 4:] == -7).all()), "past the end"
+        # in place: every vector read and written back unchanged, nothing past the end
+        xr.probe_copy(dst[:nbytes // 4], dst[:nbytes // 4], workgroups=workgroups,
+                      threads=threads)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes // 4], src ^ src1), "in place"
         assert bool((dst[nbytes // 4:] == -7).all()), "past the end"
