@@ -110,6 +110,17 @@ bool spans_overlap(const void* a, uint64_t abytes, const void* b, uint64_t bbyte
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return abytes && bbytes && a0 < b0 + bbytes && b0 < a0 + abytes;
 }
+// Largest byte span of one operand, 2^48 bytes (256 TiB, far beyond any device's memory): a
+// larger one is refused (XR_ERR_SHAPE) before any arithmetic on its sizes or addresses.
+constexpr uint64_t kMaxSpanBytes = uint64_t(1) << 48;
+// An [M, n] matrix of row stride ld (elements of eb bytes; 1 <= n <= ld) spans fewer than
+// kMaxSpanBytes bytes; so does every product of its sizes computed later.
+bool span_ok(int64_t M, int64_t ld, int64_t n, int eb) {
+  const uint64_t lim = kMaxSpanBytes / (uint64_t)eb;  // in elements
+  if ((uint64_t)ld >= lim || n > ld) return false;
+  // (M - 1) ld + n < lim, with n <= ld < lim
+  return M <= 1 || (uint64_t)(M - 1) <= (lim - (uint64_t)n - 1) / (uint64_t)ld;
+}
 // Bytes from the first element of an [M, n] matrix of row stride ld to past its last element.
 uint64_t matrix_span(int64_t M, int64_t ld, int64_t n, int eb) {
   return M > 0 ? (uint64_t)((M - 1) * ld + n) * (uint64_t)eb : 0;
@@ -184,6 +195,7 @@ const void* row_kernel(int op, xr_dtype_t dt, Shape sh, bool nt) {
 // 16-byte boundary (then a row touches exactly ceil(N / elements-per-vector) vectors).
 xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned, bool on16,
                       Plan* plan, bool can_split = false, const DeviceInfo* model = nullptr) {
+  if (!span_ok(M, N, N, elt_bytes(dt))) return XR_ERR_SHAPE;  // keeps M * S and the like exact
   int dev = 0;
   DeviceInfo di;
   if (model) di = *model;
@@ -603,6 +615,8 @@ xr_status_t xr_softmax_fwd_ex(void* y, int64_t ld_y, const void* x, int64_t ld_x
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_x < N || ld_y < N) return XR_ERR_STRIDE;
   if (M == 0) return XR_OK;
+  if (!span_ok(M, ld_x, N, elt_bytes(dtype)) || !span_ok(M, ld_y, N, elt_bytes(dtype)))
+    return XR_ERR_SHAPE;
   if (!x || !y) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if (!aligned_to(x, eb) || !aligned_to(y, eb)) return XR_ERR_ALIGN;
@@ -647,6 +661,8 @@ xr_status_t xr_nll_fwd(void* out, int64_t ld_out, const void* x, int64_t ld_x,
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_x < N || ld_out < N) return XR_ERR_STRIDE;
   if (M == 0) return XR_OK;
+  if (!span_ok(M, ld_x, N, elt_bytes(dtype)) || !span_ok(M, ld_out, N, elt_bytes(dtype)))
+    return XR_ERR_SHAPE;
   if (!x || !out || !idx || !loss) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if (!aligned_to(x, eb) || !aligned_to(out, eb) || !aligned_to(idx, 8) || !aligned_to(loss, 4))
@@ -687,6 +703,8 @@ xr_status_t xr_layernorm_fwd(void* y, int64_t ld_y, const void* x, int64_t ld_x,
   if (ld_x < N || ld_y < N) return XR_ERR_STRIDE;
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return XR_ERR_VALUE;
   if (M == 0) return XR_OK;
+  if (!span_ok(M, ld_x, N, elt_bytes(dtype)) || !span_ok(M, ld_y, N, elt_bytes(dtype)))
+    return XR_ERR_SHAPE;
   if (!y || !x || !w || !b || !mean || !rstd) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if (!aligned_to(y, eb) || !aligned_to(x, eb) || !aligned_to(w, eb) || !aligned_to(b, eb) ||
@@ -730,6 +748,9 @@ xr_status_t xr_layernorm_bwd(void* dx, int64_t ld_dx, const void* dy, int64_t ld
   if (!valid_dtype(dtype)) return XR_ERR_DTYPE;
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_dx < N || ld_dy < N || ld_x < N) return XR_ERR_STRIDE;
+  if (!span_ok(M, ld_dx, N, elt_bytes(dtype)) || !span_ok(M, ld_dy, N, elt_bytes(dtype)) ||
+      !span_ok(M, ld_x, N, elt_bytes(dtype)))
+    return XR_ERR_SHAPE;
   if (!w || !dw || !db || !workspace) return XR_ERR_NULL;
   if (M > 0 && (!dx || !dy || !x || !mean || !rstd)) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
@@ -786,11 +807,16 @@ xr_status_t xr_bsr_softmax_bwd(const void* y, int64_t stride_zy, void* dx, int64
       (block & (block - 1)) != 0)
     return XR_ERR_SHAPE;
   if (!(scale == scale)) return XR_ERR_VALUE;
+  // one batch's blocks under 2 GiB (checked before the product can wrap)
+  if ((uint64_t)n_blocks >= (1ull << 31) / ((uint64_t)block * (uint64_t)block * eb))
+    return XR_ERR_SHAPE;
   const uint64_t batch_bytes = (uint64_t)n_blocks * (uint64_t)block * (uint64_t)block * eb;
-  if (batch_bytes >= (1ull << 31)) return XR_ERR_SHAPE;
   if (lut_len < 2 * n_brows || lut_len >= (1ll << 29)) return XR_ERR_SHAPE;
   if (stride_zy < n_blocks * block * block || stride_zdx < n_blocks * block * block)
     return XR_ERR_STRIDE;
+  if (!span_ok(Z, stride_zy, n_blocks * block * block, eb) ||
+      !span_ok(Z, stride_zdx, n_blocks * block * block, eb))
+    return XR_ERR_SHAPE;
   if (Z == 0 || n_brows == 0 || n_blocks == 0) return XR_OK;
   if (!y || !dx || !lut) return XR_ERR_NULL;
   if (!aligned_to(y, 16) || !aligned_to(dx, 16) || !aligned_to(lut, 4) ||
@@ -828,6 +854,9 @@ xr_status_t xr_softmax_bwd_ex(void* dx, int64_t ld_dx, const void* y, int64_t ld
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld_dx < N || ld_y < N || ld_dy < N) return XR_ERR_STRIDE;
   if (M == 0) return XR_OK;
+  if (!span_ok(M, ld_dx, N, elt_bytes(dtype)) || !span_ok(M, ld_y, N, elt_bytes(dtype)) ||
+      !span_ok(M, ld_dy, N, elt_bytes(dtype)))
+    return XR_ERR_SHAPE;
   if (!dx || !y || !dy) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if (!aligned_to(dx, eb) || !aligned_to(y, eb) || !aligned_to(dy, eb)) return XR_ERR_ALIGN;
@@ -883,6 +912,10 @@ xr_status_t xr_xent_fwd_bwd_ex(void* logits, int64_t ld, const int64_t* target, 
   if (grad_scale_stride < 0) return XR_ERR_VALUE;
   if (M < 0 || V < 1) return XR_ERR_SHAPE;
   if (ld < V) return XR_ERR_STRIDE;
+  // the logits, and the upstream values read at i * grad_scale_stride
+  if (!span_ok(M, ld, V, elt_bytes(dtype)) ||
+      (grad_scale && !span_ok(M, std::max<int64_t>(grad_scale_stride, 1), 1, 4)))
+    return XR_ERR_SHAPE;
   if (reduction != XR_REDUCTION_NONE && !loss) return XR_ERR_NULL;
   if (reduction == XR_REDUCTION_NONE) loss = nullptr;
   if (!workspace) return XR_ERR_NULL;
@@ -970,6 +1003,9 @@ xr_status_t xr_element_mul(void* x, int64_t ld, int64_t M, int64_t N, xr_dtype_t
   if (M < 0 || N < 1) return XR_ERR_SHAPE;
   if (ld < N) return XR_ERR_STRIDE;
   if (M == 0) return XR_OK;
+  if (!span_ok(M, ld, N, elt_bytes(dtype)) ||
+      !span_ok(M, std::max<int64_t>(grad_output_stride, 1), 1, 4))
+    return XR_ERR_SHAPE;
   if (!x || !grad_output) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   if (!aligned_to(x, eb) || !aligned_to(grad_output, 4)) return XR_ERR_ALIGN;
@@ -1009,6 +1045,8 @@ xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void
   if (M < 0 || N < 1 || split < 1) return XR_ERR_SHAPE;
   if (ld_in < N || ld_out < N) return XR_ERR_STRIDE;
   if (M == 0) return XR_OK;
+  if (!span_ok(M, ld_in, N, elt_bytes(dtype)) || !span_ok(M, ld_out, N, elt_bytes(dtype)))
+    return XR_ERR_SHAPE;
   if (!out || !in0) return XR_ERR_NULL;
   const int eb = elt_bytes(dtype);
   // whole 16-byte vectors only: every row on a 16-byte boundary, N a whole number of vectors
@@ -1033,7 +1071,7 @@ xr_status_t xr_probe_rows(void* out, int64_t ld_out, const void* in0, const void
 
 xr_status_t xr_probe_copy(void* out, const void* in, const void* in1, int64_t bytes,
                           int32_t workgroups, int32_t threads, void* stream) {
-  if (bytes < 0 || workgroups < 0) return XR_ERR_SHAPE;
+  if (bytes < 0 || (uint64_t)bytes >= kMaxSpanBytes || workgroups < 0) return XR_ERR_SHAPE;
   if (bytes == 0) return XR_OK;
   if (!out || !in) return XR_ERR_NULL;
   if (!aligned_to(out, 16) || !aligned_to(in, 16) || (in1 && !aligned_to(in1, 16)) ||

@@ -17,6 +17,9 @@
  *   - Arguments, and the launch limits of the sizes given, are validated before anything is
  *     enqueued; on an error nothing is enqueued and the status says what is wrong. No C++
  *     exception crosses this ABI.
+ *   - No operand may span 2^48 bytes or more from its first to past its last element (far
+ *     beyond any device's memory): such sizes and strides return XR_ERR_SHAPE before any
+ *     arithmetic on them, and the workspace queries return 0 for them.
  *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
  *   - The library keeps no state across calls except a per-device cache of device
  *     properties, the process-wide overrides of xr_set_option() and the profiling events

@@ -49,6 +49,11 @@ int main(void) {
   CHECK(xr_probe_copy(q, p, p, 4096, 0, 256, NULL) == XR_ERR_VALUE);
   CHECK(xr_probe_copy(q, q, NULL, 4096, 0, 256, NULL) == XR_ERR_ALIAS);
   CHECK(xr_probe_copy(q, q, p, 4096, 8, 256, NULL) == XR_ERR_VALUE);
+  /* operands spanning 2^48 bytes or more */
+  CHECK(xr_softmax_fwd(p, (int64_t)1 << 24, q, (int64_t)1 << 24, (int64_t)1 << 24,
+                       (int64_t)1 << 24, XR_BF16, NULL) == XR_ERR_SHAPE);
+  CHECK(xr_element_mul(p, 8, 4, 8, XR_F32, f, (int64_t)1 << 50, NULL) == XR_ERR_SHAPE);
+  CHECK(xr_probe_copy(q, p, NULL, (int64_t)1 << 48, 8, 256, NULL) == XR_ERR_SHAPE);
   CHECK(xr_element_mul(p, 8, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_nll_fwd(p, 8, q, 8, NULL, f, 4, 8, XR_F32, NULL, 0, NULL) == XR_ERR_NULL);
   CHECK(xr_layernorm_fwd(p, 8, q, 8, q, q, f, f, 4, 8, -1.0f, XR_F32, NULL) == XR_ERR_VALUE);

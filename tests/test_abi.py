@@ -321,6 +321,53 @@ def test_bsr_argument_errors(xr):
     assert f(Y, 4096, D, 4096, 0, L, 20, 4, 4, 32, one, 0, None) == XR_OK
 
 
+def test_spans_beyond_the_limit_are_refused(xr):
+    """An operand spanning 2^48 bytes or more is refused with XR_ERR_SHAPE before any arithmetic
+    on its sizes or addresses (none of these calls gets as far as a device query)."""
+    lib = xr.lib
+    P, Q, R, S, T = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
+    big, half = 1 << 24, 1 << 46   # 2^24 x 2^24 bf16 rows: 2^49 bytes
+    one = ctypes.c_float(1.0)
+    assert lib.xr_softmax_fwd(P, big, Q, big, big, big, 1, None) == XR_ERR_SHAPE
+    assert lib.xr_softmax_fwd(P, 1 << 47, Q, 8, 2, 8, 1, None) == XR_ERR_SHAPE  # the stride alone
+    # just under the limit the sizes pass; the spans then overlap (nothing is enqueued)
+    assert lib.xr_softmax_fwd(P, half, Q, 8, 2, 8, 1, None) == XR_ERR_ALIAS
+    # (M - 1) ld + N elements of 2 bytes: 2^48 - 2 bytes passes, 2^48 does not
+    assert lib.xr_softmax_fwd(P, half, Q, half, 2, half - 1, 1, None) == XR_ERR_ALIAS
+    assert lib.xr_softmax_fwd(P, half, Q, half, 2, half, 1, None) == XR_ERR_SHAPE
+    assert lib.xr_softmax_bwd(P, big, Q, big, R, big, big, big, 1, None) == XR_ERR_SHAPE
+    assert lib.xr_softmax_fwd_ex(P, big, Q, big, big, big, 1, S, 4096, None) == XR_ERR_SHAPE
+    assert lib.xr_nll_fwd(P, big, Q, big, R, S, big, big, 1, None, 0, None) == XR_ERR_SHAPE
+    assert lib.xr_xent_fwd_bwd_ex(P, big, Q, big, big, -100, 1, 0, None, 0, R, S, T, T, 4096,
+                                  None) == XR_ERR_SHAPE
+    # upstream values read at i * stride: (M - 1) * 2^50 floats
+    assert lib.xr_xent_fwd_bwd_ex(P, 8, Q, 4, 8, -100, 1, 0, R, 1 << 50, S, T, None, T, 4096,
+                                  None) == XR_ERR_SHAPE
+    assert lib.xr_element_mul(P, big, big, big, 1, Q, 0, None) == XR_ERR_SHAPE
+    assert lib.xr_element_mul(P, 8, 4, 8, 1, Q, 1 << 50, None) == XR_ERR_SHAPE
+    assert lib.xr_layernorm_fwd(P, big, Q, big, R, S, T, T, big, big, ctypes.c_float(1e-5), 1,
+                                None) == XR_ERR_SHAPE
+    assert lib.xr_layernorm_bwd(P, big, Q, big, R, big, S, T, T, S, T, big, big, 1, T, 1 << 20,
+                                None) == XR_ERR_SHAPE
+    assert lib.xr_probe_rows(P, big, Q, None, big, big, big, 1, 256, 8, 1, None, -100,
+                             None) == XR_ERR_SHAPE
+    assert lib.xr_probe_copy(P, Q, None, 1 << 48, 64, 256, None) == XR_ERR_SHAPE
+    # block-sparse: a block count whose byte product would wrap a 64-bit integer, and a batch
+    # count past the limit
+    assert lib.xr_bsr_softmax_bwd(P, 4096, Q, 4096, 2, R, 20, 4, 1 << 61, 32, one, 1,
+                                  None) == XR_ERR_SHAPE
+    assert lib.xr_bsr_softmax_bwd(P, 4096, Q, 4096, 1 << 40, R, 20, 4, 4, 32, one, 1,
+                                  None) == XR_ERR_SHAPE
+    # plans and workspace queries of such sizes
+    out = xr.XrPlan()
+    assert lib.xr_plan_model(0, big, big, 1, 1, 256, 8, ctypes.byref(out)) == XR_ERR_SHAPE
+    assert lib.xr_plan_model(0, 4, 1 << 48, 0, 1, 256, 8, ctypes.byref(out)) == XR_ERR_SHAPE
+    assert lib.xr_plan_model(0, 4, 8, 0, 1, 256, 8, ctypes.byref(out)) == XR_OK
+    for q in (lib.xr_softmax_workspace_bytes, lib.xr_xent_workspace_bytes,
+              lib.xr_nll_fwd_workspace_bytes):
+        assert q(big, big, 1) == 0
+
+
 def test_header_is_plain_c_and_links(tmp_path, xr):
     """include/xr.h compiles as C99 on its own, and a C program linked against libxr.so
     runs its argument checks (tests/c/abi_check.c)."""
