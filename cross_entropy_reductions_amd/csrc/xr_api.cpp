@@ -19,7 +19,7 @@
 namespace xr {
 namespace {
 
-constexpr int32_t kVersion = 10300;  // 1.3.0
+constexpr int32_t kVersion = 10400;  // 1.4.0
 constexpr int64_t kMinChunkVecs = 256;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups in one launch
 

@@ -22,7 +22,7 @@ int main(void) {
   void* q = (void*)0x20000;
   float* f = (float*)0x30000;
   int64_t* t = (int64_t*)0x40000;
-  CHECK(xr_version() >= 10300);
+  CHECK(xr_version() >= 10400);
   CHECK(strcmp(xr_status_string(XR_OK), "ok") == 0);
   CHECK(xr_softmax_fwd(p, 10, q, 10, 4, 10, (xr_dtype_t)7, NULL) == XR_ERR_DTYPE);
   CHECK(xr_softmax_fwd(p, 9, q, 10, 4, 10, XR_F32, NULL) == XR_ERR_STRIDE);

@@ -42,7 +42,7 @@ def test_status_strings_and_version(xr):
     for code in range(1, 13):
         assert xr.status_string(code) != "unknown status"
     assert xr.status_string(99) == "unknown status"
-    assert xr.version() == 10300
+    assert xr.version() == 10400
 
 
 XR_OK, XR_ERR_NULL, XR_ERR_SHAPE, XR_ERR_STRIDE, XR_ERR_DTYPE, XR_ERR_ALIAS = 0, 1, 2, 3, 4, 5
