@@ -26,6 +26,13 @@ __device__ __forceinline__ u32x4 nll_slot(u32x4 v, float c) {
   return o.bits();
 }
 
+// Wave priority while a row-resident softmax wave issues its row's loads (s_setprio; 0 is
+// the default): the wave's requests then go out ahead of the arithmetic of the waves that
+// already hold their rows, and the waves of a launch get their loads in flight sooner. Not
+// used where chunks of a row exchange statistics (the cross-entropy and the split rows),
+// whose waiting and writing waves it would hold back.
+constexpr int kLoadIssuePriority = 3;
+
 // ============================================================================ softmax forward
 // NLL = false: y = softmax(x). NLL = true: y = -log softmax(x) and loss[r] = y[r, idx[r]] as
 // stored (NaN when idx[r] lies outside the row).
@@ -41,7 +48,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
 
   u32x4 v[VPT];
   int64_t r = blockIdx.x;
+  __builtin_amdgcn_s_setprio(kLoadIssuePriority);
   if (r < p.M) issue_loads<D, THREADS, VPT, LP>(v, Chunk<D>(p.x + r * p.ldx_bytes, p.N, 0, cv));
+  __builtin_amdgcn_s_setprio(0);
   while (r < p.M) {
     const int64_t rn = r + G;
     const Chunk<D> cx(p.x + r * p.ldx_bytes, p.N, 0, cv);
@@ -309,8 +318,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   u32x4 vy[VPT], vd[VPT];
   int64_t r = blockIdx.x;
   if (r >= p.M) return;
+  __builtin_amdgcn_s_setprio(kLoadIssuePriority);
   issue_loads2<D, THREADS, VPT, LP>(vy, Chunk<D>(p.y + r * p.ldy_bytes, p.N, 0, cv), vd,
                                     Chunk<D>(p.dy + r * p.lddy_bytes, p.N, 0, cv));
+  __builtin_amdgcn_s_setprio(0);
   if constexpr (ONE_ROW) {
     softmax_bwd_row<D, THREADS, VPT, LP, false>(p, r, p.M, vy, vd, red[0]);
   } else {
