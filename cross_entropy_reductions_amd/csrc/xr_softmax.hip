@@ -28,9 +28,10 @@ __device__ __forceinline__ u32x4 nll_slot(u32x4 v, float c) {
 
 // Wave priority while a row-resident softmax wave issues its row's loads (s_setprio; 0 is
 // the default): the wave's requests then go out ahead of the arithmetic of the waves that
-// already hold their rows, and the waves of a launch get their loads in flight sooner. Not
-// used where chunks of a row exchange statistics (the cross-entropy and the split rows),
-// whose waiting and writing waves it would hold back.
+// already hold their rows, and the waves of a launch get their loads in flight sooner
+// (measured on 4096 x 4096 bf16: backward 19.0 -> 16.9 us, forward 12.0 -> 11.7 us; levels
+// 1 to 3 alike). Not used where chunks of a row exchange statistics (the cross-entropy and
+// the split rows), whose waiting and writing waves it would hold back (measured slower).
 constexpr int kLoadIssuePriority = 3;
 
 // ============================================================================ softmax forward
