@@ -88,7 +88,7 @@ lib.xr_version.restype = _i32
 class XrPlan(ctypes.Structure):
     _fields_ = [("path", _i32), ("threads", _i32), ("vec_per_thread", _i32), ("split", _i32),
                 ("grid", _i32), ("cooperative", _i32), ("chunk_vecs", _i64),
-                ("group_rows", _i32), ("reserved", _i32), ("grid_total", _i64)]
+                ("group_rows", _i32), ("load_priority", _i32), ("grid_total", _i64)]
 
 
 lib.xr_plan.argtypes = [_i32, _i64, _i64, ctypes.c_int, _i32, ctypes.POINTER(XrPlan)]
@@ -610,7 +610,8 @@ def _plan_dict(out: XrPlan) -> dict:
     return {"path": PATHS.get(out.path, str(out.path)), "threads": out.threads,
             "vec_per_thread": out.vec_per_thread, "split": out.split, "grid": out.grid,
             "cooperative": bool(out.cooperative), "chunk_vecs": out.chunk_vecs,
-            "group_rows": out.group_rows, "grid_total": out.grid_total}
+            "group_rows": out.group_rows, "load_priority": bool(out.load_priority),
+            "grid_total": out.grid_total}
 
 
 def plan_model(op: str, M: int, N: int, dtype: torch.dtype, compute_units: int,

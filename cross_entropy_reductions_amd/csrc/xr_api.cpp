@@ -156,6 +156,7 @@ struct Plan {
   bool coop = false;
   int64_t chunk_vecs = 0;
   int group_rows = 1;  // cross-entropy split rows: adjacent rows written back together
+  bool load_prio = false;  // softmax whole rows: raised wave priority for the row's loads
   const void* kernel = nullptr;
 };
 
@@ -302,6 +303,9 @@ xr_status_t make_plan(int op, int64_t M, int64_t N, xr_dtype_t dt, bool aligned,
     // the backward's loop-free form when every row has a workgroup of its own
     if (bwd && p.grid >= M) p.kernel = softmax_bwd_kernel_ptr(dt, *sh, nt_loads, true);
     if (!p.kernel) return XR_ERR_SHAPE;
+    // softmax rows issue their loads at a raised wave priority when the whole grid is
+    // resident at once (measured faster there, slower on grids the GPU takes in rounds)
+    p.load_prio = (op == kOpSoftmaxFwd || bwd) && p.grid <= resident;
   } else if (other_split || (g_opt.grid <= 0 && M * S <= 0x7FFFFFFF)) {
     // (only the cross-entropy has a persistent split form). A row's S chunks must be able
     // to be resident together, or its first chunks could wait for chunks that cannot start
@@ -576,6 +580,7 @@ static xr_status_t plan_query(int32_t op, int64_t M, int64_t N, xr_dtype_t dtype
   out->cooperative = p.coop ? 1 : 0;
   out->chunk_vecs = p.chunk_vecs;
   out->group_rows = p.path == kPathSplit ? p.group_rows : 1;
+  out->load_priority = p.load_prio ? 1 : 0;
   out->grid_total = p.grid;
   return XR_OK;
 }
@@ -629,7 +634,8 @@ xr_status_t xr_softmax_fwd_ex(void* y, int64_t ld_y, const void* x, int64_t ld_x
     return st;
   if (!grid_fits(p)) return XR_ERR_SHAPE;
   SoftmaxFwdParams prm{static_cast<const char*>(x), ld_x * eb, static_cast<char*>(y), ld_y * eb, M, N,
-                       nullptr, nullptr, p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
+                       nullptr, nullptr, p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows,
+                       p.load_prio ? 1 : 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Span mats[] = {{y, matrix_span(M, ld_y, N, eb), true}, {x, matrix_span(M, ld_x, N, eb), false}};
   if (xr_status_t st = use_workspace(p, M, N, workspace, workspace_bytes, mats, 2, s, &prm.partials,
@@ -873,7 +879,7 @@ xr_status_t xr_softmax_bwd_ex(void* dx, int64_t ld_dx, const void* y, int64_t ld
   if (!grid_fits(p)) return XR_ERR_SHAPE;
   SoftmaxBwdParams prm{static_cast<const char*>(y), ld_y * eb, static_cast<const char*>(dy),
                        ld_dy * eb, static_cast<char*>(dx), ld_dx * eb, M, N,
-                       p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows};
+                       p.S, p.chunk_vecs, nullptr, nullptr, p.group_rows, p.load_prio ? 1 : 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Span mats[] = {{dx, matrix_span(M, ld_dx, N, eb), true},
                        {y, matrix_span(M, ld_y, N, eb), false},

@@ -66,6 +66,7 @@ struct SoftmaxFwdParams {
   uint64_t* partials;
   int32_t* flags;
   int group_rows;  // split rows written back in groups of kWriteGroupRows rows (or 1: none)
+  int load_prio = 0;  // whole rows: raise the wave priority while issuing the row's loads
 };
 
 // Layer norm forward: y = (x - mean) rstd w + b per row; mean and rstd saved.
@@ -170,6 +171,7 @@ struct SoftmaxBwdParams {
   uint64_t* partials;
   int32_t* flags;
   int group_rows;  // split rows written back in groups of kWriteGroupRows rows (or 1: none)
+  int load_prio = 0;  // whole rows: raise the wave priority while issuing the row's loads
 };
 
 // One kernel configuration: workgroup size and 16-byte vectors per thread.

@@ -27,11 +27,13 @@ __device__ __forceinline__ u32x4 nll_slot(u32x4 v, float c) {
 }
 
 // Wave priority while a row-resident softmax wave issues its row's loads (s_setprio; 0 is
-// the default): the wave's requests then go out ahead of the arithmetic of the waves that
-// already hold their rows, and the waves of a launch get their loads in flight sooner
-// (measured on 4096 x 4096 bf16: backward 19.0 -> 16.9 us, forward 12.0 -> 11.7 us; levels
-// 1 to 3 alike). Not used where chunks of a row exchange statistics (the cross-entropy and
-// the split rows), whose waiting and writing waves it would hold back (measured slower).
+// the default), when the plan asks for it (p.load_prio): the wave's requests then go out
+// ahead of the arithmetic of the waves that already hold their rows. The plans ask for it
+// only when the whole grid is resident at once (measured on 4096 x 4096 bf16: backward
+// 19.0 -> 16.9 us, forward 12.0 -> 11.7 us; levels 1 to 3 alike); with more workgroups than
+// the GPU holds, waves starting their rows at a raised priority hold back the output passes
+// whose end frees the next workgroups' slots (2-7 % slower on four such shapes). Not used
+// where chunks of a row exchange statistics (the cross-entropy, the split rows): slower.
 constexpr int kLoadIssuePriority = 3;
 
 // ============================================================================ softmax forward
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
 
   u32x4 v[VPT];
   int64_t r = blockIdx.x;
-  __builtin_amdgcn_s_setprio(kLoadIssuePriority);
+  if (p.load_prio) __builtin_amdgcn_s_setprio(kLoadIssuePriority);
   if (r < p.M) issue_loads<D, THREADS, VPT, LP>(v, Chunk<D>(p.x + r * p.ldx_bytes, p.N, 0, cv));
   __builtin_amdgcn_s_setprio(0);
   while (r < p.M) {
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   u32x4 vy[VPT], vd[VPT];
   int64_t r = blockIdx.x;
   if (r >= p.M) return;
-  __builtin_amdgcn_s_setprio(kLoadIssuePriority);
+  if (p.load_prio) __builtin_amdgcn_s_setprio(kLoadIssuePriority);
   issue_loads2<D, THREADS, VPT, LP>(vy, Chunk<D>(p.y + r * p.ldy_bytes, p.N, 0, cv), vd,
                                     Chunk<D>(p.dy + r * p.lddy_bytes, p.N, 0, cv));
   __builtin_amdgcn_s_setprio(0);

@@ -395,7 +395,8 @@ typedef struct xr_plan {
   int32_t cooperative;     /* 1 if launched as a cooperative grid */
   int64_t chunk_vecs;      /* 16-byte vectors per workgroup chunk of a row */
   int32_t group_rows;      /* split rows: adjacent rows whose chunks store together (1: none) */
-  int32_t reserved;
+  int32_t load_priority;   /* 1 if the row kernel raises its wave priority for the row's loads
+                              (whole softmax rows whose grid the device holds at once) */
   int64_t grid_total;      /* workgroups the plan asks for (above INT32_MAX the call fails) */
 } xr_plan_t;
 

@@ -95,3 +95,22 @@ def test_model_argument_errors(xr):
         xr.plan_model("xent", 4, 100, torch.float32, 0, 1)
     with pytest.raises(xr.XrError):
         xr.plan_model("xent", 4, 100, torch.float32, 256, 0)
+
+
+@pytest.mark.parametrize("per_cu", [1, 2, 4, 8, 16, 32])
+def test_load_priority_only_for_one_round_softmax_grids(xr, per_cu):
+    """Whole softmax rows issue their loads at a raised wave priority exactly when the grid is
+    resident at once (grid <= compute units x workgroups per compute unit); no other plan
+    (the cross-entropy, the negative log-softmax, split rows, the stream kernels) does."""
+    resident = CUS * per_cu
+    for M, N, dt in SHAPES + [(2048, 4096, torch.bfloat16), (16384, 1024, torch.float32)]:
+        for op in ("softmax_fwd", "softmax_bwd", "softmax_fwd_ws", "softmax_bwd_ws", "xent",
+                   "nll_fwd"):
+            p = xr.plan_model(op, M, N, dt, CUS, per_cu)
+            want = (op in ("softmax_fwd", "softmax_bwd", "softmax_fwd_ws", "softmax_bwd_ws")
+                    and p["path"] == "resident" and p["grid_total"] <= resident)
+            assert p["load_priority"] == want, (op, M, N, dt, per_cu, p)
+    # 4096 x 4096 bf16: 4096 one-wave workgroups, resident at once from 16 per compute unit
+    p = xr.plan_model("softmax_bwd", 4096, 4096, torch.bfloat16, CUS, 16)
+    assert p["load_priority"] and p["threads"] == 64 and p["grid_total"] == 4096
+    assert not xr.plan_model("softmax_bwd", 4096, 4096, torch.bfloat16, CUS, 8)["load_priority"]
