@@ -795,7 +795,7 @@ def run_softmax(args, name: str) -> dict:
                 "softmax_split_kernel" if p["split"] > 1 else "softmax_fwd_kernel",
                 {"M": M, "N": N, "bytes_min": b_fwd + b_bwd, "path": p["path"],
                  "threads": p["threads"], "split": p["split"], "grid": p["grid"],
-                 "input_sets": nsets},
+                 "load_priority": p["load_priority"], "input_sets": nsets},
                 w["dtype"], kernel_bytes=b_fwd)
     if bwd:
         kavg = statistics.mean(bwd_ms)
