@@ -165,7 +165,10 @@ class Oracle:
         ix = np.ascontiguousarray(idx, dtype=np.int64)
         if ix.shape != (M,):
             raise ValueError("idx must hold one index per row")
-        out = np.full((M, N), np.nan, dtype=np.float64)
+        # -1 is no value of -log p: an entry left unwritten fails every check of the output,
+        # and a read past a row's end (another row's first entry, written or not) is never
+        # the NaN that an index outside the row gives
+        out = np.full((M, N), -1.0, dtype=np.float64)
         loss = np.full(M, np.nan, dtype=np.float64)
         self.lib.xro_nll_fwd(ptr, ld, ix.ctypes.data, M, N, code, out.ctypes.data,
                              loss.ctypes.data)

@@ -24,6 +24,8 @@ and -inf target logits, are outside the contract and are not drawn.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -32,8 +34,9 @@ from hypothesis import strategies as st
 import oracle
 import synth
 
-# derandomized: every run draws the same cases
-SETTINGS = settings(max_examples=40, deadline=None, derandomize=True,
+# derandomized: every run draws the same cases (XR_PROPERTY_EXAMPLES draws more of them)
+SETTINGS = settings(max_examples=int(os.environ.get("XR_PROPERTY_EXAMPLES", "40")),
+                    deadline=None, derandomize=True,
                     suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 
 
