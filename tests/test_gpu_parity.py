@@ -501,6 +501,51 @@ def test_softmax_neg_inf(orc):
     assert np.all(y[np.isneginf(x)] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nonfinite_inputs(orc, dtype):
+    """A row holding a NaN or a +inf gives NaN in every output of that row, on every launch
+    path, as the oracle does: the softmax, its backward, the cross-entropy's gradient and row
+    loss, and then the mean. An ignored row is not read, so a NaN in it changes nothing (zero
+    gradient, zero loss). The other rows match the oracle as usual."""
+    M, N = 6, 3001
+    x = synth.random_rows(12300, M, N, dtype=dtype, scale=3.0)
+    nan, inf = (0x7FC0, 0x7F80) if dtype == "bf16" else (np.nan, np.inf)
+    x[1, 17] = nan
+    x[3, 2900] = inf
+    x[5, 0] = nan
+    bad, good = [1, 3], [0, 2, 4]
+    dy = synth.random_rows(12301, M, N, dtype=dtype, scale=1.0)
+    t = synth.random_targets(12302, M, N)
+    t[5] = -100
+    for name, path, split in (("auto", 0, 0), ("resident", 1, 0), ("split2", 2, 2),
+                              ("stream", 3, 0)):
+        xr.set_option("path", path)
+        xr.set_option("split", split)
+        what = f"{dtype} {name}"
+        # softmax forward and backward
+        y = to_host(xr.softmax_fwd(to_device(x)))
+        want = orc.softmax_fwd(x)
+        assert np.array_equal(np.isnan(widen(y)), np.isnan(want)), f"{what}: softmax NaN pattern"
+        assert np.all(np.isnan(widen(y)[bad + [5]])), f"{what}: softmax rows with NaN / +inf"
+        check_probs(y[good], want[good], f"{what}: softmax")
+        dx = to_host(xr.softmax_bwd(to_device(y), to_device(dy)))
+        want_dx = orc.softmax_bwd(y, dy)
+        assert np.array_equal(np.isnan(widen(dx)), np.isnan(want_dx)), f"{what}: backward NaN pattern"
+        check_output(dx[good], want_dx[good], f"{what}: backward")
+        # cross-entropy: row 5 is ignored, so its NaN is never read
+        g, rows, mean, counts = run_xent(x, t, N)
+        n, nbad = orc.xent_count(t, N, -100)
+        assert int(counts[0]) == n and int(counts[1]) == nbad and int(counts[2]) == 0, what
+        gw, lw = orc.xent_rows(x, t, N, n, -100)
+        assert np.all(np.isnan(widen(g)[bad])) and np.all(np.isnan(gw[bad])), f"{what}: gradient"
+        assert np.all(np.isnan(rows[bad])) and np.all(np.isnan(lw[bad])), f"{what}: row losses"
+        assert np.all(widen(g)[5] == 0) and rows[5] == 0 and lw[5] == 0, f"{what}: ignored row"
+        assert math.isnan(mean), f"{what}: mean"
+        check_xent_grad(g[good], gw[good], t[good], N, n, f"{what}: gradient")
+        check_losses(rows[good], 0.0, lw[good], 0.0, f"{what}: row losses")
+    xr.reset_options()
+
+
 def test_partial_overlap_is_rejected():
     x = torch.zeros((4, 100), dtype=torch.float32, device="cuda")
     with pytest.raises(xr.XrError, match="overlap"):
