@@ -232,7 +232,8 @@ size_t xr_xent_workspace_bytes(int64_t M, int64_t V, xr_dtype_t dtype);
  *   workspace      device scratch of at least xr_xent_workspace_bytes(M, V, dtype) bytes
  *   M >= 0 (M == 0 still writes mean_loss = NaN and counts = {0, 0, 0}), V >= 1
  * Rows whose only finite logits are missing (all -inf), or a target logit of -inf, give
- * NaN / +inf; NaN and +inf logits are outside the contract.
+ * NaN / +inf; a NaN or +inf logit in a row that is not ignored makes that row's gradient and
+ * loss NaN (and so the mean or sum); an ignored row is never read, whatever it holds.
  * No written buffer (logits, row_loss, mean_loss, counts, the workspace) may overlap another
  * buffer of the call (XR_ERR_ALIAS); target and grad_scale are only read.
  */
