@@ -364,7 +364,9 @@ void xro_xent_rows_ex(const void* logits, int64_t ld, const int64_t* target, con
     double d = 0.0;
     for (int64_t j = 0; j < V; ++j) d += exp(load_elem(logits, off + j, dtype) - m);
     double xt = load_elem(logits, off + t, dtype);
-    loss[r] = m + log(d) - xt;
+    /* logsumexp - x_t with the difference first: float64 keeps log d at any magnitude
+       of m (m + log d rounds log d away once |m| passes about 1e16) */
+    loss[r] = (m - xt) + log(d);
     if (g) {
       /* d(loss_i)/d(x_ij) = p_j - [j == t]; the reduction and the upstream value scale it. */
       double w = scale ? scale[i * scale_stride] : 1.0;

@@ -30,8 +30,8 @@ MUTANTS = {
     "softmax backward uses y's stride for dy": (
         "s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_dy + j, dtype);",
         "s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_y + j, dtype);"),
-    "loss adds the target logit": ("loss[r] = m + log(d) - xt;", "loss[r] = m + log(d) + xt;"),
-    "loss drops log d": ("loss[r] = m + log(d) - xt;", "loss[r] = m - xt;"),
+    "loss adds the target logit": ("loss[r] = (m - xt) + log(d);", "loss[r] = (m + xt) + log(d);"),
+    "loss drops log d": ("loss[r] = (m - xt) + log(d);", "loss[r] = (m - xt);"),
     "target logit read from row 0": ("double xt = load_elem(logits, off + t, dtype);",
                                      "double xt = load_elem(logits, t, dtype);"),
     "gradient not divided by n": ("if (reduction == XRO_MEAN) w = w / (double)n;",
