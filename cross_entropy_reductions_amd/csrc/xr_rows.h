@@ -10,10 +10,28 @@ namespace xr {
 inline constexpr float kNegInf = -__builtin_inff();
 constexpr int kSpinLimit = 1 << 20;
 
-// m log2e rounded once to fp32. The sum pass subtracts this value from every x log2e, and
-// the output pass builds its exponent constant on the same value, so the rounding cancels
-// between the two passes instead of entering every output (hence no contraction of the
-// product into a neighbouring add).
+// Exponentials are taken relative to the row maximum m; the results must depend only on the
+// differences x - m, not on m's magnitude (a row filled with a large negative mask value
+// keeps the maximum's term at exactly 1).
+//  * Sum pass: exp2(x log2e - mL), mL = m log2e rounded once (one fma per element), with a
+//    per-thread correction of the sum where mL's rounding would matter (thread_sum_exp).
+//  * Output pass, exp(x - m) / D = exp2 of (x - m) log2e - off with off = log2 D (log2 d,
+//    plus log2 n and -log2|s| for the cross-entropy), in one of two forms:
+//      scaled    exp2(x log2e - c), c = mL + off: one fma per element;
+//      relative  exp2((x - m) log2e - off): one subtraction more.
+//    The scaled form carries the roundings of mL and c into every exponent: at most 2^-18
+//    (2.6e-6 relative in a result) while both stay under 2^7 in magnitude (|m| under about
+//    88), growing with |m| past that (emulated over rows of 32000 fp32 logits with the
+//    maximum near 1e3 / 1e5 / -1e6: 6.0e-5 / 4.2e-3 / 5.9e-2 relative, against 3.9e-6 in
+//    the relative form); mL itself overflows past |m| = 2.4e38. The relative form instead
+//    rounds x - m where x lies far below m: over the 2048 x 256000 fp32 cross-entropy rows
+//    the emulated worst case is 9.3e-6 scaled, 1.0e-5 relative. So rows whose mL and c stay
+//    under 2^7 take the scaled form and all others the relative one, the same choice in
+//    every lane (one scalar branch around the pass).
+// In the scaled form the thread holding the maximum forms its term and the output constant
+// on the same mL, whose rounding then cancels: a one-column row gets p = 1 and a zero
+// gradient exactly.
+// m log2e rounded once to fp32 (no contraction into a neighbouring operation).
 __device__ __forceinline__ float scaled_max(float m) {
 #pragma clang fp contract(off)
   return m * kLog2e;
@@ -26,6 +44,54 @@ __device__ __forceinline__ float scaled_max(float m) {
 __device__ __forceinline__ float exp_offset(float mL, float small) {
 #pragma clang fp contract(off)
   return mL + small;
+}
+// Magnitude below which the scaled form's rounded values keep their error within 2^-18.
+constexpr float kScaledLimit = 0x1p7f;
+// |m| below which the sum pass splits m log2e into mL + lo with |lo| <= 32.
+constexpr float kSplitLimit = 0x1p29f;
+
+// How a row's outputs exp2((x - m) log2e - off) are evaluated; the same in every lane.
+struct ExpForm {
+  float m;      // the row maximum
+  float c;      // scaled: exp_offset(scaled_max(m), off); relative: off
+  bool scaled;
+};
+__device__ __forceinline__ ExpForm exp_form(float m, float off) {
+  const float mL = scaled_max(m);
+  const float c = exp_offset(mL, off);
+  // m and off are the same in every lane: readfirstlane makes the choice a scalar one
+  const bool scaled =
+      __builtin_amdgcn_readfirstlane(fabsf(mL) < kScaledLimit && fabsf(c) < kScaledLimit) != 0;
+  return {m, scaled ? c : off, scaled};
+}
+template <bool SCALED>
+__device__ __forceinline__ float exp_of(float x, const ExpForm& f) {
+  return __builtin_amdgcn_exp2f(SCALED ? __builtin_fmaf(x, kLog2e, -f.c)
+                                       : __builtin_fmaf(x - f.m, kLog2e, -f.c));
+}
+// The negative log-softmax's -log p = m + log d - x in the same two forms: scaled c - x with
+// c = m + log d (one rounding of c, at most 2^-18 while |c| < 2^7), relative
+// log d - (x - m).
+__device__ __forceinline__ ExpForm nll_form(float m, float lg) {
+  const float c = m + lg;
+  const bool scaled =
+      __builtin_amdgcn_readfirstlane(fabsf(m) < kScaledLimit && fabsf(c) < kScaledLimit) != 0;
+  return {m, scaled ? c : lg, scaled};
+}
+template <bool SCALED>
+__device__ __forceinline__ float nll_of(float x, const ExpForm& f) {
+  return SCALED ? f.c - x : f.c - (x - f.m);
+}
+
+// Runs body(Form<true>()) or body(Form<false>()) as the row's form says: each form gets a
+// whole pass of straight-line code under one scalar branch. The row kernels issue their
+// next row's loads after it, not inside the bodies: the compiler hoists loads common to both
+// arms ahead of the branch, where two rows of registers are then live at once.
+template <bool B> struct Form { static constexpr bool value = B; };
+template <class F>
+__device__ __forceinline__ void with_form(const ExpForm& f, F&& body) {
+  if (f.scaled) body(Form<true>());
+  else body(Form<false>());
 }
 
 __device__ __forceinline__ u32x4 splat(uint32_t w) { return (u32x4){w, w, w, w}; }
@@ -174,21 +240,36 @@ __device__ __forceinline__ float thread_max(const u32x4 (&v)[VPT], const Chunk<D
   return fmaxf(a, b);
 }
 
-// sum_j exp(x_j - m) over the chunk elements this thread holds, computed as
-// exp2(x*log2e - m*log2e), four partial sums.
+// sum_j exp(x_j - m) over the chunk elements this thread holds, as the sum of
+// exp2(x*k - hi), four partial sums; k and hi are chosen once per thread:
+//   |m| < 2^29  k = log2e, hi = mL = m log2e rounded. Where |mL| < 2^7 that is the scaled
+//               form as it stands; past it the sum is scaled once by 2^-lo, lo = m log2e - mL
+//               exactly (an fma gives a product's rounding error exactly), which makes the
+//               terms relative to m itself; |lo| <= 32 keeps every term in range.
+//   otherwise   k is a power of two with k|m| in [2^40, 2^41), hi = k m (both exact): the
+//               maximum's terms are exp2(0) = 1, and every other element lies at least
+//               2^-25 |m| below m, where exp(x - m) is 0 in fp32 and exp2(k (x - m)) is too.
+// One straight-line loop for every row (no branch: the maximum's reduction can overlap it).
 template <int D, int THREADS, int VPT>
-__device__ __forceinline__ float thread_sum_exp(const u32x4 (&v)[VPT], const Chunk<D>& c, float mL) {
+__device__ __forceinline__ float thread_sum_exp(const u32x4 (&v)[VPT], const Chunk<D>& c, float m) {
   constexpr int EPV = Elt<D>::kPerVec;
+  const float mL = scaled_max(m);
+  const bool split = fabsf(m) < kSplitLimit;
+  // 2^(40 - e) for |m| in [2^e, 2^(e+1)): exponent field 167 - e
+  const float kbig = as_f32(((127u + 40u + 127u) << 23) - (as_u32(m) & 0x7f800000u));
+  const float k = split ? kLog2e : kbig;
+  const float hi = split ? mL : kbig * m;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    if (slot_kind<THREADS>(k, c.nvec) == kSlotNone) continue;
-    const u32x4 x = masked_slot<D, THREADS>(v[k], k, c, Elt<D>::kNegInfWord);
+  for (int q = 0; q < VPT; ++q) {
+    if (slot_kind<THREADS>(q, c.nvec) == kSlotNone) continue;
+    const u32x4 x = masked_slot<D, THREADS>(v[q], q, c, Elt<D>::kNegInfWord);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e)
-      s[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(x, e), kLog2e, -mL));
+    for (int e = 0; e < EPV; ++e) s[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(x, e), k, -hi));
   }
-  return (s[0] + s[1]) + (s[2] + s[3]);
+  const float sum = (s[0] + s[1]) + (s[2] + s[3]);
+  const bool corr = split && !(fabsf(mL) < kScaledLimit);
+  return corr ? sum * __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -mL)) : sum;
 }
 
 // This thread's (m, d) over its chunk elements: its own maximum, then the sum of
@@ -198,7 +279,7 @@ template <int D, int THREADS, int VPT>
 __device__ __forceinline__ Stats thread_stats(u32x4 (&v)[VPT], const Chunk<D>& c) {
   const float m = thread_max<D, THREADS, VPT>(v, c);
   reg_barrier(v);
-  const float d = (m == kNegInf) ? 0.f : thread_sum_exp<D, THREADS, VPT>(v, c, scaled_max(m));
+  const float d = (m == kNegInf) ? 0.f : thread_sum_exp<D, THREADS, VPT>(v, c, m);
   reg_barrier(v);
   return {m, d};
 }
@@ -379,12 +460,11 @@ __device__ __forceinline__ void online_add_vec(Stats& st, u32x4 x) {
 #pragma unroll
   for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, elem<D>(x, e));
   const float mn = fmaxf(st.m, vm);
-  const float mnL = scaled_max(mn);
   float s = 0.f;
 #pragma unroll
   for (int e = 0; e < EPV; ++e) {
     const float xe = elem<D>(x, e);
-    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(xe, kLog2e, -mnL));
+    const float t = __builtin_amdgcn_exp2f((xe - mn) * kLog2e);
     s += xe == kNegInf ? 0.f : t;
   }
   st.d = (st.m == mn ? st.d : st.d * __builtin_amdgcn_exp2f((st.m - mn) * kLog2e)) + s;
@@ -401,15 +481,17 @@ __device__ __forceinline__ void store_vec(const Chunk<D>& c, int v, const u32x4&
   else buf_store(c.rsrc, off, bits);
 }
 
-// exp2(x*log2e - coff) for every element of one slot, in the element type, XOR-ed with
+// exp_of<SCALED>(x, f) for every element of one slot, in the element type, XOR-ed with
 // `sign` (0, or Elt<D>::kSignWord to negate every result: a negative upstream gradient).
-template <int D>
-__device__ __forceinline__ u32x4 exp_slot(u32x4 v, float coff, uint32_t sign = 0) {
-  pin_slot<D>(v);
+// The relative form pins the slot for fp32 too: its subtraction x - m is cheap enough that
+// the compiler would otherwise form it for every slot of the row at once and spill.
+template <int D, bool SCALED>
+__device__ __forceinline__ u32x4 exp_slot(u32x4 v, const ExpForm& f, uint32_t sign = 0) {
+  if (SCALED) pin_slot<D>(v);
+  else pin(v);
   OutVec<D> o;
 #pragma unroll
-  for (int e = 0; e < Elt<D>::kPerVec; ++e)
-    o.v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(v, e), kLog2e, -coff));
+  for (int e = 0; e < Elt<D>::kPerVec; ++e) o.v[e] = exp_of<SCALED>(elem<D>(v, e), f);
   return o.bits() ^ splat(sign);
 }
 

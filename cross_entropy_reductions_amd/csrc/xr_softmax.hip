@@ -1,8 +1,8 @@
 // xr_softmax.hip -- softmax forward and backward kernels for gfx950 (the row-kernel design
 // is described at the top of xr_xent.hip), and the negative log-softmax forward with a
 // gathered loss (page "python sum function examples", Triton kernel _forward): the same
-// row pass, writing log d - (x - m) = -log p instead of p, and loss[i] = the written
-// element at idx[i].
+// row pass, writing -log p = m + log d - x instead of p, and loss[i] = the written element
+// at idx[i].
 #include "xr_rows.h"
 
 namespace xr {
@@ -15,14 +15,14 @@ const Shape kFwdShapes[kNumFwdShapes] = {{64, 4},   {64, 8},   {64, 16},  {128, 
 const Shape kBwdShapes[kNumBwdShapes] = {{64, 4},  {64, 8},   {128, 8},
                                          {256, 8}, {512, 8}, {1024, 8}};
 
-// (m + log d) - x for every element of one slot, in the element type: -log p.
-template <int D>
-__device__ __forceinline__ u32x4 nll_slot(u32x4 v, float c) {
+// -log p = nll_of<SCALED>(x, f) for every element of one slot, in the element type.
+template <int D, bool SCALED>
+__device__ __forceinline__ u32x4 nll_slot(u32x4 v, const ExpForm& f) {
   pin(v);  // fp32 too: the subtraction is cheap enough that, unpinned, the compiler computes
            // every slot's result at once and spills
   OutVec<D> o;
 #pragma unroll
-  for (int e = 0; e < Elt<D>::kPerVec; ++e) o.v[e] = c - elem<D>(v, e);
+  for (int e = 0; e < Elt<D>::kPerVec; ++e) o.v[e] = nll_of<SCALED>(elem<D>(v, e), f);
   return o.bits();
 }
 
@@ -71,27 +71,24 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
     const Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, cx), red[buf]);
     buf ^= 1;
-    // softmax: exp2(x*log2e - coff), coff = m*log2e + log2 d.  NLL: c - x, c = m + log d.
-    const float coff = NLL ? st.m + logf(st.d) : exp_offset(scaled_max(st.m), log2f(st.d));
-    auto out_slot = [coff](u32x4 x) { return NLL ? nll_slot<D>(x, coff) : exp_slot<D>(x, coff); };
-    if (rn < p.M) {
+    // softmax: exp2((x - m) log2e - log2 d).  NLL: m + log d - x.
+    const ExpForm f = NLL ? nll_form(st.m, logf(st.d)) : exp_form(st.m, log2f(st.d));
+    with_form(f, [&](auto form) {
+      constexpr bool SC = decltype(form)::value;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k)
+        store_slot<D, THREADS>(cy, k, NLL ? nll_slot<D, SC>(v[k], f) : exp_slot<D, SC>(v[k], f));
+      store_partials<D, THREADS>(cy, cx, [&f](float x) {
+        return NLL ? nll_of<SC>(x, f) : exp_of<SC>(x, f);
+      });
+      if (NLL && owner) p.loss[r] = round_elem<D>(nll_of<SC>(xi, f));
+    });
+    if (NLL && vi < 0 && threadIdx.x == 0) p.loss[r] = __builtin_nanf("");
+    if (rn < p.M) {  // the next row's loads, once this row is written out
       const Chunk<D> cn(p.x + rn * p.ldx_bytes, p.N, 0, cv);
       const uint32_t off = threadIdx.x * 16u;
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        store_slot<D, THREADS>(cy, k, out_slot(v[k]));
-        v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(cy, k, out_slot(v[k]));
-    }
-    store_partials<D, THREADS>(cy, cx, [coff](float x) {
-      return NLL ? coff - x : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
-    });
-    if (NLL) {
-      if (owner) p.loss[r] = round_elem<D>(coff - xi);
-      else if (vi < 0 && threadIdx.x == 0) p.loss[r] = __builtin_nanf("");
+      for (int k = 0; k < VPT; ++k) v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
     }
     r = rn;
   }
@@ -130,18 +127,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   st = exchange_row_stats<THREADS>(st, p.partials + r * S, S, chunk, p.flags, bcast);
   if (p.group_rows > 1)
     wait_row_group<kWriteGroupRows>(p.partials, nullptr, 0, 0, r, p.M, S, p.flags);
-  // softmax: exp2(x*log2e - c), c = m*log2e + log2 d.  NLL: c - x, c = m + log d.
-  const float c = NLL ? st.m + logf(st.d) : exp_offset(scaled_max(st.m), log2f(st.d));
+  // softmax: exp2((x - m) log2e - log2 d).  NLL: m + log d - x.
+  const ExpForm f = NLL ? nll_form(st.m, logf(st.d)) : exp_form(st.m, log2f(st.d));
+  with_form(f, [&](auto form) {
+    constexpr bool SC = decltype(form)::value;
 #pragma unroll
-  for (int k = 0; k < VPT; ++k)
-    store_slot<D, THREADS>(cy, k, NLL ? nll_slot<D>(v[k], c) : exp_slot<D>(v[k], c));
-  store_partials<D, THREADS>(cy, cx, [c](float x) {
-    return NLL ? c - x : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -c));
+    for (int k = 0; k < VPT; ++k)
+      store_slot<D, THREADS>(cy, k, NLL ? nll_slot<D, SC>(v[k], f) : exp_slot<D, SC>(v[k], f));
+    store_partials<D, THREADS>(cy, cx, [&f](float x) {
+      return NLL ? nll_of<SC>(x, f) : exp_of<SC>(x, f);
+    });
+    if (NLL && owner) p.loss[r] = round_elem<D>(nll_of<SC>(xi, f));
   });
-  if (NLL) {
-    if (owner) p.loss[r] = round_elem<D>(c - xi);
-    else if (!in_row && chunk == 0 && tid == 0) p.loss[r] = __builtin_nanf("");
-  }
+  if (NLL && !in_row && chunk == 0 && tid == 0) p.loss[r] = __builtin_nanf("");
 }
 
 // Two-pass stream form (rows too long for the row-resident shapes, rows split over no
@@ -186,37 +184,41 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream_kernel(Soft
   st = block_reduce_stats<T>(st, red);
   // In place (y == x) is safe: each vector is re-read and written by the same thread, and
   // all reads of the statistics pass finished before the barrier above.
-  const float coff = NLL ? st.m + logf(st.d) : exp_offset(scaled_max(st.m), log2f(st.d));
-  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
-    const Chunk<D> cx(row, p.N, lo, kStreamWindow);
-    const Chunk<D> cy(out, p.N, lo, kStreamWindow);  // the output's geometry when `same`
-    for (int v0 = tid; v0 < cx.nvec; v0 += U * T) {
-      u32x4 a[U];
+  const ExpForm f = NLL ? nll_form(st.m, logf(st.d)) : exp_form(st.m, log2f(st.d));
+  with_form(f, [&](auto form) {
+    constexpr bool SC = decltype(form)::value;
+    for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+      const Chunk<D> cx(row, p.N, lo, kStreamWindow);
+      const Chunk<D> cy(out, p.N, lo, kStreamWindow);  // the output's geometry when `same`
+      for (int v0 = tid; v0 < cx.nvec; v0 += U * T) {
+        u32x4 a[U];
 #pragma unroll
-      for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyNT>(cx.rsrc, (uint32_t)(v0 + q * T) * 16u);
+        for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyNT>(cx.rsrc, (uint32_t)(v0 + q * T) * 16u);
 #pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int v = v0 + q * T;
-        if (v >= cx.nvec) break;
-        const u32x4 o = NLL ? nll_slot<D>(a[q], coff) : exp_slot<D>(a[q], coff);
-        if (same) {
-          store_vec<D>(cy, v, o);
-        } else {
-          // element stores at the output's own addresses
-          const int e0 = v == cx.head ? cx.h0 : 0;
-          const int e1 = v == cx.head ? cx.h1 : (v == cx.tail ? cx.t1 : EPV);
-          const int64_t j0 = (lo + v) * EPV - lead;  // row index of the vector's element 0
+        for (int q = 0; q < U; ++q) {
+          const int v = v0 + q * T;
+          if (v >= cx.nvec) break;
+          const u32x4 o = NLL ? nll_slot<D, SC>(a[q], f) : exp_slot<D, SC>(a[q], f);
+          if (same) {
+            store_vec<D>(cy, v, o);
+          } else {
+            // element stores at the output's own addresses
+            const int e0 = v == cx.head ? cx.h0 : 0;
+            const int e1 = v == cx.head ? cx.h1 : (v == cx.tail ? cx.t1 : EPV);
+            const int64_t j0 = (lo + v) * EPV - lead;  // row index of the vector's element 0
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            if (e < e0 || e >= e1) continue;
-            if (D == kF32) reinterpret_cast<uint32_t*>(out)[j0 + e] = o[e];
-            else reinterpret_cast<uint16_t*>(out)[j0 + e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < EPV; ++e) {
+              if (e < e0 || e >= e1) continue;
+              if (D == kF32) reinterpret_cast<uint32_t*>(out)[j0 + e] = o[e];
+              else reinterpret_cast<uint16_t*>(out)[j0 + e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
     }
-  }
-  if (NLL && tid == 0) p.loss[r] = in_row ? round_elem<D>(coff - xi) : __builtin_nanf("");
+    if (NLL && tid == 0 && in_row) p.loss[r] = round_elem<D>(nll_of<SC>(xi, f));
+  });
+  if (NLL && tid == 0 && !in_row) p.loss[r] = __builtin_nanf("");
 }
 
 // ============================================================================ softmax backward

@@ -21,12 +21,12 @@
 //   * Row-resident kernels keep a whole row (or, for split rows, one chunk of it) in
 //     registers as raw 16-byte vectors, so the logits are read from HBM exactly once:
 //     max pass, then sum pass with that max (one exp per element, no online rescale),
-//     then the output pass. The output is exp2(x*log2e - c) with c = m*log2e + log2(d*n),
-//     which folds the division by d and by n into the exponent.
+//     then the output pass. The output is exp2((x - m)*log2e - log2(d*n)), which folds the
+//     division by d and by n into the exponent (x - m keeps rows of any magnitude exact).
 //   * One workgroup per row, or per row chunk, by default: the dispatcher starts a new
 //     workgroup as soon as one retires. A persistent form (workgroup g handles rows g,
-//     g + G, ... and, while it writes row r, issues the loads of row r + G into the
-//     registers it has just written out) is kept for grids set explicitly.
+//     g + G, ... and, once it has issued row r's stores, issues the loads of row r + G
+//     into the same registers) is kept for grids set explicitly.
 //   * Long rows, and batches too short to fill the GPU, are split over S workgroups. Each
 //     publishes its chunk's (m_c, d_c) pair as one 64-bit word; the chunks of a row
 //     combine them with the online-softmax rule
@@ -179,13 +179,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     float xt = 0.f;
     if (owner) xt = buf_load_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes));
 
-    float m = 0.f, d = 1.f, coff;
+    float m = 0.f, d = 1.f, off;  // outputs exp2((x - m) log2e - off)
     if (ignored) {
       // Ignored (or out-of-range) target: the row was not loaded; with every input at
-      // -inf and c = +inf the output pass below writes exact zeros.
+      // -inf, m = 0 and off = +inf the output pass below writes exact zeros.
 #pragma unroll
       for (int k = 0; k < VPT; ++k) v[k] = splat(Elt<D>::kNegInfWord);
-      coff = __builtin_inff();
+      off = __builtin_inff();
     } else {
       // (m, d) of the chunk; an all -inf chunk gives (-inf, 0).
       const Stats st = block_reduce_stats<THREADS>(thread_stats<D, THREADS, VPT>(v, c), red[buf]);
@@ -203,38 +203,39 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
           wait_row_group<kWriteGroupRows>(p.partials, p.target, p.ignore_index, p.V, r, p.M, S,
                                          p.ws_flags);
       }
-      // g_j = exp2(x_j*log2e - c) with c = m*log2e + log2(d) + log2(n) - log2|s| is
+      // g_j = exp2((x_j - m) log2e - off) with off = log2(d) + log2(n) - log2|s| is
       // |s| p_j / n (n = 1 unless the reduction is the mean); the sign of s is applied to
       // the result bits.
-      coff = exp_offset(scaled_max(m), log2f(d) + log2n - log2f(fabsf(sc)));
+      off = log2f(d) + log2n - log2f(fabsf(sc));
       neg = __builtin_signbit(sc) != 0;
     }
 
-    // Output pass, with the next row's loads issued into each slot once it is written out.
+    // Output pass; then the next row's loads.
     const uint32_t sign = neg ? Elt<D>::kSignWord : 0u;
+    const ExpForm f = exp_form(m, off);
+    with_form(f, [&](auto form) {
+      constexpr bool SC = decltype(form)::value;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(c, k, exp_slot<D, SC>(v[k], f, sign));
+      store_partials<D, THREADS>(c, c, [&f, ignored, neg](float x) {
+        const float g = exp_of<SC>(x, f);
+        return ignored ? 0.f : (neg ? -g : g);
+      });
+    });
     if (pf) {
       const Chunk<D> cn(row_ptr(rn), p.V, lo, p.chunk_vecs);
-      const uint32_t off = tid * 16u;
+      const uint32_t voff = tid * 16u;
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff, sign));
-        v[k] = buf_load<LP>(cn.slot(k * THREADS), off);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) store_slot<D, THREADS>(c, k, exp_slot<D>(v[k], coff, sign));
+      for (int k = 0; k < VPT; ++k) v[k] = buf_load<LP>(cn.slot(k * THREADS), voff);
     }
-    store_partials<D, THREADS>(c, c, [coff, ignored, neg](float x) {
-      const float g = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -coff));
-      return ignored ? 0.f : (neg ? -g : g);
-    });
     if (owner) {
       // Target column: s (p_t - 1)/n, stored after this thread's vector store. p_t's
-      // numerator is formed as the sum pass forms the terms of d, so that p_t near 1 keeps
-      // its accuracy (p_t - 1 cancels).
-      const float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -scaled_max(m))) / d;
+      // numerator is formed as the sum pass forms the terms of d (in the row's form), so
+      // that p_t near 1 keeps its accuracy (p_t - 1 cancels).
+      const float et = f.scaled ? __builtin_fmaf(xt, kLog2e, -scaled_max(m)) : (xt - m) * kLog2e;
+      const float pt = __builtin_amdgcn_exp2f(et) / d;
       store_elem<D>(c.rsrc, (uint32_t)(vt * Elt<D>::kBytes), (pt - 1.0f) * inv_n * sc);
-      p.row_loss[r] = m + logf(d) - xt;
+      p.row_loss[r] = (m - xt) + logf(d);  // m - xt exact near the maximum, at any magnitude
     }
     if (ignored && chunk == 0 && tid == 0) p.row_loss[r] = 0.f;
     r = rn;
@@ -289,38 +290,41 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream_kernel(XentParams 
   }
   st = block_reduce_stats<T>(st, red);
   const float m = st.m, d = st.d;
-  // gradient exp2(x*log2e - coff) = s p_j / n for j != target; s (p_t - 1) / n at the target
-  const float mL = scaled_max(m);
-  const float coff = exp_offset(mL, log2f(d) + log2f((float)n) - log2f(fabsf(sc)));
-  const float gt = (__builtin_amdgcn_exp2f(__builtin_fmaf(xt, kLog2e, -mL)) / d - 1.0f) * inv_n * sc;
+  // gradient exp2((x - m) log2e - off) = s p_j / n for j != target; s (p_t - 1) / n at the
+  // target (p_t's numerator formed as the online sums form their terms)
+  const ExpForm f = exp_form(m, log2f(d) + log2f((float)n) - log2f(fabsf(sc)));
+  const float gt = (__builtin_amdgcn_exp2f((xt - m) * kLog2e) / d - 1.0f) * inv_n * sc;
   const int64_t tv = (lead + t) / EPV;  // the target's row vector and element in it
   const int te = (int)((lead + t) % EPV);
-  for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
-    const Chunk<D> c(row, p.V, lo, kStreamWindow);
-    for (int v0 = tid; v0 < c.nvec; v0 += U * T) {
-      u32x4 a[U];
+  with_form(f, [&](auto form) {
+    constexpr bool SC = decltype(form)::value;
+    for (int64_t lo = 0; lo < nv; lo += kStreamWindow) {
+      const Chunk<D> c(row, p.V, lo, kStreamWindow);
+      for (int v0 = tid; v0 < c.nvec; v0 += U * T) {
+        u32x4 a[U];
 #pragma unroll
-      for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyNT>(c.rsrc, (uint32_t)(v0 + q * T) * 16u);
+        for (int q = 0; q < U; ++q) a[q] = buf_load<kPolicyNT>(c.rsrc, (uint32_t)(v0 + q * T) * 16u);
 #pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int v = v0 + q * T;
-        if (v >= c.nvec) break;
-        OutVec<D> o;
+        for (int q = 0; q < U; ++q) {
+          const int v = v0 + q * T;
+          if (v >= c.nvec) break;
+          OutVec<D> o;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float g = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<D>(a[q], e), kLog2e, -coff));
-          o.v[e] = neg ? -g : g;
+          for (int e = 0; e < EPV; ++e) {
+            const float g = exp_of<SC>(elem<D>(a[q], e), f);
+            o.v[e] = neg ? -g : g;
+          }
+          if (lo + v == tv) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e)
+              if (e == te) o.v[e] = gt;
+          }
+          store_vec<D>(c, v, o.bits());
         }
-        if (lo + v == tv) {
-#pragma unroll
-          for (int e = 0; e < EPV; ++e)
-            if (e == te) o.v[e] = gt;
-        }
-        store_vec<D>(c, v, o.bits());
       }
     }
-  }
-  if (tid == 0) p.row_loss[r] = m + logf(d) - xt;
+  });
+  if (tid == 0) p.row_loss[r] = (m - xt) + logf(d);
 }
 
 // ============================================================================ element_mul

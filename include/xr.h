@@ -11,6 +11,10 @@
  *   - dtype selects the floating type of every floating tensor argument of the call except
  *     row_loss / mean_loss, which are always fp32. bf16 values are rounded to nearest-even
  *     when stored. All arithmetic is fp32 whatever the storage type.
+ *   - The softmax-family results depend on the differences x - max of a row, not on its
+ *     magnitude: rows of large finite values (a row filled with a large negative mask value
+ *     gives the uniform softmax, -log p = log N and the loss log N) keep the accuracy of
+ *     ordinary rows, up to what fp32 holds of the differences themselves.
  *   - stream is a hipStream_t (NULL = the legacy default stream). Every entry point only
  *     enqueues work on it: nothing is synchronised, nothing is allocated or freed, and no
  *     device memory is read or written by the host.

@@ -546,6 +546,56 @@ def test_nonfinite_inputs(orc, dtype):
     xr.reset_options()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_magnitude_rows(orc, dtype):
+    """Rows of large magnitude keep the results of the definitions, on every launch path: a
+    row filled with a large negative mask value (-1e10) gives the uniform softmax, -log p =
+    log N and the loss log N; rows of values up to +-1e30, a maximum of 3e38 over -3e38, a
+    common offset of 1e9 and one of 5000 keep the maximum's term at exactly 1 (such rows form
+    their exponents from x - m; only rows whose m log2 e stays under 2^7 fold m into the
+    exponent's constant). Softmax, negative log-softmax and cross-entropy against the
+    oracle."""
+    M, N = 6, 3001
+    rng = np.random.default_rng(12400)
+    xf = rng.standard_normal((M, N)).astype(np.float32)          # row 4: an ordinary row
+    xf[0] = -1e10                                                 # a fully masked row
+    xf[1] = ((rng.random(N) * 2 - 1) * 1e30).astype(np.float32)
+    xf[2] = -3e38
+    xf[2, 7] = 3e38
+    xf[3] = (1e9 + rng.standard_normal(N) * 300).astype(np.float32)
+    xf[5] = (5000 + rng.standard_normal(N) * 4).astype(np.float32)  # a moderate offset
+    x = synth.bf16_bits_from_f32(xf) if dtype == "bf16" else xf
+    t = np.array([5, int(np.argmax(widen(x)[1])), 7, 11, 13, 17], dtype=np.int64)
+    idx = np.array([5, 100, 7, 11, 13, 17], dtype=np.int64)
+    for name, path, split in (("auto", 0, 0), ("resident", 1, 0), ("split2", 2, 2),
+                              ("stream", 3, 0)):
+        xr.set_option("path", path)
+        xr.set_option("split", split)
+        what = f"{dtype} {name}"
+        y = to_host(xr.softmax_fwd(to_device(x)))
+        want = orc.softmax_fwd(x)
+        check_probs(y, want, f"{what}: softmax")
+        assert np.allclose(widen(y)[0], 1.0 / N, rtol=2.0 ** -7, atol=0), f"{what}: uniform row"
+        out, loss = xr.nll_fwd(to_device(x), to_device(idx))
+        out_h, loss_h = widen(to_host(out)), to_host(loss).astype(np.float64)
+        out_w, loss_w = orc.nll_fwd(x, idx)
+        rel = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -20
+        # -log p beyond the fp32 range (6e38 in the 3e38 row) is stored as +inf
+        big = np.abs(out_w) > float(np.finfo(np.float32).max)
+        assert np.all(np.isposinf(out_h[big])), f"{what}: -log p past the fp32 range"
+        scale = np.max(np.where(big, 0.0, np.abs(out_w)), axis=1, keepdims=True)
+        assert np.all((np.abs(out_h - out_w) <= rel * np.abs(out_w) + 2.0 ** -20 * scale) | big), \
+            f"{what}: -log softmax"
+        assert np.all(np.abs(loss_h - loss_w) <= rel * np.abs(loss_w) + 2.0 ** -20 * scale[:, 0]), \
+            f"{what}: gathered loss"
+        one = 2.0 ** -8 if dtype == "bf16" else 1e-5  # the stored -log p: one rounding
+        assert abs(out_h[0, 0] - math.log(N)) <= one * math.log(N), f"{what}: -log p of the masked row"
+        g, rows, mean, counts = run_xent(x, t, N)
+        compare_xent(orc, x, t, N, g, rows, mean, counts, f"{what}: cross-entropy")
+        assert abs(rows[0] - math.log(N)) <= 1e-4 * math.log(N), f"{what}: loss of the masked row"
+    xr.reset_options()
+
+
 def test_partial_overlap_is_rejected():
     x = torch.zeros((4, 100), dtype=torch.float32, device="cuda")
     with pytest.raises(xr.XrError, match="overlap"):
