@@ -1,6 +1,7 @@
 """Seeded random cases for every entry point against the float64 oracle: random sizes
 (ragged, one element to several chunks), row pitches, dtypes, ignore fractions, reductions,
-upstream gradients and forced launch paths. Each case prints its parameters before it runs,
+upstream gradients, forced launch paths and, for the softmax family, rows moved by large
+offsets. Each case prints its parameters before it runs,
 so a failure names its case."""
 from __future__ import annotations
 
@@ -47,6 +48,22 @@ def draw(rng, seed):
     return M, N, dtype, ld, path
 
 
+def shift_rows(seed, x, N, dtype):
+    """A third of the cases move each row by a common offset of large magnitude (+-100,
+    +-1e4 or +-1e6, one per row; padding untouched): the results depend only on x - max, and
+    such rows take the kernels' other exponent forms. Drawn from a generator of its own, so
+    the other draws of a case stay as they are. Returns the rows and the offsets (or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if rng.random() >= 1.0 / 3.0:
+        return x, None
+    off = rng.choice([-1e6, -1e4, -100.0, 100.0, 1e4, 1e6], size=x.shape[0])
+    vals = synth.f32_from_bf16_bits(x[:, :N]) if dtype == "bf16" else x[:, :N]
+    vals = (vals.astype(np.float64) + off[:, None]).astype(np.float32)
+    x = x.copy()
+    x[:, :N] = synth.bf16_bits_from_f32(vals) if dtype == "bf16" else vals
+    return x, off
+
+
 def force(path, N, dtype):
     xr.reset_options()
     if path:
@@ -62,8 +79,10 @@ def test_random_xent(orc, case):
     reduction = str(rng.choice(["mean", "sum", "none"]))
     ign = float(rng.choice([0.0, 0.3, 1.0]))
     scale = [None, 1.5, -0.5][int(rng.integers(3))]
-    print(f"xent case {case}: M={M} V={V} ld={ld} {dtype} path={path} {reduction} ignore={ign} scale={scale}", flush=True)
     x = synth.random_rows(16100 + case, M, V, ld=ld, dtype=dtype, scale=3.0, pad_nan=ld > V)
+    x, off = shift_rows(16300 + case, x, V, dtype)
+    print(f"xent case {case}: M={M} V={V} ld={ld} {dtype} path={path} {reduction} ignore={ign} "
+          f"scale={scale} offsets={None if off is None else sorted(set(off.tolist()))}", flush=True)
     t = synth.random_targets(16200 + case, M, V, ignore_frac=ign)
     force(path, V, dtype)
     xd = to_device(x)
@@ -95,9 +114,10 @@ def test_random_softmax(orc, case):
     M, N, dtype, ld, path = draw(rng, case)
     # rows split over workgroups need a workspace; without one they stay whole
     use_ws = path == 2 or bool(rng.integers(2))
-    print(f"softmax case {case}: M={M} N={N} ld={ld} {dtype} path={path} workspace={use_ws}",
-          flush=True)
     x = synth.random_rows(17100 + case, M, N, ld=ld, dtype=dtype, scale=3.0, pad_nan=ld > N)
+    x, off = shift_rows(17300 + case, x, N, dtype)
+    print(f"softmax case {case}: M={M} N={N} ld={ld} {dtype} path={path} workspace={use_ws} "
+          f"offsets={None if off is None else sorted(set(off.tolist()))}", flush=True)
     dy = synth.random_rows(17200 + case, M, N, ld=ld, dtype=dtype, scale=1.0, pad_nan=ld > N)
     force(path, N, dtype)
     xd, dyd = to_device(x), to_device(dy)
@@ -152,8 +172,10 @@ def test_random_softmax_bwd_resident(orc, case):
 def test_random_nll(orc, case):
     rng = np.random.Generator(np.random.PCG64(18000 + case))
     M, N, dtype, ld, path = draw(rng, case)
-    print(f"nll case {case}: M={M} N={N} ld={ld} {dtype} path={path}", flush=True)
     x = synth.random_rows(18100 + case, M, N, ld=ld, dtype=dtype, scale=3.0, pad_nan=ld > N)
+    x, off = shift_rows(18300 + case, x, N, dtype)
+    print(f"nll case {case}: M={M} N={N} ld={ld} {dtype} path={path} "
+          f"offsets={None if off is None else sorted(set(off.tolist()))}", flush=True)
     idx = synth.random_targets(18200 + case, M, N)
     if M > 1:
         idx[0] = N  # outside the row
