@@ -82,6 +82,37 @@ def pin_softmax_shift_invariance(o):
             assert np.max(np.abs(y1 - y0) / y0) <= 1e-12, f"softmax not invariant to shift {c}"
 
 
+def pin_large_magnitude_rows(o):
+    """The definitions depend only on x - max. fp32 rows moved by +-2^20 (exact for inputs on
+    a 1/8 grid under 16 in magnitude) give the same softmax, -log p, row losses and gradient;
+    rows of one value at +-1e30 give 1/N, -log p = log N and the loss log N (a loss formed as
+    (m + log d) - x_t would lose log N to cancellation in float64 there)."""
+    V = 40
+    base = _grid_rows(14, 5, V, 1.0 / 8, -8.0, 8.0)
+    t = np.array([0, 3, 39, 17, 20], dtype=np.int64)
+    y0 = o.softmax_fwd(base)
+    out0, nl0 = o.nll_fwd(base, t)
+    g0, l0, _, _ = o.xent(base, t, V)
+    for c in (2.0 ** 20, -(2.0 ** 20)):
+        sh = (base + np.float32(c)).astype(np.float32)
+        assert np.array_equal(sh - np.float32(c), base), "shift must be exact"
+        assert np.max(np.abs(o.softmax_fwd(sh) - y0) / y0) <= 1e-12, f"softmax, shift {c}"
+        out1, nl1 = o.nll_fwd(sh, t)
+        assert np.max(np.abs(out1 - out0)) <= 1e-12 * np.max(out0), f"-log p, shift {c}"
+        g1, l1, _, _ = o.xent(sh, t, V)
+        assert np.max(np.abs(l1 - l0)) <= 1e-12 * np.max(l0), f"row losses, shift {c}"
+        assert np.max(np.abs(g1 - g0)) <= 1e-15, f"gradient, shift {c}"
+    N = 5
+    for c in (1e30, -1e30):
+        x = np.full((2, N), c, dtype=np.float32)
+        idx = np.array([1, 4], dtype=np.int64)
+        assert np.max(np.abs(o.softmax_fwd(x) - 1.0 / N)) <= 1e-15, f"uniform row at {c}"
+        out, _ = o.nll_fwd(x, idx)
+        assert np.max(np.abs(out - math.log(N))) <= 1e-12, f"-log p of a uniform row at {c}"
+        _, loss, _, _ = o.xent(x, idx, N)
+        assert np.max(np.abs(loss - math.log(N))) <= 1e-12, f"loss of a uniform row at {c}"
+
+
 def pin_softmax_uniform_row(o):
     for N in (1, 3, 1000, 4096):
         y = o.softmax_fwd(np.full((2, N), 7.25, dtype=np.float32))

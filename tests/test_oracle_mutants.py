@@ -32,6 +32,8 @@ MUTANTS = {
         "s += load_elem(y, i * ld_y + j, dtype) * load_elem(dy, i * ld_y + j, dtype);"),
     "loss adds the target logit": ("loss[r] = (m - xt) + log(d);", "loss[r] = (m + xt) + log(d);"),
     "loss drops log d": ("loss[r] = (m - xt) + log(d);", "loss[r] = (m - xt);"),
+    "loss formed as (m + log d) - x_t": ("loss[r] = (m - xt) + log(d);",
+                                         "loss[r] = (m + log(d)) - xt;"),
     "target logit read from row 0": ("double xt = load_elem(logits, off + t, dtype);",
                                      "double xt = load_elem(logits, t, dtype);"),
     "gradient not divided by n": ("if (reduction == XRO_MEAN) w = w / (double)n;",
