@@ -93,8 +93,23 @@ def check_bf16(gpu: np.ndarray, want: np.ndarray, what: str, abs_allow=0.0) -> f
     return worst
 
 
-def check_output(gpu: np.ndarray, want: np.ndarray, what: str) -> float:
-    return check_bf16(gpu, want, what) if gpu.dtype == np.uint16 else check_fp32(gpu, want, what)
+def check_output(gpu: np.ndarray, want: np.ndarray, what: str, allow=None) -> float:
+    """allow: an absolute allowance per element for bf16 outputs (softmax_bwd_allow)."""
+    if gpu.dtype == np.uint16:
+        return check_bf16(gpu, want, what, abs_allow=0.0 if allow is None else allow)
+    return check_fp32(gpu, want, what)
+
+
+def softmax_bwd_allow(y: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """The absolute error fp32 arithmetic may leave in dx = y (dy - s), s = sum_j y_j dy_j:
+    the dot product s carries at most d 2^-24 sum_j |y_j dy_j|, d the additions it is deep
+    (at most 32 sequential per thread, then the reduction tree: d <= 32 + ceil(log2 N)), and
+    y dy one rounding. Where dy_i is close to s that error is the whole result, however small
+    the result is; elsewhere it is far below the relative bound."""
+    yw, dw = widen(y), widen(dy)
+    depth = 32 + int(np.ceil(np.log2(max(yw.shape[-1], 2))))
+    mass = np.sum(np.abs(yw * dw), axis=-1, keepdims=True)
+    return 2.0 ** -24 * np.abs(yw) * ((depth + 1) * mass + np.abs(dw))
 
 
 def _check_rel(g: np.ndarray, want: np.ndarray, rel: float, extra, what: str) -> float:

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_bf16, check_probs, check_xent_grad
+from gpu_util import check_bf16, check_output, check_probs, check_xent_grad, softmax_bwd_allow
 
 
 @pytest.fixture(scope="module")
@@ -152,3 +152,33 @@ def test_cancelling_checker_has_no_absolute_floor():
     check_bf16(stored(want, "bf16"), want, "rounded")
     with pytest.raises(AssertionError):
         check_bf16(stored(np.array([[1e-6, -3e-7, 0.0, 0.0]]), "bf16"), want, "entry dropped")
+
+
+def test_softmax_bwd_allowance(orc):
+    """The softmax backward's arithmetic allowance (softmax_bwd_allow): the oracle's result
+    rounded once to bf16 passes; a result 4 % off, one that drops a column's term of s, and
+    one whose s carries the wrong sign still fail. On a row where dy_i is close to s (y_i
+    about 1) the allowance covers the fp32 rounding of s, which is all such an entry holds."""
+    M, N = 64, 1000
+    x = synth.random_rows(31, M, N, dtype="f32", scale=3.0)
+    y = synth.bf16_bits_from_f32(orc.softmax_fwd(x).astype(np.float32))
+    dy = synth.random_rows(32, M, N, dtype="bf16", scale=1.0)
+    want = orc.softmax_bwd(y, dy)
+    allow = softmax_bwd_allow(y, dy)
+    check_output(synth.bf16_bits_from_f32(want.astype(np.float32)), want, "rounded once", allow)
+    yw, dw = synth.f32_from_bf16_bits(y).astype(np.float64), synth.f32_from_bf16_bits(dy).astype(np.float64)
+    s = np.sum(yw * dw, axis=1, keepdims=True)
+    s_drop = s - (yw * dw)[:, :1]
+    for name, bad in (("4 % off", want * 1.04), ("a term of s dropped", yw * (dw - s_drop)),
+                      ("s with the wrong sign", yw * (dw + s))):
+        with pytest.raises(AssertionError):
+            check_output(synth.bf16_bits_from_f32(bad.astype(np.float32)), want, name, allow)
+    # one dominant column whose dy equals s up to fp32 rounding: dx there is cancellation
+    y1 = np.full((1, 7), 1e-6, dtype=np.float32)
+    y1[0, 3] = 1.0
+    dy1 = np.array([[-0.115, -0.715, -0.081, 1.3984375, 1.22, -0.416, 0.9375]], dtype=np.float32)
+    w1 = orc.softmax_bwd(y1, dy1)
+    s1 = np.float32(np.sum((y1 * dy1).astype(np.float32), dtype=np.float32))
+    got = (y1 * (dy1 - s1)).astype(np.float32)  # the fp32 formula, as a kernel computes it
+    check_output(synth.bf16_bits_from_f32(got), w1, "cancellation row",
+                 softmax_bwd_allow(y1, dy1))
