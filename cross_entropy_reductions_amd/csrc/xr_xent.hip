@@ -22,7 +22,8 @@
 //     registers as raw 16-byte vectors, so the logits are read from HBM exactly once:
 //     max pass, then sum pass with that max (one exp per element, no online rescale),
 //     then the output pass. The output is exp2((x - m)*log2e - log2(d*n)), which folds the
-//     division by d and by n into the exponent (x - m keeps rows of any magnitude exact).
+//     division by d and by n into the exponent; ordinary rows fold m into its constant too,
+//     rows of large magnitude form x - m first (xr_rows.h).
 //   * One workgroup per row, or per row chunk, by default: the dispatcher starts a new
 //     workgroup as soon as one retires. A persistent form (workgroup g handles rows g,
 //     g + G, ... and, once it has issued row r's stores, issues the loads of row r + G
